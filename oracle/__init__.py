@@ -1,0 +1,177 @@
+"""fp64 CPU oracle for the hybrid attention path (thin ctypes wrapper).
+
+TEST INFRASTRUCTURE ONLY: the tests, the smoke check and the benchmark's
+CPU-baseline leg may import this package; the product path (the HIP library and
+its binding) never does. The arithmetic lives in ``attn_oracle.c`` (plain fp64
+loops); this module only converts arrays to contiguous fp64 and calls it.
+
+Sources: "Gemma 4: End-to-End Architecture Walkthrough" (Phase 3, sections
+3a-3c), "Gemma 4 Architecture Reference" ("Attention Architecture",
+"Positional Encoding: Proportional RoPE (p-RoPE)"), "Gemma 4 Technical Report"
+reader ("Core Model Architecture").
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "attn_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+ROPE_Q = 1
+ROPE_K = 2
+
+
+def build() -> str:
+    """Compile the C oracle with gcc (OpenMP, fp64, no HIP)."""
+    tmp = _LIB + ".tmp"
+    cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-Wall", "-Wextra",
+           "-o", tmp, _SRC, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        build()
+    lib = ctypes.CDLL(_LIB)
+    dp = ctypes.POINTER(ctypes.c_double)
+    i64p = ctypes.POINTER(ctypes.c_int64)
+    i32p = ctypes.POINTER(ctypes.c_int32)
+    lib.oracle_rope.argtypes = [dp, dp, i64p, ctypes.c_int64, ctypes.c_int,
+                                ctypes.c_int, ctypes.c_int, ctypes.c_double]
+    lib.oracle_rope.restype = None
+    lib.oracle_prefill.argtypes = [dp, dp, dp, dp] + [ctypes.c_int] * 7 + [
+        ctypes.c_double, ctypes.c_int, ctypes.c_double, ctypes.c_int,
+        ctypes.c_int64, i32p, ctypes.c_int, ctypes.c_int]
+    lib.oracle_prefill.restype = ctypes.c_int
+    lib.oracle_decode_one.argtypes = [dp, dp, dp, ctypes.c_int64,
+                                      ctypes.c_int64, dp] + [ctypes.c_int] * 5 + [
+        ctypes.c_double, ctypes.c_int, ctypes.c_double, ctypes.c_int]
+    lib.oracle_decode_one.restype = ctypes.c_int
+    lib.oracle_max_threads.argtypes = []
+    lib.oracle_max_threads.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def max_threads() -> int:
+    return int(_load().oracle_max_threads())
+
+
+def _f64(a) -> np.ndarray:
+    """Exact conversion of a torch tensor / array to contiguous fp64 numpy."""
+    if hasattr(a, "detach"):  # torch tensor (bf16 and fp32 widen exactly)
+        a = a.detach().to("cpu").double().numpy()
+    return np.ascontiguousarray(np.asarray(a, dtype=np.float64))
+
+
+def _ptr(a: np.ndarray, ctype=ctypes.c_double):
+    return a.ctypes.data_as(ctypes.POINTER(ctype))
+
+
+def rope(x, positions, rotary_dims: int, theta: float) -> np.ndarray:
+    """x [N, H, D] -> rotated copy (fp64). positions [N] integers."""
+    lib = _load()
+    x = _f64(x)
+    N, H, D = x.shape
+    pos = np.ascontiguousarray(np.asarray(positions, dtype=np.int64).reshape(N))
+    y = np.empty_like(x)
+    lib.oracle_rope(_ptr(x), _ptr(y), _ptr(pos, ctypes.c_int64), N, H, D,
+                    int(rotary_dims), float(theta))
+    return y
+
+
+def prefill(q, k, v, *, window: int, scale: float, rotary_dims: int = 0,
+            theta: float = 10000.0, rope_mask: int = ROPE_Q | ROPE_K,
+            pos0: int = 0, rows=None, nthreads: int | None = None) -> np.ndarray:
+    """Causal (optionally windowed) GQA attention, fp64.
+
+    q [B, n_rows, Hq, Dk] holds the query rows at positions ``rows`` (all T
+    rows when ``rows`` is None); k [B, T, Hkv, Dk], v [B, T, Hkv, Dv].
+    Returns o [B, n_rows, Hq, Dv].
+    """
+    lib = _load()
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, T, Hkv, Dk = k.shape
+    Dv = v.shape[3]
+    Hq = q.shape[2]
+    if rows is None:
+        rows_arr = None
+        n_rows = T
+        assert q.shape == (B, T, Hq, Dk)
+    else:
+        rows_arr = np.ascontiguousarray(np.asarray(rows, dtype=np.int32))
+        n_rows = rows_arr.size
+        assert q.shape == (B, n_rows, Hq, Dk)
+        assert rows_arr.min(initial=0) >= 0 and rows_arr.max(initial=0) < max(T, 1)
+    o = np.zeros((B, n_rows, Hq, Dv), dtype=np.float64)
+    nt = nthreads or max_threads()
+    rc = lib.oracle_prefill(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(o), B, T, Hq, Hkv, Dk, Dv, int(window),
+        float(scale), int(rotary_dims), float(theta), int(rope_mask), int(pos0),
+        _ptr(rows_arr, ctypes.c_int32) if rows_arr is not None else None,
+        int(n_rows), int(nt))
+    if rc != 0:
+        raise RuntimeError("oracle_prefill failed (bad arguments or out of memory)")
+    return o
+
+
+def decode_one(q, k_rows, v_rows, *, kv_len: int, row0: int = 0, window: int,
+               scale: float, rotary_dims: int = 0, theta: float = 10000.0,
+               nthreads: int | None = None) -> np.ndarray:
+    """One sequence of kv_len cache rows: q [Hq, Dk] (unrotated, position
+    kv_len-1); k_rows [kv_len-row0, Hkv, Dk] (already rotated) and v_rows
+    [kv_len-row0, Hkv, Dv] are cache rows row0..kv_len-1; rows before row0 must
+    be outside the window. Returns o [Hq, Dv]."""
+    lib = _load()
+    q, k_rows, v_rows = _f64(q), _f64(k_rows), _f64(v_rows)
+    Hq, Dk = q.shape
+    n, Hkv, _ = k_rows.shape
+    assert n == kv_len - row0 and v_rows.shape[0] == n
+    Dv = v_rows.shape[2]
+    o = np.zeros((Hq, Dv), dtype=np.float64)
+    nt = nthreads or max_threads()
+    rc = lib.oracle_decode_one(_ptr(q), _ptr(k_rows), _ptr(v_rows), int(row0),
+                               int(kv_len), _ptr(o), Hq, Hkv, Dk, Dv, int(window),
+                               float(scale), int(rotary_dims), float(theta), int(nt))
+    if rc != 0:
+        raise RuntimeError("oracle_decode_one failed (bad arguments, a visible "
+                           "row before row0, or out of memory)")
+    return o
+
+
+def decode(q, k_cache, v_cache, row_offset, kv_len, *, window: int, scale: float,
+           rotary_dims: int = 0, theta: float = 10000.0, seqs=None,
+           nthreads: int | None = None) -> np.ndarray:
+    """Ragged-cache decode: q [B, Hq, Dk]; caches [rows, Hkv, D]; sequence b
+    occupies cache rows row_offset[b] .. row_offset[b] + kv_len[b] - 1.
+    Only the rows inside the window are handed over (the oracle checks that the
+    rest are invisible), and only the sequences in ``seqs`` (default: all) are
+    computed. Returns [len(seqs), Hq, Dv].
+    """
+    row_offset = [int(x) for x in (row_offset.tolist() if hasattr(row_offset, "tolist") else row_offset)]
+    kv_len = [int(x) for x in (kv_len.tolist() if hasattr(kv_len, "tolist") else kv_len)]
+    if seqs is None:
+        seqs = range(len(kv_len))
+    outs = []
+    for b in seqs:
+        n = kv_len[b]
+        lo = max(0, n - window) if window > 0 else 0
+        off = row_offset[b]
+        outs.append(decode_one(q[b], k_cache[off + lo: off + n],
+                               v_cache[off + lo: off + n], kv_len=n, row0=lo,
+                               window=window, scale=scale, rotary_dims=rotary_dims,
+                               theta=theta, nthreads=nthreads))
+    Hq = q.shape[1]
+    Dv = v_cache.shape[2]
+    return np.stack(outs) if outs else np.zeros((0, Hq, Dv))

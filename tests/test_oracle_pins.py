@@ -1,0 +1,323 @@
+"""Pins of the fp64 oracle against what the pages and mathematics fix.
+
+Each test checks the oracle against something other than itself: values the
+pages state (fixtures under tests/golden/), closed forms, invariants the pages
+name (p-RoPE leaves 75 % of dims alone and preserves norms, rotated q.k depends
+only on the offset, a window >= T is full causal, GQA equals repeated KV heads,
+masks equal brute-force enumeration), textbook special cases and a library
+routine (torch CPU fp64 scaled_dot_product_attention).
+
+Pairing convention (adjacent dims vs. half split) and the frequency denominator
+are readings the pages do not fix: parity unpinned for those two choices; the
+tests below pin everything else about the rotation.
+"""
+import cmath
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+rng = np.random.default_rng(12345)
+
+
+def _gold(name):
+    with open(os.path.join(GOLD, name)) as f:
+        return json.load(f)
+
+
+# ----------------------------------------------------------------- RoPE ----
+
+@pytest.mark.parametrize("case", _gold("prope_dims.json")["cases"])
+def test_prope_untouched_dims_from_pages(case):
+    """p = 0.25: exactly the first quarter of dims move, the rest are
+    bit-identical at every position (p-RoPE section of the pages)."""
+    g = _gold("prope_dims.json")
+    D = case["head_dim"]
+    R = int(g["p"] * D)
+    assert R == case["rotated_dims"] and D - R == case["unrotated_dims"]
+    x = rng.standard_normal((6, 3, D))
+    pos = [0, 1, 7, 1000, 65536, 131072]
+    y = oracle.rope(x, pos, R, g["theta"])
+    assert np.array_equal(y[:, :, R:], x[:, :, R:])
+    # every rotated pair actually moves at a nonzero position (pair 0 turns by
+    # `pos` radians, so it moves whenever pos is not a multiple of 2*pi)
+    assert np.all(np.abs(y[1:, :, :2] - x[1:, :, :2]).sum(-1) > 0)
+
+
+def test_rope_identity_at_position_zero_and_p_zero():
+    x = rng.standard_normal((4, 2, 64))
+    assert np.array_equal(oracle.rope(x, [0] * 4, 64, 1e4), x)
+    assert np.array_equal(oracle.rope(x, [5, 9, 100, 7], 0, 1e4), x)
+
+
+def test_rope_preserves_pair_norms():
+    x = rng.standard_normal((5, 4, 128))
+    y = oracle.rope(x, [3, 17, 255, 4096, 131072], 128, 1e6)
+    nx = np.hypot(x[..., 0::2], x[..., 1::2])
+    ny = np.hypot(y[..., 0::2], y[..., 1::2])
+    np.testing.assert_allclose(ny, nx, rtol=1e-12, atol=0)
+    np.testing.assert_allclose(np.linalg.norm(y, axis=-1),
+                               np.linalg.norm(x, axis=-1), rtol=1e-12)
+
+
+@pytest.mark.parametrize("D,R,theta", [(128, 32, 1e6), (512, 128, 1e6), (256, 256, 1e4)])
+def test_rope_relative_position(D, R, theta):
+    """(R_m q).(R_n k) depends only on n - m (shift both by c)."""
+    q = rng.standard_normal((1, 1, D))
+    k = rng.standard_normal((1, 1, D))
+    for m, n, c in [(0, 5, 11), (100, 37, 1000), (4000, 4095, 60000), (7, 7, 123456)]:
+        a = np.dot(oracle.rope(q, [m], R, theta).ravel(), oracle.rope(k, [n], R, theta).ravel())
+        b = np.dot(oracle.rope(q, [m + c], R, theta).ravel(), oracle.rope(k, [n + c], R, theta).ravel())
+        assert abs(a - b) <= 1e-9 * (1 + abs(a))
+
+
+@pytest.mark.parametrize("D,R,theta", [(16, 16, 1e4), (128, 32, 1e6), (512, 128, 1e6)])
+def test_rope_matches_textbook_complex_form(D, R, theta):
+    """Textbook RoPE: view dims (2p, 2p+1) as z_p = x_2p + i x_2p+1 and
+    multiply by exp(i * pos * theta^(-2p/D)); p-RoPE keeps that for the first
+    R/2 pairs and leaves the remaining pairs unrotated."""
+    x = rng.standard_normal((3, 2, D))
+    pos = [1, 250, 131072]
+    y = oracle.rope(x, pos, R, theta)
+    for n, m in enumerate(pos):
+        for h in range(2):
+            for p in range(D // 2):
+                z = complex(x[n, h, 2 * p], x[n, h, 2 * p + 1])
+                if p < R // 2:
+                    z *= cmath.exp(1j * m * theta ** (-2.0 * p / D))
+                assert abs(z.real - y[n, h, 2 * p]) < 1e-9
+                assert abs(z.imag - y[n, h, 2 * p + 1]) < 1e-9
+
+
+def test_rope_frequency_schedule():
+    """Angles at position 1 recovered by atan2: pair 0 turns by exactly 1 rad,
+    consecutive pairs form a geometric series of ratio theta^(-2/D) (so the
+    frequency decreases along the vector), and pairs past R/2 do not turn."""
+    D, R, theta = 64, 48, 1e4
+    x = np.zeros((1, D // 2, D))
+    for p in range(D // 2):
+        x[0, p, 2 * p] = 1.0  # unit vector on pair p, one head per pair
+    y = oracle.rope(x, [1], R, theta)
+    ang = np.array([math.atan2(y[0, p, 2 * p + 1], y[0, p, 2 * p]) for p in range(D // 2)])
+    assert abs(ang[0] - 1.0) < 1e-15
+    ratio = ang[1:R // 2] / ang[:R // 2 - 1]
+    np.testing.assert_allclose(ratio, theta ** (-2.0 / D), rtol=1e-12)
+    assert np.all(ang[R // 2:] == 0.0)
+
+
+def test_rope_large_position_closed_form():
+    """Pair 0 at position 131072 turns by 131072 rad: compare with math.cos/sin."""
+    x = np.zeros((1, 1, 8))
+    x[0, 0, 0] = 1.0
+    y = oracle.rope(x, [131072], 8, 1e6)
+    assert abs(y[0, 0, 0] - math.cos(131072.0)) < 1e-12
+    assert abs(y[0, 0, 1] - math.sin(131072.0)) < 1e-12
+
+
+# ------------------------------------------------------------ the masks ----
+
+def _visible_sets(T, W):
+    """Read the oracle's effective mask: scale 0 makes every visible key weigh
+    the same, and one-hot values V = I report each key's weight."""
+    q = rng.standard_normal((1, T, 1, 4))
+    k = rng.standard_normal((1, T, 1, 4))
+    v = np.eye(T).reshape(1, T, 1, T)
+    o = oracle.prefill(q, k, v, window=W, scale=0.0, rotary_dims=0)[0, :, 0, :]
+    return o
+
+
+@pytest.mark.parametrize("T", [1, 2, 7, 33, 64])
+def test_mask_brute_force(T):
+    for W in sorted({1, 2, 3, max(1, T - 1), T, T + 5, 0}):
+        o = _visible_sets(T, W)
+        for i in range(T):
+            allowed = [j for j in range(T) if j <= i and (W == 0 or i - j < W)]
+            expect = np.zeros(T)
+            expect[allowed] = 1.0 / len(allowed)
+            np.testing.assert_allclose(o[i], expect, rtol=0, atol=1e-15)
+
+
+@pytest.mark.parametrize("case", _gold("window_ranges.json")["cases"])
+def test_window_ranges_from_pages(case):
+    """First/last visible key for the window sizes the pages give."""
+    W, i = case["window"], case["query"]
+    T = i + 1
+    # Only row i matters: ask the oracle for that one row, keys 0..i.
+    q = np.zeros((1, 1, 1, 1))
+    k = np.zeros((1, T, 1, 1))
+    v = np.arange(T, dtype=np.float64).reshape(1, T, 1, 1)
+    v2 = v ** 2
+    vv = np.concatenate([np.ones_like(v), v, v2], axis=3)
+    o = oracle.prefill(q, k, vv, window=W, scale=1.0, rotary_dims=0, rows=[i])[0, 0, 0]
+    # Uniform weights over keys a..b: mean = (a+b)/2, count from the variance.
+    a, b = case["first_key"], case["last_key"]
+    assert abs(o[0] - 1.0) < 1e-12
+    assert abs(o[1] - (a + b) / 2) < 1e-9
+    n = b - a + 1
+    assert abs(o[2] - (o[1] ** 2 + (n * n - 1) / 12.0)) < 1e-6 * (1 + o[2])
+
+
+def test_window_at_least_T_is_causal():
+    B, T, H, D = 2, 40, 2, 16
+    q, k, v = (rng.standard_normal((B, T, H, D)) for _ in range(3))
+    causal = oracle.prefill(q, k, v, window=0, scale=0.3, rotary_dims=16, theta=1e4)
+    for W in (T, T + 1, 10 * T):
+        np.testing.assert_array_equal(
+            oracle.prefill(q, k, v, window=W, scale=0.3, rotary_dims=16, theta=1e4), causal)
+
+
+# ------------------------------------------------- softmax closed forms ----
+
+def test_window_one_returns_own_value():
+    B, T, H, D = 1, 20, 3, 8
+    q, k, v = (rng.standard_normal((B, T, H, D)) for _ in range(3))
+    o = oracle.prefill(q, k, v, window=1, scale=0.7, rotary_dims=8, theta=1e4)
+    np.testing.assert_allclose(o, v, rtol=0, atol=1e-14)
+
+
+def test_constant_values_give_constant_output():
+    B, T, H, D = 1, 30, 2, 8
+    q, k = rng.standard_normal((B, T, H, D)), rng.standard_normal((B, T, H, D))
+    v = np.full((B, T, H, 5), 3.25)
+    o = oracle.prefill(q, k, v, window=7, scale=1.3, rotary_dims=8, theta=1e4)
+    np.testing.assert_allclose(o, 3.25, rtol=1e-14)
+
+
+def test_first_token_sees_only_itself():
+    q, k, v = (rng.standard_normal((2, 5, 4, 8)) for _ in range(3))
+    o = oracle.prefill(q, k, v, window=0, scale=0.5, rotary_dims=8, theta=1e6)
+    np.testing.assert_allclose(o[:, 0], v[:, 0], atol=1e-14)
+
+
+def test_two_token_closed_form():
+    """Row 1 of a 2-token, 1-dim problem without RoPE: weights
+    e^{s q k_j} / (e^{s q k_0} + e^{s q k_1})."""
+    q = np.array([0.0, 1.5]).reshape(1, 2, 1, 1)
+    k = np.array([0.4, -0.9]).reshape(1, 2, 1, 1)
+    v = np.array([2.0, -1.0]).reshape(1, 2, 1, 1)
+    s = 0.8
+    o = oracle.prefill(q, k, v, window=0, scale=s, rotary_dims=0)[0, 1, 0, 0]
+    e0, e1 = math.exp(s * 1.5 * 0.4), math.exp(s * 1.5 * -0.9)
+    assert abs(o - (2.0 * e0 - 1.0 * e1) / (e0 + e1)) < 1e-14
+
+
+# ----------------------------------------------- library routine + GQA ----
+
+def _torch_sdpa(q, k, v, W, scale, G):
+    """torch CPU fp64 SDPA with repeat_interleave'd KV and a boolean mask."""
+    qt = torch.from_numpy(q).permute(0, 2, 1, 3)  # B H T D
+    kt = torch.from_numpy(k).permute(0, 2, 1, 3).repeat_interleave(G, dim=1)
+    vt = torch.from_numpy(v).permute(0, 2, 1, 3).repeat_interleave(G, dim=1)
+    T = q.shape[1]
+    i = torch.arange(T).view(T, 1)
+    j = torch.arange(T).view(1, T)
+    mask = j <= i
+    if W > 0:
+        mask &= (i - j) < W
+    o = torch.nn.functional.scaled_dot_product_attention(
+        qt, kt.contiguous(), vt.contiguous(), attn_mask=mask, scale=scale)
+    return o.permute(0, 2, 1, 3).numpy()
+
+
+@pytest.mark.parametrize("B,T,Hq,Hkv,Dk,Dv,W", [
+    (1, 9, 1, 1, 8, 8, 0), (2, 33, 4, 2, 16, 8, 5), (1, 40, 8, 1, 32, 16, 0),
+    (2, 17, 6, 3, 8, 12, 1), (1, 64, 16, 8, 16, 16, 20)])
+def test_oracle_matches_torch_sdpa(B, T, Hq, Hkv, Dk, Dv, W):
+    q = rng.standard_normal((B, T, Hq, Dk))
+    k = rng.standard_normal((B, T, Hkv, Dk))
+    v = rng.standard_normal((B, T, Hkv, Dv))
+    scale = 1 / math.sqrt(Dk)
+    ref = _torch_sdpa(q, k, v, W, scale, Hq // Hkv)
+    o = oracle.prefill(q, k, v, window=W, scale=scale, rotary_dims=0)
+    np.testing.assert_allclose(o, ref, rtol=1e-12, atol=1e-12)
+
+
+def test_oracle_with_rope_matches_torch_on_prerotated_inputs():
+    """RoPE inside the oracle equals rotating q and k first (positions pos0+t)
+    and running the library routine without RoPE."""
+    B, T, Hq, Hkv, D, R, theta, pos0 = 1, 24, 4, 1, 32, 8, 1e6, 1000
+    q = rng.standard_normal((B, T, Hq, D))
+    k = rng.standard_normal((B, T, Hkv, D))
+    v = rng.standard_normal((B, T, Hkv, D))
+    pos = np.arange(T) + pos0
+    qr = oracle.rope(q[0], pos, R, theta)[None]
+    kr = oracle.rope(k[0], pos, R, theta)[None]
+    ref = _torch_sdpa(qr, kr, v, 0, 0.2, Hq // Hkv)
+    o = oracle.prefill(q, k, v, window=0, scale=0.2, rotary_dims=R, theta=theta, pos0=pos0)
+    np.testing.assert_allclose(o, ref, rtol=1e-12, atol=1e-12)
+
+
+def test_gqa_equals_repeated_heads():
+    B, T, Hq, Hkv, D = 2, 21, 8, 2, 16
+    q = rng.standard_normal((B, T, Hq, D))
+    k = rng.standard_normal((B, T, Hkv, D))
+    v = rng.standard_normal((B, T, Hkv, D))
+    kw = dict(window=6, scale=0.25, rotary_dims=8, theta=1e6)
+    a = oracle.prefill(q, k, v, **kw)
+    b = oracle.prefill(q, np.repeat(k, Hq // Hkv, axis=2), np.repeat(v, Hq // Hkv, axis=2), **kw)
+    np.testing.assert_array_equal(a, b)
+
+
+def test_position_offset_invariance():
+    """Rotating q and k with a common offset pos0 leaves every score, hence
+    every output, unchanged (relative-position property)."""
+    q, k, v = (rng.standard_normal((1, 16, 2, 32)) for _ in range(3))
+    kw = dict(window=0, scale=0.3, rotary_dims=32, theta=1e4)
+    np.testing.assert_allclose(oracle.prefill(q, k, v, pos0=0, **kw),
+                               oracle.prefill(q, k, v, pos0=5000, **kw), atol=1e-11)
+
+
+def test_row_subset_equals_full():
+    q, k, v = (rng.standard_normal((2, 30, 4, 16)) for _ in range(3))
+    kw = dict(window=7, scale=0.3, rotary_dims=16, theta=1e4)
+    full = oracle.prefill(q, k, v, **kw)
+    rows = [0, 6, 7, 29, 13]
+    sub = oracle.prefill(q[:, rows], k, v, rows=rows, **kw)
+    np.testing.assert_array_equal(sub, full[:, rows])
+
+
+# -------------------------------------------------------------- decode ----
+
+@pytest.mark.parametrize("W", [0, 1, 5, 64])
+def test_decode_equals_last_prefill_row(W):
+    """Decode at kv_len = L+1 with pre-rotated cache keys equals the last row
+    of a prefill over the same L+1 tokens that rotates keys itself."""
+    L, Hq, Hkv, Dk, Dv, R, theta = 40, 8, 2, 32, 16, 16, 1e6
+    q = rng.standard_normal((1, L + 1, Hq, Dk))
+    k = rng.standard_normal((1, L + 1, Hkv, Dk))
+    v = rng.standard_normal((1, L + 1, Hkv, Dv))
+    ref = oracle.prefill(q, k, v, window=W, scale=0.2, rotary_dims=R, theta=theta)[0, L]
+    k_rot = oracle.rope(k[0], np.arange(L + 1), R, theta)
+    out = oracle.decode(q[:, L], k_rot, v[0], [0], [L + 1], window=W, scale=0.2,
+                        rotary_dims=R, theta=theta)[0]
+    np.testing.assert_allclose(out, ref, rtol=1e-12, atol=1e-12)
+
+
+def test_decode_ragged_and_empty():
+    Hq, Hkv, D = 4, 2, 8
+    lens = [0, 1, 9, 30]
+    offs = np.concatenate([[0], np.cumsum(lens)[:-1]])
+    kc = rng.standard_normal((sum(lens), Hkv, D))
+    vc = rng.standard_normal((sum(lens), Hkv, D))
+    q = rng.standard_normal((4, Hq, D))
+    out = oracle.decode(q, kc, vc, offs, lens, window=4, scale=0.5, rotary_dims=8, theta=1e4)
+    assert np.all(out[0] == 0.0)
+    np.testing.assert_allclose(out[1], np.repeat(vc[0], Hq // Hkv, axis=0), atol=1e-14)
+    for b in (2, 3):
+        n = lens[b]
+        full = oracle.decode_one(q[b], kc[offs[b]:offs[b] + n], vc[offs[b]:offs[b] + n],
+                                 kv_len=n, row0=0, window=4, scale=0.5, rotary_dims=8, theta=1e4)
+        np.testing.assert_allclose(out[b], full, atol=1e-14)
+
+
+def test_decode_rejects_visible_rows_before_row0():
+    q = rng.standard_normal((2, 8))
+    kc = rng.standard_normal((5, 1, 8))
+    with pytest.raises(RuntimeError):
+        oracle.decode_one(q, kc, kc, kv_len=10, row0=5, window=6, scale=1.0)
