@@ -1,0 +1,188 @@
+"""Python binding of the MI355X hybrid-attention library (libattn_rope.so).
+
+Argument marshalling only: every step of the path runs in the library's HIP
+kernels. torch provides device memory and the current stream. The entry
+points mirror the C ABI in include/attn_rope.h:
+
+    prefill(q, k, v, *, window, scale, rotary_dims, theta, rope_mask, pos0)
+    decode(q, k_cache, v_cache, row_offset, kv_len, *, window, scale,
+           rotary_dims, theta, max_kv_len)
+    prope(x, positions, *, rotary_dims, theta, out=None)
+
+There is no CPU fallback: if the shared library is missing or fails to load,
+every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch  # imported first so the HIP runtime torch ships is the one in use
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libattn_rope.so")
+
+ATTN_F32, ATTN_BF16 = 0, 1
+ROPE_Q, ROPE_K = 1, 2
+STATUS = {0: "ok", 1: "null pointer", 2: "invalid shape or argument",
+          3: "unsupported configuration", 4: "workspace missing or too small",
+          5: "kernel launch failed", 6: "output overlaps an input"}
+
+# Every symbol the header declares (checked by the tests).
+EXPORTS = ("attn_rope_table", "attn_rope_table_bytes", "attn_prefill", "attn_decode",
+           "attn_decode_workspace_bytes", "prope_apply", "attn_status_string",
+           "attn_last_error")
+
+
+class AttnError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        super().__init__(f"{STATUS.get(status, status)}: {detail}")
+        self.status = status
+
+
+class _Rope(ctypes.Structure):
+    _fields_ = [("rotary_dims", ctypes.c_int32), ("theta", ctypes.c_double)]
+
+
+_lib = None
+
+
+def load(path: str = LIB_PATH):
+    """Load the shared library (once). Raises if it is not built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with "
+                           "`python -c 'import __graft_entry__ as g; g.build()'`")
+    lib = ctypes.CDLL(path)
+    vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+    lib.attn_rope_table_bytes.argtypes = [i32, i32]
+    lib.attn_rope_table_bytes.restype = sz
+    lib.attn_rope_table.argtypes = [vp, i32, i32, i32, _Rope, vp]
+    lib.attn_rope_table.restype = ctypes.c_int
+    lib.attn_prefill.argtypes = [vp, vp, vp, vp] + [i32] * 7 + [
+        ctypes.c_float, _Rope, i32, vp, ctypes.c_int, vp]
+    lib.attn_prefill.restype = ctypes.c_int
+    lib.attn_decode_workspace_bytes.argtypes = [i32] * 5
+    lib.attn_decode_workspace_bytes.restype = sz
+    lib.attn_decode.argtypes = [vp] * 6 + [i32] * 6 + [
+        ctypes.c_float, _Rope, i32, vp, sz, ctypes.c_int, vp]
+    lib.attn_decode.restype = ctypes.c_int
+    lib.prope_apply.argtypes = [vp, vp, vp, i32, i32, i32, _Rope, ctypes.c_int, vp]
+    lib.prope_apply.restype = ctypes.c_int
+    lib.attn_status_string.argtypes = [ctypes.c_int]
+    lib.attn_status_string.restype = ctypes.c_char_p
+    lib.attn_last_error.argtypes = []
+    lib.attn_last_error.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def _check(rc: int):
+    if rc != 0:
+        raise AttnError(rc, _lib.attn_last_error().decode())
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return ATTN_BF16
+    if t.dtype == torch.float32:
+        return ATTN_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _dev(t: torch.Tensor, name: str):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(t: torch.Tensor):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def rope_table(T: int, *, head_dim: int, rotary_dims: int, theta: float, pos0: int = 0,
+               device="cuda", out=None):
+    """cos/sin table [T, rotary_dims/2, 2] fp32 for positions pos0..pos0+T-1
+    (None when there is nothing to rotate)."""
+    lib = load()
+    if T == 0 or rotary_dims == 0:
+        return None
+    tab = out if out is not None else torch.empty((T, rotary_dims // 2, 2),
+                                                  dtype=torch.float32, device=device)
+    _check(lib.attn_rope_table(_dev(tab, "table"), T, pos0, head_dim,
+                               _Rope(rotary_dims, theta), _stream(tab)))
+    return tab
+
+
+def prefill(q, k, v, *, window: int = 0, scale: float | None = None,
+            rotary_dims: int = 0, theta: float = 10000.0,
+            rope_mask: int = ROPE_Q | ROPE_K, pos0: int = 0, out=None,
+            table=None):
+    """q [B,T,Hq,Dk], k [B,T,Hkv,Dk], v [B,T,Hkv,Dv] -> o [B,T,Hq,Dv].
+
+    ``table`` is a cos/sin table from rope_table() for the same T, pos0 and
+    RoPE settings; it is built here when not given."""
+    lib = load()
+    B, T, Hq, Dk = q.shape
+    Hkv, Dv = k.shape[2], v.shape[3]
+    if k.shape != (B, T, Hkv, Dk) or v.shape != (B, T, Hkv, Dv):
+        raise ValueError("q/k/v shapes disagree")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k, v must share a dtype")
+    if scale is None:
+        scale = Dk ** -0.5
+    o = out if out is not None else torch.empty((B, T, Hq, Dv), dtype=q.dtype, device=q.device)
+    if table is None and rotary_dims > 0 and rope_mask and T > 0:
+        table = rope_table(T, head_dim=Dk, rotary_dims=rotary_dims, theta=theta, pos0=pos0,
+                           device=q.device)
+    tab_ptr = _dev(table, "table") if table is not None else None
+    _check(lib.attn_prefill(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(o, "o"),
+                            B, T, Hq, Hkv, Dk, Dv, int(window), float(scale),
+                            _Rope(rotary_dims, theta), int(rope_mask), tab_ptr,
+                            _dtype_code(q), _stream(q)))
+    return o
+
+
+def decode_workspace_bytes(B: int, Hq: int, Dv: int, max_kv_len: int, window: int) -> int:
+    return int(load().attn_decode_workspace_bytes(B, Hq, Dv, max_kv_len, window))
+
+
+def decode(q, k_cache, v_cache, row_offset, kv_len, *, window: int = 0,
+           scale: float | None = None, rotary_dims: int = 0, theta: float = 10000.0,
+           max_kv_len: int, out=None, workspace=None):
+    """q [B,Hq,Dk]; caches [rows,Hkv,Dk|Dv]; row_offset int64 [B]; kv_len int32 [B]."""
+    lib = load()
+    B, Hq, Dk = q.shape
+    Hkv, Dv = k_cache.shape[1], v_cache.shape[2]
+    if row_offset.dtype != torch.int64 or kv_len.dtype != torch.int32:
+        raise TypeError("row_offset must be int64 and kv_len int32")
+    if scale is None:
+        scale = Dk ** -0.5
+    o = out if out is not None else torch.empty((B, Hq, Dv), dtype=q.dtype, device=q.device)
+    need = decode_workspace_bytes(B, Hq, Dv, max_kv_len, window)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    _check(lib.attn_decode(_dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
+                           _dev(row_offset, "row_offset"), _dev(kv_len, "kv_len"),
+                           _dev(o, "o"), B, Hq, Hkv, Dk, Dv, int(window), float(scale),
+                           _Rope(rotary_dims, theta), int(max_kv_len),
+                           ctypes.c_void_p(workspace.data_ptr()),
+                           workspace.numel() * workspace.element_size(),
+                           _dtype_code(q), _stream(q)))
+    return o
+
+
+def prope(x, positions, *, rotary_dims: int, theta: float, out=None):
+    """x [N,H,D] -> rotated copy (or in place when out is x); positions int32 [N]."""
+    lib = load()
+    N, H, D = x.shape
+    if positions.dtype != torch.int32:
+        raise TypeError("positions must be int32")
+    y = out if out is not None else torch.empty_like(x)
+    _check(lib.prope_apply(_dev(x, "x"), _dev(y, "y"), _dev(positions, "positions"),
+                           N, H, D, _Rope(rotary_dims, theta), _dtype_code(x), _stream(x)))
+    return y

@@ -1,0 +1,239 @@
+// abi.cpp — the C ABI of the hybrid-attention library: argument validation,
+// workspace accounting, kernel selection and error reporting. Every check runs
+// on the host before any HIP call; a failed check launches nothing.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <string>
+
+#include "../../include/attn_rope.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+attn_status_t fail(attn_status_t s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+attn_status_t ok() {
+  g_last_error.clear();
+  return ATTN_OK;
+}
+
+attn_status_t launch_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(ATTN_ERR_LAUNCH, "%s: HIP error %d (%s)", what, (int)e, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+  if (!a || !b || na == 0 || nb == 0) return false;
+  const uintptr_t x0 = reinterpret_cast<uintptr_t>(a), y0 = reinterpret_cast<uintptr_t>(b);
+  return x0 < y0 + nb && y0 < x0 + na;
+}
+
+size_t elem_size(attn_dtype_t d) { return d == ATTN_F32 ? 4 : 2; }
+
+attn_status_t check_rope(attn_rope_t rope, int32_t D) {
+  if (rope.rotary_dims < 0 || rope.rotary_dims > D || rope.rotary_dims % 2 != 0)
+    return fail(ATTN_ERR_SHAPE, "rotary_dims=%d must be even and in [0, %d]",
+                rope.rotary_dims, D);
+  if (rope.rotary_dims > 0 && !(std::isfinite(rope.theta) && rope.theta > 0.0))
+    return fail(ATTN_ERR_SHAPE, "rope theta must be finite and > 0");
+  return ATTN_OK;
+}
+
+bool prefill_uses_table(attn_rope_t rope, int32_t rope_mask) {
+  return rope.rotary_dims > 0 && (rope_mask & (ATTN_ROPE_Q | ATTN_ROPE_K)) != 0;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* attn_status_string(attn_status_t s) {
+  switch (s) {
+    case ATTN_OK: return "ok";
+    case ATTN_ERR_NULL: return "null pointer";
+    case ATTN_ERR_SHAPE: return "invalid shape or argument";
+    case ATTN_ERR_UNSUPPORTED: return "unsupported configuration";
+    case ATTN_ERR_WORKSPACE: return "workspace missing or too small";
+    case ATTN_ERR_LAUNCH: return "kernel launch failed";
+    case ATTN_ERR_ALIAS: return "output overlaps an input";
+  }
+  return "unknown status";
+}
+
+const char* attn_last_error(void) { return g_last_error.c_str(); }
+
+size_t attn_rope_table_bytes(int32_t T, int32_t rotary_dims) {
+  if (T <= 0 || rotary_dims <= 0) return 0;
+  return (size_t)T * (size_t)(rotary_dims / 2) * sizeof(float2);
+}
+
+attn_status_t attn_rope_table(void* table, int32_t T, int32_t pos0, int32_t head_dim,
+                              attn_rope_t rope, void* stream) {
+  if (T < 0) return fail(ATTN_ERR_SHAPE, "T=%d must be >= 0", T);
+  if (head_dim < 2 || head_dim % 2)
+    return fail(ATTN_ERR_SHAPE, "head_dim=%d must be even and >= 2", head_dim);
+  attn_status_t rs = check_rope(rope, head_dim);
+  if (rs != ATTN_OK) return rs;
+  if (pos0 < 0 || (int64_t)pos0 + T > INT32_MAX)
+    return fail(ATTN_ERR_SHAPE, "positions pos0=%d .. pos0+T-1 must lie in [0, 2^31-1)", pos0);
+  if (T == 0 || rope.rotary_dims == 0) return ok();
+  if (!table) return fail(ATTN_ERR_NULL, "table must be non-NULL");
+  if (!aligned16(table)) return fail(ATTN_ERR_SHAPE, "table must be 16-byte aligned");
+  return launch_status(attn::launch_rope_table(reinterpret_cast<float2*>(table), T,
+                                               rope.rotary_dims / 2, head_dim, pos0,
+                                               rope.theta,
+                                               reinterpret_cast<hipStream_t>(stream)),
+                       "rope table");
+}
+
+attn_status_t attn_prefill(const void* q, const void* k, const void* v, void* o,
+                           int32_t B, int32_t T, int32_t Hq, int32_t Hkv, int32_t Dk,
+                           int32_t Dv, int32_t window, float scale, attn_rope_t rope,
+                           int32_t rope_mask, const void* rope_table, attn_dtype_t dtype,
+                           void* stream) {
+  if (dtype != ATTN_F32 && dtype != ATTN_BF16)
+    return fail(ATTN_ERR_UNSUPPORTED, "dtype %d is not ATTN_F32 or ATTN_BF16", (int)dtype);
+  if (B < 0 || T < 0) return fail(ATTN_ERR_SHAPE, "B=%d and T=%d must be >= 0", B, T);
+  if (Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0)
+    return fail(ATTN_ERR_SHAPE, "Hq=%d must be a positive multiple of Hkv=%d", Hq, Hkv);
+  if (Dk < 2 || Dv < 2 || Dk > 512 || Dv > 512 || Dk % 2 || Dv % 2)
+    return fail(ATTN_ERR_SHAPE, "head dims Dk=%d Dv=%d must be even and in [2, 512]", Dk, Dv);
+  if (!std::isfinite(scale)) return fail(ATTN_ERR_SHAPE, "scale must be finite");
+  if (rope_mask & ~(ATTN_ROPE_Q | ATTN_ROPE_K))
+    return fail(ATTN_ERR_SHAPE, "rope_mask=%d has unknown bits", rope_mask);
+  attn_status_t rs = check_rope(rope, Dk);
+  if (rs != ATTN_OK) return rs;
+  if (B == 0 || T == 0) return ok();
+  if (!q || !k || !v || !o) return fail(ATTN_ERR_NULL, "q, k, v and o must be non-NULL");
+  const bool rot = prefill_uses_table(rope, rope_mask);
+  if (rot && !rope_table)
+    return fail(ATTN_ERR_NULL, "rope_table must be non-NULL when a rotation applies");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) ||
+      (rot && !aligned16(rope_table)))
+    return fail(ATTN_ERR_SHAPE, "q, k, v, o and rope_table must be 16-byte aligned");
+  const size_t es = elem_size(dtype);
+  const size_t nq = (size_t)B * T * Hq * Dk * es, nk = (size_t)B * T * Hkv * Dk * es;
+  const size_t nv = (size_t)B * T * Hkv * Dv * es, no = (size_t)B * T * Hq * Dv * es;
+  if (overlap(o, no, q, nq) || overlap(o, no, k, nk) || overlap(o, no, v, nv) ||
+      (rot && overlap(o, no, rope_table, attn_rope_table_bytes(T, rope.rotary_dims))))
+    return fail(ATTN_ERR_ALIAS, "o must not overlap q, k, v or rope_table");
+  if ((int64_t)B * T * Hq / 4 + 1 > INT32_MAX)
+    return fail(ATTN_ERR_SHAPE, "B*T*Hq too large");
+
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  attn::PrefillArgs a{};
+  a.q = q; a.k = k; a.v = v; a.o = o;
+  a.B = B; a.T = T; a.Hq = Hq; a.Hkv = Hkv; a.Dk = Dk; a.Dv = Dv;
+  a.window = (window > 0 && window < T) ? window : 0;
+  a.rot_pairs = rot ? rope.rotary_dims / 2 : 0;
+  a.rope_q = rot && (rope_mask & ATTN_ROPE_Q);
+  a.rope_k = rot && (rope_mask & ATTN_ROPE_K);
+  a.scale = scale;
+  a.rope_tab = rot ? reinterpret_cast<const float2*>(rope_table) : nullptr;
+  if (dtype == ATTN_BF16 && attn::prefill_mfma_supported(Dk, Dv, Hq / Hkv, scale)) {
+    hipError_t e = attn::launch_prefill_mfma(a, st);
+    if (e != hipErrorNotSupported) return launch_status(e, "prefill (mfma)");
+  }
+  return launch_status(attn::launch_prefill_general(a, dtype == ATTN_BF16, st),
+                       "prefill (general)");
+}
+
+size_t attn_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t Dv, int32_t max_kv_len,
+                                   int32_t window) {
+  return attn::decode_workspace_bytes(B, Hq, Dv, max_kv_len, window);
+}
+
+attn_status_t attn_decode(const void* q, const void* k_cache, const void* v_cache,
+                          const int64_t* row_offset, const int32_t* kv_len, void* o,
+                          int32_t B, int32_t Hq, int32_t Hkv, int32_t Dk, int32_t Dv,
+                          int32_t window, float scale, attn_rope_t rope,
+                          int32_t max_kv_len, void* workspace, size_t workspace_bytes,
+                          attn_dtype_t dtype, void* stream) {
+  if (dtype != ATTN_BF16)
+    return fail(ATTN_ERR_UNSUPPORTED, "decode supports the ATTN_BF16 cache only");
+  if (B < 0 || B > 65535) return fail(ATTN_ERR_SHAPE, "B=%d must be in [0, 65535]", B);
+  if (Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0)
+    return fail(ATTN_ERR_SHAPE, "Hq=%d must be a positive multiple of Hkv=%d", Hq, Hkv);
+  if (!attn::decode_supported(Dk, Dv, Hq / Hkv))
+    return fail(ATTN_ERR_UNSUPPORTED,
+                "decode supports Dk in {128,256,512}, Dv in {128,256}, Hq/Hkv <= 16 "
+                "(got Dk=%d Dv=%d G=%d)", Dk, Dv, Hq / Hkv);
+  if (!std::isfinite(scale) || scale < 0.f)
+    return fail(ATTN_ERR_UNSUPPORTED, "decode needs a finite scale >= 0");
+  attn_status_t rs = check_rope(rope, Dk);
+  if (rs != ATTN_OK) return rs;
+  if (B == 0) return ok();
+  if (max_kv_len < 1) return fail(ATTN_ERR_SHAPE, "max_kv_len=%d must be >= 1", max_kv_len);
+  if (!q || !k_cache || !v_cache || !row_offset || !kv_len || !o)
+    return fail(ATTN_ERR_NULL, "q, caches, row_offset, kv_len and o must be non-NULL");
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o))
+    return fail(ATTN_ERR_SHAPE, "q, caches and o must be 16-byte aligned");
+  const size_t need = attn::decode_workspace_bytes(B, Hq, Dv, max_kv_len, window);
+  if (!workspace || workspace_bytes < need)
+    return fail(ATTN_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+                workspace ? workspace_bytes : (size_t)0);
+  if (!aligned16(workspace)) return fail(ATTN_ERR_WORKSPACE, "workspace must be 16-byte aligned");
+  const size_t no = (size_t)B * Hq * Dv * 2;
+  if (overlap(o, no, q, (size_t)B * Hq * Dk * 2) || overlap(workspace, need, o, no) ||
+      overlap(workspace, need, q, (size_t)B * Hq * Dk * 2))
+    return fail(ATTN_ERR_ALIAS, "o / workspace must not overlap q or each other");
+
+  attn::DecodeArgs a{};
+  a.q = q; a.k_cache = k_cache; a.v_cache = v_cache;
+  a.row_offset = row_offset; a.kv_len = kv_len; a.o = o;
+  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.Dk = Dk; a.Dv = Dv;
+  a.window = window > 0 ? window : 0;
+  a.rot_pairs = rope.rotary_dims / 2;
+  a.theta = rope.rotary_dims > 0 ? rope.theta : 1.0;
+  a.scale = scale;
+  a.max_kv_len = max_kv_len;
+  a.workspace = workspace;
+  return launch_status(attn::launch_decode(a, reinterpret_cast<hipStream_t>(stream)),
+                       "decode");
+}
+
+attn_status_t prope_apply(const void* x, void* y, const int32_t* positions, int32_t N,
+                          int32_t H, int32_t D, attn_rope_t rope, attn_dtype_t dtype,
+                          void* stream) {
+  if (dtype != ATTN_F32 && dtype != ATTN_BF16)
+    return fail(ATTN_ERR_UNSUPPORTED, "dtype %d is not ATTN_F32 or ATTN_BF16", (int)dtype);
+  if (N < 0 || H < 0) return fail(ATTN_ERR_SHAPE, "N=%d and H=%d must be >= 0", N, H);
+  if (D < 2 || D > 1024 || D % 2) return fail(ATTN_ERR_SHAPE, "D=%d must be even, 2..1024", D);
+  attn_status_t rs = check_rope(rope, D);
+  if (rs != ATTN_OK) return rs;
+  if (N == 0 || H == 0) return ok();
+  if (!x || !y || !positions) return fail(ATTN_ERR_NULL, "x, y and positions must be non-NULL");
+  const size_t es = elem_size(dtype);
+  if ((reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(y)) & (2 * es - 1))
+    return fail(ATTN_ERR_SHAPE, "x and y must be aligned to a pair of elements");
+  const size_t n = (size_t)N * H * D * es;
+  if (x != y && overlap(x, n, y, n)) return fail(ATTN_ERR_ALIAS, "y partially overlaps x");
+  if ((int64_t)N * (rope.rotary_dims / 2) > (int64_t)INT32_MAX * 256)
+    return fail(ATTN_ERR_SHAPE, "N too large");
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  if (rope.rotary_dims == 0) {
+    if (x == y) return ok();
+    return launch_status(hipMemcpyAsync(y, x, n, hipMemcpyDeviceToDevice, st), "prope copy");
+  }
+  return launch_status(attn::launch_prope(x, y, positions, N, H, D, rope.rotary_dims / 2,
+                                          rope.theta, dtype == ATTN_BF16, st),
+                       "prope");
+}
+
+}  // extern "C"

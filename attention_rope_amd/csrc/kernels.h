@@ -1,0 +1,59 @@
+// kernels.h — host-side launch functions of the gfx950 kernels. All launches
+// go onto the given stream and return the launch status; nothing synchronises.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace attn {
+
+// ---- RoPE -----------------------------------------------------------------
+hipError_t launch_rope_table(float2* tab, int T, int P, int D, int pos0,
+                             double theta, hipStream_t st);
+hipError_t launch_prope(const void* x, void* y, const int32_t* pos, int N, int H,
+                        int D, int P, double theta, bool bf16, hipStream_t st);
+
+// ---- prefill ----------------------------------------------------------------
+struct PrefillArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  const float2* rope_tab;  // [T][rot_pairs] cos/sin, or nullptr
+  int B, T, Hq, Hkv, Dk, Dv;
+  int window;              // 0: full causal
+  int rot_pairs;           // rotary pairs (0: none)
+  int rope_q, rope_k;      // apply rotation to q / k
+  float scale;
+};
+
+// MFMA flash kernel (bf16). Returns hipErrorNotSupported for shapes it has no
+// instantiation for; the caller then uses the general kernel.
+hipError_t launch_prefill_mfma(const PrefillArgs& a, hipStream_t st);
+bool prefill_mfma_supported(int Dk, int Dv, int G, float scale);
+
+// General kernel: any supported shape, fp32 or bf16.
+hipError_t launch_prefill_general(const PrefillArgs& a, bool bf16, hipStream_t st);
+
+// ---- decode -----------------------------------------------------------------
+struct DecodeArgs {
+  const void* q;
+  const void* k_cache;
+  const void* v_cache;
+  const int64_t* row_offset;
+  const int32_t* kv_len;
+  void* o;
+  int B, Hq, Hkv, Dk, Dv;
+  int window;              // 0: all rows
+  int rot_pairs;
+  double theta;
+  float scale;
+  int max_kv_len;
+  void* workspace;
+};
+
+size_t decode_workspace_bytes(int B, int Hq, int Dv, int max_kv_len, int window);
+bool decode_supported(int Dk, int Dv, int G);
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t st);
+
+}  // namespace attn

@@ -1,0 +1,159 @@
+/*
+ * attn_rope.h — C ABI of the MI355X (gfx950) hybrid-attention library.
+ *
+ * The library computes the decoder attention of the Gemma 4 family as its
+ * pages describe it: causal grouped-query attention in a sliding-window
+ * (local) form and a full-context (global) form, with proportional RoPE on the
+ * queries and keys.
+ *   - "Gemma 4: End-to-End Architecture Walkthrough", Phase 3: section 3a
+ *     (local layers see a fixed recent window — 512 or 1024 tokens — global
+ *     layers the whole preceding context), section 3b (8 query heads per KV
+ *     head in global layers, 2 in local ones, wider global keys) and section
+ *     3c (p-RoPE: only the first quarter of the rotary pairs turn).
+ *   - "Gemma 4 Architecture Reference": "Attention Architecture",
+ *     "Positional Encoding: Proportional RoPE (p-RoPE)" (p = 0.25, theta = 1e6)
+ *     and "Shared KV Cache" (later layers reuse an earlier layer's K/V: pass
+ *     the same k/v pointers again; no separate entry point is needed).
+ *
+ * Conventions shared by every entry point
+ *   - Tensor pointers are DEVICE pointers owned by the caller. The library
+ *     never allocates or frees device memory, keeps no state between calls,
+ *     never synchronises, and enqueues its kernels on `stream` (a hipStream_t;
+ *     NULL = the default stream). Calls return as soon as the work is queued.
+ *   - Layouts are dense row-major with the last dimension contiguous.
+ *   - Element type: ATTN_BF16 (bfloat16 in and out, fp32 accumulation) or
+ *     ATTN_F32 (fp32 throughout). All tensors of one call share it.
+ *   - Every argument is validated on the host before any HIP call; on error
+ *     nothing is launched and a status != ATTN_OK is returned, with detail in
+ *     attn_last_error(). No call prints, throws or aborts.
+ *   - Thread-safe: calls may come from several host threads at once.
+ *
+ * RoPE reading (the pages leave pairing and frequency base open): dims
+ * (2p, 2p+1) form pair p, which turns by angle pos * theta^(-2p/D), D the full
+ * head dim; only pairs p < rotary_dims/2 turn, the rest pass through
+ * unchanged. rotary_dims = D is textbook RoPE, rotary_dims = D/4 is p-RoPE
+ * with p = 0.25, rotary_dims = 0 disables rotation.
+ */
+#ifndef ATTN_ROPE_H
+#define ATTN_ROPE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { ATTN_F32 = 0, ATTN_BF16 = 1 } attn_dtype_t;
+
+typedef enum {
+  ATTN_OK = 0,
+  ATTN_ERR_NULL = 1,        /* a required pointer is NULL */
+  ATTN_ERR_SHAPE = 2,       /* sizes inconsistent or out of range */
+  ATTN_ERR_UNSUPPORTED = 3, /* valid but not implemented (e.g. head dim) */
+  ATTN_ERR_WORKSPACE = 4,   /* workspace missing or too small */
+  ATTN_ERR_LAUNCH = 5,      /* the HIP runtime refused a launch */
+  ATTN_ERR_ALIAS = 6        /* an output overlaps an input it must not */
+} attn_status_t;
+
+/* Rotary settings: rotary_dims even, 0 <= rotary_dims <= head dim; theta > 0. */
+typedef struct {
+  int32_t rotary_dims;
+  double theta;
+} attn_rope_t;
+
+enum { ATTN_ROPE_Q = 1, ATTN_ROPE_K = 2 };
+
+/*
+ * RoPE cos/sin table for token positions pos0 .. pos0 + T - 1:
+ * table[t][p] = (cos, sin) of (pos0 + t) * theta^(-2p/head_dim) as two fp32,
+ * for pairs p < rope.rotary_dims / 2 (angles formed and evaluated in fp64).
+ * It depends on positions and RoPE settings only, so one table serves every
+ * layer of a type (and every batch row) that shares them.
+ *   table: device buffer of attn_rope_table_bytes(T, rope.rotary_dims) bytes,
+ *   16-byte aligned. head_dim even, rotary_dims <= head_dim, T >= 0,
+ *   pos0 >= 0, pos0 + T <= 2^31 - 1.
+ */
+size_t attn_rope_table_bytes(int32_t T, int32_t rotary_dims);
+
+attn_status_t attn_rope_table(void *table, int32_t T, int32_t pos0, int32_t head_dim,
+                              attn_rope_t rope, void *stream);
+
+/*
+ * Prefill: o = softmax(scale * rope(q) rope(k)^T + mask) v for every query
+ * row, per batch b and query head h, with KV head h / (Hq / Hkv).
+ *   q [B, T, Hq, Dk], k [B, T, Hkv, Dk], v [B, T, Hkv, Dv]: unrotated inputs;
+ *   o [B, T, Hq, Dv] output; must not overlap q, k or v.
+ *   Token t's rotation comes from row t of rope_table (made by attn_rope_table
+ *   for the same T, head_dim = Dk and rope settings; the caller keeps them
+ *   consistent). rope_mask: ATTN_ROPE_Q | ATTN_ROPE_K selects which of q and k
+ *   are rotated; with rope.rotary_dims == 0 or rope_mask == 0 nothing turns
+ *   and rope_table may be NULL.
+ *   window: <= 0 or >= T gives full causal attention; otherwise query i sees
+ *   keys j with i - window < j <= i (the window includes the query itself).
+ *   scale: finite (1/sqrt(Dk) in the usual model).
+ * Supported: B, T >= 0 (an empty problem is a no-op), Hq % Hkv == 0,
+ *   Dk, Dv even and <= 512. bf16 with (Dk, Dv) in {(128,128), (256,256),
+ *   (512,256)}, Hq/Hkv in {1, 2, 4, 8}, scale >= 0 and rotary_dims a multiple
+ *   of 8 in {0, Dk/4, Dk} runs the MFMA flash kernel; every other supported
+ *   case runs a slower general kernel with the same results.
+ * All tensor pointers must be 16-byte aligned.
+ */
+attn_status_t attn_prefill(const void *q, const void *k, const void *v, void *o,
+                           int32_t B, int32_t T, int32_t Hq, int32_t Hkv,
+                           int32_t Dk, int32_t Dv, int32_t window, float scale,
+                           attn_rope_t rope, int32_t rope_mask,
+                           const void *rope_table, attn_dtype_t dtype,
+                           void *stream);
+
+/*
+ * Decode: one new token per sequence over a ragged KV cache (bf16 only).
+ *   q [B, Hq, Dk]: the new tokens' queries, unrotated; sequence b's query sits
+ *     at position kv_len[b] - 1 and is rotated there (rope applies to q only).
+ *   k_cache [rows, Hkv, Dk], v_cache [rows, Hkv, Dv]: cached keys (stored
+ *     already rotated) and values; sequence b owns rows
+ *     row_offset[b] .. row_offset[b] + kv_len[b] - 1, the last one being the
+ *     new token's own row (the caller appends it before the call).
+ *   row_offset: device int64 [B]; kv_len: device int32 [B], 0 <= kv_len[b] <=
+ *     max_kv_len. kv_len[b] == 0 gives o[b] = 0.
+ *   window: <= 0: all rows; otherwise only the last `window` rows
+ *     [kv_len - window, kv_len) are read (rows before are never touched, so
+ *     they may hold anything).
+ *   o [B, Hq, Dv] output.
+ * Supported: Hq % Hkv == 0 with Hq / Hkv <= 16, Dk in {128, 256, 512},
+ *   Dv in {128, 256}; max_kv_len >= 1.
+ * Workspace: attn_decode_workspace_bytes() bytes of device memory for the
+ *   split-K partial results; contents are scratch.
+ */
+size_t attn_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t Dv,
+                                   int32_t max_kv_len, int32_t window);
+
+attn_status_t attn_decode(const void *q, const void *k_cache, const void *v_cache,
+                          const int64_t *row_offset, const int32_t *kv_len,
+                          void *o, int32_t B, int32_t Hq, int32_t Hkv,
+                          int32_t Dk, int32_t Dv, int32_t window, float scale,
+                          attn_rope_t rope, int32_t max_kv_len, void *workspace,
+                          size_t workspace_bytes, attn_dtype_t dtype,
+                          void *stream);
+
+/*
+ * (p-)RoPE on its own: y[n, h, :] = rope(x[n, h, :], positions[n]).
+ *   x, y [N, H, D]; positions: device int32 [N], each >= 0.
+ *   y may equal x (in place: dims >= rotary_dims are then not touched);
+ *   partial overlap is rejected. D even, 2 <= D <= 1024.
+ */
+attn_status_t prope_apply(const void *x, void *y, const int32_t *positions,
+                          int32_t N, int32_t H, int32_t D, attn_rope_t rope,
+                          attn_dtype_t dtype, void *stream);
+
+/* Static text for a status code. */
+const char *attn_status_string(attn_status_t s);
+
+/* Detail of the last non-OK status returned on this host thread ("" if none). */
+const char *attn_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_ROPE_H */

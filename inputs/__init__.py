@@ -146,9 +146,9 @@ def decode_inputs(c: DecodeCase, seed: int, device="cpu", kv_len=None,
         row_offset[1:] = torch.cumsum(lens, 0)[:-1]
     rows = int(lens.sum())
     q = normal((c.n_seq, c.Hq, c.Dk), seed, STREAM_Q, c.dtype, device)
-    kc = torch.empty((rows, c.Hkv, c.Dk), dtype=c.dtype, device=device)
-    vc = torch.empty((rows, c.Hkv, c.Dv), dtype=c.dtype, device=device)
     if c.window > 0 and poison_outside_window:
+        kc = torch.empty((rows, c.Hkv, c.Dk), dtype=c.dtype, device=device)
+        vc = torch.empty((rows, c.Hkv, c.Dv), dtype=c.dtype, device=device)
         kc.fill_(float("nan"))
         vc.fill_(float("nan"))
         # Draw only the visible rows of each sequence, one sequence at a time
@@ -162,8 +162,8 @@ def decode_inputs(c: DecodeCase, seed: int, device="cpu", kv_len=None,
             vc[off + lo: off + n] = normal((n - lo, c.Hkv, c.Dv), seed,
                                            2001 + 2 * b, c.dtype, device)
     else:
-        kc.copy_(normal((rows, c.Hkv, c.Dk), seed, STREAM_K, c.dtype, device))
-        vc.copy_(normal((rows, c.Hkv, c.Dv), seed, STREAM_V, c.dtype, device))
+        kc = normal((rows, c.Hkv, c.Dk), seed, STREAM_K, c.dtype, device)
+        vc = normal((rows, c.Hkv, c.Dv), seed, STREAM_V, c.dtype, device)
     return q, kc, vc, row_offset, kv_len
 
 

@@ -1,0 +1,137 @@
+"""Host-side checks of the C ABI (no GPU needed, no compute calls).
+
+The library must load, export every symbol include/attn_rope.h declares, and
+reject invalid arguments with the right status before any HIP call.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import attention_rope_amd as ar
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HDR = os.path.join(ROOT, "include", "attn_rope.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(ar.LIB_PATH):
+        from attention_rope_amd import _build
+        _build.build()
+    return ar.load()
+
+
+def _declared():
+    text = open(HDR).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"\b([a-z_][a-z0-9_]*)\s*\(", text)
+    return sorted({n for n in names if n.startswith(("attn_", "prope_"))})
+
+
+def test_header_symbols_exported(lib):
+    names = _declared()
+    assert set(names) == set(ar.EXPORTS)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings(lib):
+    for s, text in ar.STATUS.items():
+        assert lib.attn_status_string(s).decode() == text
+    assert lib.attn_status_string(99).decode() == "unknown status"
+
+
+R = ar._Rope
+P = ctypes.c_void_p
+FAKE = P(0x10000)      # never dereferenced: every call below fails validation
+FAKE2 = P(0x20000000)
+
+
+def _prefill(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE2, B=1, T=8, Hq=4, Hkv=2, Dk=64, Dv=64,
+             window=0, scale=0.125, rope=R(0, 1e4), rope_mask=3, tab=None,
+             dtype=ar.ATTN_BF16, stream=None)
+    a.update(kw)
+    return lib.attn_prefill(a["q"], a["k"], a["v"], a["o"], a["B"], a["T"], a["Hq"],
+                            a["Hkv"], a["Dk"], a["Dv"], a["window"], a["scale"], a["rope"],
+                            a["rope_mask"], a["tab"], a["dtype"], a["stream"])
+
+
+def test_prefill_validation(lib):
+    assert _prefill(lib, q=None) == 1
+    assert _prefill(lib, Hq=3, Hkv=2) == 2
+    assert _prefill(lib, Dk=63) == 2
+    assert _prefill(lib, Dk=1024) == 2
+    assert _prefill(lib, scale=float("nan")) == 2
+    assert _prefill(lib, rope=R(3, 1e4)) == 2
+    assert _prefill(lib, rope=R(66, 1e4)) == 2
+    assert _prefill(lib, rope=R(32, -1.0)) == 2
+    assert _prefill(lib, rope_mask=4) == 2
+    assert _prefill(lib, dtype=7) == 3
+    assert _prefill(lib, o=FAKE) == 6                 # o aliases q
+    assert _prefill(lib, q=P(0x10001)) == 2          # misaligned
+    # a rotation needs its cos/sin table
+    assert _prefill(lib, rope=R(32, 1e4)) == 1
+    assert b"rope_table" in lib.attn_last_error()
+    assert _prefill(lib, rope=R(32, 1e4), tab=P(0x30000008)) == 2   # misaligned table
+    # empty problems are a no-op success, even with NULL pointers
+    assert _prefill(lib, q=None, k=None, v=None, o=None, T=0) == 0
+    assert lib.attn_last_error() == b""
+
+
+def test_rope_table_validation(lib):
+    assert lib.attn_rope_table_bytes(100, 0) == 0
+    assert lib.attn_rope_table_bytes(32768, 128) == 32768 * 64 * 8
+    assert lib.attn_rope_table(None, 8, 0, 64, R(32, 1e4), None) == 1
+    assert lib.attn_rope_table(FAKE, 8, -1, 64, R(32, 1e4), None) == 2
+    assert lib.attn_rope_table(FAKE, 8, 2**31 - 4, 64, R(32, 1e4), None) == 2
+    assert lib.attn_rope_table(FAKE, 8, 0, 64, R(66, 1e4), None) == 2
+    assert lib.attn_rope_table(FAKE, 8, 0, 63, R(32, 1e4), None) == 2
+    assert lib.attn_rope_table(None, 0, 0, 64, R(32, 1e4), None) == 0
+
+
+def _decode(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, off=FAKE, kvl=FAKE, o=FAKE2, B=2, Hq=8, Hkv=1,
+             Dk=128, Dv=128, window=0, scale=0.1, rope=R(32, 1e6), max_kv_len=100,
+             ws=P(0x40000000), ws_bytes=1 << 30, dtype=ar.ATTN_BF16, stream=None)
+    a.update(kw)
+    return lib.attn_decode(a["q"], a["k"], a["v"], a["off"], a["kvl"], a["o"], a["B"],
+                           a["Hq"], a["Hkv"], a["Dk"], a["Dv"], a["window"], a["scale"],
+                           a["rope"], a["max_kv_len"], a["ws"], a["ws_bytes"], a["dtype"],
+                           a["stream"])
+
+
+def test_decode_validation(lib):
+    assert _decode(lib, dtype=ar.ATTN_F32) == 3
+    assert _decode(lib, kvl=None) == 1
+    assert _decode(lib, Dk=64) == 3
+    assert _decode(lib, Hq=34, Hkv=2) == 3          # 17 heads per KV head
+    assert _decode(lib, Hq=7, Hkv=2) == 2
+    assert _decode(lib, max_kv_len=0) == 2
+    assert _decode(lib, scale=-1.0) == 3
+    assert _decode(lib, ws_bytes=16) == 4
+    assert _decode(lib, ws=None) == 4
+    assert _decode(lib, o=FAKE) == 6
+    assert _decode(lib, B=0, q=None) == 0
+
+
+def test_decode_workspace_bytes(lib):
+    # global: chunks of 1024 rows; local: chunks of 256 rows within the window
+    assert lib.attn_decode_workspace_bytes(64, 32, 256, 131073, 0) == 64 * 32 * 129 * 258 * 4
+    assert lib.attn_decode_workspace_bytes(64, 16, 256, 131073, 1024) == 64 * 16 * 4 * 258 * 4
+    assert lib.attn_decode_workspace_bytes(0, 16, 256, 10, 0) == 0
+
+
+def test_prope_validation(lib):
+    f = lambda **kw: lib.prope_apply(kw.get("x", FAKE), kw.get("y", FAKE2),
+                                     kw.get("pos", FAKE), kw.get("N", 4), kw.get("H", 2),
+                                     kw.get("D", 64), kw.get("rope", R(16, 1e4)),
+                                     kw.get("dtype", ar.ATTN_BF16), None)
+    assert f(x=None) == 1
+    assert f(D=63) == 2
+    assert f(rope=R(80, 1e4)) == 2
+    assert f(y=P(0x10000 + 64)) == 6                 # partial overlap
+    assert f(dtype=5) == 3
+    assert f(N=0) == 0

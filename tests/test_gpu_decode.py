@@ -1,0 +1,87 @@
+"""attn_decode (HIP) vs the fp64 oracle on ragged caches."""
+import numpy as np
+import pytest
+import torch
+
+import inputs
+import oracle
+from parity import assert_close, to64
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+BF = torch.bfloat16
+
+
+def run(ar, Hq, Hkv, Dk, Dv, W, R, theta, lens, seed=3, poison=True):
+    c = inputs.DecodeCase(len(lens), Hq, Hkv, Dk, Dv, window=W, rotary_dims=R, theta=theta,
+                          len_lo=1, len_hi=1)
+    kvl = torch.tensor(lens, dtype=torch.int32)
+    print(f"decode Hq={Hq} Hkv={Hkv} Dk={Dk} Dv={Dv} W={W} lens={lens}", flush=True)
+    q, kc, vc, off, kvl = inputs.decode_inputs(c, seed, device=DEV, kv_len=kvl,
+                                              poison_outside_window=poison)
+    o = ar.decode(q, kc, vc, off.to(DEV), kvl.to(DEV), window=W, scale=c.scale,
+                  rotary_dims=R, theta=theta, max_kv_len=max(1, max(lens)))
+    torch.cuda.synchronize()
+    ref = oracle.decode(q.cpu(), kc.cpu(), vc.cpu(), off, kvl, window=W, scale=c.scale,
+                        rotary_dims=R, theta=theta)
+    assert_close(o, ref, BF, "decode")
+    return o
+
+
+LENS = [1, 2, 31, 32, 33, 127, 128, 129, 1023, 1024, 1025, 3000, 5000]
+
+
+def test_decode_global(gpu_lib):
+    run(gpu_lib, 32, 4, 512, 256, 0, 128, 1e6, LENS)
+
+
+def test_decode_local_window(gpu_lib):
+    # rows outside the window are NaN: reading any would poison the output
+    run(gpu_lib, 16, 8, 256, 256, 1024, 256, 1e4, LENS)
+    run(gpu_lib, 16, 8, 256, 256, 100, 256, 1e4, [1, 50, 99, 100, 101, 700])
+
+
+@pytest.mark.parametrize("Hq,Hkv,Dk,Dv,R", [(8, 1, 128, 128, 32), (4, 4, 256, 128, 0),
+                                            (16, 1, 512, 256, 512), (6, 2, 128, 256, 128)])
+def test_decode_shapes(gpu_lib, Hq, Hkv, Dk, Dv, R):
+    run(gpu_lib, Hq, Hkv, Dk, Dv, 0, R, 1e4, [5, 64, 700, 2049])
+
+
+def test_decode_empty_sequence_is_zero(gpu_lib):
+    o = run(gpu_lib, 32, 4, 512, 256, 0, 128, 1e6, [0, 10, 0, 300])
+    assert torch.all(o[0] == 0) and torch.all(o[2] == 0)
+
+
+def test_decode_equals_last_prefill_row(gpu_lib):
+    """Decode over a cache whose keys were rotated by prope_apply equals the
+    last row of a prefill over the same tokens (both on the GPU)."""
+    T, Hq, Hkv, Dk, Dv, R, th = 700, 32, 4, 512, 256, 128, 1e6
+    c = inputs.PrefillCase(1, T, Hq, Hkv, Dk, Dv, window=0, rotary_dims=R, theta=th, dtype=BF)
+    q, k, v = inputs.prefill_inputs(c, 12, device=DEV)
+    o_pre = gpu_lib.prefill(q, k, v, window=0, scale=c.scale, rotary_dims=R, theta=th)
+    pos = torch.arange(T, dtype=torch.int32, device=DEV)
+    k_rot = gpu_lib.prope(k[0], pos, rotary_dims=R, theta=th)
+    o_dec = gpu_lib.decode(q[:, T - 1].contiguous(), k_rot, v[0].contiguous(),
+                           torch.zeros(1, dtype=torch.int64, device=DEV),
+                           torch.full((1,), T, dtype=torch.int32, device=DEV),
+                           window=0, scale=c.scale, rotary_dims=R, theta=th, max_kv_len=T)
+    torch.cuda.synchronize()
+    d = np.abs(to64(o_dec[0]) - to64(o_pre[0, T - 1]))
+    assert d.max() < 2e-2
+
+
+def test_decode_kv_len_over_max_is_poisoned(gpu_lib):
+    c = inputs.DecodeCase(2, 8, 1, 128, 128, window=0, rotary_dims=0, theta=1e4,
+                          len_lo=1, len_hi=1)
+    q, kc, vc, off, kvl = inputs.decode_inputs(c, 1, device=DEV,
+                                              kv_len=torch.tensor([10, 20], dtype=torch.int32))
+    o = gpu_lib.decode(q, kc, vc, off.to(DEV), kvl.to(DEV), max_kv_len=15)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o[0].float()).all()
+    assert torch.isnan(o[1].float()).all()
+
+
+def test_decode_deterministic(gpu_lib):
+    a = run(gpu_lib, 32, 4, 512, 256, 0, 128, 1e6, [4000, 17], seed=9)
+    b = run(gpu_lib, 32, 4, 512, 256, 0, 128, 1e6, [4000, 17], seed=9)
+    assert torch.equal(a, b)
