@@ -13,24 +13,31 @@
 // before the P.V product, and everything accumulates in fp32.
 //
 // Design for CDNA4:
-//  * A workgroup owns one (batch, KV head) and PW consecutive query positions
-//    for all G query heads that share the KV head: NW*32 (head, position)
-//    rows, so each K/V tile staged in LDS serves G heads (GQA packing).
-//  * Each wavefront owns 32 rows and computes S^T = K Q^T (M = 32 keys,
-//    N = 32 rows): in the MFMA output layout every lane then holds 16 scores
-//    of a single query row, so the softmax max/sum need one cross-lane swap
-//    (lane ^ 32) instead of a 32-lane reduction. Q^T lives in registers for
-//    the whole kernel; K tiles stream through LDS.
-//  * O^T = V^T P^T accumulates in registers (every lane again owns one row).
-//    The P^T operand is the lane's own scores — no data movement — provided
-//    the key order inside each 16-key MFMA step matches the score layout; V^T
-//    is staged in LDS in exactly that permuted key order.
-//  * Key tiles of 32 are double-buffered in LDS; the next tile's global loads
-//    are issued before the current tile's matrix work.
+//  * A workgroup (4 waves, one per SIMD) owns one (batch, KV head) and PW
+//    consecutive query positions for all G query heads sharing that KV head:
+//    128 (head, position) rows, so each staged K/V tile serves G heads.
+//  * Each wave owns 32 rows and computes S^T = K Q^T (M = 32 keys, N = 32
+//    rows): in the MFMA output layout every lane holds 16 scores of one query
+//    row, so the softmax needs a single cross-lane swap (lane ^ 32). Q^T stays
+//    in registers for the whole kernel.
+//  * O^T = V^T P^T: the P^T operand is the lane's own scores when the key
+//    order inside each 16-key MFMA step matches the score layout; V tiles are
+//    written to LDS transposed, in exactly that key order.
+//  * K tiles (32 keys) move HBM -> LDS by direct DMA (buffer loads with the
+//    lds flag): no staging registers, out-of-range rows read as zero. The
+//    rotated chunks of each K row sit in their own LDS region, so every thread
+//    turns exactly the chunks its own DMA wrote (no extra barrier, all lanes
+//    busy), with cos/sin from the per-position table prefetched one tile
+//    ahead. Tiles are double-buffered; the next tile's loads overlap the
+//    current tile's matrix work.
+//  * K rows are XOR-swizzled in 16-byte chunks so the MFMA operand reads are
+//    bank-conflict free without the padding the 1 KB DMA blocks cannot have.
 //  * Only key tiles intersecting the causal band / sliding window are visited
-//    (window-aware skipping), and masking runs only on tiles that cross the
+//    (window-aware skipping); masking runs only on tiles that cross the
 //    diagonal or the window edge.
-//  * The O accumulator is rescaled only when some row's running max changed.
+//  * The running max is updated lazily: O is rescaled only when a row's block
+//    max exceeds the max in use by more than 2^8 (probabilities stay <= 256,
+//    exact after the final division).
 //  * Causal tiles are issued longest-first; sliding-window launches map
 //    neighbouring query tiles onto the same XCD so their K/V windows share L2.
 #include "attn_common.h"
@@ -40,29 +47,77 @@ namespace attn {
 namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLazy = 8.0f;  // log2 headroom before the running max moves
+constexpr int NW = 4;          // waves per workgroup
+constexpr int NT = NW * 64;
+constexpr int BN = 32;         // keys per tile
+// Buffer descriptor word 3 for raw (stride 0) 32-bit-format buffers on gfx9.
+constexpr int kBufFlags = 0x00020000;
 
-template <int DK, int DV, int G, int NW, int RK>
+typedef __attribute__((address_space(3))) void lds_void;
+
+template <int DK, int DV, int G, int RCH>
 struct Cfg {
-  static constexpr int NT = NW * 64;        // threads
-  static constexpr int ROWS = NW * 32;      // (head, position) rows per WG
-  static constexpr int PW = ROWS / G;       // query positions per WG
-  static constexpr int BN = 32;             // keys per tile
-  static constexpr int KS = DK + 8;         // K row stride in LDS (elements)
-  static constexpr int VS = BN + 8;         // V^T row stride in LDS (elements)
-  static constexpr int KT = BN * KS;
-  static constexpr int VT = DV * VS;
-  static constexpr int STAGE = KT + VT;     // elements per LDS stage
-  static constexpr int NC = DK / 8;         // 16-byte chunks per K row
-  static constexpr int KCH = BN * NC / NT;  // K chunks per thread per tile
-  static constexpr int NRC = BN * RK;       // rotated K chunks per tile
-  static constexpr int KR = (NRC + NT - 1) / NT;  // iterations holding rotated chunks
-  static constexpr int VU = (BN / 4) * (DV / 8);  // V units: 4 keys x 8 dims
+  static constexpr int ROWS = NW * 32;        // (head, position) rows per WG
+  static constexpr int PW = ROWS / G;         // query positions per WG
+  static constexpr int NC = DK / 8;           // 16-byte chunks per K row
+  static constexpr int NP = NC - RCH;         // plain (unrotated) chunks per K row
+  // K tile: rotated region [32][RCH] chunks, then plain region [32][NP].
+  static constexpr int KR_BYTES = BN * RCH * 16;
+  static constexpr int KT_BYTES = BN * NC * 16;
+  static constexpr int KR_DMA = KR_BYTES / 1024;   // 1 KB DMA blocks per region
+  static constexpr int KP_DMA = (KT_BYTES - KR_BYTES) / 1024;
+  // V^T tile: [DV][VS] bf16, keys in the permuted order of the score layout.
+  static constexpr int VS = BN + 8;           // padded row (80 bytes)
+  static constexpr int VT_BYTES = DV * VS * 2;
+  static constexpr int STAGE = KT_BYTES + VT_BYTES;
+  static constexpr int VU = (BN / 4) * (DV / 8);   // V units: 4 keys x 8 dims
   static constexpr int VUT = (VU + NT - 1) / NT;
+  static constexpr int KROT = (KR_DMA + NW - 1) / NW;  // rotated blocks per wave
   static_assert(ROWS % G == 0, "rows must split evenly over the heads");
   static_assert(PW >= 32 ? PW % 32 == 0 : 32 % PW == 0, "wave/row layout");
-  static_assert((BN * NC) % NT == 0, "K tile must split evenly");
+  static_assert(KR_BYTES % 1024 == 0 && KT_BYTES % 1024 == 0, "DMA blocks");
   static_assert(DK % 16 == 0 && DV % 32 == 0, "MFMA tiling");
-  static_assert(RK >= 0 && RK <= NC, "rotary chunks");
+};
+
+// XOR swizzle of 16-byte chunks inside a K region row of `width` chunks. The
+// mask P-1 uses the largest power of two P <= 16 dividing the width, so the
+// swizzled index stays inside the row; with P = 16, 16 consecutive rows
+// reading the same chunk hit 16 distinct bank groups.
+template <int width>
+struct Swz {
+  static constexpr int P = (width & 15) == 0 ? 16 : (width & 7) == 0 ? 8 : (width & 3) == 0 ? 4
+                           : (width & 1) == 0 ? 2 : 1;
+  static constexpr int M = P - 1;
+};
+template <int width>
+__device__ __forceinline__ int kswz(int r, int c) {
+  return c ^ (r & Swz<width>::M);
+}
+
+// Byte offset of chunk c (0..NC-1) of K row r inside a K tile.
+template <int NC, int RCH>
+__device__ __forceinline__ int k_off(int r, int c) {
+  if (c < RCH) return (r * RCH + kswz<RCH>(r, c)) * 16;
+  return BN * RCH * 16 + (r * (NC - RCH) + kswz<NC - RCH>(r, c - RCH)) * 16;
+}
+
+// Per-lane addressing of the K operand reads (row r, chunk 2k + h for
+// k = 0, 1, ...) inside a region of `width` chunks starting at byte `base`:
+// the offset is row_base + ((k & H) << 5 ^ x1s) + ((k & ~H) << 5) with
+// H = P/2 - 1, so one XOR with a per-lane constant and an immediate remain.
+template <int width>
+struct KAddr {
+  int row_base, x1s;
+  __device__ __forceinline__ KAddr(int base, int r, int h) {
+    const int x = r & Swz<width>::M;
+    row_base = base + r * width * 16 + ((h ^ (x & 1)) << 4);
+    x1s = (x >> 1) << 5;
+  }
+  __device__ __forceinline__ int operator()(int k) const {
+    constexpr int H = Swz<width>::P / 2 - 1;
+    return row_base + (((k & H) << 5) ^ x1s) + ((k & ~H) << 5);
+  }
 };
 
 __device__ __forceinline__ uint32_t rot_pair(uint32_t w, float c, float s) {
@@ -80,13 +135,16 @@ __device__ __forceinline__ u32x4 rotate4(u32x4 w, f32x4 t0, f32x4 t1) {
   return r;
 }
 
-template <int DK, int DV, int G, int NW, int RK>
-__global__ __launch_bounds__(NW * 64) void prefill_mfma_kernel(PrefillArgs a, int n_qt,
-                                                               int contig) {
-  using C = Cfg<DK, DV, G, NW, RK>;
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * C::STAGE];
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+template <int DK, int DV, int G, int RCH>
+__global__ __launch_bounds__(NT) void prefill_mfma_kernel(PrefillArgs a, int n_qt,
+                                                          int contig) {
+  using C = Cfg<DK, DV, G, RCH>;
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[2 * C::STAGE];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lr = lane & 31, hh = lane >> 5;
   const int T = a.T, W = a.window;
   const int n_wg = n_qt * a.Hkv * a.B;
@@ -104,103 +162,94 @@ __global__ __launch_bounds__(NW * 64) void prefill_mfma_kernel(PrefillArgs a, in
   const int wlo = p0 + (wave * 32) % C::PW;
   const int whi = wlo + (C::PW < 32 ? C::PW : 32) - 1;
 
-  // ---- Q^T operands in registers, rotated at the row's position ----------
-  bf16x8 qf[DK / 16];
-  {
-    const int prow = valid ? pos : T - 1;
-    const uint16_t* qrow =
-        (const uint16_t*)a.q + (((int64_t)b * T + prow) * a.Hq + head) * DK;
-    const float2* tab = a.rope_tab + (int64_t)prow * a.rot_pairs;
-#pragma unroll
-    for (int s = 0; s < DK / 16; ++s) {
-      const int d0 = 16 * s + 8 * hh;
-      u32x4 w = *(const u32x4*)(qrow + d0);
-      if (a.rope_q && d0 < 2 * a.rot_pairs) {
-        const f32x4 t0 = *(const f32x4*)(tab + d0 / 2);
-        const f32x4 t1 = *(const f32x4*)(tab + d0 / 2 + 2);
-        w = rotate4(w, t0, t1);
-      }
-      if (!valid) w = u32x4{0, 0, 0, 0};
-      qf[s] = __builtin_bit_cast(bf16x8, w);
-    }
-  }
-
   const int kv_lo = (W > 0) ? max(0, p0 - W + 1) : 0;
   const int kv_hi = min(T, p0 + C::PW);
-  const int kb_lo = kv_lo / C::BN;
-  const int kb_hi = (kv_hi + C::BN - 1) / C::BN;
+  const int kb_lo = kv_lo / BN;
+  const int kb_hi = (kv_hi + BN - 1) / BN;
 
-  const uint16_t* kbase = (const uint16_t*)a.k + ((int64_t)b * T * a.Hkv + kvh) * DK;
-  const uint16_t* vbase = (const uint16_t*)a.v + ((int64_t)b * T * a.Hkv + kvh) * DV;
-  const int64_t krs = (int64_t)a.Hkv * DK, vrs = (int64_t)a.Hkv * DV;
+  // Buffer descriptors: K and V of this (batch, KV head); rows past T read 0.
+  const int krow = a.Hkv * DK * 2, vrow = a.Hkv * DV * 2;  // bytes per token
+  const __amdgpu_buffer_rsrc_t kres = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)((const char*)a.k + ((int64_t)b * T * a.Hkv + kvh) * DK * 2), (short)0,
+      (T - 1) * krow + DK * 2, kBufFlags);
+  const __amdgpu_buffer_rsrc_t vres = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)((const char*)a.v + ((int64_t)b * T * a.Hkv + kvh) * DV * 2), (short)0,
+      (T - 1) * vrow + DV * 2, kBufFlags);
+  const bool rot_k = RCH > 0 && a.rope_k;
+  const bool rot_q = RCH > 0 && a.rope_q;
+  const int tab_row = a.rot_pairs * 8;  // bytes per table row
+  const __amdgpu_buffer_rsrc_t tres = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)a.rope_tab, (short)0, (RCH > 0 && (rot_k || rot_q)) ? T * tab_row : 0, kBufFlags);
 
-  // ---- staging registers --------------------------------------------------
-  u32x4 kreg[C::KCH];
-  f32x4 ktab[C::KR > 0 ? C::KR : 1][2];
-  u32x4 vreg[C::VUT][4];
-
-  auto chunk_of = [&](int it, int& row, int& col8) {
-    const int c = tid + C::NT * it;
-    if (RK > 0 && c < C::NRC) {
-      row = c / (RK > 0 ? RK : 1);
-      col8 = c % (RK > 0 ? RK : 1);
-    } else {
-      constexpr int NP = (C::NC - RK > 0) ? C::NC - RK : 1;  // plain chunks per row
-      const int c2 = c - C::NRC;
-      row = c2 / NP;
-      col8 = RK + c2 % NP;
-    }
+  // ---- K: DMA into LDS; this thread turns the rotated chunks it loaded -----
+  // Rotated-region block n (n = wave, wave + NW, ...): lane -> chunk q.
+  f32x4 ktab[C::KROT > 0 ? C::KROT : 1][2];
+  auto rot_chunk = [&](int i, int& r, int& c) {
+    const int q = (i * NW + wave) * 64 + lane;
+    r = q / (RCH > 0 ? RCH : 1);
+    c = kswz<RCH>(r, q % (RCH > 0 ? RCH : 1));  // swizzle is an involution
   };
-
-  auto load_tile = [&](int kb) {
-    const int j0 = kb * C::BN;
+  auto dma_k = [&](int kb, unsigned char* st) {
+    const int j0 = kb * BN;
 #pragma unroll
-    for (int it = 0; it < C::KCH; ++it) {
-      int row, col8;
-      chunk_of(it, row, col8);
-      const int j = j0 + row;
-      kreg[it] = (j < T) ? *(const u32x4*)(kbase + j * krs + col8 * 8) : u32x4{0, 0, 0, 0};
-      if (it < C::KR) {
-        const int c = tid + C::NT * it;
-        if (c < C::NRC && j < T) {
-          const float2* t = a.rope_tab + (int64_t)j * a.rot_pairs + 4 * col8;
-          ktab[it][0] = *(const f32x4*)t;
-          ktab[it][1] = *(const f32x4*)(t + 2);
-        } else {
-          ktab[it][0] = f32x4{1.f, 0.f, 1.f, 0.f};
-          ktab[it][1] = f32x4{1.f, 0.f, 1.f, 0.f};
+    for (int i = 0; i < C::KROT; ++i) {
+      if (C::KR_DMA % NW == 0 || i * NW + wave < C::KR_DMA) {
+        int r, c;
+        rot_chunk(i, r, c);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(kres, (lds_void*)(st + (i * NW + wave) * 1024),
+                                                 16, (j0 + r) * krow + c * 16, 0, 0, 0);
+        if (rot_k) {
+          const int off = min(j0 + r, T - 1) * tab_row + c * 32;
+          ktab[i][0] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(tres, off, 0, 0));
+          ktab[i][1] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(tres, off + 16, 0, 0));
         }
       }
     }
 #pragma unroll
-    for (int ut = 0; ut < C::VUT; ++ut) {
-      const int u = tid + C::NT * ut;
-      const int kg = u % 8, d8 = u / 8;
+    for (int i = 0; i < (C::KP_DMA + NW - 1) / NW; ++i) {
+      const int n = i * NW + wave;
+      if (C::KP_DMA % NW == 0 || n < C::KP_DMA) {
+        const int q = n * 64 + lane;
+        const int r = q / C::NP;
+        const int c = RCH + kswz<C::NP>(r, q % C::NP);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            kres, (lds_void*)(st + C::KR_BYTES + n * 1024), 16, (j0 + r) * krow + c * 16, 0, 0,
+            0);
+      }
+    }
+  };
+  auto rotate_k = [&](unsigned char* st) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int j = j0 + 4 * kg + e;
-        vreg[ut][e] = (u < C::VU && j < T) ? *(const u32x4*)(vbase + j * vrs + d8 * 8)
-                                          : u32x4{0, 0, 0, 0};
+    for (int i = 0; i < C::KROT; ++i) {
+      if (C::KR_DMA % NW == 0 || i * NW + wave < C::KR_DMA) {
+        u32x4* p = (u32x4*)(st + ((i * NW + wave) * 64 + lane) * 16);
+        *p = rotate4(*p, ktab[i][0], ktab[i][1]);
       }
     }
   };
 
-  auto store_tile = [&](uint16_t* Ks, uint16_t* Vt) {
-#pragma unroll
-    for (int it = 0; it < C::KCH; ++it) {
-      int row, col8;
-      chunk_of(it, row, col8);
-      u32x4 w = kreg[it];
-      if (it < C::KR) {
-        const int c = tid + C::NT * it;
-        if (c < C::NRC) w = rotate4(w, ktab[it][0], ktab[it][1]);
-      }
-      *(u32x4*)(Ks + row * C::KS + col8 * 8) = w;
-    }
+  // ---- V: registers, then LDS transposed in the score-matched key order ----
+  u32x4 vreg[C::VUT][4];
+  auto load_v = [&](int kb) {
+    const int j0 = kb * BN;
 #pragma unroll
     for (int ut = 0; ut < C::VUT; ++ut) {
-      const int u = tid + C::NT * ut;
-      if (u < C::VU) {
+      const int u = tid + NT * ut;
+      const int kg = u % 8, d8 = u / 8;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        vreg[ut][e] = (C::VU % NT == 0 || u < C::VU)
+                          ? __builtin_amdgcn_raw_buffer_load_b128(vres, (j0 + 4 * kg + e) * vrow + d8 * 16, 0, 0)
+                          : u32x4{0, 0, 0, 0};
+      }
+    }
+  };
+  auto store_v = [&](unsigned char* st) {
+    uint16_t* Vt = (uint16_t*)(st + C::KT_BYTES);
+#pragma unroll
+    for (int ut = 0; ut < C::VUT; ++ut) {
+      const int u = tid + NT * ut;
+      if (C::VU % NT == 0 || u < C::VU) {
         const int kg = u % 8, d8 = u / 8;
         // keys 4kg..4kg+3 occupy 4 consecutive slots of the permuted key order
         const int slot = 16 * (kg / 4) + 8 * (kg % 2) + 4 * ((kg % 4) / 2);
@@ -221,93 +270,144 @@ __global__ __launch_bounds__(NW * 64) void prefill_mfma_kernel(PrefillArgs a, in
     }
   };
 
+  // ---- prologue: first tile's loads and the Q rows, all in flight ---------
+  if (kb_lo < kb_hi) {
+    dma_k(kb_lo, lds);
+    load_v(kb_lo);
+  }
+  bf16x8 qf[DK / 16];
+  {
+    const int prow = valid ? pos : T - 1;
+    const uint16_t* qrow =
+        (const uint16_t*)a.q + (((int64_t)b * T + prow) * a.Hq + head) * DK + 8 * hh;
+    u32x4 qw[DK / 16];
+#pragma unroll
+    for (int s = 0; s < DK / 16; ++s) qw[s] = *(const u32x4*)(qrow + 16 * s);
+    if (rot_q) {
+      // rotated chunks: s < RCH/2 for both halves (16s + 8hh < 8*RCH)
+#pragma unroll
+      for (int s0 = 0; s0 < RCH / 2; s0 += 4) {
+        f32x4 t[4][2];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int off = prow * tab_row + (16 * (s0 + u) + 8 * hh) * 4;
+          t[u][0] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(tres, off, 0, 0));
+          t[u][1] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(tres, off + 16, 0, 0));
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          if (s0 + u < RCH / 2) qw[s0 + u] = rotate4(qw[s0 + u], t[u][0], t[u][1]);
+      }
+    }
+#pragma unroll
+    for (int s = 0; s < DK / 16; ++s) {
+      u32x4 w = valid ? qw[s] : u32x4{0, 0, 0, 0};
+      qf[s] = __builtin_bit_cast(bf16x8, w);
+    }
+  }
+  if (kb_lo < kb_hi) {
+    __builtin_amdgcn_s_waitcnt(0);  // own DMA landed, V and table in registers
+    if (rot_k) rotate_k(lds);
+    store_v(lds);
+    __syncthreads();
+  }
+
   // ---- online softmax state (one row per lane; halves share the row) -------
   const float c2 = a.scale * kLog2e;  // scores to log2 units (>= 0)
+  const unsigned wcap = (W > 0) ? (unsigned)W : 0x80000000u;
   float m_run = -INFINITY, l_run = 0.f;
   f32x16 oacc[DV / 32];
 #pragma unroll
   for (int d = 0; d < DV / 32; ++d) oacc[d] = f32x16{};
 
-  auto compute = [&](const uint16_t* Ks, const uint16_t* Vt, int kb) {
-    const int j0 = kb * C::BN;
-    if (j0 > whi) return;                          // beyond every row (causal)
-    if (W > 0 && j0 + C::BN - 1 <= wlo - W) return;  // before every row's window
+  const KAddr<(RCH > 0 ? RCH : 16)> kaddr_r(0, lr, hh);
+  const KAddr<(C::NP > 0 ? C::NP : 16)> kaddr_p(C::KR_BYTES, lr, hh);
+  auto compute = [&](const unsigned char* st, int kb) {
+    const int j0 = kb * BN;
+    if (j0 > whi) return;                            // beyond every row (causal)
+    if (W > 0 && j0 + BN - 1 <= wlo - W) return;     // before every row's window
     f32x16 s = f32x16{};
+    // chunks 2k + hh: k < RCH/2 in the rotated region, the rest in the plain one
 #pragma unroll
-    for (int st = 0; st < DK / 16; ++st) {
-      const bf16x8 ka = *(const bf16x8*)(Ks + lr * C::KS + 16 * st + 8 * hh);
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[st], s, 0, 0, 0);
+    for (int k = 0; k < RCH / 2; ++k) {
+      const bf16x8 ka = *(const bf16x8*)(st + kaddr_r(k));
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[k], s, 0, 0, 0);
+    }
+#pragma unroll
+    for (int k = RCH / 2; k < DK / 16; ++k) {
+      const bf16x8 ka = *(const bf16x8*)(st + kaddr_p(k - RCH / 2));
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[k], s, 0, 0, 0);
     }
     // lane holds keys j0 + 8(i/4) + 4hh + (i%4) of its row, i = 0..15
-    const bool need_mask = (j0 + C::BN - 1 > wlo) || (W > 0 && j0 <= whi - W);
-    uint32_t okbits = 0xffffu;
-    float mx = -INFINITY;
+    const bool need_mask = (j0 + BN - 1 > wlo) || (W > 0 && j0 <= whi - W);
     if (need_mask) {
-      okbits = 0;
+      const int d0 = pos - j0 - 4 * hh;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const int j = j0 + 8 * (i / 4) + 4 * hh + (i % 4);
-        const bool ok = (j <= pos) && (W <= 0 || pos - j < W);
-        okbits |= (ok ? 1u : 0u) << i;
-        mx = fmaxf(mx, ok ? s[i] : -INFINITY);
+        const unsigned d = (unsigned)(d0 - (8 * (i / 4) + (i % 4)));  // pos - key
+        s[i] = (d < wcap) ? s[i] : -INFINITY;
       }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[i]);
     }
+    float mx = s[0];
+#pragma unroll
+    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[i]);
     mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float mb = (mx == -INFINITY) ? -INFINITY : mx * c2;
-    const float m_new = fmaxf(m_run, mb);
-    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-    const float alpha = exp2f(m_run - m_use);
+    const float mc = (mx == -INFINITY) ? -INFINITY : mx * c2;
+    if (__any(mc > m_run + kLazy)) {
+      const float m_new = fmaxf(m_run, mc);
+      const float alpha = (m_run == -INFINITY) ? 0.f : fast_exp2(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int d = 0; d < DV / 32; ++d) oacc[d] *= alpha;
+      m_run = m_new;
+    }
+    const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
     float pv[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) pv[i] = fast_exp2(fmaf(s[i], c2, -m_use));
+    if (need_mask) {
+      // masked scores are -inf; with scale 0 the product above is NaN
+#pragma unroll
+      for (int i = 0; i < 16; ++i) pv[i] = (s[i] == -INFINITY) ? 0.f : pv[i];
+    }
     float psum = 0.f;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      float p = exp2f(fmaf(s[i], c2, -m_use));
-      if (need_mask) p = ((okbits >> i) & 1u) ? p : 0.f;
-      pv[i] = p;
-      psum += p;
-    }
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
-    if (__any(alpha != 1.f)) {
-#pragma unroll
-      for (int d = 0; d < DV / 32; ++d)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) oacc[d][i] *= alpha;
-    }
+    for (int i = 0; i < 16; ++i) psum += pv[i];
+    l_run += psum;
     f32x4 lo0 = {pv[0], pv[1], pv[2], pv[3]}, lo1 = {pv[4], pv[5], pv[6], pv[7]};
     f32x4 hi0 = {pv[8], pv[9], pv[10], pv[11]}, hi1 = {pv[12], pv[13], pv[14], pv[15]};
-    bf16x4 a0 = __builtin_convertvector(lo0, bf16x4), a1 = __builtin_convertvector(lo1, bf16x4);
-    bf16x4 b0 = __builtin_convertvector(hi0, bf16x4), b1 = __builtin_convertvector(hi1, bf16x4);
+    const bf16x4 a0 = __builtin_convertvector(lo0, bf16x4), a1 = __builtin_convertvector(lo1, bf16x4);
+    const bf16x4 b0 = __builtin_convertvector(hi0, bf16x4), b1 = __builtin_convertvector(hi1, bf16x4);
     const bf16x8 pb0 = __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7);
     const bf16x8 pb1 = __builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7);
+    const uint16_t* Vt = (const uint16_t*)(st + C::KT_BYTES);
 #pragma unroll
     for (int d = 0; d < DV / 32; ++d) {
-      const uint16_t* vrow = Vt + (32 * d + lr) * C::VS + 8 * hh;
-      const bf16x8 v0 = *(const bf16x8*)(vrow);
-      const bf16x8 v1 = *(const bf16x8*)(vrow + 16);
+      const uint16_t* vrow_p = Vt + (32 * d + lr) * C::VS + 8 * hh;
+      const bf16x8 v0 = *(const bf16x8*)(vrow_p);
+      const bf16x8 v1 = *(const bf16x8*)(vrow_p + 16);
       oacc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v0, pb0, oacc[d], 0, 0, 0);
       oacc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v1, pb1, oacc[d], 0, 0, 0);
     }
   };
 
   // ---- main loop: double-buffered key tiles -------------------------------
-  if (kb_lo < kb_hi) {
-    load_tile(kb_lo);
-    store_tile(lds, lds + C::KT);
-    __syncthreads();
-  }
   for (int kb = kb_lo; kb < kb_hi; ++kb) {
     const int cur = (kb - kb_lo) & 1;
-    uint16_t* cs = lds + cur * C::STAGE;
-    uint16_t* ns = lds + (cur ^ 1) * C::STAGE;
+    unsigned char* cs = lds + cur * C::STAGE;
+    unsigned char* ns = lds + (cur ^ 1) * C::STAGE;
     const bool more = kb + 1 < kb_hi;
-    if (more) load_tile(kb + 1);
-    compute(cs, cs + C::KT, kb);
-    if (more) store_tile(ns, ns + C::KT);
-    __syncthreads();
+    if (more) {
+      dma_k(kb + 1, ns);
+      load_v(kb + 1);
+    }
+    compute(cs, kb);
+    if (more) {
+      __builtin_amdgcn_s_waitcnt(0);  // own DMA landed, V and table in registers
+      if (rot_k) rotate_k(ns);
+      store_v(ns);
+    }
+    __syncthreads();  // next tile complete everywhere; current tile free
   }
 
   // ---- epilogue: O = O^T / l, bf16, 4 consecutive dims per store ----------
@@ -326,9 +426,9 @@ __global__ __launch_bounds__(NW * 64) void prefill_mfma_kernel(PrefillArgs a, in
   }
 }
 
-template <int DK, int DV, int G, int NW, int RK>
+template <int DK, int DV, int G, int RCH>
 hipError_t launch_one(const PrefillArgs& a, hipStream_t st) {
-  using C = Cfg<DK, DV, G, NW, RK>;
+  using C = Cfg<DK, DV, G, RCH>;
   const int n_qt = (a.T + C::PW - 1) / C::PW;
   const int64_t n = (int64_t)n_qt * a.Hkv * a.B;
   if (n == 0) return hipSuccess;
@@ -336,27 +436,27 @@ hipError_t launch_one(const PrefillArgs& a, hipStream_t st) {
   // Sliding-window tiles reuse their neighbours' K/V: keep neighbours on one
   // XCD. Causal tiles share the prefix of every key stream: interleave.
   const int contig = (a.window > 0 && a.window < a.T) ? 1 : 0;
-  hipLaunchKernelGGL((prefill_mfma_kernel<DK, DV, G, NW, RK>), dim3((unsigned)n),
-                     dim3(C::NT), 0, st, a, n_qt, contig);
+  hipLaunchKernelGGL((prefill_mfma_kernel<DK, DV, G, RCH>), dim3((unsigned)n), dim3(NT), 0,
+                     st, a, n_qt, contig);
   return hipGetLastError();
 }
 
 template <int DK, int DV, int G>
-hipError_t dispatch_rk(const PrefillArgs& a, hipStream_t st) {
-  const int rk = a.rope_k ? (2 * a.rot_pairs) / 8 : 0;
-  if (rk == 0) return launch_one<DK, DV, G, 4, 0>(a, st);
-  if (rk == DK / 32) return launch_one<DK, DV, G, 4, DK / 32>(a, st);
-  if (rk == DK / 8) return launch_one<DK, DV, G, 4, DK / 8>(a, st);
+hipError_t dispatch_rot(const PrefillArgs& a, hipStream_t st) {
+  const int rch = (a.rope_q || a.rope_k) ? (2 * a.rot_pairs) / 8 : 0;
+  if (rch == 0) return launch_one<DK, DV, G, 0>(a, st);
+  if (rch == DK / 32) return launch_one<DK, DV, G, DK / 32>(a, st);
+  if (rch == DK / 8) return launch_one<DK, DV, G, DK / 8>(a, st);
   return hipErrorNotSupported;
 }
 
 template <int DK, int DV>
 hipError_t dispatch_g(const PrefillArgs& a, hipStream_t st) {
   switch (a.Hq / a.Hkv) {
-    case 1: return dispatch_rk<DK, DV, 1>(a, st);
-    case 2: return dispatch_rk<DK, DV, 2>(a, st);
-    case 4: return dispatch_rk<DK, DV, 4>(a, st);
-    case 8: return dispatch_rk<DK, DV, 8>(a, st);
+    case 1: return dispatch_rot<DK, DV, 1>(a, st);
+    case 2: return dispatch_rot<DK, DV, 2>(a, st);
+    case 4: return dispatch_rot<DK, DV, 4>(a, st);
+    case 8: return dispatch_rot<DK, DV, 8>(a, st);
     default: return hipErrorNotSupported;
   }
 }
@@ -370,9 +470,11 @@ bool prefill_mfma_supported(int Dk, int Dv, int G, float scale) {
 }
 
 hipError_t launch_prefill_mfma(const PrefillArgs& a, hipStream_t st) {
-  if (a.rope_q || a.rope_k) {
-    if ((2 * a.rot_pairs) % 8 != 0) return hipErrorNotSupported;
-  }
+  if ((a.rope_q || a.rope_k) && (2 * a.rot_pairs) % 8 != 0) return hipErrorNotSupported;
+  // 32-bit buffer offsets: one batch's K or V, and the cos/sin table, < 2 GiB.
+  const int64_t per_b = (int64_t)a.T * a.Hkv * (a.Dk > a.Dv ? a.Dk : a.Dv) * 2;
+  if (per_b >= (int64_t)1 << 31 || (int64_t)a.T * a.rot_pairs * 8 >= (int64_t)1 << 31)
+    return hipErrorNotSupported;
   if (a.Dk == 512 && a.Dv == 256) return dispatch_g<512, 256>(a, st);
   if (a.Dk == 256 && a.Dv == 256) return dispatch_g<256, 256>(a, st);
   if (a.Dk == 128 && a.Dv == 128) return dispatch_g<128, 128>(a, st);

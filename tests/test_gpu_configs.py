@@ -1,0 +1,127 @@
+"""The five workloads at full size, in the launch configuration the bench
+times, against the fp64 oracle on sampled outputs.
+
+Sampled rows always include the first rows, 32-row tile edges, window edges
+and the last rows, plus seeded random rows; every batch and head of a sampled
+row is compared. Decode compares the shortest, the longest and random
+sequences.
+"""
+import numpy as np
+import pytest
+import torch
+
+import attention_rope_amd as ar
+import inputs
+import oracle
+from parity import assert_close
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def sample_rows(T, W, n_random, seed):
+    fixed = {0, 1, 2, 15, 16, 31, 32, 33, 63, 64, 127, 128, T // 2, T - 33, T - 32,
+             T - 2, T - 1}
+    if W:
+        fixed |= {W - 2, W - 1, W, W + 1, 2 * W}
+    rng = np.random.default_rng(seed)
+    rows = fixed | set(rng.choice(T, size=n_random, replace=False).tolist())
+    return np.array(sorted(r for r in rows if 0 <= r < T), dtype=np.int32)
+
+
+def prefill_case(cfg_id, rows_random):
+    cfg = inputs.CONFIGS[cfg_id]
+    c = cfg["case"]
+    q, k, v = inputs.prefill_inputs(c, cfg["seed"], device=DEV)
+    tab = ar.rope_table(c.T, head_dim=c.Dk, rotary_dims=c.rotary_dims, theta=c.theta)
+    o = ar.prefill(q, k, v, window=c.window, scale=c.scale, rotary_dims=c.rotary_dims,
+                   theta=c.theta, table=tab)
+    torch.cuda.synchronize()
+    rows = None if rows_random is None else sample_rows(c.T, c.window, rows_random, cfg_id)
+    qh = q.cpu() if rows is None else q.cpu()[:, rows]
+    ref = oracle.prefill(qh, k.cpu(), v.cpu(), window=c.window, scale=c.scale,
+                         rotary_dims=c.rotary_dims, theta=c.theta, rows=rows)
+    got = o if rows is None else o[:, torch.as_tensor(rows, device=DEV, dtype=torch.long)]
+    mx, rel = assert_close(got, ref, c.dtype, f"config {cfg_id}")
+    print(f"config {cfg_id}: rows={'all' if rows is None else len(rows)} "
+          f"max_abs={mx:.3e} rel_rms={rel:.3e}", flush=True)
+
+
+def test_config1_fp32_global_full():
+    prefill_case(1, None)
+
+
+def test_config2_local_prefill():
+    prefill_case(2, 96)
+
+
+def test_config3_global_prefill():
+    prefill_case(3, 40)
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("kind", ["glob", "loc"])
+def test_config4_decode(kind):
+    cfg = inputs.CONFIGS[4]
+    d = cfg["cases"][kind]
+    seed = cfg["seed"] + (0 if kind == "glob" else 100)
+    kvl = inputs.decode_lengths(d, cfg["seed"])
+    q, kc, vc, off, kvl = inputs.decode_inputs(d, seed, device=DEV, kv_len=kvl)
+    maxl = int(kvl.max())
+    o = ar.decode(q, kc, vc, off.to(DEV), kvl.to(DEV), window=d.window, scale=d.scale,
+                  rotary_dims=d.rotary_dims, theta=d.theta, max_kv_len=maxl)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o.float()).all()
+    lens = kvl.tolist()
+    rng = np.random.default_rng(4)
+    seqs = sorted({int(np.argmin(lens)), int(np.argmax(lens))} |
+                  set(rng.choice(len(lens), size=4, replace=False).tolist()))
+    for b in seqs:
+        n = lens[b]
+        lo = max(0, n - d.window) if d.window else 0
+        a = int(off[b])
+        ref = oracle.decode_one(q[b].cpu(), kc[a + lo:a + n].cpu(), vc[a + lo:a + n].cpu(),
+                                kv_len=n, row0=lo, window=d.window, scale=d.scale,
+                                rotary_dims=d.rotary_dims, theta=d.theta)
+        mx, rel = assert_close(o[b], ref, torch.bfloat16, f"config 4 {kind} seq {b} len {n}")
+        print(f"config 4 {kind}: seq {b} kv_len={n} max_abs={mx:.3e} rel_rms={rel:.3e}",
+              flush=True)
+    del kc, vc
+    torch.cuda.empty_cache()
+
+
+def test_config5_stack():
+    cfg = inputs.CONFIGS[5]
+    sc = cfg["case"]
+    layers = []
+    tabs = {}
+    for li, (c, kv_from) in enumerate(sc.layers):
+        q, k, v = inputs.prefill_inputs(c, cfg["seed"], device=DEV, layer=li,
+                                        draw_kv=kv_from is None)
+        if kv_from is not None:
+            k, v = layers[kv_from][1], layers[kv_from][2]
+        key = (c.Dk, c.rotary_dims, c.theta)
+        if key not in tabs:
+            tabs[key] = ar.rope_table(c.T, head_dim=c.Dk, rotary_dims=c.rotary_dims,
+                                      theta=c.theta)
+        o = ar.prefill(q, k, v, window=c.window, scale=c.scale, rotary_dims=c.rotary_dims,
+                       theta=c.theta, table=tabs[key])
+        layers.append((q, k, v, o, c))
+    torch.cuda.synchronize()
+    # the shared-KV layer equals a standalone call on layer 6's K/V, bit for bit
+    q7, k6, v6, o7, c7 = layers[-1]
+    assert k6.data_ptr() == layers[-2][1].data_ptr()
+    alone = ar.prefill(q7, k6.clone(), v6.clone(), window=0, scale=c7.scale,
+                       rotary_dims=c7.rotary_dims, theta=c7.theta)
+    torch.cuda.synchronize()
+    assert torch.equal(alone, o7)
+    for li, (q, k, v, o, c) in enumerate(layers):
+        rows = sample_rows(c.T, c.window, 12, 50 + li)
+        ref = oracle.prefill(q.cpu()[:, rows], k.cpu(), v.cpu(), window=c.window,
+                             scale=c.scale, rotary_dims=c.rotary_dims, theta=c.theta,
+                             rows=rows)
+        got = o[:, torch.as_tensor(rows, device=DEV, dtype=torch.long)]
+        mx, rel = assert_close(got, ref, c.dtype, f"config 5 layer {li + 1}")
+        print(f"config 5 layer {li + 1}: max_abs={mx:.3e} rel_rms={rel:.3e}", flush=True)
+    del layers
+    torch.cuda.empty_cache()
