@@ -43,6 +43,23 @@ __device__ __forceinline__ void rope_cos_sin(int64_t pos, double w, float* c, fl
   *s = (float)sd;
 }
 
+// Reductions over the 4 lanes {l, l^16, l^32, l^48} with the gfx950 row-swap
+// instructions (no LDS traffic): v_permlane32_swap exchanges lane halves and
+// v_permlane16_swap exchanges neighbouring 16-lane rows, so each step leaves
+// {x[l], x[l^32]} (then {y[l], y[l^16]}) in the two results of every lane.
+__device__ __forceinline__ float xor32_16_max(float x) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const float y = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(y), __float_as_uint(y), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float xor32_16_sum(float x) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const float y = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(y), __float_as_uint(y), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 // Blocks are dispatched round-robin over the 8 XCDs (block x runs on XCD x%8).
 // Return the logical index such that each XCD receives one contiguous range of
 // logical indices, keeping neighbouring tiles on the same L2.

@@ -146,8 +146,7 @@ __global__ __launch_bounds__(kNW * 64) void decode_partial_kernel(DecodeArgs a, 
         if (tail && key >= c1) s[sb][i] = -INFINITY;
         mx = fmaxf(mx, s[sb][i]);
       }
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    mx = xor32_16_max(mx);
     const float m_new = fmaxf(m_run, mx * c2);
     const float alpha = exp2f(m_run - m_new);
     float pv[8], psum = 0.f;
@@ -201,8 +200,7 @@ __global__ __launch_bounds__(kNW * 64) void decode_partial_kernel(DecodeArgs a, 
 
   // Each lane's running sum covers only its own keys; the 4 lanes of a head
   // (col, col+16, col+32, col+48) share the same running max, so sum them.
-  l_run += __shfl_xor(l_run, 16);
-  l_run += __shfl_xor(l_run, 32);
+  l_run = xor32_16_sum(l_run);
 
   // ---- merge the 4 waves through LDS, write this split's partial ---------
   __syncthreads();

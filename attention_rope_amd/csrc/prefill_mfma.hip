@@ -1,5 +1,5 @@
 // prefill_mfma.hip — flash-style causal / sliding-window GQA prefill on gfx950
-// bf16 matrix cores (v_mfma_f32_32x32x16_bf16), with RoPE fused into the Q and
+// bf16 matrix cores (v_mfma_f32_16x16x32_bf16), with RoPE fused into the Q and
 // K loads.
 //
 // What it computes (Gemma 4 pages): "Gemma 4: End-to-End Architecture
@@ -13,21 +13,23 @@
 // before the P.V product, and everything accumulates in fp32.
 //
 // Design for CDNA4:
-//  * A workgroup (4 waves, one per SIMD) owns one (batch, KV head) and PW
+//  * A workgroup of 8 waves (2 per SIMD) owns one (batch, KV head) and PW
 //    consecutive query positions for all G query heads sharing that KV head:
-//    128 (head, position) rows, so each staged K/V tile serves G heads.
-//  * Each wave owns 32 rows and computes S^T = K Q^T (M = 32 keys, N = 32
-//    rows): in the MFMA output layout every lane holds 16 scores of one query
-//    row, so the softmax needs a single cross-lane swap (lane ^ 32). Q^T stays
-//    in registers for the whole kernel.
-//  * O^T = V^T P^T: the P^T operand is the lane's own scores when the key
-//    order inside each 16-key MFMA step matches the score layout; V tiles are
-//    written to LDS transposed, in exactly that key order.
+//    128 (head, position) rows, so each K/V tile staged in LDS serves G heads.
+//    Two waves per SIMD let one wave's softmax overlap the other's MFMAs.
+//  * Each wave owns 16 rows and computes S^T = K Q^T with 16x16x32 MFMAs
+//    (M = 16 keys, N = 16 rows): every lane holds 8 scores of one query row,
+//    so the softmax max/sum need two cross-lane swaps. Q^T (DK/32 x 16 bytes
+//    per lane) and the O^T accumulator (DV/4 fp32 per lane) stay in registers;
+//    at 16 rows a wave fits in half the register file.
+//  * O^T = V^T P^T (K = 32 keys per MFMA): the P^T operand is the lane's own
+//    scores when the key order inside the MFMA matches the score layout; V
+//    tiles are written to LDS transposed, in exactly that key order.
 //  * K tiles (32 keys) move HBM -> LDS by direct DMA (buffer loads with the
 //    lds flag): no staging registers, out-of-range rows read as zero. The
 //    rotated chunks of each K row sit in their own LDS region, so every thread
-//    turns exactly the chunks its own DMA wrote (no extra barrier, all lanes
-//    busy), with cos/sin from the per-position table prefetched one tile
+//    turns exactly the chunks its own DMA wrote (one barrier per tile, all
+//    lanes busy), with cos/sin from the per-position table prefetched one tile
 //    ahead. Tiles are double-buffered; the next tile's loads overlap the
 //    current tile's matrix work.
 //  * K rows are XOR-swizzled in 16-byte chunks so the MFMA operand reads are
@@ -48,8 +50,9 @@ namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLazy = 8.0f;  // log2 headroom before the running max moves
-constexpr int NW = 4;          // waves per workgroup
+constexpr int NW = 8;          // waves per workgroup
 constexpr int NT = NW * 64;
+constexpr int RW = 16;         // query rows per wave
 constexpr int BN = 32;         // keys per tile
 // Buffer descriptor word 3 for raw (stride 0) 32-bit-format buffers on gfx9.
 constexpr int kBufFlags = 0x00020000;
@@ -58,7 +61,7 @@ typedef __attribute__((address_space(3))) void lds_void;
 
 template <int DK, int DV, int G, int RCH>
 struct Cfg {
-  static constexpr int ROWS = NW * 32;        // (head, position) rows per WG
+  static constexpr int ROWS = NW * RW;        // (head, position) rows per WG
   static constexpr int PW = ROWS / G;         // query positions per WG
   static constexpr int NC = DK / 8;           // 16-byte chunks per K row
   static constexpr int NP = NC - RCH;         // plain (unrotated) chunks per K row
@@ -74,10 +77,9 @@ struct Cfg {
   static constexpr int VU = (BN / 4) * (DV / 8);   // V units: 4 keys x 8 dims
   static constexpr int VUT = (VU + NT - 1) / NT;
   static constexpr int KROT = (KR_DMA + NW - 1) / NW;  // rotated blocks per wave
-  static_assert(ROWS % G == 0, "rows must split evenly over the heads");
-  static_assert(PW >= 32 ? PW % 32 == 0 : 32 % PW == 0, "wave/row layout");
+  static_assert(ROWS % G == 0 && PW % RW == 0, "rows must split evenly over the heads");
   static_assert(KR_BYTES % 1024 == 0 && KT_BYTES % 1024 == 0, "DMA blocks");
-  static_assert(DK % 16 == 0 && DV % 32 == 0, "MFMA tiling");
+  static_assert(DK % 32 == 0 && DV % 16 == 0, "MFMA tiling");
 };
 
 // XOR swizzle of 16-byte chunks inside a K region row of `width` chunks. The
@@ -95,28 +97,21 @@ __device__ __forceinline__ int kswz(int r, int c) {
   return c ^ (r & Swz<width>::M);
 }
 
-// Byte offset of chunk c (0..NC-1) of K row r inside a K tile.
-template <int NC, int RCH>
-__device__ __forceinline__ int k_off(int r, int c) {
-  if (c < RCH) return (r * RCH + kswz<RCH>(r, c)) * 16;
-  return BN * RCH * 16 + (r * (NC - RCH) + kswz<NC - RCH>(r, c - RCH)) * 16;
-}
-
-// Per-lane addressing of the K operand reads (row r, chunk 2k + h for
-// k = 0, 1, ...) inside a region of `width` chunks starting at byte `base`:
-// the offset is row_base + ((k & H) << 5 ^ x1s) + ((k & ~H) << 5) with
-// H = P/2 - 1, so one XOR with a per-lane constant and an immediate remain.
+// Per-lane addressing of the K operand reads (row r, chunk 4s + g for
+// s = 0, 1, ...) inside a region of `width` chunks starting at byte `base`:
+// chunk (4s + g) ^ x = 4((s ^ x2)) + ((g ^ x) & 3) with x2 = x >> 2, so the
+// offset is row_base + (((s & H) << 6) ^ x2s) + ((s & ~H) << 6).
 template <int width>
 struct KAddr {
-  int row_base, x1s;
-  __device__ __forceinline__ KAddr(int base, int r, int h) {
+  int row_base, x2s;
+  __device__ __forceinline__ KAddr(int base, int r, int g) {
     const int x = r & Swz<width>::M;
-    row_base = base + r * width * 16 + ((h ^ (x & 1)) << 4);
-    x1s = (x >> 1) << 5;
+    row_base = base + r * width * 16 + (((g ^ x) & 3) << 4);
+    x2s = (x >> 2) << 6;
   }
-  __device__ __forceinline__ int operator()(int k) const {
-    constexpr int H = Swz<width>::P / 2 - 1;
-    return row_base + (((k & H) << 5) ^ x1s) + ((k & ~H) << 5);
+  __device__ __forceinline__ int operator()(int s) const {
+    constexpr int H = (Swz<width>::P >= 4 ? Swz<width>::P / 4 : 1) - 1;
+    return row_base + (((s & H) << 6) ^ x2s) + ((s & ~H) << 6);
   }
 };
 
@@ -138,14 +133,14 @@ __device__ __forceinline__ u32x4 rotate4(u32x4 w, f32x4 t0, f32x4 t1) {
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 template <int DK, int DV, int G, int RCH>
-__global__ __launch_bounds__(NT) void prefill_mfma_kernel(PrefillArgs a, int n_qt,
-                                                          int contig) {
+__global__ __launch_bounds__(NT, 1) void prefill_mfma_kernel(PrefillArgs a, int n_qt,
+                                                             int contig) {
   using C = Cfg<DK, DV, G, RCH>;
   __shared__ __attribute__((aligned(1024))) unsigned char lds[2 * C::STAGE];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int lr = lane & 31, hh = lane >> 5;
+  const int r16 = lane & 15, g = lane >> 4;
   const int T = a.T, W = a.window;
   const int n_wg = n_qt * a.Hkv * a.B;
   const int L = contig ? xcd_contiguous((int)blockIdx.x, n_wg) : (int)blockIdx.x;
@@ -154,13 +149,13 @@ __global__ __launch_bounds__(NT) void prefill_mfma_kernel(PrefillArgs a, int n_q
   const int kvh = grp % a.Hkv, b = grp / a.Hkv;
   const int p0 = qt * C::PW;
 
-  // This lane's query row and the wave's position range.
-  const int R = wave * 32 + lr;
+  // This lane's query row; the wave's 16 rows are 16 positions of one head.
+  const int R = wave * RW + r16;
   const int head = kvh * G + R / C::PW;
   const int pos = p0 + R % C::PW;
   const bool valid = pos < T;
-  const int wlo = p0 + (wave * 32) % C::PW;
-  const int whi = wlo + (C::PW < 32 ? C::PW : 32) - 1;
+  const int wlo = p0 + (wave * RW) % C::PW;
+  const int whi = wlo + RW - 1;
 
   const int kv_lo = (W > 0) ? max(0, p0 - W + 1) : 0;
   const int kv_hi = min(T, p0 + C::PW);
@@ -182,7 +177,6 @@ __global__ __launch_bounds__(NT) void prefill_mfma_kernel(PrefillArgs a, int n_q
       (void*)a.rope_tab, (short)0, (RCH > 0 && (rot_k || rot_q)) ? T * tab_row : 0, kBufFlags);
 
   // ---- K: DMA into LDS; this thread turns the rotated chunks it loaded -----
-  // Rotated-region block n (n = wave, wave + NW, ...): lane -> chunk q.
   f32x4 ktab[C::KROT > 0 ? C::KROT : 1][2];
   auto rot_chunk = [&](int i, int& r, int& c) {
     const int q = (i * NW + wave) * 64 + lane;
@@ -229,6 +223,8 @@ __global__ __launch_bounds__(NT) void prefill_mfma_kernel(PrefillArgs a, int n_q
   };
 
   // ---- V: registers, then LDS transposed in the score-matched key order ----
+  // Slot 8g + i of a V^T row holds key 16(i/4) + 4g + (i%4): key 16a + 4g + r
+  // sits in slot 8g + 4a + r, so 4 consecutive keys fill 4 consecutive slots.
   u32x4 vreg[C::VUT][4];
   auto load_v = [&](int kb) {
     const int j0 = kb * BN;
@@ -251,8 +247,7 @@ __global__ __launch_bounds__(NT) void prefill_mfma_kernel(PrefillArgs a, int n_q
       const int u = tid + NT * ut;
       if (C::VU % NT == 0 || u < C::VU) {
         const int kg = u % 8, d8 = u / 8;
-        // keys 4kg..4kg+3 occupy 4 consecutive slots of the permuted key order
-        const int slot = 16 * (kg / 4) + 8 * (kg % 2) + 4 * ((kg % 4) / 2);
+        const int slot = 8 * (kg % 4) + 4 * (kg / 4);  // keys 4kg..4kg+3
 #pragma unroll
         for (int dd = 0; dd < 8; ++dd) {
           const int wi = dd / 2;
@@ -275,32 +270,33 @@ __global__ __launch_bounds__(NT) void prefill_mfma_kernel(PrefillArgs a, int n_q
     dma_k(kb_lo, lds);
     load_v(kb_lo);
   }
-  bf16x8 qf[DK / 16];
+  // Q^T operand: step s covers dims 32s + 8g .. 32s + 8g + 7 of this row.
+  bf16x8 qf[DK / 32];
   {
     const int prow = valid ? pos : T - 1;
     const uint16_t* qrow =
-        (const uint16_t*)a.q + (((int64_t)b * T + prow) * a.Hq + head) * DK + 8 * hh;
-    u32x4 qw[DK / 16];
+        (const uint16_t*)a.q + (((int64_t)b * T + prow) * a.Hq + head) * DK + 8 * g;
+    u32x4 qw[DK / 32];
 #pragma unroll
-    for (int s = 0; s < DK / 16; ++s) qw[s] = *(const u32x4*)(qrow + 16 * s);
+    for (int s = 0; s < DK / 32; ++s) qw[s] = *(const u32x4*)(qrow + 32 * s);
     if (rot_q) {
-      // rotated chunks: s < RCH/2 for both halves (16s + 8hh < 8*RCH)
+      // rotated chunks: 32s + 8g < 8*RCH  <=>  s < RCH/4 for every g
 #pragma unroll
-      for (int s0 = 0; s0 < RCH / 2; s0 += 4) {
+      for (int s0 = 0; s0 < RCH / 4; s0 += 4) {
         f32x4 t[4][2];
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-          const int off = prow * tab_row + (16 * (s0 + u) + 8 * hh) * 4;
+          const int off = prow * tab_row + (32 * (s0 + u) + 8 * g) * 4;
           t[u][0] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(tres, off, 0, 0));
           t[u][1] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(tres, off + 16, 0, 0));
         }
 #pragma unroll
         for (int u = 0; u < 4; ++u)
-          if (s0 + u < RCH / 2) qw[s0 + u] = rotate4(qw[s0 + u], t[u][0], t[u][1]);
+          if (s0 + u < RCH / 4) qw[s0 + u] = rotate4(qw[s0 + u], t[u][0], t[u][1]);
       }
     }
 #pragma unroll
-    for (int s = 0; s < DK / 16; ++s) {
+    for (int s = 0; s < DK / 32; ++s) {
       u32x4 w = valid ? qw[s] : u32x4{0, 0, 0, 0};
       qf[s] = __builtin_bit_cast(bf16x8, w);
     }
@@ -312,82 +308,78 @@ __global__ __launch_bounds__(NT) void prefill_mfma_kernel(PrefillArgs a, int n_q
     __syncthreads();
   }
 
-  // ---- online softmax state (one row per lane; halves share the row) -------
-  const float c2 = a.scale * kLog2e;  // scores to log2 units (>= 0)
+  // ---- online softmax state (one row per lane; 4 lanes share a row) --------
+  // scores to log2 units; kept > 0 so a masked -inf score never meets a zero
+  // factor (scale 0 then acts as 1e-30: every visible key weighs the same)
+  const float c2 = fmaxf(a.scale * kLog2e, 1e-30f);
   const unsigned wcap = (W > 0) ? (unsigned)W : 0x80000000u;
   float m_run = -INFINITY, l_run = 0.f;
-  f32x16 oacc[DV / 32];
+  f32x4 oacc[DV / 16];
 #pragma unroll
-  for (int d = 0; d < DV / 32; ++d) oacc[d] = f32x16{};
+  for (int d = 0; d < DV / 16; ++d) oacc[d] = f32x4{};
 
-  const KAddr<(RCH > 0 ? RCH : 16)> kaddr_r(0, lr, hh);
-  const KAddr<(C::NP > 0 ? C::NP : 16)> kaddr_p(C::KR_BYTES, lr, hh);
+  // K operand: key 16mb + r16, chunk 4s + g.
+  const KAddr<(RCH > 0 ? RCH : 16)> kaddr_r0(0, r16, g), kaddr_r1(0, r16 + 16, g);
+  const KAddr<(C::NP > 0 ? C::NP : 16)> kaddr_p0(C::KR_BYTES, r16, g),
+      kaddr_p1(C::KR_BYTES, r16 + 16, g);
+  const int vt_off = C::KT_BYTES + (r16 * C::VS + 8 * g) * 2;  // + 16*db*VS*2
+
   auto compute = [&](const unsigned char* st, int kb) {
     const int j0 = kb * BN;
     if (j0 > whi) return;                            // beyond every row (causal)
     if (W > 0 && j0 + BN - 1 <= wlo - W) return;     // before every row's window
-    f32x16 s = f32x16{};
-    // chunks 2k + hh: k < RCH/2 in the rotated region, the rest in the plain one
+    f32x4 s0 = f32x4{}, s1 = f32x4{};
+    // dims 32s + 8g..: s < RCH/4 in the rotated region, the rest in the plain one
 #pragma unroll
-    for (int k = 0; k < RCH / 2; ++k) {
-      const bf16x8 ka = *(const bf16x8*)(st + kaddr_r(k));
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[k], s, 0, 0, 0);
+    for (int s = 0; s < RCH / 4; ++s) {
+      const bf16x8 k0 = *(const bf16x8*)(st + kaddr_r0(s));
+      const bf16x8 k1 = *(const bf16x8*)(st + kaddr_r1(s));
+      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qf[s], s0, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qf[s], s1, 0, 0, 0);
     }
 #pragma unroll
-    for (int k = RCH / 2; k < DK / 16; ++k) {
-      const bf16x8 ka = *(const bf16x8*)(st + kaddr_p(k - RCH / 2));
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[k], s, 0, 0, 0);
+    for (int s = RCH / 4; s < DK / 32; ++s) {
+      const bf16x8 k0 = *(const bf16x8*)(st + kaddr_p0(s - RCH / 4));
+      const bf16x8 k1 = *(const bf16x8*)(st + kaddr_p1(s - RCH / 4));
+      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qf[s], s0, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qf[s], s1, 0, 0, 0);
     }
-    // lane holds keys j0 + 8(i/4) + 4hh + (i%4) of its row, i = 0..15
+    // lane holds keys j0 + 4g + i (s0) and j0 + 16 + 4g + i (s1) of its row
+    float sv[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
     const bool need_mask = (j0 + BN - 1 > wlo) || (W > 0 && j0 <= whi - W);
     if (need_mask) {
-      const int d0 = pos - j0 - 4 * hh;
+      const int d0 = pos - j0 - 4 * g;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const unsigned d = (unsigned)(d0 - (8 * (i / 4) + (i % 4)));  // pos - key
-        s[i] = (d < wcap) ? s[i] : -INFINITY;
+      for (int i = 0; i < 8; ++i) {
+        const unsigned d = (unsigned)(d0 - (16 * (i / 4) + (i % 4)));  // pos - key
+        sv[i] = (d < wcap) ? sv[i] : -INFINITY;
       }
     }
-    float mx = s[0];
-#pragma unroll
-    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[i]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    float mx = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])),
+                     fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
+    mx = xor32_16_max(mx);
     const float mc = (mx == -INFINITY) ? -INFINITY : mx * c2;
     if (__any(mc > m_run + kLazy)) {
       const float m_new = fmaxf(m_run, mc);
       const float alpha = (m_run == -INFINITY) ? 0.f : fast_exp2(m_run - m_new);
       l_run *= alpha;
 #pragma unroll
-      for (int d = 0; d < DV / 32; ++d) oacc[d] *= alpha;
+      for (int d = 0; d < DV / 16; ++d) oacc[d] *= alpha;
       m_run = m_new;
     }
     const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
-    float pv[16];
+    float pv[8];  // masked scores are -inf and c2 > 0, so they give exactly 0
 #pragma unroll
-    for (int i = 0; i < 16; ++i) pv[i] = fast_exp2(fmaf(s[i], c2, -m_use));
-    if (need_mask) {
-      // masked scores are -inf; with scale 0 the product above is NaN
+    for (int i = 0; i < 8; ++i) pv[i] = fast_exp2(fmaf(sv[i], c2, -m_use));
+    l_run += ((pv[0] + pv[1]) + (pv[2] + pv[3])) + ((pv[4] + pv[5]) + (pv[6] + pv[7]));
+    const f32x4 plo = {pv[0], pv[1], pv[2], pv[3]}, phi = {pv[4], pv[5], pv[6], pv[7]};
+    const bf16x4 pa = __builtin_convertvector(plo, bf16x4);
+    const bf16x4 pb = __builtin_convertvector(phi, bf16x4);
+    const bf16x8 pop = __builtin_shufflevector(pa, pb, 0, 1, 2, 3, 4, 5, 6, 7);
 #pragma unroll
-      for (int i = 0; i < 16; ++i) pv[i] = (s[i] == -INFINITY) ? 0.f : pv[i];
-    }
-    float psum = 0.f;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) psum += pv[i];
-    l_run += psum;
-    f32x4 lo0 = {pv[0], pv[1], pv[2], pv[3]}, lo1 = {pv[4], pv[5], pv[6], pv[7]};
-    f32x4 hi0 = {pv[8], pv[9], pv[10], pv[11]}, hi1 = {pv[12], pv[13], pv[14], pv[15]};
-    const bf16x4 a0 = __builtin_convertvector(lo0, bf16x4), a1 = __builtin_convertvector(lo1, bf16x4);
-    const bf16x4 b0 = __builtin_convertvector(hi0, bf16x4), b1 = __builtin_convertvector(hi1, bf16x4);
-    const bf16x8 pb0 = __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7);
-    const bf16x8 pb1 = __builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7);
-    const uint16_t* Vt = (const uint16_t*)(st + C::KT_BYTES);
-#pragma unroll
-    for (int d = 0; d < DV / 32; ++d) {
-      const uint16_t* vrow_p = Vt + (32 * d + lr) * C::VS + 8 * hh;
-      const bf16x8 v0 = *(const bf16x8*)(vrow_p);
-      const bf16x8 v1 = *(const bf16x8*)(vrow_p + 16);
-      oacc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v0, pb0, oacc[d], 0, 0, 0);
-      oacc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v1, pb1, oacc[d], 0, 0, 0);
+    for (int d = 0; d < DV / 16; ++d) {
+      const bf16x8 va = *(const bf16x8*)(st + vt_off + d * 16 * C::VS * 2);
+      oacc[d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pop, oacc[d], 0, 0, 0);
     }
   };
 
@@ -411,18 +403,16 @@ __global__ __launch_bounds__(NT) void prefill_mfma_kernel(PrefillArgs a, int n_q
   }
 
   // ---- epilogue: O = O^T / l, bf16, 4 consecutive dims per store ----------
-  const float lt = l_run + __shfl_xor(l_run, 32);
+  l_run = xor32_16_sum(l_run);
   if (valid) {
-    const float inv = 1.f / lt;
-    uint16_t* orow = (uint16_t*)a.o + (((int64_t)b * T + pos) * a.Hq + head) * DV;
+    const float inv = 1.f / l_run;
+    uint16_t* orow = (uint16_t*)a.o + (((int64_t)b * T + pos) * a.Hq + head) * DV + 4 * g;
 #pragma unroll
-    for (int d = 0; d < DV / 32; ++d)
-#pragma unroll
-      for (int bq = 0; bq < 4; ++bq) {
-        const uint32_t w0 = pack_bf16x2(oacc[d][4 * bq] * inv, oacc[d][4 * bq + 1] * inv);
-        const uint32_t w1 = pack_bf16x2(oacc[d][4 * bq + 2] * inv, oacc[d][4 * bq + 3] * inv);
-        *(u32x2*)(orow + 32 * d + 8 * bq + 4 * hh) = u32x2{w0, w1};
-      }
+    for (int d = 0; d < DV / 16; ++d) {
+      const uint32_t w0 = pack_bf16x2(oacc[d][0] * inv, oacc[d][1] * inv);
+      const uint32_t w1 = pack_bf16x2(oacc[d][2] * inv, oacc[d][3] * inv);
+      *(u32x2*)(orow + 16 * d) = u32x2{w0, w1};
+    }
   }
 }
 
