@@ -73,10 +73,15 @@ struct Cfg {
   // V^T tile: [DV][VS] bf16, keys in the permuted order of the score layout.
   static constexpr int VS = BN + 8;           // padded row (80 bytes)
   static constexpr int VT_BYTES = DV * VS * 2;
-  static constexpr int STAGE = KT_BYTES + VT_BYTES;
-  static constexpr int VU = (BN / 4) * (DV / 8);   // V units: 4 keys x 8 dims
+  static constexpr int KSTAGES = 3;           // K tiles in flight: t, t+1, t+2
+  static constexpr int LDS_BYTES = KSTAGES * KT_BYTES + 2 * VT_BYTES;
+  static constexpr int VU = (BN / 2) * (DV / 8);   // V units: 2 keys x 8 dims
   static constexpr int VUT = (VU + NT - 1) / NT;
   static constexpr int KROT = (KR_DMA + NW - 1) / NW;  // rotated blocks per wave
+  static constexpr int KDMA_W = KROT + (KP_DMA + NW - 1) / NW;  // K DMA issues per wave (max)
+  // Every wave issues the same number of K DMAs per tile, so "everything but
+  // the newest K tile has landed" is one vmcnt value.
+  static constexpr bool UNIFORM = KR_DMA % NW == 0 && KP_DMA % NW == 0;
   static_assert(ROWS % G == 0 && PW % RW == 0, "rows must split evenly over the heads");
   static_assert(KR_BYTES % 1024 == 0 && KT_BYTES % 1024 == 0, "DMA blocks");
   static_assert(DK % 32 == 0 && DV % 16 == 0, "MFMA tiling");
@@ -132,11 +137,37 @@ __device__ __forceinline__ u32x4 rotate4(u32x4 w, f32x4 t0, f32x4 t1) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// LDS byte address of a pointer into a __shared__ array.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// LDS stores issued as plain instructions. The compiler treats every LDS
+// access that may alias an in-flight LDS DMA as needing that DMA to finish
+// first, which would drain the tile loaded two steps ahead. These stores never
+// touch a DMA target, so they are issued directly with no memory clobber: they
+// keep their order with the other volatile asm (the barrier below) and their
+// register dependences, and lds_barrier waits for them before publishing.
+__device__ __forceinline__ void lds_store_b128(uint32_t addr, u32x4 v) {
+  asm volatile("ds_write_b128 %0, %1" ::"v"(addr), "v"(v));
+}
+__device__ __forceinline__ void lds_store_b32(uint32_t addr, uint32_t v) {
+  asm volatile("ds_write_b32 %0, %1" ::"v"(addr), "v"(v));
+}
+// Publish this wave's LDS stores to the workgroup and synchronise, without the
+// workgroup-scope fence of __syncthreads (which would also wait for the
+// in-flight DMA); the memory clobber keeps compiler-visible LDS accesses on
+// their side of the barrier.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 template <int DK, int DV, int G, int RCH>
 __global__ __launch_bounds__(NT, 1) void prefill_mfma_kernel(PrefillArgs a, int n_qt,
                                                              int contig) {
   using C = Cfg<DK, DV, G, RCH>;
-  __shared__ __attribute__((aligned(1024))) unsigned char lds[2 * C::STAGE];
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[C::LDS_BYTES];
+  unsigned char* const vt_base = lds + C::KSTAGES * C::KT_BYTES;  // 2 V^T buffers
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -183,6 +214,19 @@ __global__ __launch_bounds__(NT, 1) void prefill_mfma_kernel(PrefillArgs a, int 
     r = q / (RCH > 0 ? RCH : 1);
     c = kswz<RCH>(r, q % (RCH > 0 ? RCH : 1));  // swizzle is an involution
   };
+  auto load_ktab = [&](int kb) {
+    const int j0 = kb * BN;
+#pragma unroll
+    for (int i = 0; i < C::KROT; ++i) {
+      if (C::KR_DMA % NW == 0 || i * NW + wave < C::KR_DMA) {
+        int r, c;
+        rot_chunk(i, r, c);
+        const int off = min(j0 + r, T - 1) * tab_row + c * 32;
+        ktab[i][0] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(tres, off, 0, 0));
+        ktab[i][1] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(tres, off + 16, 0, 0));
+      }
+    }
+  };
   auto dma_k = [&](int kb, unsigned char* st) {
     const int j0 = kb * BN;
 #pragma unroll
@@ -192,11 +236,6 @@ __global__ __launch_bounds__(NT, 1) void prefill_mfma_kernel(PrefillArgs a, int 
         rot_chunk(i, r, c);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(kres, (lds_void*)(st + (i * NW + wave) * 1024),
                                                  16, (j0 + r) * krow + c * 16, 0, 0, 0);
-        if (rot_k) {
-          const int off = min(j0 + r, T - 1) * tab_row + c * 32;
-          ktab[i][0] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(tres, off, 0, 0));
-          ktab[i][1] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(tres, off + 16, 0, 0));
-        }
       }
     }
 #pragma unroll
@@ -204,8 +243,9 @@ __global__ __launch_bounds__(NT, 1) void prefill_mfma_kernel(PrefillArgs a, int 
       const int n = i * NW + wave;
       if (C::KP_DMA % NW == 0 || n < C::KP_DMA) {
         const int q = n * 64 + lane;
-        const int r = q / C::NP;
-        const int c = RCH + kswz<C::NP>(r, q % C::NP);
+        constexpr int NPd = C::NP > 0 ? C::NP : 1;  // loop is empty when NP == 0
+        const int r = q / NPd;
+        const int c = RCH + kswz<NPd>(r, q % NPd);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
             kres, (lds_void*)(st + C::KR_BYTES + n * 1024), 16, (j0 + r) * krow + c * 16, 0, 0,
             0);
@@ -216,59 +256,78 @@ __global__ __launch_bounds__(NT, 1) void prefill_mfma_kernel(PrefillArgs a, int 
 #pragma unroll
     for (int i = 0; i < C::KROT; ++i) {
       if (C::KR_DMA % NW == 0 || i * NW + wave < C::KR_DMA) {
-        u32x4* p = (u32x4*)(st + ((i * NW + wave) * 64 + lane) * 16);
-        *p = rotate4(*p, ktab[i][0], ktab[i][1]);
+        const unsigned char* p = st + ((i * NW + wave) * 64 + lane) * 16;
+        lds_store_b128(lds_addr(p), rotate4(*(const u32x4*)p, ktab[i][0], ktab[i][1]));
       }
     }
   };
 
   // ---- V: registers, then LDS transposed in the score-matched key order ----
   // Slot 8g + i of a V^T row holds key 16(i/4) + 4g + (i%4): key 16a + 4g + r
-  // sits in slot 8g + 4a + r, so 4 consecutive keys fill 4 consecutive slots.
-  u32x4 vreg[C::VUT][4];
-  auto load_v = [&](int kb) {
+  // sits in slot 8g + 4a + r, so an even/odd key pair fills 2 adjacent slots.
+  // Unit u = key pair kp (keys 2kp, 2kp+1) x 8 dims d8; a step loads the next
+  // tile's units and writes them transposed at its end.
+  u32x4 vreg[C::VUT][2];
+  auto load_v = [&](int kb, u32x4 (&vr)[C::VUT][2]) {
     const int j0 = kb * BN;
 #pragma unroll
     for (int ut = 0; ut < C::VUT; ++ut) {
       const int u = tid + NT * ut;
-      const int kg = u % 8, d8 = u / 8;
+      const int kp = u % 16, d8 = u / 16;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        vreg[ut][e] = (C::VU % NT == 0 || u < C::VU)
-                          ? __builtin_amdgcn_raw_buffer_load_b128(vres, (j0 + 4 * kg + e) * vrow + d8 * 16, 0, 0)
-                          : u32x4{0, 0, 0, 0};
+      for (int e = 0; e < 2; ++e) {
+        vr[ut][e] = (C::VU % NT == 0 || u < C::VU)
+                        ? __builtin_amdgcn_raw_buffer_load_b128(vres, (j0 + 2 * kp + e) * vrow + d8 * 16, 0, 0)
+                        : u32x4{0, 0, 0, 0};
       }
     }
   };
-  auto store_v = [&](unsigned char* st) {
-    uint16_t* Vt = (uint16_t*)(st + C::KT_BYTES);
+  auto store_v = [&](const u32x4 (&vr)[C::VUT][2], unsigned char* vt) {
+    uint16_t* Vt = (uint16_t*)vt;
 #pragma unroll
     for (int ut = 0; ut < C::VUT; ++ut) {
       const int u = tid + NT * ut;
       if (C::VU % NT == 0 || u < C::VU) {
-        const int kg = u % 8, d8 = u / 8;
-        const int slot = 8 * (kg % 4) + 4 * (kg / 4);  // keys 4kg..4kg+3
+        const int kp = u % 16, d8 = u / 16;
+        const int k = 2 * kp;  // = 16a + 4g' + r with r even
+        const int slot = 8 * ((k % 16) / 4) + 4 * (k / 16) + (k % 4);
 #pragma unroll
         for (int dd = 0; dd < 8; ++dd) {
           const int wi = dd / 2;
-          uint32_t lo, hi;
-          if (dd % 2 == 0) {
-            lo = (vreg[ut][0][wi] & 0xffffu) | (vreg[ut][1][wi] << 16);
-            hi = (vreg[ut][2][wi] & 0xffffu) | (vreg[ut][3][wi] << 16);
-          } else {
-            lo = (vreg[ut][0][wi] >> 16) | (vreg[ut][1][wi] & 0xffff0000u);
-            hi = (vreg[ut][2][wi] >> 16) | (vreg[ut][3][wi] & 0xffff0000u);
-          }
-          *(u32x2*)(Vt + (8 * d8 + dd) * C::VS + slot) = u32x2{lo, hi};
+          const uint32_t w = (dd % 2 == 0) ? ((vr[ut][0][wi] & 0xffffu) | (vr[ut][1][wi] << 16))
+                                           : ((vr[ut][0][wi] >> 16) | (vr[ut][1][wi] & 0xffff0000u));
+          lds_store_b32(lds_addr(Vt + (8 * d8 + dd) * C::VS + slot), w);
         }
       }
     }
   };
 
-  // ---- prologue: first tile's loads and the Q rows, all in flight ---------
-  if (kb_lo < kb_hi) {
+  // Wait until every load issued before the newest K tile's DMAs has
+  // completed (loads complete in issue order and those DMAs are always the
+  // last loads issued), then keep the scheduler from hoisting LDS reads of the
+  // landed tile above the wait.
+  auto wait_all_but_newest_k = [&]() {
+    if constexpr (C::UNIFORM) {
+      constexpr int n = C::KDMA_W;  // K DMAs per wave per tile
+      static_assert(n < 16, "vmcnt field");
+      // s_waitcnt: vmcnt[3:0] = n, expcnt = 7 (no wait), lgkmcnt = 15 (no wait)
+      __builtin_amdgcn_s_waitcnt(0x0F70 | n);
+    } else {
+      __builtin_amdgcn_s_waitcnt(0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  auto wait_all = [&]() {
+    __builtin_amdgcn_s_waitcnt(0);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  // ---- prologue: tile 0 (K, V, table), the Q rows, then tile 1's K DMA ----
+  const int n_tiles = kb_hi - kb_lo;
+  if (n_tiles > 0) {
     dma_k(kb_lo, lds);
-    load_v(kb_lo);
+    if (rot_k) load_ktab(kb_lo);
+    load_v(kb_lo, vreg);
   }
   // Q^T operand: step s covers dims 32s + 8g .. 32s + 8g + 7 of this row.
   bf16x8 qf[DK / 32];
@@ -301,12 +360,14 @@ __global__ __launch_bounds__(NT, 1) void prefill_mfma_kernel(PrefillArgs a, int 
       qf[s] = __builtin_bit_cast(bf16x8, w);
     }
   }
-  if (kb_lo < kb_hi) {
-    __builtin_amdgcn_s_waitcnt(0);  // own DMA landed, V and table in registers
+  if (n_tiles > 0) {
+    dma_k(kb_lo + 1, lds + C::KT_BYTES);  // may lie past the range: never read
+    wait_all_but_newest_k();  // tile 0 landed; tile 1's K may still be in flight
     if (rot_k) rotate_k(lds);
-    store_v(lds);
-    __syncthreads();
+    store_v(vreg, vt_base);
+    lds_barrier();
   }
+
 
   // ---- online softmax state (one row per lane; 4 lanes share a row) --------
   // scores to log2 units; kept > 0 so a masked -inf score never meets a zero
@@ -322,9 +383,9 @@ __global__ __launch_bounds__(NT, 1) void prefill_mfma_kernel(PrefillArgs a, int 
   const KAddr<(RCH > 0 ? RCH : 16)> kaddr_r0(0, r16, g), kaddr_r1(0, r16 + 16, g);
   const KAddr<(C::NP > 0 ? C::NP : 16)> kaddr_p0(C::KR_BYTES, r16, g),
       kaddr_p1(C::KR_BYTES, r16 + 16, g);
-  const int vt_off = C::KT_BYTES + (r16 * C::VS + 8 * g) * 2;  // + 16*db*VS*2
+  const int vt_off = (r16 * C::VS + 8 * g) * 2;  // + 16*db*VS*2
 
-  auto compute = [&](const unsigned char* st, int kb) {
+  auto compute = [&](const unsigned char* st, const unsigned char* vt, int kb) {
     const int j0 = kb * BN;
     if (j0 > whi) return;                            // beyond every row (causal)
     if (W > 0 && j0 + BN - 1 <= wlo - W) return;     // before every row's window
@@ -378,29 +439,37 @@ __global__ __launch_bounds__(NT, 1) void prefill_mfma_kernel(PrefillArgs a, int 
     const bf16x8 pop = __builtin_shufflevector(pa, pb, 0, 1, 2, 3, 4, 5, 6, 7);
 #pragma unroll
     for (int d = 0; d < DV / 16; ++d) {
-      const bf16x8 va = *(const bf16x8*)(st + vt_off + d * 16 * C::VS * 2);
+      const bf16x8 va = *(const bf16x8*)(vt + vt_off + d * 16 * C::VS * 2);
       oacc[d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pop, oacc[d], 0, 0, 0);
     }
   };
 
-  // ---- main loop: double-buffered key tiles -------------------------------
-  for (int kb = kb_lo; kb < kb_hi; ++kb) {
-    const int cur = (kb - kb_lo) & 1;
-    unsigned char* cs = lds + cur * C::STAGE;
-    unsigned char* ns = lds + (cur ^ 1) * C::STAGE;
-    const bool more = kb + 1 < kb_hi;
-    if (more) {
-      dma_k(kb + 1, ns);
-      load_v(kb + 1);
+  // ---- main loop: K tiles in 3 LDS stages, V^T in 2 buffers ---------------
+  // Step t computes tile t while K(t+1) (issued a step ago) and K(t+2)
+  // (issued now, last) load, with V(t+1) and the cos/sin of K(t+1); it then
+  // turns K(t+1) and writes V^T(t+1). Every step issues the same loads, also
+  // the last two (their tiles may lie past the range or past T, where the
+  // buffer descriptors return zeros, and are never read), so one vmcnt value
+  // separates the newest K tile from everything older on every path.
+  for (int t = 0; t < n_tiles; ++t) {
+    const int kb = kb_lo + t;
+    unsigned char* ks = lds + (t % 3) * C::KT_BYTES;
+    unsigned char* k1 = lds + ((t + 1) % 3) * C::KT_BYTES;
+    unsigned char* k2 = lds + ((t + 2) % 3) * C::KT_BYTES;
+    unsigned char* vt = vt_base + (t & 1) * C::VT_BYTES;
+    unsigned char* vt1 = vt_base + ((t + 1) & 1) * C::VT_BYTES;
+    if (rot_k) load_ktab(kb + 1);
+    load_v(kb + 1, vreg);
+    dma_k(kb + 2, k2);
+    compute(ks, vt, kb);
+    wait_all_but_newest_k();  // K(t+1), V(t+1) and its table landed
+    if (t + 1 < n_tiles) {
+      if (rot_k) rotate_k(k1);
+      store_v(vreg, vt1);
     }
-    compute(cs, kb);
-    if (more) {
-      __builtin_amdgcn_s_waitcnt(0);  // own DMA landed, V and table in registers
-      if (rot_k) rotate_k(ns);
-      store_v(ns);
-    }
-    __syncthreads();  // next tile complete everywhere; current tile free
+    lds_barrier();  // tile t+1 complete everywhere; tile t buffers free
   }
+  wait_all();  // no DMA may still target LDS when the block ends
 
   // ---- epilogue: O = O^T / l, bf16, 4 consecutive dims per store ----------
   l_run = xor32_16_sum(l_run);
