@@ -29,7 +29,8 @@ STATUS = {0: "ok", 1: "null pointer", 2: "invalid shape or argument",
           5: "kernel launch failed", 6: "output overlaps an input"}
 
 # Every symbol the header declares (checked by the tests).
-EXPORTS = ("attn_rope_table", "attn_rope_table_bytes", "attn_prefill", "attn_decode",
+EXPORTS = ("attn_rope_table", "attn_rope_table_bytes", "attn_prefill",
+           "attn_prefill_workspace_bytes", "attn_decode",
            "attn_decode_workspace_bytes", "prope_apply", "attn_status_string",
            "attn_last_error")
 
@@ -61,8 +62,10 @@ def load(path: str = LIB_PATH):
     lib.attn_rope_table_bytes.restype = sz
     lib.attn_rope_table.argtypes = [vp, i32, i32, i32, _Rope, vp]
     lib.attn_rope_table.restype = ctypes.c_int
+    lib.attn_prefill_workspace_bytes.argtypes = [i32, i32, i32, i32, _Rope, i32, ctypes.c_int]
+    lib.attn_prefill_workspace_bytes.restype = sz
     lib.attn_prefill.argtypes = [vp, vp, vp, vp] + [i32] * 7 + [
-        ctypes.c_float, _Rope, i32, vp, ctypes.c_int, vp]
+        ctypes.c_float, _Rope, i32, vp, vp, sz, ctypes.c_int, vp]
     lib.attn_prefill.restype = ctypes.c_int
     lib.attn_decode_workspace_bytes.argtypes = [i32] * 5
     lib.attn_decode_workspace_bytes.restype = sz
@@ -118,14 +121,24 @@ def rope_table(T: int, *, head_dim: int, rotary_dims: int, theta: float, pos0: i
     return tab
 
 
+def prefill_workspace_bytes(B: int, T: int, Hkv: int, Dk: int, *, rotary_dims: int,
+                            theta: float = 10000.0, rope_mask: int = 3,
+                            dtype=torch.bfloat16) -> int:
+    code = 0 if dtype == torch.float32 else 1
+    return int(load().attn_prefill_workspace_bytes(B, T, Hkv, Dk, _Rope(rotary_dims, theta),
+                                                   rope_mask, code))
+
+
 def prefill(q, k, v, *, window: int = 0, scale: float | None = None,
             rotary_dims: int = 0, theta: float = 10000.0,
             rope_mask: int = ROPE_Q | ROPE_K, pos0: int = 0, out=None,
-            table=None):
+            table=None, workspace=None):
     """q [B,T,Hq,Dk], k [B,T,Hkv,Dk], v [B,T,Hkv,Dv] -> o [B,T,Hq,Dv].
 
     ``table`` is a cos/sin table from rope_table() for the same T, pos0 and
-    RoPE settings; it is built here when not given."""
+    RoPE settings; it is built here when not given. ``workspace`` is a device
+    byte buffer of at least prefill_workspace_bytes(); allocated here when not
+    given."""
     lib = load()
     B, T, Hq, Dk = q.shape
     Hkv, Dv = k.shape[2], v.shape[3]
@@ -140,10 +153,16 @@ def prefill(q, k, v, *, window: int = 0, scale: float | None = None,
         table = rope_table(T, head_dim=Dk, rotary_dims=rotary_dims, theta=theta, pos0=pos0,
                            device=q.device)
     tab_ptr = _dev(table, "table") if table is not None else None
+    need = int(lib.attn_prefill_workspace_bytes(B, T, Hkv, Dk, _Rope(rotary_dims, theta),
+                                                int(rope_mask), _dtype_code(q)))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = _dev(workspace, "workspace") if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(lib.attn_prefill(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(o, "o"),
                             B, T, Hq, Hkv, Dk, Dv, int(window), float(scale),
                             _Rope(rotary_dims, theta), int(rope_mask), tab_ptr,
-                            _dtype_code(q), _stream(q)))
+                            ws_ptr, ws_bytes, _dtype_code(q), _stream(q)))
     return o
 
 

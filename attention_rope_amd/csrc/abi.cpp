@@ -59,6 +59,14 @@ bool prefill_uses_table(attn_rope_t rope, int32_t rope_mask) {
   return rope.rotary_dims > 0 && (rope_mask & (ATTN_ROPE_Q | ATTN_ROPE_K)) != 0;
 }
 
+// The bf16 MFMA path turns K's rotary dims ahead of the attention kernel, into
+// the workspace, for the rotary widths it is built for.
+bool prefill_turns_k_ahead(int32_t Dk, attn_rope_t rope, int32_t rope_mask) {
+  const int r = rope.rotary_dims;
+  return (rope_mask & ATTN_ROPE_K) && r > 0 && (r == Dk || r == Dk / 4) && r % 8 == 0 &&
+         (Dk == 128 || Dk == 256 || Dk == 512);
+}
+
 }  // namespace
 
 extern "C" {
@@ -102,11 +110,18 @@ attn_status_t attn_rope_table(void* table, int32_t T, int32_t pos0, int32_t head
                        "rope table");
 }
 
+size_t attn_prefill_workspace_bytes(int32_t B, int32_t T, int32_t Hkv, int32_t Dk,
+                                    attn_rope_t rope, int32_t rope_mask, attn_dtype_t dtype) {
+  if (B <= 0 || T <= 0 || Hkv <= 0 || dtype != ATTN_BF16) return 0;
+  if (!prefill_turns_k_ahead(Dk, rope, rope_mask)) return 0;
+  return (size_t)B * T * Hkv * rope.rotary_dims * 2;
+}
+
 attn_status_t attn_prefill(const void* q, const void* k, const void* v, void* o,
                            int32_t B, int32_t T, int32_t Hq, int32_t Hkv, int32_t Dk,
                            int32_t Dv, int32_t window, float scale, attn_rope_t rope,
-                           int32_t rope_mask, const void* rope_table, attn_dtype_t dtype,
-                           void* stream) {
+                           int32_t rope_mask, const void* rope_table, void* workspace,
+                           size_t workspace_bytes, attn_dtype_t dtype, void* stream) {
   if (dtype != ATTN_F32 && dtype != ATTN_BF16)
     return fail(ATTN_ERR_UNSUPPORTED, "dtype %d is not ATTN_F32 or ATTN_BF16", (int)dtype);
   if (B < 0 || T < 0) return fail(ATTN_ERR_SHAPE, "B=%d and T=%d must be >= 0", B, T);
@@ -135,6 +150,17 @@ attn_status_t attn_prefill(const void* q, const void* k, const void* v, void* o,
     return fail(ATTN_ERR_ALIAS, "o must not overlap q, k, v or rope_table");
   if ((int64_t)B * T * Hq / 4 + 1 > INT32_MAX)
     return fail(ATTN_ERR_SHAPE, "B*T*Hq too large");
+  const size_t nws = attn_prefill_workspace_bytes(B, T, Hkv, Dk, rope, rope_mask, dtype);
+  if (nws > 0) {
+    if (!workspace || workspace_bytes < nws)
+      return fail(ATTN_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu at %p)", nws,
+                  workspace_bytes, workspace);
+    if (!aligned16(workspace)) return fail(ATTN_ERR_SHAPE, "workspace must be 16-byte aligned");
+    if (overlap(workspace, nws, q, nq) || overlap(workspace, nws, k, nk) ||
+        overlap(workspace, nws, v, nv) || overlap(workspace, nws, o, no) ||
+        overlap(workspace, nws, rope_table, attn_rope_table_bytes(T, rope.rotary_dims)))
+      return fail(ATTN_ERR_ALIAS, "workspace must not overlap q, k, v, o or rope_table");
+  }
 
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   attn::PrefillArgs a{};
@@ -146,7 +172,16 @@ attn_status_t attn_prefill(const void* q, const void* k, const void* v, void* o,
   a.rope_k = rot && (rope_mask & ATTN_ROPE_K);
   a.scale = scale;
   a.rope_tab = rot ? reinterpret_cast<const float2*>(rope_table) : nullptr;
-  if (dtype == ATTN_BF16 && attn::prefill_mfma_supported(Dk, Dv, Hq / Hkv, scale)) {
+  if (dtype == ATTN_BF16 &&
+      attn::prefill_mfma_supported(Dk, Dv, Hq / Hkv, scale, rot ? rope.rotary_dims : 0)) {
+    if (a.rope_k) {
+      // K's rotary dims turn once here, not once per query tile in the kernel.
+      attn_status_t r = launch_status(
+          attn::launch_rope_k_lead(k, workspace, a.rope_tab, B, T, Hkv, Dk, rope.rotary_dims, st),
+          "prefill (K rotation)");
+      if (r != ATTN_OK) return r;
+      a.k_rot = workspace;
+    }
     hipError_t e = attn::launch_prefill_mfma(a, st);
     if (e != hipErrorNotSupported) return launch_status(e, "prefill (mfma)");
   }

@@ -12,6 +12,10 @@ hipError_t launch_rope_table(float2* tab, int T, int P, int D, int pos0,
                              double theta, hipStream_t st);
 hipError_t launch_prope(const void* x, void* y, const int32_t* pos, int N, int H,
                         int D, int P, double theta, bool bf16, hipStream_t st);
+// out[b, t, h, 0:R] = rotation of the first R dims of k[b, t, h, :] (bf16) by
+// the table row of token t; R = 2 * table pairs, a multiple of 8.
+hipError_t launch_rope_k_lead(const void* k, void* out, const float2* tab, int B, int T,
+                              int H, int D, int R, hipStream_t st);
 
 // ---- prefill ----------------------------------------------------------------
 struct PrefillArgs {
@@ -20,6 +24,7 @@ struct PrefillArgs {
   const void* v;
   void* o;
   const float2* rope_tab;  // [T][rot_pairs] cos/sin, or nullptr
+  const void* k_rot;       // [B][T][Hkv][2*rot_pairs] K's rotary dims, turned (bf16 MFMA path)
   int B, T, Hq, Hkv, Dk, Dv;
   int window;              // 0: full causal
   int rot_pairs;           // rotary pairs (0: none)
@@ -28,9 +33,10 @@ struct PrefillArgs {
 };
 
 // MFMA flash kernel (bf16). Returns hipErrorNotSupported for shapes it has no
-// instantiation for; the caller then uses the general kernel.
+// instantiation for; the caller then uses the general kernel. When K turns,
+// k_rot must hold K's rotary dims already turned (launch_rope_k_lead).
 hipError_t launch_prefill_mfma(const PrefillArgs& a, hipStream_t st);
-bool prefill_mfma_supported(int Dk, int Dv, int G, float scale);
+bool prefill_mfma_supported(int Dk, int Dv, int G, float scale, int rotary_dims);
 
 // General kernel: any supported shape, fp32 or bf16.
 hipError_t launch_prefill_general(const PrefillArgs& a, bool bf16, hipStream_t st);

@@ -1,6 +1,6 @@
 // prefill_mfma.hip — flash-style causal / sliding-window GQA prefill on gfx950
-// bf16 matrix cores (v_mfma_f32_16x16x32_bf16), with RoPE fused into the Q and
-// K loads.
+// bf16 matrix cores (v_mfma_f32_16x16x32_bf16), with RoPE applied on the way
+// in.
 //
 // What it computes (Gemma 4 pages): "Gemma 4: End-to-End Architecture
 // Walkthrough", Phase 3 — section 3a (local layers: query i sees the window of
@@ -20,20 +20,24 @@
 //  * Each wave owns 16 rows and computes S^T = K Q^T with 16x16x32 MFMAs
 //    (M = 16 keys, N = 16 rows): every lane holds 8 scores of one query row,
 //    so the softmax max/sum need two cross-lane swaps. Q^T (DK/32 x 16 bytes
-//    per lane) and the O^T accumulator (DV/4 fp32 per lane) stay in registers;
-//    at 16 rows a wave fits in half the register file.
+//    per lane) and the O^T accumulator (DV/4 fp32 per lane) stay in registers.
 //  * O^T = V^T P^T (K = 32 keys per MFMA): the P^T operand is the lane's own
-//    scores when the key order inside the MFMA matches the score layout; V
-//    tiles are written to LDS transposed, in exactly that key order.
-//  * K tiles (32 keys) move HBM -> LDS by direct DMA (buffer loads with the
-//    lds flag): no staging registers, out-of-range rows read as zero. The
-//    rotated chunks of each K row sit in their own LDS region, so every thread
-//    turns exactly the chunks its own DMA wrote (one barrier per tile, all
-//    lanes busy), with cos/sin from the per-position table prefetched one tile
-//    ahead. Tiles are double-buffered; the next tile's loads overlap the
-//    current tile's matrix work.
-//  * K rows are XOR-swizzled in 16-byte chunks so the MFMA operand reads are
-//    bank-conflict free without the padding the 1 KB DMA blocks cannot have.
+//    scores when the key order inside the MFMA matches the score layout. V
+//    tiles sit in LDS in their natural [key][dim] layout and the V^T operand
+//    is read with the transposing LDS read (ds_read_b64_tr_b16), two reads
+//    of 4 keys each per operand, in that key order.
+//  * K and V tiles (32 keys) move HBM -> LDS by direct DMA (buffer loads with
+//    the lds flag): no staging registers, no VALU work, rows past T read as
+//    zero. The rotated leading dims of K come already turned from a rotation
+//    pass that runs once per key (not once per query tile) into a workspace;
+//    each K tile keeps them in a region of its own, so every DMA block has
+//    one source. Tiles run in a 3-stage ring, loaded two tiles ahead, with one
+//    barrier per tile. The DMAs are issued from inline asm: the compiler then
+//    sees no LDS DMA and adds none of its conservative "wait for every LDS
+//    DMA" stalls before LDS reads; the kernel waits explicitly instead.
+//  * K and V rows are XOR-swizzled in 16-byte chunks so the MFMA operand reads
+//    (plain and transposing) are bank-conflict free without the padding that
+//    1 KB DMA blocks cannot have.
 //  * Only key tiles intersecting the causal band / sliding window are visited
 //    (window-aware skipping); masking runs only on tiles that cross the
 //    diagonal or the window edge.
@@ -55,9 +59,9 @@ constexpr int NT = NW * 64;
 constexpr int RW = 16;         // query rows per wave
 constexpr int BN = 32;         // keys per tile
 // Buffer descriptor word 3 for raw (stride 0) 32-bit-format buffers on gfx9.
-constexpr int kBufFlags = 0x00020000;
+constexpr uint32_t kBufWord3 = 0x00020000u;
 
-typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 
 template <int DK, int DV, int G, int RCH>
 struct Cfg {
@@ -68,26 +72,33 @@ struct Cfg {
   // K tile: rotated region [32][RCH] chunks, then plain region [32][NP].
   static constexpr int KR_BYTES = BN * RCH * 16;
   static constexpr int KT_BYTES = BN * NC * 16;
-  static constexpr int KR_DMA = KR_BYTES / 1024;   // 1 KB DMA blocks per region
+  static constexpr int VC = DV / 8;           // 16-byte chunks per V row
+  static constexpr int VT_BYTES = BN * VC * 16;
+  static constexpr int ST_BYTES = KT_BYTES + VT_BYTES;  // one ring stage
+  static constexpr int STAGES = 3;
+  static constexpr int LDS_BYTES = STAGES * ST_BYTES;
+  // 1 KB DMA blocks per tile: rotated K, plain K, V.
+  static constexpr int KR_DMA = KR_BYTES / 1024;
   static constexpr int KP_DMA = (KT_BYTES - KR_BYTES) / 1024;
-  // V^T tile: [DV][VS] bf16, keys in the permuted order of the score layout.
-  static constexpr int VS = BN + 8;           // padded row (80 bytes)
-  static constexpr int VT_BYTES = DV * VS * 2;
-  static constexpr int KSTAGES = 3;           // K tiles in flight: t, t+1, t+2
-  static constexpr int LDS_BYTES = KSTAGES * KT_BYTES + 2 * VT_BYTES;
-  static constexpr int VU = (BN / 2) * (DV / 8);   // V units: 2 keys x 8 dims
-  static constexpr int VUT = (VU + NT - 1) / NT;
-  static constexpr int KROT = (KR_DMA + NW - 1) / NW;  // rotated blocks per wave
-  static constexpr int KDMA_W = KROT + (KP_DMA + NW - 1) / NW;  // K DMA issues per wave (max)
-  // Every wave issues the same number of K DMAs per tile, so "everything but
-  // the newest K tile has landed" is one vmcnt value.
-  static constexpr bool UNIFORM = KR_DMA % NW == 0 && KP_DMA % NW == 0;
+  static constexpr int V_DMA = VT_BYTES / 1024;
+  static constexpr int N_DMA = KR_DMA + KP_DMA + V_DMA;
+  static constexpr int DMA_W = N_DMA / NW;    // DMA issues per wave per tile
+  // Region boundaries fall on whole issue slots: slot i's region is the same
+  // for every wave and known at compile time.
+  static constexpr bool ALIGNED = KR_DMA % NW == 0 && KP_DMA % NW == 0;
+  __host__ __device__ static constexpr int region(int n) {
+    return n < KR_DMA ? 0 : n < KR_DMA + KP_DMA ? 1 : 2;
+  }
   static_assert(ROWS % G == 0 && PW % RW == 0, "rows must split evenly over the heads");
-  static_assert(KR_BYTES % 1024 == 0 && KT_BYTES % 1024 == 0, "DMA blocks");
+  static_assert(KR_BYTES % 1024 == 0 && KT_BYTES % 1024 == 0 && VT_BYTES % 1024 == 0,
+                "DMA blocks");
+  static_assert(N_DMA % NW == 0, "every wave issues the same number of DMAs per tile");
+  static_assert(DMA_W < 16, "vmcnt field");
+  static_assert(LDS_BYTES <= 160 * 1024, "LDS");
   static_assert(DK % 32 == 0 && DV % 16 == 0, "MFMA tiling");
 };
 
-// XOR swizzle of 16-byte chunks inside a K region row of `width` chunks. The
+// XOR swizzle of 16-byte chunks inside a region row of `width` chunks. The
 // mask P-1 uses the largest power of two P <= 16 dividing the width, so the
 // swizzled index stays inside the row; with P = 16, 16 consecutive rows
 // reading the same chunk hit 16 distinct bank groups.
@@ -142,24 +153,43 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
 
-// LDS stores issued as plain instructions. The compiler treats every LDS
-// access that may alias an in-flight LDS DMA as needing that DMA to finish
-// first, which would drain the tile loaded two steps ahead. These stores never
-// touch a DMA target, so they are issued directly with no memory clobber: they
-// keep their order with the other volatile asm (the barrier below) and their
-// register dependences, and lds_barrier waits for them before publishing.
-__device__ __forceinline__ void lds_store_b128(uint32_t addr, u32x4 v) {
-  asm volatile("ds_write_b128 %0, %1" ::"v"(addr), "v"(v));
+// Raw buffer descriptor (stride 0): reads at byte offsets >= bytes return 0.
+__device__ __forceinline__ u32x4 buffer_desc(const void* base, uint32_t bytes) {
+  const uint64_t p = (uint64_t)(uintptr_t)base;
+  return u32x4{(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)p),
+               (uint32_t)__builtin_amdgcn_readfirstlane((int)((uint32_t)(p >> 32) & 0xffffu)),
+               (uint32_t)__builtin_amdgcn_readfirstlane((int)bytes), kBufWord3};
 }
-__device__ __forceinline__ void lds_store_b32(uint32_t addr, uint32_t v) {
-  asm volatile("ds_write_b32 %0, %1" ::"v"(addr), "v"(v));
+
+// One DMA: lane l copies 16 bytes at byte offset voff of the buffer into LDS
+// at lds + 16 l. M0 carries the LDS base and is restored afterwards. The
+// instruction counts in vmcnt like any buffer load; the caller waits for it.
+__device__ __forceinline__ void dma16(u32x4 desc, uint32_t lds, uint32_t voff) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds), "v"(voff), "s"(desc));
 }
-// Publish this wave's LDS stores to the workgroup and synchronise, without the
-// workgroup-scope fence of __syncthreads (which would also wait for the
-// in-flight DMA); the memory clobber keeps compiler-visible LDS accesses on
-// their side of the barrier.
+
+// Synchronise the workgroup after this wave's LDS reads have returned. Unlike
+// __syncthreads this carries no memory fence, which would also wait for the
+// DMAs still in flight; the memory clobber keeps LDS accesses on their side.
 __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Wait until at most n vector-memory operations of this wave are in flight
+// (vmcnt[3:0] = n, expcnt and lgkmcnt left alone), and keep the scheduler
+// from hoisting LDS reads of what landed above the wait.
+template <int n>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(n >= 0 && n < 16, "vmcnt field");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | n);
+  __builtin_amdgcn_sched_barrier(0);
 }
 
 template <int DK, int DV, int G, int RCH>
@@ -167,7 +197,6 @@ __global__ __launch_bounds__(NT, 1) void prefill_mfma_kernel(PrefillArgs a, int 
                                                              int contig) {
   using C = Cfg<DK, DV, G, RCH>;
   __shared__ __attribute__((aligned(1024))) unsigned char lds[C::LDS_BYTES];
-  unsigned char* const vt_base = lds + C::KSTAGES * C::KT_BYTES;  // 2 V^T buffers
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -193,145 +222,68 @@ __global__ __launch_bounds__(NT, 1) void prefill_mfma_kernel(PrefillArgs a, int 
   const int kb_lo = kv_lo / BN;
   const int kb_hi = (kv_hi + BN - 1) / BN;
 
-  // Buffer descriptors: K and V of this (batch, KV head); rows past T read 0.
+  // ---- DMA sources: K (plain dims), K's rotated dims, V of this (b, head) --
   const int krow = a.Hkv * DK * 2, vrow = a.Hkv * DV * 2;  // bytes per token
-  const __amdgpu_buffer_rsrc_t kres = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)((const char*)a.k + ((int64_t)b * T * a.Hkv + kvh) * DK * 2), (short)0,
-      (T - 1) * krow + DK * 2, kBufFlags);
-  const __amdgpu_buffer_rsrc_t vres = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)((const char*)a.v + ((int64_t)b * T * a.Hkv + kvh) * DV * 2), (short)0,
-      (T - 1) * vrow + DV * 2, kBufFlags);
-  const bool rot_k = RCH > 0 && a.rope_k;
   const bool rot_q = RCH > 0 && a.rope_q;
-  const int tab_row = a.rot_pairs * 8;  // bytes per table row
-  const __amdgpu_buffer_rsrc_t tres = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)a.rope_tab, (short)0, (RCH > 0 && (rot_k || rot_q)) ? T * tab_row : 0, kBufFlags);
+  const bool krot_ws = RCH > 0 && a.rope_k;  // rotated dims from the workspace
+  const int rrow = krot_ws ? a.Hkv * RCH * 16 : krow;
+  const u32x4 kdesc = buffer_desc((const char*)a.k + ((int64_t)b * T * a.Hkv + kvh) * DK * 2,
+                                  (T - 1) * krow + DK * 2);
+  const u32x4 vdesc = buffer_desc((const char*)a.v + ((int64_t)b * T * a.Hkv + kvh) * DV * 2,
+                                  (T - 1) * vrow + DV * 2);
+  const u32x4 rdesc =
+      krot_ws ? buffer_desc((const char*)a.k_rot + ((int64_t)b * T * a.Hkv + kvh) * RCH * 16,
+                            (T - 1) * rrow + RCH * 16)
+              : kdesc;
 
-  // ---- K: DMA into LDS; this thread turns the rotated chunks it loaded -----
-  f32x4 ktab[C::KROT > 0 ? C::KROT : 1][2];
-  auto rot_chunk = [&](int i, int& r, int& c) {
-    const int q = (i * NW + wave) * 64 + lane;
-    r = q / (RCH > 0 ? RCH : 1);
-    c = kswz<RCH>(r, q % (RCH > 0 ? RCH : 1));  // swizzle is an involution
-  };
-  auto load_ktab = [&](int kb) {
-    const int j0 = kb * BN;
+  // Block n of a tile (n = i*NW + wave) covers 64 chunks; this lane's chunk's
+  // byte offset inside tile row 0 and row stride are fixed, so a tile adds
+  // j0 * stride. Region by block: rotated K, plain K, V.
+  uint32_t dma_off[C::DMA_W];
 #pragma unroll
-    for (int i = 0; i < C::KROT; ++i) {
-      if (C::KR_DMA % NW == 0 || i * NW + wave < C::KR_DMA) {
-        int r, c;
-        rot_chunk(i, r, c);
-        const int off = min(j0 + r, T - 1) * tab_row + c * 32;
-        ktab[i][0] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(tres, off, 0, 0));
-        ktab[i][1] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(tres, off + 16, 0, 0));
-      }
-    }
-  };
-  auto dma_k = [&](int kb, unsigned char* st) {
-    const int j0 = kb * BN;
-#pragma unroll
-    for (int i = 0; i < C::KROT; ++i) {
-      if (C::KR_DMA % NW == 0 || i * NW + wave < C::KR_DMA) {
-        int r, c;
-        rot_chunk(i, r, c);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(kres, (lds_void*)(st + (i * NW + wave) * 1024),
-                                                 16, (j0 + r) * krow + c * 16, 0, 0, 0);
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < (C::KP_DMA + NW - 1) / NW; ++i) {
-      const int n = i * NW + wave;
-      if (C::KP_DMA % NW == 0 || n < C::KP_DMA) {
-        const int q = n * 64 + lane;
-        constexpr int NPd = C::NP > 0 ? C::NP : 1;  // loop is empty when NP == 0
-        const int r = q / NPd;
-        const int c = RCH + kswz<NPd>(r, q % NPd);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            kres, (lds_void*)(st + C::KR_BYTES + n * 1024), 16, (j0 + r) * krow + c * 16, 0, 0,
-            0);
-      }
-    }
-  };
-  auto rotate_k = [&](unsigned char* st) {
-#pragma unroll
-    for (int i = 0; i < C::KROT; ++i) {
-      if (C::KR_DMA % NW == 0 || i * NW + wave < C::KR_DMA) {
-        const unsigned char* p = st + ((i * NW + wave) * 64 + lane) * 16;
-        lds_store_b128(lds_addr(p), rotate4(*(const u32x4*)p, ktab[i][0], ktab[i][1]));
-      }
-    }
-  };
-
-  // ---- V: registers, then LDS transposed in the score-matched key order ----
-  // Slot 8g + i of a V^T row holds key 16(i/4) + 4g + (i%4): key 16a + 4g + r
-  // sits in slot 8g + 4a + r, so an even/odd key pair fills 2 adjacent slots.
-  // Unit u = key pair kp (keys 2kp, 2kp+1) x 8 dims d8; a step loads the next
-  // tile's units and writes them transposed at its end.
-  u32x4 vreg[C::VUT][2];
-  auto load_v = [&](int kb, u32x4 (&vr)[C::VUT][2]) {
-    const int j0 = kb * BN;
-#pragma unroll
-    for (int ut = 0; ut < C::VUT; ++ut) {
-      const int u = tid + NT * ut;
-      const int kp = u % 16, d8 = u / 16;
-#pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        vr[ut][e] = (C::VU % NT == 0 || u < C::VU)
-                        ? __builtin_amdgcn_raw_buffer_load_b128(vres, (j0 + 2 * kp + e) * vrow + d8 * 16, 0, 0)
-                        : u32x4{0, 0, 0, 0};
-      }
-    }
-  };
-  auto store_v = [&](const u32x4 (&vr)[C::VUT][2], unsigned char* vt) {
-    uint16_t* Vt = (uint16_t*)vt;
-#pragma unroll
-    for (int ut = 0; ut < C::VUT; ++ut) {
-      const int u = tid + NT * ut;
-      if (C::VU % NT == 0 || u < C::VU) {
-        const int kp = u % 16, d8 = u / 16;
-        const int k = 2 * kp;  // = 16a + 4g' + r with r even
-        const int slot = 8 * ((k % 16) / 4) + 4 * (k / 16) + (k % 4);
-#pragma unroll
-        for (int dd = 0; dd < 8; ++dd) {
-          const int wi = dd / 2;
-          const uint32_t w = (dd % 2 == 0) ? ((vr[ut][0][wi] & 0xffffu) | (vr[ut][1][wi] << 16))
-                                           : ((vr[ut][0][wi] >> 16) | (vr[ut][1][wi] & 0xffff0000u));
-          lds_store_b32(lds_addr(Vt + (8 * d8 + dd) * C::VS + slot), w);
-        }
-      }
-    }
-  };
-
-  // Wait until every load issued before the newest K tile's DMAs has
-  // completed (loads complete in issue order and those DMAs are always the
-  // last loads issued), then keep the scheduler from hoisting LDS reads of the
-  // landed tile above the wait.
-  auto wait_all_but_newest_k = [&]() {
-    if constexpr (C::UNIFORM) {
-      constexpr int n = C::KDMA_W;  // K DMAs per wave per tile
-      static_assert(n < 16, "vmcnt field");
-      // s_waitcnt: vmcnt[3:0] = n, expcnt = 7 (no wait), lgkmcnt = 15 (no wait)
-      __builtin_amdgcn_s_waitcnt(0x0F70 | n);
+  for (int i = 0; i < C::DMA_W; ++i) {
+    const int n = i * NW + wave;
+    if (n < C::KR_DMA) {
+      constexpr int RCHd = RCH > 0 ? RCH : 1;  // branch is dead when RCH == 0
+      const int q = n * 64 + lane, r = q / RCHd;
+      dma_off[i] = r * rrow + kswz<RCHd>(r, q % RCHd) * 16;
+    } else if (n < C::KR_DMA + C::KP_DMA) {
+      constexpr int NPd = C::NP > 0 ? C::NP : 1;
+      const int q = (n - C::KR_DMA) * 64 + lane, r = q / NPd;
+      dma_off[i] = r * krow + (RCH + kswz<NPd>(r, q % NPd)) * 16;
     } else {
-      __builtin_amdgcn_s_waitcnt(0);
+      const int q = (n - C::KR_DMA - C::KP_DMA) * 64 + lane, r = q / C::VC;
+      dma_off[i] = r * vrow + kswz<C::VC>(r, q % C::VC) * 16;
     }
-    __builtin_amdgcn_sched_barrier(0);
-  };
-  auto wait_all = [&]() {
-    __builtin_amdgcn_s_waitcnt(0);
-    __builtin_amdgcn_sched_barrier(0);
+  }
+  auto dma_tile = [&](int kb, int stage) {
+    const int j0 = kb * BN;
+    const uint32_t st = lds_addr(lds) + stage * C::ST_BYTES;
+    // Blocks are laid out back to back (rotated K, plain K, V), so block n
+    // lands at st + 1024 n whatever its region.
+#pragma unroll
+    for (int i = 0; i < C::DMA_W; ++i) {
+      const int n = i * NW + wave;
+      const int reg = C::ALIGNED ? C::region(i * NW) : C::region(n);
+      if (reg == 0)
+        dma16(rdesc, st + n * 1024, dma_off[i] + j0 * rrow);
+      else if (reg == 1)
+        dma16(kdesc, st + n * 1024, dma_off[i] + j0 * krow);
+      else
+        dma16(vdesc, st + n * 1024, dma_off[i] + j0 * vrow);
+    }
   };
 
-  // ---- prologue: tile 0 (K, V, table), the Q rows, then tile 1's K DMA ----
+  // ---- prologue: tiles 0 and 1 in flight around the Q load ----------------
   const int n_tiles = kb_hi - kb_lo;
-  if (n_tiles > 0) {
-    dma_k(kb_lo, lds);
-    if (rot_k) load_ktab(kb_lo);
-    load_v(kb_lo, vreg);
-  }
+  if (n_tiles > 0) dma_tile(kb_lo, 0);
+
   // Q^T operand: step s covers dims 32s + 8g .. 32s + 8g + 7 of this row.
   bf16x8 qf[DK / 32];
   {
+    const int tab_row = a.rot_pairs * 8;  // bytes per table row
+    const __amdgpu_buffer_rsrc_t tres = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)a.rope_tab, (short)0, rot_q ? T * tab_row : 0, (int)kBufWord3);
     const int prow = valid ? pos : T - 1;
     const uint16_t* qrow =
         (const uint16_t*)a.q + (((int64_t)b * T + prow) * a.Hq + head) * DK + 8 * g;
@@ -361,13 +313,10 @@ __global__ __launch_bounds__(NT, 1) void prefill_mfma_kernel(PrefillArgs a, int 
     }
   }
   if (n_tiles > 0) {
-    dma_k(kb_lo + 1, lds + C::KT_BYTES);  // may lie past the range: never read
-    wait_all_but_newest_k();  // tile 0 landed; tile 1's K may still be in flight
-    if (rot_k) rotate_k(lds);
-    store_v(vreg, vt_base);
+    dma_tile(kb_lo + 1, 1);  // may lie past the range: never read
+    wait_vm<C::DMA_W>();     // tile 0 landed; tile 1 may still be in flight
     lds_barrier();
   }
-
 
   // ---- online softmax state (one row per lane; 4 lanes share a row) --------
   // scores to log2 units; kept > 0 so a masked -inf score never meets a zero
@@ -383,12 +332,22 @@ __global__ __launch_bounds__(NT, 1) void prefill_mfma_kernel(PrefillArgs a, int 
   const KAddr<(RCH > 0 ? RCH : 16)> kaddr_r0(0, r16, g), kaddr_r1(0, r16 + 16, g);
   const KAddr<(C::NP > 0 ? C::NP : 16)> kaddr_p0(C::KR_BYTES, r16, g),
       kaddr_p1(C::KR_BYTES, r16 + 16, g);
-  const int vt_off = (r16 * C::VS + 8 * g) * 2;  // + 16*db*VS*2
+  // V^T operand, transposing reads: in each 16-lane group, lane 4r + c reads
+  // dims 16d + 4c .. 16d + 4c + 3 of key 16h + 4g + r; the row's swizzle is
+  // x = 4g + r (both halves), so chunk 2d + (c >> 1) sits at
+  // 2(d ^ (x >> 1)) + ((c >> 1) ^ (x & 1)).
+  const int vx = 4 * g + (r16 >> 2), vc = r16 & 3;
+  const int v_lane =
+      C::KT_BYTES + vx * C::VC * 16 + (((vc >> 1) ^ (vx & 1)) << 4) + ((vc & 1) << 3);
+  const int v_x2 = vx >> 1;
 
-  auto compute = [&](const unsigned char* st, const unsigned char* vt, int kb) {
+  auto live = [&](int kb) {
     const int j0 = kb * BN;
-    if (j0 > whi) return;                            // beyond every row (causal)
-    if (W > 0 && j0 + BN - 1 <= wlo - W) return;     // before every row's window
+    return j0 <= whi && !(W > 0 && j0 + BN - 1 <= wlo - W);
+  };
+
+  auto compute = [&](const unsigned char* st, int kb) {
+    const int j0 = kb * BN;
     f32x4 s0 = f32x4{}, s1 = f32x4{};
     // dims 32s + 8g..: s < RCH/4 in the rotated region, the rest in the plain one
 #pragma unroll
@@ -439,37 +398,30 @@ __global__ __launch_bounds__(NT, 1) void prefill_mfma_kernel(PrefillArgs a, int 
     const bf16x8 pop = __builtin_shufflevector(pa, pb, 0, 1, 2, 3, 4, 5, 6, 7);
 #pragma unroll
     for (int d = 0; d < DV / 16; ++d) {
-      const bf16x8 va = *(const bf16x8*)(vt + vt_off + d * 16 * C::VS * 2);
+      // d ^ v_x2 only changes the low 3 bits of d, staying inside the row
+      const unsigned char* p = st + v_lane + ((d ^ v_x2) << 5);
+      const bf16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)p);
+      const bf16x4 v1 =
+          __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p + 16 * C::VC * 16));
+      const bf16x8 va = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
       oacc[d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pop, oacc[d], 0, 0, 0);
     }
   };
 
-  // ---- main loop: K tiles in 3 LDS stages, V^T in 2 buffers ---------------
-  // Step t computes tile t while K(t+1) (issued a step ago) and K(t+2)
-  // (issued now, last) load, with V(t+1) and the cos/sin of K(t+1); it then
-  // turns K(t+1) and writes V^T(t+1). Every step issues the same loads, also
+  // ---- main loop: a 3-stage ring, tiles loaded two ahead --------------------
+  // Step t issues tile t+2 into the stage tile t-1 used, computes tile t, then
+  // waits for tile t+1 (everything but the newest DMAs, which are always the
+  // last loads issued) and synchronises. Every step issues the same DMAs, also
   // the last two (their tiles may lie past the range or past T, where the
-  // buffer descriptors return zeros, and are never read), so one vmcnt value
-  // separates the newest K tile from everything older on every path.
+  // descriptors return zeros, and are never read).
   for (int t = 0; t < n_tiles; ++t) {
     const int kb = kb_lo + t;
-    unsigned char* ks = lds + (t % 3) * C::KT_BYTES;
-    unsigned char* k1 = lds + ((t + 1) % 3) * C::KT_BYTES;
-    unsigned char* k2 = lds + ((t + 2) % 3) * C::KT_BYTES;
-    unsigned char* vt = vt_base + (t & 1) * C::VT_BYTES;
-    unsigned char* vt1 = vt_base + ((t + 1) & 1) * C::VT_BYTES;
-    if (rot_k) load_ktab(kb + 1);
-    load_v(kb + 1, vreg);
-    dma_k(kb + 2, k2);
-    compute(ks, vt, kb);
-    wait_all_but_newest_k();  // K(t+1), V(t+1) and its table landed
-    if (t + 1 < n_tiles) {
-      if (rot_k) rotate_k(k1);
-      store_v(vreg, vt1);
-    }
-    lds_barrier();  // tile t+1 complete everywhere; tile t buffers free
+    dma_tile(kb + 2, (t + 2) % 3);
+    if (live(kb)) compute(lds + (t % 3) * C::ST_BYTES, kb);
+    wait_vm<C::DMA_W>();  // tile t+1 landed
+    lds_barrier();        // ... for every wave; stage of tile t free
   }
-  wait_all();  // no DMA may still target LDS when the block ends
+  wait_vm<0>();  // no DMA may still target LDS when the block ends
 
   // ---- epilogue: O = O^T / l, bf16, 4 consecutive dims per store ----------
   l_run = xor32_16_sum(l_run);
@@ -522,14 +474,18 @@ hipError_t dispatch_g(const PrefillArgs& a, hipStream_t st) {
 
 }  // namespace
 
-bool prefill_mfma_supported(int Dk, int Dv, int G, float scale) {
+bool prefill_mfma_supported(int Dk, int Dv, int G, float scale, int rotary_dims) {
   const bool shape = (Dk == 128 && Dv == 128) || (Dk == 256 && Dv == 256) ||
                      (Dk == 512 && Dv == 256);
-  return shape && (G == 1 || G == 2 || G == 4 || G == 8) && scale >= 0.f;
+  const bool rot = rotary_dims == 0 || rotary_dims == Dk / 4 || rotary_dims == Dk;
+  return shape && rot && (G == 1 || G == 2 || G == 4 || G == 8) && scale >= 0.f;
 }
 
 hipError_t launch_prefill_mfma(const PrefillArgs& a, hipStream_t st) {
-  if ((a.rope_q || a.rope_k) && (2 * a.rot_pairs) % 8 != 0) return hipErrorNotSupported;
+  const int rdims = (a.rope_q || a.rope_k) ? 2 * a.rot_pairs : 0;
+  if (!prefill_mfma_supported(a.Dk, a.Dv, a.Hq / a.Hkv, a.scale, rdims))
+    return hipErrorNotSupported;
+  if (a.rope_k && rdims > 0 && !a.k_rot) return hipErrorInvalidValue;
   // 32-bit buffer offsets: one batch's K or V, and the cos/sin table, < 2 GiB.
   const int64_t per_b = (int64_t)a.T * a.Hkv * (a.Dk > a.Dv ? a.Dk : a.Dv) * 2;
   if (per_b >= (int64_t)1 << 31 || (int64_t)a.T * a.rot_pairs * 8 >= (int64_t)1 << 31)

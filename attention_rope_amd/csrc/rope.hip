@@ -69,6 +69,45 @@ __global__ void prope_kernel(const T_* __restrict__ x, T_* __restrict__ y,
   }
 }
 
+// K's rotary dims, turned once per key for the MFMA prefill: one thread per
+// (token, head, 8-dim chunk c < R/8) turns 4 pairs with the table row of its
+// token and writes them to out[b, t, h, 8c .. 8c+7] (bf16, fp32 arithmetic).
+__global__ void rope_k_lead_kernel(const uint16_t* __restrict__ k, uint16_t* __restrict__ out,
+                                   const float2* __restrict__ tab, int64_t n_chunks, int T,
+                                   int H, int D, int RC) {
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= n_chunks) return;
+  const int c = (int)(idx % RC);
+  const int64_t nh = idx / RC;  // (b*T + t)*H + h
+  const int t = (int)((nh / H) % T);
+  const u32x4 w = *reinterpret_cast<const u32x4*>(k + nh * D + 8 * c);
+  const f32x4 t0 = *reinterpret_cast<const f32x4*>(tab + (int64_t)t * (4 * RC) + 4 * c);
+  const f32x4 t1 = *reinterpret_cast<const f32x4*>(tab + (int64_t)t * (4 * RC) + 4 * c + 2);
+  u32x4 r;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const float cs = (j < 2) ? t0[2 * j] : t1[2 * (j - 2)];
+    const float sn = (j < 2) ? t0[2 * j + 1] : t1[2 * (j - 2) + 1];
+    const float x0 = bf16_lo(w[j]), x1 = bf16_hi(w[j]);
+    r[j] = pack_bf16x2(x0 * cs - x1 * sn, x0 * sn + x1 * cs);
+  }
+  *reinterpret_cast<u32x4*>(out + nh * (8 * RC) + 8 * c) = r;
+}
+
+hipError_t launch_rope_k_lead(const void* k, void* out, const float2* tab, int B, int T,
+                              int H, int D, int R, hipStream_t st) {
+  if (R % 8 != 0 || D % 8 != 0 || R > D) return hipErrorInvalidValue;
+  const int64_t n = (int64_t)B * T * H * (R / 8);
+  if (n == 0) return hipSuccess;
+  const int threads = 256;
+  const int64_t blocks = (n + threads - 1) / threads;
+  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(rope_k_lead_kernel, dim3((unsigned)blocks), dim3(threads), 0, st,
+                     reinterpret_cast<const uint16_t*>(k), reinterpret_cast<uint16_t*>(out),
+                     tab, n, T, H, D, R / 8);
+  return hipGetLastError();
+}
+
 hipError_t launch_rope_table(float2* tab, int T, int P, int D, int pos0,
                              double theta, hipStream_t st) {
   if ((int64_t)T * P == 0) return hipSuccess;

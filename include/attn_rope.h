@@ -97,13 +97,23 @@ attn_status_t attn_rope_table(void *table, int32_t T, int32_t pos0, int32_t head
  *   (512,256)}, Hq/Hkv in {1, 2, 4, 8}, scale >= 0 and rotary_dims a multiple
  *   of 8 in {0, Dk/4, Dk} runs the MFMA flash kernel; every other supported
  *   case runs a slower general kernel with the same results.
+ * Workspace: attn_prefill_workspace_bytes() bytes of device memory (0 when no
+ *   workspace is needed, then workspace may be NULL). The bf16 path turns the
+ *   rotary dims of every key once into it before attending; contents are
+ *   scratch, owned by the caller, and must not overlap any other argument.
+ *   Too small or NULL when needed: ATTN_ERR_WORKSPACE.
  * All tensor pointers must be 16-byte aligned.
  */
+size_t attn_prefill_workspace_bytes(int32_t B, int32_t T, int32_t Hkv, int32_t Dk,
+                                    attn_rope_t rope, int32_t rope_mask,
+                                    attn_dtype_t dtype);
+
 attn_status_t attn_prefill(const void *q, const void *k, const void *v, void *o,
                            int32_t B, int32_t T, int32_t Hq, int32_t Hkv,
                            int32_t Dk, int32_t Dv, int32_t window, float scale,
                            attn_rope_t rope, int32_t rope_mask,
-                           const void *rope_table, attn_dtype_t dtype,
+                           const void *rope_table, void *workspace,
+                           size_t workspace_bytes, attn_dtype_t dtype,
                            void *stream);
 
 /*

@@ -51,12 +51,13 @@ FAKE2 = P(0x20000000)
 
 def _prefill(lib, **kw):
     a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE2, B=1, T=8, Hq=4, Hkv=2, Dk=64, Dv=64,
-             window=0, scale=0.125, rope=R(0, 1e4), rope_mask=3, tab=None,
-             dtype=ar.ATTN_BF16, stream=None)
+             window=0, scale=0.125, rope=R(0, 1e4), rope_mask=3, tab=None, ws=None,
+             ws_bytes=0, dtype=ar.ATTN_BF16, stream=None)
     a.update(kw)
     return lib.attn_prefill(a["q"], a["k"], a["v"], a["o"], a["B"], a["T"], a["Hq"],
                             a["Hkv"], a["Dk"], a["Dv"], a["window"], a["scale"], a["rope"],
-                            a["rope_mask"], a["tab"], a["dtype"], a["stream"])
+                            a["rope_mask"], a["tab"], a["ws"], a["ws_bytes"], a["dtype"],
+                            a["stream"])
 
 
 def test_prefill_validation(lib):
@@ -79,6 +80,28 @@ def test_prefill_validation(lib):
     # empty problems are a no-op success, even with NULL pointers
     assert _prefill(lib, q=None, k=None, v=None, o=None, T=0) == 0
     assert lib.attn_last_error() == b""
+
+
+def test_prefill_workspace(lib):
+    # bf16 with K turning at a width the MFMA path serves: B*T*Hkv*R bf16
+    assert lib.attn_prefill_workspace_bytes(2, 8, 4, 128, R(32, 1e6), 3, ar.ATTN_BF16) == \
+        2 * 8 * 4 * 32 * 2
+    assert lib.attn_prefill_workspace_bytes(2, 8, 4, 256, R(256, 1e4), 2, ar.ATTN_BF16) == \
+        2 * 8 * 4 * 256 * 2
+    # nothing to turn ahead: q only, no rope, fp32, or a width the general path serves
+    assert lib.attn_prefill_workspace_bytes(2, 8, 4, 128, R(32, 1e6), 1, ar.ATTN_BF16) == 0
+    assert lib.attn_prefill_workspace_bytes(2, 8, 4, 128, R(0, 1e6), 3, ar.ATTN_BF16) == 0
+    assert lib.attn_prefill_workspace_bytes(2, 8, 4, 128, R(32, 1e6), 3, ar.ATTN_F32) == 0
+    assert lib.attn_prefill_workspace_bytes(2, 8, 4, 128, R(64, 1e6), 3, ar.ATTN_BF16) == 0
+    assert lib.attn_prefill_workspace_bytes(0, 8, 4, 128, R(32, 1e6), 3, ar.ATTN_BF16) == 0
+    kw = dict(Dk=128, Dv=128, rope=R(32, 1e6), tab=P(0x30000000))
+    need = 1 * 8 * 2 * 32 * 2
+    assert _prefill(lib, **kw) == 4                                   # missing
+    assert _prefill(lib, ws=P(0x50000000), ws_bytes=need - 1, **kw) == 4  # too small
+    assert b"workspace" in lib.attn_last_error()
+    assert _prefill(lib, ws=P(0x50000008), ws_bytes=need, **kw) == 2    # misaligned
+    assert _prefill(lib, ws=FAKE, ws_bytes=need, **kw) == 6             # overlaps q/k/v
+    assert _prefill(lib, ws=FAKE2, ws_bytes=need, **kw) == 6            # overlaps o
 
 
 def test_rope_table_validation(lib):
