@@ -62,6 +62,8 @@ constexpr int BN = 32;         // keys per tile
 constexpr uint32_t kBufWord3 = 0x00020000u;
 
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
+typedef __attribute__((address_space(3))) unsigned char lds_u8;
 
 template <int DK, int DV, int G, int RCH>
 struct Cfg {
@@ -328,46 +330,78 @@ __global__ __launch_bounds__(NT, 1) void prefill_mfma_kernel(PrefillArgs a, int 
 #pragma unroll
   for (int d = 0; d < DV / 16; ++d) oacc[d] = f32x4{};
 
-  // K operand: key 16mb + r16, chunk 4s + g.
-  const KAddr<(RCH > 0 ? RCH : 16)> kaddr_r0(0, r16, g), kaddr_r1(0, r16 + 16, g);
-  const KAddr<(C::NP > 0 ? C::NP : 16)> kaddr_p0(C::KR_BYTES, r16, g),
-      kaddr_p1(C::KR_BYTES, r16 + 16, g);
+  // K operand: key 16mb + r16, chunk 4s + g. Keys r16 and r16 + 16 share the
+  // swizzle, so the second is the first plus a constant; the lane-dependent
+  // part of the offset takes H+1 values (s & H), the rest is an immediate.
+  using KR = KAddr<(RCH > 0 ? RCH : 16)>;
+  using KP = KAddr<(C::NP > 0 ? C::NP : 16)>;
+  constexpr int HR = (Swz<(RCH > 0 ? RCH : 16)>::P >= 4 ? Swz<(RCH > 0 ? RCH : 16)>::P / 4 : 1);
+  constexpr int HP = (Swz<(C::NP > 0 ? C::NP : 16)>::P >= 4 ? Swz<(C::NP > 0 ? C::NP : 16)>::P / 4 : 1);
+  constexpr int KR_ROW16 = 16 * (RCH > 0 ? RCH : 16) * 16;   // 16 rows of the rotated region
+  constexpr int KP_ROW16 = 16 * (C::NP > 0 ? C::NP : 16) * 16;
+  int kro[HR], kpo[HP];
+  {
+    const KR kr(0, r16, g);
+    const KP kp(C::KR_BYTES, r16, g);
+#pragma unroll
+    for (int h = 0; h < HR; ++h) kro[h] = kr(h);
+#pragma unroll
+    for (int h = 0; h < HP; ++h) kpo[h] = kp(h);
+  }
   // V^T operand, transposing reads: in each 16-lane group, lane 4r + c reads
   // dims 16d + 4c .. 16d + 4c + 3 of key 16h + 4g + r; the row's swizzle is
   // x = 4g + r (both halves), so chunk 2d + (c >> 1) sits at
-  // 2(d ^ (x >> 1)) + ((c >> 1) ^ (x & 1)).
-  const int vx = 4 * g + (r16 >> 2), vc = r16 & 3;
-  const int v_lane =
-      C::KT_BYTES + vx * C::VC * 16 + (((vc >> 1) ^ (vx & 1)) << 4) + ((vc & 1) << 3);
-  const int v_x2 = vx >> 1;
+  // 2(d ^ (x >> 1)) + ((c >> 1) ^ (x & 1)). With d = 8A + B, d ^ (x >> 1) =
+  // 8A + (B ^ (x >> 1)): 8 lane-dependent offsets, A and h immediates.
+  int vto[8];
+  {
+    const int vx = 4 * g + (r16 >> 2), vc = r16 & 3;
+    const int v_lane =
+        C::KT_BYTES + vx * C::VC * 16 + (((vc >> 1) ^ (vx & 1)) << 4) + ((vc & 1) << 3);
+#pragma unroll
+    for (int B = 0; B < 8; ++B) vto[B] = v_lane + ((B ^ (vx >> 1)) << 5);
+  }
 
   auto live = [&](int kb) {
     const int j0 = kb * BN;
     return j0 <= whi && !(W > 0 && j0 + BN - 1 <= wlo - W);
   };
 
-  auto compute = [&](const unsigned char* st, int kb) {
+  // One tile, read from the ring stage at LDS pointer st.
+  auto compute = [&](const lds_u8* st, int kb) {
     const int j0 = kb * BN;
+    const lds_u8* krb[HR];
+    const lds_u8* kpb[HP];
+#pragma unroll
+    for (int h = 0; h < HR; ++h) krb[h] = st + kro[h];
+#pragma unroll
+    for (int h = 0; h < HP; ++h) kpb[h] = st + kpo[h];
     f32x4 s0 = f32x4{}, s1 = f32x4{};
     // dims 32s + 8g..: s < RCH/4 in the rotated region, the rest in the plain one
 #pragma unroll
     for (int s = 0; s < RCH / 4; ++s) {
-      const bf16x8 k0 = *(const bf16x8*)(st + kaddr_r0(s));
-      const bf16x8 k1 = *(const bf16x8*)(st + kaddr_r1(s));
+      const lds_u8* p = krb[s % HR] + (s / HR) * HR * 64;
+      const bf16x8 k0 = *(const lds_bf16x8*)p;
+      const bf16x8 k1 = *(const lds_bf16x8*)(p + KR_ROW16);
       s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qf[s], s0, 0, 0, 0);
       s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qf[s], s1, 0, 0, 0);
     }
 #pragma unroll
     for (int s = RCH / 4; s < DK / 32; ++s) {
-      const bf16x8 k0 = *(const bf16x8*)(st + kaddr_p0(s - RCH / 4));
-      const bf16x8 k1 = *(const bf16x8*)(st + kaddr_p1(s - RCH / 4));
+      const int sp = s - RCH / 4;
+      const lds_u8* p = kpb[sp % HP] + (sp / HP) * HP * 64;
+      const bf16x8 k0 = *(const lds_bf16x8*)p;
+      const bf16x8 k1 = *(const lds_bf16x8*)(p + KP_ROW16);
       s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qf[s], s0, 0, 0, 0);
       s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qf[s], s1, 0, 0, 0);
     }
     // lane holds keys j0 + 4g + i (s0) and j0 + 16 + 4g + i (s1) of its row
     float sv[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
-    const bool need_mask = (j0 + BN - 1 > wlo) || (W > 0 && j0 <= whi - W);
-    if (need_mask) {
+    // Only tiles crossing the diagonal or a window edge of this wave's rows
+    // pay for the per-score test; the empty asm keeps this a branch (the
+    // compiler would otherwise run the selects on every tile).
+    if ((j0 + BN - 1 > wlo) || (W > 0 && j0 <= whi - W)) {
+      asm volatile("");
       const int d0 = pos - j0 - 4 * g;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
@@ -396,10 +430,12 @@ __global__ __launch_bounds__(NT, 1) void prefill_mfma_kernel(PrefillArgs a, int 
     const bf16x4 pa = __builtin_convertvector(plo, bf16x4);
     const bf16x4 pb = __builtin_convertvector(phi, bf16x4);
     const bf16x8 pop = __builtin_shufflevector(pa, pb, 0, 1, 2, 3, 4, 5, 6, 7);
+    const lds_u8* vb[8];
+#pragma unroll
+    for (int B = 0; B < 8; ++B) vb[B] = st + vto[B];
 #pragma unroll
     for (int d = 0; d < DV / 16; ++d) {
-      // d ^ v_x2 only changes the low 3 bits of d, staying inside the row
-      const unsigned char* p = st + v_lane + ((d ^ v_x2) << 5);
+      const lds_u8* p = vb[d % 8] + (d / 8) * 256;
       const bf16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)p);
       const bf16x4 v1 =
           __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p + 16 * C::VC * 16));
@@ -407,17 +443,23 @@ __global__ __launch_bounds__(NT, 1) void prefill_mfma_kernel(PrefillArgs a, int 
       oacc[d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pop, oacc[d], 0, 0, 0);
     }
   };
-
   // ---- main loop: a 3-stage ring, tiles loaded two ahead --------------------
   // Step t issues tile t+2 into the stage tile t-1 used, computes tile t, then
   // waits for tile t+1 (everything but the newest DMAs, which are always the
   // last loads issued) and synchronises. Every step issues the same DMAs, also
   // the last two (their tiles may lie past the range or past T, where the
   // descriptors return zeros, and are never read).
+  int cur = 0;  // stage of tile t
   for (int t = 0; t < n_tiles; ++t) {
     const int kb = kb_lo + t;
-    dma_tile(kb + 2, (t + 2) % 3);
-    if (live(kb)) compute(lds + (t % 3) * C::ST_BYTES, kb);
+    const int nxt2 = cur == 0 ? 2 : cur - 1;  // stage of tile t+2 (= that of t-1)
+    dma_tile(kb + 2, nxt2);
+    // The stage offset goes through readfirstlane so the compiler treats it as
+    // an opaque scalar: every LDS read is then base register + immediate,
+    // instead of strength-reduced per-read induction registers.
+    const int so = __builtin_amdgcn_readfirstlane(cur * C::ST_BYTES);
+    if (live(kb)) compute((const lds_u8*)lds + so, kb);
+    cur = cur == 2 ? 0 : cur + 1;
     wait_vm<C::DMA_W>();  // tile t+1 landed
     lds_barrier();        // ... for every wave; stage of tile t free
   }

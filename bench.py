@@ -7,9 +7,10 @@ Prints ONE JSON line. `value` is the throughput of the headline workload
 (default: the local sliding-window prefill, B=4 T=4096 16q/8kv D=256 W=512,
 RoPE theta=1e4), in algorithmic TFLOP/s: FLOPs of allowed (query, key) pairs
 only, B*Hq*pairs(T,W)*2*(Dk+Dv). A step is one pass of the hot path over that
-batch: the RoPE cos/sin table for the positions plus the flash prefill kernel
-(RoPE fused into its Q/K loads, window-aware tile skipping, QK^T and PV on
-bf16 MFMA, online softmax). The other workloads (global prefill, batched
+batch: the RoPE cos/sin table for the positions, then attn_prefill, which
+turns K's rotary dims once into a workspace and runs the flash prefill kernel
+(Q rotated on load, window-aware tile skipping, QK^T and PV on bf16 MFMA,
+online softmax). The roofline entry times the attention kernel alone. The other workloads (global prefill, batched
 decode, the 7-layer local/global/shared-KV stack) are measured in the same
 run and reported under "secondary", each with its own roofline.
 
@@ -90,10 +91,15 @@ class Timer:
 
 
 def bench_prefill(ar, torch, inputs, cfg, steps, warmup):
+    """Time the step (cos/sin table, then attn_prefill: K rotation pre-pass and
+    the attention kernel) and, separately, the attention kernel alone."""
     c = cfg["case"]
     q, k, v = inputs.prefill_inputs(c, cfg["seed"], device="cuda")
     o = torch.empty((c.B, c.T, c.Hq, c.Dv), dtype=c.dtype, device="cuda")
     tab = torch.empty((c.T, max(c.rotary_dims // 2, 1), 2), dtype=torch.float32, device="cuda")
+    nws = ar.prefill_workspace_bytes(c.B, c.T, c.Hkv, c.Dk, rotary_dims=c.rotary_dims,
+                                     theta=c.theta, dtype=c.dtype)
+    ws = torch.empty(max(nws, 16), dtype=torch.uint8, device="cuda")
 
     def step(t=None, i=0):
         if t: t.mark(i, 0)
@@ -101,8 +107,18 @@ def bench_prefill(ar, torch, inputs, cfg, steps, warmup):
                       pos0=c.pos0, out=tab)
         if t: t.mark(i, 1)
         ar.prefill(q, k, v, window=c.window, scale=c.scale, rotary_dims=c.rotary_dims,
-                   theta=c.theta, pos0=c.pos0, out=o, table=tab)
+                   theta=c.theta, pos0=c.pos0, out=o, table=tab, workspace=ws)
         if t: t.mark(i, 2)
+
+    def kernel_only(t, i):
+        # Q-only rotation: the same kernel instantiation and launch with the
+        # same DMA volume (K's rotary dims are then read from k itself), and
+        # no pre-pass, so the events bracket the attention kernel alone.
+        t.mark(i, 0)
+        ar.prefill(q, k, v, window=c.window, scale=c.scale, rotary_dims=c.rotary_dims,
+                   theta=c.theta, pos0=c.pos0, out=o, table=tab, workspace=ws,
+                   rope_mask=ar.ROPE_Q)
+        t.mark(i, 1)
 
     for _ in range(warmup):
         step()
@@ -114,11 +130,17 @@ def bench_prefill(ar, torch, inputs, cfg, steps, warmup):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     step_ms = sum(t.ms(i, 0, 2) for i in range(steps)) / steps
-    kern_ms = sum(t.ms(i, 1, 2) for i in range(steps)) / steps
+    call_ms = sum(t.ms(i, 1, 2) for i in range(steps)) / steps
     span_ms = t.ev[0][0].elapsed_time(t.ev[-1][2])
+    tk = Timer(torch, steps)
+    for i in range(steps):
+        kernel_only(tk, i)
+    torch.cuda.synchronize()
+    kern_ms = sum(tk.ms(i, 0, 1) for i in range(steps)) / steps
+    step()  # leave o holding the full result
     flops = prefill_flops(c)
-    return dict(flops=flops, bytes=prefill_bytes(c), step_ms=step_ms, kern_ms=kern_ms,
-                span_ms=span_ms, wall_s=wall, tensors=(q, k, v, o))
+    return dict(flops=flops, bytes=prefill_bytes(c), step_ms=step_ms, call_ms=call_ms,
+                kern_ms=kern_ms, span_ms=span_ms, wall_s=wall, tensors=(q, k, v, o))
 
 
 def bench_decode(ar, torch, inputs, cfg, steps, warmup):
@@ -185,6 +207,9 @@ def bench_stack(ar, torch, inputs, cfg, steps, warmup):
     for c in (loc, glo):
         tabs[id(c)] = torch.empty((c.T, c.rotary_dims // 2, 2), dtype=torch.float32,
                                   device="cuda")
+    nws = max(ar.prefill_workspace_bytes(c.B, c.T, c.Hkv, c.Dk, rotary_dims=c.rotary_dims,
+                                         theta=c.theta, dtype=c.dtype) for c in (loc, glo))
+    ws = torch.empty(max(nws, 16), dtype=torch.uint8, device="cuda")  # reused layer by layer
 
     def step(t=None, i=0):
         if t: t.mark(i, 0)
@@ -195,7 +220,7 @@ def bench_stack(ar, torch, inputs, cfg, steps, warmup):
             c = L["c"]
             ar.prefill(L["q"], L["k"], L["v"], window=c.window, scale=c.scale,
                        rotary_dims=c.rotary_dims, theta=c.theta, out=L["o"],
-                       table=tabs[id(c)])
+                       table=tabs[id(c)], workspace=ws)
         if t: t.mark(i, 2)
 
     for _ in range(warmup):
@@ -251,6 +276,8 @@ def main():
                     help="other workloads measured in the same run ('' for none)")
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run 3 plain device copies of MIB MiB (HBM counter scale)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -267,6 +294,16 @@ def main():
         print(json.dumps({"error": "no GPU visible"}), flush=True)
         sys.exit(1)
 
+    if args.calibrate_copy:
+        n = args.calibrate_copy << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes": n, "launches": 3}), flush=True)
+        return
+
     cfg = inputs.CONFIGS[args.workload]
     if cfg["kind"] == "stack":
         r = bench_stack(ar, torch, inputs, cfg, args.steps, args.warmup)
@@ -281,6 +318,7 @@ def main():
                             _traffic("prefill_mfma", wl))
         bound_rl["kernel"] = "prefill_mfma_kernel"
         bound_rl["kernel_ms"] = round(r["kern_ms"], 5)
+        bound_rl["prefill_call_ms"] = round(r["call_ms"], 5)  # K rotation + kernel
         bound_rl["hbm_frac_at_algorithmic_bytes"] = round(
             r["bytes"] / (r["kern_ms"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)
     out = {
