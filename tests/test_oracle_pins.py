@@ -189,6 +189,21 @@ def test_constant_values_give_constant_output():
     np.testing.assert_allclose(o, 3.25, rtol=1e-14)
 
 
+def test_zero_scale_gives_mean_of_visible_values():
+    """scale = 0 makes every visible key weigh the same: o_i is the plain mean
+    of v_j over j in (i - W, i]."""
+    B, T, Hq, Hkv, D = 2, 23, 4, 2, 8
+    q, k = rng.standard_normal((B, T, Hq, D)), rng.standard_normal((B, T, Hkv, D))
+    v = rng.standard_normal((B, T, Hkv, 6))
+    for W in (0, 5):
+        o = oracle.prefill(q, k, v, window=W, scale=0.0, rotary_dims=8, theta=1e4)
+        for i in range(T):
+            lo = 0 if W == 0 else max(0, i - W + 1)
+            mean = v[:, lo:i + 1].mean(axis=1)               # [B, Hkv, 6]
+            np.testing.assert_allclose(o[:, i], np.repeat(mean, Hq // Hkv, axis=1),
+                                       rtol=0, atol=1e-13)
+
+
 def test_first_token_sees_only_itself():
     q, k, v = (rng.standard_normal((2, 5, 4, 8)) for _ in range(3))
     o = oracle.prefill(q, k, v, window=0, scale=0.5, rotary_dims=8, theta=1e6)
