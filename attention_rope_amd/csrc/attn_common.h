@@ -14,6 +14,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 // bf16 bits -> fp32 (exact).
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
@@ -67,6 +68,59 @@ __device__ __forceinline__ int xcd_contiguous(int x, int n) {
   const int q = n / 8, r = n % 8;
   const int xcd = x % 8, j = x / 8;
   return (xcd < r) ? xcd * (q + 1) + j : r * (q + 1) + (xcd - r) * q + j;
+}
+
+// ---- LDS DMA streaming (buffer loads with the lds flag) --------------------
+
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
+typedef __attribute__((address_space(3))) unsigned char lds_u8;
+
+// LDS byte address of a pointer into a __shared__ array.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// Raw buffer descriptor (stride 0, 32-bit format): reads at byte offsets
+// >= bytes return 0. Word 3 = 0x00020000 selects that format on gfx9.
+__device__ __forceinline__ u32x4 buffer_desc(const void* base, uint32_t bytes) {
+  const uint64_t p = (uint64_t)(uintptr_t)base;
+  return u32x4{(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)p),
+               (uint32_t)__builtin_amdgcn_readfirstlane((int)((uint32_t)(p >> 32) & 0xffffu)),
+               (uint32_t)__builtin_amdgcn_readfirstlane((int)bytes), 0x00020000u};
+}
+
+// One DMA: lane l copies 16 bytes at byte offset voff of the buffer into LDS
+// at lds + 16 l. M0 carries the LDS base and is restored afterwards. Issued
+// from inline asm, so the compiler sees no LDS DMA and adds none of its
+// conservative "wait for every LDS DMA" stalls before LDS reads: the caller
+// waits explicitly (the instruction counts in vmcnt like any buffer load).
+__device__ __forceinline__ void dma16(u32x4 desc, uint32_t lds, uint32_t voff) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds), "v"(voff), "s"(desc));
+}
+
+// Synchronise the workgroup after this wave's LDS reads have returned. Unlike
+// __syncthreads this carries no memory fence, which would also wait for the
+// DMAs still in flight; the memory clobber keeps LDS accesses on their side.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Wait until at most n vector-memory operations of this wave are in flight
+// (vmcnt = n in bits 3:0 and 15:14; expcnt and lgkmcnt left alone), and keep
+// the scheduler from hoisting LDS reads of what landed above the wait.
+template <int n>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(n >= 0 && n < 64, "vmcnt field");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (n & 15) | ((n >> 4) << 14));
+  __builtin_amdgcn_sched_barrier(0);
 }
 
 }  // namespace attn

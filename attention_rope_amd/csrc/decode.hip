@@ -32,7 +32,7 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kNW = 4;  // waves per workgroup
 
 // Rows of one sequence handled by one workgroup.
-__host__ __device__ inline int decode_chunk_rows(int window) { return window > 0 ? 256 : 1024; }
+__host__ __device__ inline int decode_chunk_rows(int window) { return window > 0 ? 512 : 1024; }
 
 __host__ __device__ inline int decode_splits(int max_kv_len, int window) {
   const int range = (window > 0 && window < max_kv_len) ? window : max_kv_len;
@@ -240,6 +240,239 @@ __global__ __launch_bounds__(kNW * 64) void decode_partial_kernel(DecodeArgs a, 
   }
 }
 
+// ---- streaming kernel: K/V tiles through an LDS DMA ring -------------------
+// Decode is bound by the bytes of the cache, and there is little arithmetic
+// per byte, so this kernel is built around keeping bytes in flight: 2 waves
+// stream 32-row tiles (K and V) into a 3-stage LDS ring by DMA, two tiles
+// ahead, with no staging registers; each wave takes 16 of a tile's rows.
+// S^T = K Q^T on v_mfma_f32_16x16x32_bf16 (16 keys x 16 head columns), then
+// O^T += V^T P^T on v_mfma_f32_16x16x16_bf16: the P^T operand (keys 4g..4g+3
+// of head col) is exactly what the score MFMA left in the lane, and V^T comes
+// from one transposing LDS read (ds_read_b64_tr_b16) per MFMA.
+constexpr int kRW = 2;    // waves per workgroup
+constexpr int kRBN = 32;  // rows per tile (16 per wave)
+
+template <int DK, int DV>
+struct RCfg {
+  static constexpr int KC = DK / 8, VC = DV / 8;  // 16-byte chunks per row
+  static constexpr int KT = kRBN * DK * 2, VT = kRBN * DV * 2;
+  static constexpr int ST = KT + VT;
+  static constexpr int STAGES = 3;
+  static constexpr int LDS = STAGES * ST;
+  static constexpr int K_DMA = KT / 1024, N_DMA = ST / 1024;
+  static constexpr int DMA_W = N_DMA / kRW;  // DMAs per wave per tile
+  static_assert(KC >= 16 && VC >= 16, "row swizzle uses 16 chunk groups");
+  static_assert(K_DMA % kRW == 0 && N_DMA % kRW == 0, "uniform DMA counts");
+  static_assert(DMA_W < 64 && LDS <= 160 * 1024, "vmcnt / LDS limits");
+};
+
+template <int DK, int DV>
+__global__ __launch_bounds__(kRW * 64, 1) void decode_ring_kernel(DecodeArgs a, int n_split) {
+  using C = RCfg<DK, DV>;
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[C::LDS];
+
+  const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int col = lane & 15, g = lane >> 4;
+  const int G = a.Hq / a.Hkv;
+
+  const int kv_len = a.kv_len[b];
+  if (kv_len <= 0 || kv_len > a.max_kv_len) return;  // the merge handles these
+  const int lo = (a.window > 0) ? max(0, kv_len - a.window) : 0;
+  const int ch = decode_chunk_rows(a.window);
+  const int c0 = lo + split * ch;
+  if (c0 >= kv_len) return;
+  const int c1 = min(kv_len, c0 + ch);
+  const int n_tiles = (c1 - c0 + kRBN - 1) / kRBN;
+  const int64_t off = a.row_offset[b];
+
+  // Descriptors over this sequence's rows of KV head kvh: rows past kv_len
+  // read 0 (they are never inside [c0, c1) and their scores are masked).
+  const int krow = a.Hkv * DK * 2, vrow = a.Hkv * DV * 2;
+  const u32x4 kdesc = buffer_desc((const char*)a.k_cache + (off * a.Hkv + kvh) * DK * 2,
+                                  (uint32_t)((int64_t)(kv_len - 1) * krow + DK * 2));
+  const u32x4 vdesc = buffer_desc((const char*)a.v_cache + (off * a.Hkv + kvh) * DV * 2,
+                                  (uint32_t)((int64_t)(kv_len - 1) * vrow + DV * 2));
+  // Block n (n = i*kRW + wave) of a tile holds 64 chunks; K rows first, then V
+  // rows, each row's chunks XOR-swizzled by (row & 15).
+  uint32_t dma_off[C::DMA_W];
+#pragma unroll
+  for (int i = 0; i < C::DMA_W; ++i) {
+    const int n = i * kRW + wave;
+    if (n < C::K_DMA) {
+      const int q = n * 64 + lane, r = q / C::KC;
+      dma_off[i] = r * krow + ((q % C::KC) ^ (r & 15)) * 16;
+    } else {
+      const int q = (n - C::K_DMA) * 64 + lane, r = q / C::VC;
+      dma_off[i] = r * vrow + ((q % C::VC) ^ (r & 15)) * 16;
+    }
+  }
+  auto dma_tile = [&](int t, int stage) {
+    const int j0 = c0 + t * kRBN;
+    const uint32_t st = lds_addr(lds) + stage * C::ST;
+#pragma unroll
+    for (int i = 0; i < C::DMA_W; ++i) {
+      const int n = i * kRW + wave;
+      if (i * kRW < C::K_DMA)  // same region for both waves (K_DMA % kRW == 0)
+        dma16(kdesc, st + n * 1024, dma_off[i] + j0 * krow);
+      else
+        dma16(vdesc, st + n * 1024, dma_off[i] + j0 * vrow);
+    }
+  };
+  dma_tile(0, 0);
+
+  // ---- rotated queries as the B operand: col = head, k = dims -------------
+  // The angle of each rotary pair is formed once per wave (one pair per lane,
+  // fp64) into a small LDS table; every lane then reads the pairs it holds.
+  __shared__ float2 cs_tab[kRW][DK / 2];
+  bf16x8 qf[DK / 32];
+  {
+    const int qpos = kv_len - 1;
+    const double l2t = log2(a.theta);
+    for (int p = lane; p < a.rot_pairs; p += 64) {
+      float c, sn;
+      rope_cos_sin(qpos, rope_freq(p, DK, l2t), &c, &sn);
+      cs_tab[wave][p] = make_float2(c, sn);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const bool hv = col < G;
+    const int head = kvh * G + (hv ? col : 0);
+    const uint16_t* qrow = (const uint16_t*)a.q + ((int64_t)b * a.Hq + head) * DK;
+#pragma unroll
+    for (int s = 0; s < DK / 32; ++s) {
+      const int d0 = 32 * s + 8 * g;
+      u32x4 w = *(const u32x4*)(qrow + d0);
+      if (d0 / 2 < a.rot_pairs) {  // rot_pairs is a multiple of 4: all 4 pairs turn
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float2 t = cs_tab[wave][d0 / 2 + e];
+          const float x0 = bf16_lo(w[e]), x1 = bf16_hi(w[e]);
+          w[e] = pack_bf16x2(x0 * t.x - x1 * t.y, x0 * t.y + x1 * t.x);
+        }
+      }
+      if (!hv) w = u32x4{0, 0, 0, 0};
+      qf[s] = __builtin_bit_cast(bf16x8, w);
+    }
+  }
+  dma_tile(1, 1);  // may lie past c1: masked, or past kv_len: zeros
+  wait_vm<C::DMA_W>();
+  lds_barrier();
+
+  // scores to log2 units; kept > 0 so a masked -inf never meets a zero factor
+  const float c2 = fmaxf(a.scale * kLog2e, 1e-30f);
+  float m_run = -INFINITY, l_run = 0.f;  // per head `col`
+  f32x4 oacc[DV / 16];
+#pragma unroll
+  for (int d = 0; d < DV / 16; ++d) oacc[d] = f32x4{};
+
+  // Per-lane LDS offsets. K: row 16*wave + col, chunk 4s + g, swizzled by
+  // col: 4(s ^ (col >> 2)) + (g ^ (col & 3)); s = 4A + B gives 4 bases plus
+  // an immediate. V^T: rows 16*wave + 4g + r (r = col >> 2), dims
+  // 16d + 4(col & 3) .. + 3; swizzle x = 4g + r, so with d = 8A + B the
+  // chunk 2(d ^ (x >> 1)) + (((col & 3) >> 1) ^ (x & 1)) gives 8 bases.
+  int ko[4], vo[8];
+  {
+    const int krow_l = (16 * wave + col) * C::KC * 16 + ((g ^ (col & 3)) << 4);
+#pragma unroll
+    for (int B = 0; B < 4; ++B) ko[B] = krow_l + ((B ^ (col >> 2)) << 6);
+    const int x = 4 * g + (col >> 2), c4 = col & 3;
+    const int vrow_l = C::KT + (16 * wave + x) * C::VC * 16 +
+                       ((((c4 >> 1) ^ (x & 1))) << 4) + ((c4 & 1) << 3);
+#pragma unroll
+    for (int B = 0; B < 8; ++B) vo[B] = vrow_l + ((B ^ (x >> 1)) << 5);
+  }
+
+  int cur = 0;
+  for (int t = 0; t < n_tiles; ++t) {
+    dma_tile(t + 2, cur == 0 ? 2 : cur - 1);
+    const lds_u8* st = (const lds_u8*)lds + __builtin_amdgcn_readfirstlane(cur * C::ST);
+    // S^T[16 keys][16 heads]: lane holds keys 4g + i of head col.
+    f32x4 s = f32x4{};
+#pragma unroll
+    for (int k = 0; k < DK / 32; ++k) {
+      const bf16x8 kv = *(const lds_bf16x8*)(st + ko[k % 4] + (k / 4) * 256);
+      s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, qf[k], s, 0, 0, 0);
+    }
+    const int key0 = c0 + t * kRBN + 16 * wave + 4 * g;
+    if (c0 + (t + 1) * kRBN > c1) {  // last tile of the chunk: mask rows >= c1
+#pragma unroll
+      for (int i = 0; i < 4; ++i) s[i] = (key0 + i < c1) ? s[i] : -INFINITY;
+    }
+    float mx = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+    mx = xor32_16_max(mx);
+    const float mc = (mx == -INFINITY) ? -INFINITY : mx * c2;
+    if (__any(mc > m_run + 8.f)) {  // move the max only when it grows by 2^8
+      const float m_new = fmaxf(m_run, mc);
+      const float alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int d = 0; d < DV / 16; ++d) oacc[d] *= alpha;
+      m_run = m_new;
+    }
+    const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
+    f32x4 p;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(fmaf(s[i], c2, -m_use));
+    l_run += (p[0] + p[1]) + (p[2] + p[3]);
+    const s16x4 pb = __builtin_bit_cast(s16x4, __builtin_convertvector(p, bf16x4));
+#pragma unroll
+    for (int d = 0; d < DV / 16; ++d) {
+      const bf16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+          (lds_bf16x4*)(st + vo[d % 8] + (d / 8) * 256));
+      oacc[d] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, v), pb,
+                                                          oacc[d], 0, 0, 0);
+    }
+    wait_vm<C::DMA_W>();  // tile t+1 landed
+    lds_barrier();
+    cur = cur == 2 ? 0 : cur + 1;
+  }
+  wait_vm<0>();
+  lds_barrier();  // every wave is done with the ring before it is reused
+
+  // The 4 lanes of a head (col, col+16, col+32, col+48) hold different keys
+  // under the same running max: sum their sums.
+  l_run = xor32_16_sum(l_run);
+
+  // ---- merge the 2 waves through LDS, write this split's partial ---------
+  float* red = reinterpret_cast<float*>(lds);  // [wave][16][DV + 2]
+  const int RS = DV + 2;
+  {
+    float* wr = red + (wave * 16 + col) * RS;
+    if (g == 0) {
+      wr[DV] = m_run;
+      wr[DV + 1] = l_run;
+    }
+    // O^T layout: lane holds dims 16d + 4g + i of head col.
+#pragma unroll
+    for (int d = 0; d < DV / 16; ++d)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) wr[16 * d + 4 * g + i] = oacc[d][i];
+  }
+  __syncthreads();
+  float* part = reinterpret_cast<float*>(a.workspace);
+  for (int idx = tid; idx < G * (DV + 2); idx += kRW * 64) {
+    const int h = idx / (DV + 2), d = idx % (DV + 2);
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kRW; ++w) M = fmaxf(M, red[(w * 16 + h) * RS + DV]);
+    float val = 0.f;
+    if (d == DV) {
+      val = M;
+    } else if (M != -INFINITY) {
+#pragma unroll
+      for (int w = 0; w < kRW; ++w) {
+        const float f = exp2f(red[(w * 16 + h) * RS + DV] - M);
+        val += f * red[(w * 16 + h) * RS + d];
+      }
+    }
+    const int64_t slot = ((int64_t)b * a.Hq + kvh * G + h) * n_split + split;
+    part[slot * (DV + 2) + d] = val;  // d == DV+1 sums the l's by the same rule
+  }
+}
+
 // Merge the splits of one (sequence, query head): O = sum_c f_c acc_c / sum_c f_c l_c.
 template <int DV>
 __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a, int n_split) {
@@ -270,11 +503,24 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a, int n_s
   o[d] = f32_to_bf16(num / den);
 }
 
+// The streaming kernel addresses one sequence's cache rows with 32-bit
+// buffer offsets: kv_len rows (plus two tiles of read-ahead) of all KV heads.
+// It also turns the query 4 pairs (one 16-byte chunk) at a time.
+template <int DK, int DV>
+bool ring_fits(const DecodeArgs& a) {
+  const int64_t row = (int64_t)a.Hkv * (DK > DV ? DK : DV) * 2;
+  return ((int64_t)a.max_kv_len + 3 * kRBN) * row < ((int64_t)1 << 31) && a.rot_pairs % 4 == 0;
+}
+
 template <int DK, int DV>
 hipError_t launch_dk_dv(const DecodeArgs& a, hipStream_t st) {
   const int ns = decode_splits(a.max_kv_len, a.window);
-  hipLaunchKernelGGL((decode_partial_kernel<DK, DV>), dim3(ns, a.Hkv, a.B),
-                     dim3(kNW * 64), 0, st, a, ns);
+  if (ring_fits<DK, DV>(a))
+    hipLaunchKernelGGL((decode_ring_kernel<DK, DV>), dim3(ns, a.Hkv, a.B), dim3(kRW * 64), 0,
+                       st, a, ns);
+  else
+    hipLaunchKernelGGL((decode_partial_kernel<DK, DV>), dim3(ns, a.Hkv, a.B),
+                       dim3(kNW * 64), 0, st, a, ns);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((decode_merge_kernel<DV>), dim3(a.B * a.Hq), dim3(256), 0, st, a, ns);

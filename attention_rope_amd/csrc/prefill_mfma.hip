@@ -58,12 +58,6 @@ constexpr int NW = 8;          // waves per workgroup
 constexpr int NT = NW * 64;
 constexpr int RW = 16;         // query rows per wave
 constexpr int BN = 32;         // keys per tile
-// Buffer descriptor word 3 for raw (stride 0) 32-bit-format buffers on gfx9.
-constexpr uint32_t kBufWord3 = 0x00020000u;
-
-typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
-typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
-typedef __attribute__((address_space(3))) unsigned char lds_u8;
 
 template <int DK, int DV, int G, int RCH>
 struct Cfg {
@@ -149,50 +143,6 @@ __device__ __forceinline__ u32x4 rotate4(u32x4 w, f32x4 t0, f32x4 t1) {
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
-
-// LDS byte address of a pointer into a __shared__ array.
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
-}
-
-// Raw buffer descriptor (stride 0): reads at byte offsets >= bytes return 0.
-__device__ __forceinline__ u32x4 buffer_desc(const void* base, uint32_t bytes) {
-  const uint64_t p = (uint64_t)(uintptr_t)base;
-  return u32x4{(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)p),
-               (uint32_t)__builtin_amdgcn_readfirstlane((int)((uint32_t)(p >> 32) & 0xffffu)),
-               (uint32_t)__builtin_amdgcn_readfirstlane((int)bytes), kBufWord3};
-}
-
-// One DMA: lane l copies 16 bytes at byte offset voff of the buffer into LDS
-// at lds + 16 l. M0 carries the LDS base and is restored afterwards. The
-// instruction counts in vmcnt like any buffer load; the caller waits for it.
-__device__ __forceinline__ void dma16(u32x4 desc, uint32_t lds, uint32_t voff) {
-  uint32_t saved;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %1\n\t"
-      "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "s"(lds), "v"(voff), "s"(desc));
-}
-
-// Synchronise the workgroup after this wave's LDS reads have returned. Unlike
-// __syncthreads this carries no memory fence, which would also wait for the
-// DMAs still in flight; the memory clobber keeps LDS accesses on their side.
-__device__ __forceinline__ void lds_barrier() {
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
-
-// Wait until at most n vector-memory operations of this wave are in flight
-// (vmcnt[3:0] = n, expcnt and lgkmcnt left alone), and keep the scheduler
-// from hoisting LDS reads of what landed above the wait.
-template <int n>
-__device__ __forceinline__ void wait_vm() {
-  static_assert(n >= 0 && n < 16, "vmcnt field");
-  __builtin_amdgcn_s_waitcnt(0x0F70 | n);
-  __builtin_amdgcn_sched_barrier(0);
-}
 
 template <int DK, int DV, int G, int RCH>
 __global__ __launch_bounds__(NT, 1) void prefill_mfma_kernel(PrefillArgs a, int n_qt,
@@ -285,7 +235,7 @@ __global__ __launch_bounds__(NT, 1) void prefill_mfma_kernel(PrefillArgs a, int 
   {
     const int tab_row = a.rot_pairs * 8;  // bytes per table row
     const __amdgpu_buffer_rsrc_t tres = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)a.rope_tab, (short)0, rot_q ? T * tab_row : 0, (int)kBufWord3);
+        (void*)a.rope_tab, (short)0, rot_q ? T * tab_row : 0, 0x00020000);
     const int prow = valid ? pos : T - 1;
     const uint16_t* qrow =
         (const uint16_t*)a.q + (((int64_t)b * T + prow) * a.Hq + head) * DK + 8 * g;
