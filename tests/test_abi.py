@@ -141,9 +141,9 @@ def test_decode_validation(lib):
 
 
 def test_decode_workspace_bytes(lib):
-    # global: chunks of 1024 rows; local: chunks of 256 rows within the window
+    # global: chunks of 1024 rows; local: chunks of 512 rows within the window
     assert lib.attn_decode_workspace_bytes(64, 32, 256, 131073, 0) == 64 * 32 * 129 * 258 * 4
-    assert lib.attn_decode_workspace_bytes(64, 16, 256, 131073, 1024) == 64 * 16 * 4 * 258 * 4
+    assert lib.attn_decode_workspace_bytes(64, 16, 256, 131073, 1024) == 64 * 16 * 2 * 258 * 4
     assert lib.attn_decode_workspace_bytes(0, 16, 256, 10, 0) == 0
 
 
