@@ -95,15 +95,27 @@ __device__ __forceinline__ u32x4 buffer_desc(const void* base, uint32_t bytes) {
 // from inline asm, so the compiler sees no LDS DMA and adds none of its
 // conservative "wait for every LDS DMA" stalls before LDS reads: the caller
 // waits explicitly (the instruction counts in vmcnt like any buffer load).
+// STREAM marks data read once (the nt cache policy), such as a KV cache during
+// decode; tiles that neighbouring workgroups re-read keep the default policy.
+template <bool STREAM = false>
 __device__ __forceinline__ void dma16(u32x4 desc, uint32_t lds, uint32_t voff) {
   uint32_t saved;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %1\n\t"
-      "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "s"(lds), "v"(voff), "s"(desc));
+  if constexpr (STREAM)
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %1\n\t"
+        "buffer_load_dwordx4 %2, %3, 0 offen nt lds\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "s"(lds), "v"(voff), "s"(desc));
+  else
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %1\n\t"
+        "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "s"(lds), "v"(voff), "s"(desc));
 }
 
 // Synchronise the workgroup after this wave's LDS reads have returned. Unlike

@@ -315,9 +315,9 @@ __global__ __launch_bounds__(kRW * 64, 1) void decode_ring_kernel(DecodeArgs a, 
     for (int i = 0; i < C::DMA_W; ++i) {
       const int n = i * kRW + wave;
       if (i * kRW < C::K_DMA)  // same region for both waves (K_DMA % kRW == 0)
-        dma16(kdesc, st + n * 1024, dma_off[i] + j0 * krow);
+        dma16<true>(kdesc, st + n * 1024, dma_off[i] + j0 * krow);
       else
-        dma16(vdesc, st + n * 1024, dma_off[i] + j0 * vrow);
+        dma16<true>(vdesc, st + n * 1024, dma_off[i] + j0 * vrow);
     }
   };
   dma_tile(0, 0);
