@@ -308,16 +308,20 @@ __global__ __launch_bounds__(kRW * 64, 1) void decode_ring_kernel(DecodeArgs a, 
       dma_off[i] = r * vrow + ((q % C::VC) ^ (r & 15)) * 16;
     }
   }
+  // Tiles past the chunk are issued too (one vmcnt value then covers every
+  // step), but at an offset past the descriptors' end: they return zeros
+  // without touching memory.
   auto dma_tile = [&](int t, int stage) {
     const int j0 = c0 + t * kRBN;
     const uint32_t st = lds_addr(lds) + stage * C::ST;
+    const uint32_t far = t < n_tiles ? 0u : 0x80000000u;
 #pragma unroll
     for (int i = 0; i < C::DMA_W; ++i) {
       const int n = i * kRW + wave;
       if (i * kRW < C::K_DMA)  // same region for both waves (K_DMA % kRW == 0)
-        dma16<true>(kdesc, st + n * 1024, dma_off[i] + j0 * krow);
+        dma16<true>(kdesc, st + n * 1024, (dma_off[i] + j0 * krow) | far);
       else
-        dma16<true>(vdesc, st + n * 1024, dma_off[i] + j0 * vrow);
+        dma16<true>(vdesc, st + n * 1024, (dma_off[i] + j0 * vrow) | far);
     }
   };
   dma_tile(0, 0);

@@ -213,9 +213,13 @@ __global__ __launch_bounds__(NT, 1) void prefill_mfma_kernel(PrefillArgs a, int 
       dma_off[i] = r * vrow + kswz<C::VC>(r, q % C::VC) * 16;
     }
   }
+  // Tiles past the range are issued too (one vmcnt value then covers every
+  // step), but at an offset past the descriptors' end: they return zeros
+  // without touching memory.
   auto dma_tile = [&](int kb, int stage) {
     const int j0 = kb * BN;
     const uint32_t st = lds_addr(lds) + stage * C::ST_BYTES;
+    const uint32_t far = kb < kb_hi ? 0u : 0x80000000u;
     // Blocks are laid out back to back (rotated K, plain K, V), so block n
     // lands at st + 1024 n whatever its region.
 #pragma unroll
@@ -223,11 +227,11 @@ __global__ __launch_bounds__(NT, 1) void prefill_mfma_kernel(PrefillArgs a, int 
       const int n = i * NW + wave;
       const int reg = C::ALIGNED ? C::region(i * NW) : C::region(n);
       if (reg == 0)
-        dma16(rdesc, st + n * 1024, dma_off[i] + j0 * rrow);
+        dma16(rdesc, st + n * 1024, (dma_off[i] + j0 * rrow) | far);
       else if (reg == 1)
-        dma16(kdesc, st + n * 1024, dma_off[i] + j0 * krow);
+        dma16(kdesc, st + n * 1024, (dma_off[i] + j0 * krow) | far);
       else
-        dma16(vdesc, st + n * 1024, dma_off[i] + j0 * vrow);
+        dma16(vdesc, st + n * 1024, (dma_off[i] + j0 * vrow) | far);
     }
   };
 

@@ -366,7 +366,7 @@ def main():
                                  "local_call": {"GB/s": round(l, 1), "ms": round(rr["l_ms"], 4),
                                                 "bytes": rr["l_bytes"]},
                                  "roofline": roofline("hbm", g, PEAK_HBM_GBS, "GB/s",
-                                                      _traffic("decode_partial", "global_decode"))}
+                                                      _traffic("decode_ring", "global_decode"))}
             del rr
         else:
             rr = bench_stack(ar, torch, inputs, sc, max(3, args.steps // 4), 1)
