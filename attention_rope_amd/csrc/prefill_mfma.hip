@@ -70,7 +70,6 @@ struct Cfg {
   static constexpr int NT = NW * 64;
   static constexpr int ROWS = NW * RW;        // (head, position) rows per WG
   static constexpr int PW = ROWS / G;         // query positions per WG
-  static constexpr int SPAN = PW < RW ? PW : RW;  // positions one wave covers
   static constexpr int NC = DK / 8;           // 16-byte chunks per K row
   static constexpr int NP = NC - RCH;         // plain (unrotated) chunks per K row
   // K tile: rotated region [32][RCH] chunks, then plain region [32][NP].
@@ -96,8 +95,7 @@ struct Cfg {
   __host__ __device__ static constexpr int region(int n) {
     return n < KR_DMA ? 0 : n < KR_DMA + KP_DMA ? 1 : 2;
   }
-  static_assert(ROWS % G == 0 && (PW % RW == 0 || RW % PW == 0),
-                "a wave's rows are whole heads or whole position runs");
+  static_assert(ROWS % G == 0, "rows split evenly over the heads");
   static_assert(KR_BYTES % 1024 == 0 && KT_BYTES % 1024 == 0 && VT_BYTES % 1024 == 0,
                 "DMA blocks");
   static_assert(N_DMA % NW == 0, "every wave issues the same number of DMAs per tile");
@@ -121,6 +119,11 @@ template <int width>
 __device__ __forceinline__ int kswz(int r, int c) {
   return c ^ (r & Swz<width>::M);
 }
+// V rows: chunk c of key row r sits at c ^ 4(r & 3). A transposing read of
+// the V^T operand takes 4 consecutive keys x 4 consecutive chunks (one
+// 32-dim tile) per 32 lanes; this swizzle puts the 16 pieces in 16 distinct
+// bank groups (an XOR by r & 15 would keep them in 4).
+__device__ __forceinline__ int vswz(int r, int c) { return c ^ ((r & 3) << 2); }
 
 __device__ __forceinline__ uint32_t rot_pair(uint32_t w, float c, float s) {
   const float x0 = bf16_lo(w), x1 = bf16_hi(w);
@@ -157,14 +160,17 @@ __global__ __launch_bounds__((Cfg<DK, DV, G, RCH>::NT), 1) void prefill_mfma_ker
   const int kvh = grp % a.Hkv, b = grp / a.Hkv;
   const int p0 = qt * C::PW;
 
-  // This lane's query row: row R of the workgroup is position R % PW of head
-  // R / PW; a wave's 32 rows cover SPAN consecutive positions.
-  const int R = wave * RW + r32;
-  const int head = kvh * G + R / C::PW;
-  const int pos = p0 + R % C::PW;
+  // This lane's query row: wave w takes head w % G and the 32 positions of
+  // block w / G. Waves w and w + 4 share a SIMD; for G < 8 they get position
+  // blocks 4 / G apart, so the tiles one of them skips (past its diagonal,
+  // before its window) are not the tiles the other skips and the SIMD's
+  // matrix pipe keeps one wave's work.
+  static_assert(C::NW % G == 0 && C::PW == RW * (C::NW / G), "wave -> (head, block) map");
+  const int head = kvh * G + wave % G;
+  const int wlo = p0 + RW * (wave / G);
+  const int pos = wlo + r32;
   const bool valid = pos < T;
-  const int wlo = p0 + (wave * RW) % C::PW;
-  const int whi = wlo + C::SPAN - 1;
+  const int whi = wlo + RW - 1;
 
   const int kv_lo = (W > 0) ? max(0, p0 - W + 1) : 0;
   const int kv_hi = min(T, p0 + C::PW);
@@ -202,7 +208,7 @@ __global__ __launch_bounds__((Cfg<DK, DV, G, RCH>::NT), 1) void prefill_mfma_ker
       dma_off[i] = r * krow + (RCH + kswz<NPd>(r, q % NPd)) * 16;
     } else {
       const int q = (n - C::KR_DMA - C::KP_DMA) * 64 + lane, r = q / C::VC;
-      dma_off[i] = r * vrow + kswz<C::VC>(r, q % C::VC) * 16;
+      dma_off[i] = r * vrow + vswz(r, q % C::VC) * 16;
     }
   }
   // Tiles past the range are issued too (one vmcnt value then covers every
@@ -300,9 +306,9 @@ __global__ __launch_bounds__((Cfg<DK, DV, G, RCH>::NT), 1) void prefill_mfma_ker
   }
   // V^T operand, transposing reads. In 16-lane group gi (h = gi >> 1, dim
   // block db = gi & 1), lane 4r + c reads dims 32dt + 16db + 4c .. +3 of key
-  // 16j + 8hs + 4h + r. The row swizzle is x = 8hs + 4h + r, so chunk
-  // 4dt + y (y = 2db + (c >> 1)) sits at 4(dt ^ (2hs + h)) + (y ^ r); with
-  // dt = 4A + B: 8 bases (hs, B) plus the immediates 256A and j * 16 rows.
+  // 16j + 8hs + 4h + r. That key row's swizzle is 4r, so chunk 4dt + y
+  // (y = 2db + (c >> 1)) sits at 4(dt ^ r) + y; with dt = 4A + B: 8 bases
+  // (hs, B) plus the immediates 256A and j * 16 rows.
   int vto[2][4];
   {
     const int li = lane & 15, gi = lane >> 4, r = li >> 2, c = li & 3;
@@ -311,8 +317,8 @@ __global__ __launch_bounds__((Cfg<DK, DV, G, RCH>::NT), 1) void prefill_mfma_ker
     for (int hs = 0; hs < 2; ++hs)
 #pragma unroll
       for (int B = 0; B < 4; ++B)
-        vto[hs][B] = C::KT_BYTES + (8 * hs + 4 * h + r) * C::VC * 16 +
-                     ((B ^ (2 * hs + h)) << 6) + ((y ^ r) << 4) + ((c & 1) << 3);
+        vto[hs][B] = C::KT_BYTES + (8 * hs + 4 * h + r) * C::VC * 16 + ((B ^ r) << 6) +
+                     (y << 4) + ((c & 1) << 3);
   }
 
   auto live = [&](int kb) {
