@@ -50,6 +50,8 @@
 //    exact after the final division).
 //  * Causal tiles are issued longest-first; sliding-window launches map
 //    neighbouring query tiles onto the same XCD so their K/V windows share L2.
+#include <type_traits>
+
 #include "attn_common.h"
 #include "kernels.h"
 
@@ -78,10 +80,10 @@ struct Cfg {
   static constexpr int VC = DV / 8;           // 16-byte chunks per V row
   static constexpr int VT_BYTES = BN * VC * 16;
   static constexpr int ST_BYTES = KT_BYTES + VT_BYTES;  // one ring stage
-  // Ring depth: as many stages as LDS holds, at most 4 (tiles loaded up to
-  // three ahead): 3 for the 512-dim keys, 4 for 256- and 128-dim heads.
-  static constexpr int STAGES = (4 * ST_BYTES <= 160 * 1024) ? 4 : 3;
-  static constexpr int AHEAD = STAGES - 1;    // tiles in flight after a step's issue
+  // Ring of 4 stages; the prologue puts tiles 0-2 in flight and step t
+  // issues tile t+3 (the phase schedule below).
+  static constexpr int STAGES = 4;
+  static constexpr int AHEAD = STAGES - 1;
   static constexpr int LDS_BYTES = STAGES * ST_BYTES;
   // 1 KB DMA blocks per tile: rotated K, plain K, V.
   static constexpr int KR_DMA = KR_BYTES / 1024;
@@ -250,20 +252,19 @@ __global__ __launch_bounds__((Cfg<DK, DV, G, RCH>::NT), 1) void prefill_mfma_ker
 #pragma unroll
     for (int s = 0; s < DK / 16; ++s) qw[s] = *(const u32x4*)(qrow + 16 * s);
     if (rot_q) {
-      // rotated chunks: chunk 2s + h < RCH  <=>  s < RCH/2 (RCH is even)
+      // rotated chunks: chunk 2s + h < RCH  <=>  s < RCH/2 (RCH is even).
+      // All cos/sin loads go out at once (one memory round trip): the O
+      // accumulators are not live yet, so their registers hold the table.
+      constexpr int NR = RCH / 2 > 0 ? RCH / 2 : 1;
+      f32x4 t[NR][2];
 #pragma unroll
-      for (int s0 = 0; s0 < RCH / 2; s0 += 4) {
-        f32x4 t[4][2];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int off = prow * tab_row + (16 * (s0 + u) + 8 * h) * 4;
-          t[u][0] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(tres, off, 0, 0));
-          t[u][1] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(tres, off + 16, 0, 0));
-        }
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-          if (s0 + u < RCH / 2) qw[s0 + u] = rotate4(qw[s0 + u], t[u][0], t[u][1]);
+      for (int u = 0; u < RCH / 2; ++u) {
+        const int off = prow * tab_row + (16 * u + 8 * h) * 4;
+        t[u][0] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(tres, off, 0, 0));
+        t[u][1] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(tres, off + 16, 0, 0));
       }
+#pragma unroll
+      for (int u = 0; u < RCH / 2; ++u) qw[u] = rotate4(qw[u], t[u][0], t[u][1]);
     }
 #pragma unroll
     for (int s = 0; s < DK / 16; ++s) {
@@ -289,36 +290,24 @@ __global__ __launch_bounds__((Cfg<DK, DV, G, RCH>::NT), 1) void prefill_mfma_ker
 #pragma unroll
   for (int d = 0; d < DV / 32; ++d) oacc[d] = f32x16{};
 
-  // K operand of step s: key r32, chunk 2s + h, swizzled by x = r32 & M:
-  // chunk (2s + h) ^ x = 2(s ^ (x >> 1)) + (h ^ (x & 1)); with s = HB*A + B
-  // that is HB lane-dependent bases plus the immediate 32*HB*A.
+  // K operand of step s: key r32, chunk 2s + h of its region row, stored at
+  // chunk (2s + h) ^ x with x = r32 & M, i.e. at byte 16((2s + h) ^ x) =
+  // 32s ^ 16(h ^ x) of the row: one XOR-add per read from a per-lane row
+  // offset and mask (precomputed addresses would hold 8 registers).
   constexpr int RW_ = RCH > 0 ? RCH : 16, PW_ = C::NP > 0 ? C::NP : 16;
-  constexpr int HBR = Swz<RW_>::HB, HBP = Swz<PW_>::HB;
-  int kro[HBR], kpo[HBP];
-  {
-    const int xr = r32 & Swz<RW_>::M, xp = r32 & Swz<PW_>::M;
-#pragma unroll
-    for (int B = 0; B < HBR; ++B)
-      kro[B] = r32 * RW_ * 16 + ((B ^ (xr >> 1)) << 5) + ((h ^ (xr & 1)) << 4);
-#pragma unroll
-    for (int B = 0; B < HBP; ++B)
-      kpo[B] = C::KR_BYTES + r32 * PW_ * 16 + ((B ^ (xp >> 1)) << 5) + ((h ^ (xp & 1)) << 4);
-  }
+  const int kr_row = r32 * RW_ * 16, kp_row = C::KR_BYTES + r32 * PW_ * 16;
+  const int kxr = 16 * (h ^ (r32 & Swz<RW_>::M)), kxp = 16 * (h ^ (r32 & Swz<PW_>::M));
   // V^T operand, transposing reads. In 16-lane group gi (h = gi >> 1, dim
   // block db = gi & 1), lane 4r + c reads dims 32dt + 16db + 4c .. +3 of key
   // 16j + 8hs + 4h + r. That key row's swizzle is 4r, so chunk 4dt + y
-  // (y = 2db + (c >> 1)) sits at 4(dt ^ r) + y; with dt = 4A + B: 8 bases
-  // (hs, B) plus the immediates 256A and j * 16 rows.
-  int vto[2][4];
+  // (y = 2db + (c >> 1)) sits at 4(dt ^ r) + y: byte 64((dt & 3) ^ r) plus
+  // 256(dt >> 2), 16y, 8(c & 1) and the row offsets of j and hs.
+  int v_row, vx;
   {
     const int li = lane & 15, gi = lane >> 4, r = li >> 2, c = li & 3;
     const int y = 2 * (gi & 1) + (c >> 1);
-#pragma unroll
-    for (int hs = 0; hs < 2; ++hs)
-#pragma unroll
-      for (int B = 0; B < 4; ++B)
-        vto[hs][B] = C::KT_BYTES + (8 * hs + 4 * h + r) * C::VC * 16 + ((B ^ r) << 6) +
-                     (y << 4) + ((c & 1) << 3);
+    v_row = C::KT_BYTES + (4 * h + r) * C::VC * 16 + (y << 4) + ((c & 1) << 3);
+    vx = r << 6;
   }
 
   auto live = [&](int kb) {
@@ -326,30 +315,79 @@ __global__ __launch_bounds__((Cfg<DK, DV, G, RCH>::NT), 1) void prefill_mfma_ker
     return j0 <= whi && !(W > 0 && j0 + BN - 1 <= wlo - W);
   };
 
-  // One tile, read from the ring stage at LDS pointer st.
-  auto compute = [&](const lds_u8* st, int kb) {
-    const int j0 = kb * BN;
-    const lds_u8* krb[HBR];
-    const lds_u8* kpb[HBP];
+  // Operand reads run OD-1 MFMAs ahead of their use, in a ring of OD
+  // registers; the scheduling barriers keep the compiler from sinking each
+  // read next to its MFMA (it would then wait out the full LDS latency
+  // before every MFMA). Read i+OD-1 reuses the registers of MFMA i-1.
+  constexpr int OD = 3;
+  constexpr int NS = DK / 16;                 // QK MFMAs per tile
+  constexpr int NDT = DV / 32, NPV = 2 * NDT;  // P.V MFMAs per tile
+  // Per-stage operand addressing: row bases for the stage and the lane masks,
+  // passed through an empty asm so the compiler neither hoists the per-read
+  // XORs out of the tile loop nor folds them into long-lived registers.
+  struct Addr {
+    const lds_u8 *kr, *kp, *v;
+    int kxr, kxp, vx;
+  };
+  auto addr = [&](const lds_u8* st) {
+    Addr ad{st + kr_row, st + kp_row, st + v_row, kxr, kxp, vx};
+    asm volatile("" : "+v"(ad.kxr), "+v"(ad.kxp), "+v"(ad.vx));
+    return ad;
+  };
+  // K operand of QK step s (one 16-byte read per lane).
+  auto kread = [&](const Addr& ad, int s) -> bf16x8 {
+    if (s < RCH / 2) return *(const lds_bf16x8*)(ad.kr + ((32 * s) ^ ad.kxr));
+    return *(const lds_bf16x8*)(ad.kp + ((32 * (s - RCH / 2)) ^ ad.kxp));
+  };
+  // V^T operand of P.V step i (key half j = i / NDT, dim tile dt = i % NDT):
+  // two transposing reads of 4 keys each, 8 key rows apart.
+  auto vread = [&](const Addr& ad, int i) -> bf16x8 {
+    const int j = i / NDT, dt = i % NDT;
+    const lds_u8* p = ad.v + (((dt & 3) << 6) ^ ad.vx) + (dt >> 2) * 256 + j * 16 * C::VC * 16;
+    const bf16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)p);
+    const bf16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p + 8 * C::VC * 16));
+    return __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+  };
+
+  // S^T[32 keys][32 rows] of the tile in flight: element e holds key
+  // 8(e/4) + 4h + (e%4). P^T operands of the tile whose softmax ran last.
+  f32x16 sc = f32x16{};
+  bf16x8 pop[2];
+  bf16x8 ob[OD];  // operand ring
+
+  // One matrix phase as a single stream of MFMAs: P.V of one tile (ops
+  // 0 .. NPV-1, V from stage sv) then QK of the next (ops NPV .. NPV+NS-1, K
+  // from stage sk); either part may be absent (PV_, QK_ are compile-time
+  // flags). The first OD-1 operands were read into the ring by stream_head.
+  auto mfma_stream = [&](auto PV_, auto QK_, const Addr& av, const Addr& ak) {
+    constexpr bool do_pv = decltype(PV_)::value, do_qk = decltype(QK_)::value;
+    constexpr int lo = do_pv ? 0 : NPV, hi = do_qk ? NPV + NS : NPV;
+    auto rd = [&](int i) { return i < NPV ? vread(av, i) : kread(ak, i - NPV); };
 #pragma unroll
-    for (int B = 0; B < HBR; ++B) krb[B] = st + kro[B];
-#pragma unroll
-    for (int B = 0; B < HBP; ++B) kpb[B] = st + kpo[B];
-    // S^T[32 keys][32 rows]: element e holds key 8(e/4) + 4h + (e%4). Two
-    // accumulators (even and odd steps) keep consecutive MFMAs independent.
-    f32x16 sacc[2] = {f32x16{}, f32x16{}};
-#pragma unroll
-    for (int s = 0; s < DK / 16; ++s) {
-      bf16x8 kf;
-      if (s < RCH / 2)
-        kf = *(const lds_bf16x8*)(krb[s % HBR] + (s / HBR) * HBR * 32);
+    for (int i = lo; i < hi; ++i) {
+      // ring slot of op i counts from the stream's first op
+      if (i + OD - 1 < hi) ob[(i - lo + OD - 1) % OD] = rd(i + OD - 1);
+      const bf16x8 op = ob[(i - lo) % OD];
+      if (i < NPV)
+        oacc[i % NDT] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op, pop[i / NDT], oacc[i % NDT], 0, 0, 0);
       else
-        kf = *(const lds_bf16x8*)(kpb[(s - RCH / 2) % HBP] + ((s - RCH / 2) / HBP) * HBP * 32);
-      sacc[s & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], sacc[s & 1], 0, 0, 0);
+        sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op, qf[i - NPV], i == NPV ? f32x16{} : sc, 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
     }
+  };
+  auto stream_head = [&](auto PV_, const Addr& av, const Addr& ak) {
+#pragma unroll
+    for (int i = 0; i < OD - 1; ++i) ob[i] = decltype(PV_)::value ? vread(av, i) : kread(ak, i);
+  };
+  using T_ = std::true_type;
+  using F_ = std::false_type;
+
+  // Softmax of the scores in sc (tile kb) into pop.
+  auto softmax = [&](int kb) {
+    const int j0 = kb * BN;
     float sv[16];
 #pragma unroll
-    for (int e = 0; e < 16; ++e) sv[e] = sacc[0][e] + sacc[1][e];
+    for (int e = 0; e < 16; ++e) sv[e] = sc[e];
     // Only tiles crossing the diagonal or a window edge of this wave's rows
     // pay for the per-score test; the empty asm keeps this a branch (the
     // compiler would otherwise run the selects on every tile).
@@ -388,7 +426,6 @@ __global__ __launch_bounds__((Cfg<DK, DV, G, RCH>::NT), 1) void prefill_mfma_ker
     for (int e = 0; e < 16; ++e) ps += pv[e];
     l_run += ps;
     // P^T operand of key step j: this lane's elements 8j .. 8j+7.
-    bf16x8 pop[2];
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const f32x4 lo = {pv[8 * j], pv[8 * j + 1], pv[8 * j + 2], pv[8 * j + 3]};
@@ -396,46 +433,75 @@ __global__ __launch_bounds__((Cfg<DK, DV, G, RCH>::NT), 1) void prefill_mfma_ker
       pop[j] = __builtin_shufflevector(__builtin_convertvector(lo, bf16x4),
                                        __builtin_convertvector(hi, bf16x4), 0, 1, 2, 3, 4, 5, 6, 7);
     }
-    const lds_u8* vb[2][4];
-#pragma unroll
-    for (int hs = 0; hs < 2; ++hs)
-#pragma unroll
-      for (int B = 0; B < 4; ++B) vb[hs][B] = st + vto[hs][B];
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int dt = 0; dt < DV / 32; ++dt) {
-        const int im = (dt / 4) * 256 + j * 16 * C::VC * 16;
-        const bf16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vb[0][dt % 4] + im));
-        const bf16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vb[1][dt % 4] + im));
-        const bf16x8 va = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
-        oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pop[j], oacc[dt], 0, 0, 0);
-      }
   };
 
-  // ---- main loop: a ring of STAGES tiles, loaded AHEAD tiles ahead --------
-  // Step t issues tile t+AHEAD into the stage tile t-1 used, computes tile t,
-  // then waits for tile t+1 (everything but the AHEAD-1 newest groups of DMAs,
-  // which are always the last loads issued) and synchronises. Every step
-  // issues the same DMAs, also the last ones (their tiles may lie past the
-  // range or past T, where the descriptors return zeros, and are never read).
-  int cur = 0;  // stage of tile t
+  // ---- main loop: softmax phases against matrix phases ----------------------
+  // Every wave runs, per tile t: softmax(t) | barrier | P.V(t) then QK(t+1) |
+  // barrier. Waves w and w + 4 share a SIMD; group 1 (waves 4-7) passes one
+  // extra barrier before the loop and group 0 one after it, so between any
+  // two barriers one wave of each SIMD does its softmax (vector ALU) while
+  // the other streams MFMAs, and the two alternate.
+  //
+  // Ring (4 stages): K(t) is read by QK(t) and V(t) by P.V(t), the latter in
+  // the phase that starts at barrier 2t+1 (group 0) or 2t+2 (group 1); the
+  // stage of tile t-1 is therefore free in the phase after barrier 2t+1,
+  // where each wave issues its share of tile t+3. A wave may leave its share
+  // of one tile in flight at a barrier (two for group 0 after a matrix
+  // phase): each tile then has landed one barrier before the QK that reads
+  // it, two steps after its issue.
+  static_assert(C::STAGES == 4, "phase schedule assumes a 4-stage ring");
+  auto stage = [&](int t) {
+    return (const lds_u8*)lds + __builtin_amdgcn_readfirstlane((t & 3) * C::ST_BYTES);
+  };
+  const int lag = wave >> 2;
+  if (n_tiles > 0) {
+    if (live(kb_lo)) {
+      const Addr a0 = addr(stage(0));
+      stream_head(F_{}, a0, a0);
+      mfma_stream(F_{}, T_{}, a0, a0);
+    }
+    if (lag) {
+      wait_vm<C::DMA_W>();
+      lds_barrier();
+    }
+  }
   for (int t = 0; t < n_tiles; ++t) {
     const int kb = kb_lo + t;
-    const int prev = cur == 0 ? C::STAGES - 1 : cur - 1;  // stage of t-1 = of t+AHEAD
-    dma_tile(kb + C::AHEAD, prev);
-    // The stage offset goes through readfirstlane so the compiler treats it as
-    // an opaque scalar: every LDS read is then base register + immediate,
+    const bool lv = live(kb), lv_next = t + 1 < n_tiles && live(kb + 1);
+    // The stage offset goes through readfirstlane so the compiler treats it
+    // as an opaque scalar: every LDS read is then base register + immediate,
     // instead of strength-reduced per-read induction registers.
-    const int so = __builtin_amdgcn_readfirstlane(cur * C::ST_BYTES);
-    if (live(kb)) compute((const lds_u8*)lds + so, kb);
-    cur = cur == C::STAGES - 1 ? 0 : cur + 1;
-    wait_vm<(C::AHEAD - 1) * C::DMA_W>();  // tile t+1 landed
-    lds_barrier();  // ... for every wave; stage of tile t free
+    const Addr at = addr(stage(t)), an = addr(stage(t + 1));
+    if (lv)
+      softmax(kb);
+    else
+      pop[0] = pop[1] = bf16x8{};
+    // The first operands of the matrix phase read landed stages: they
+    // overlap the barrier wait.
+    // A tile dead for this wave next to a live one still runs through the
+    // stream: its P^T is zero (P.V adds nothing) or its scores are never
+    // used (the softmax skips it).
+    const bool any = lv || lv_next;
+    if (any) stream_head(T_{}, at, an);
+    wait_vm<C::DMA_W>();
+    lds_barrier();
+    dma_tile(kb + 3, (t + 3) & 3);
+    if (any) mfma_stream(T_{}, T_{}, at, an);
+    if (lag)
+      wait_vm<C::DMA_W>();
+    else
+      wait_vm<2 * C::DMA_W>();
+    lds_barrier();
   }
-  wait_vm<0>();  // no DMA may still target LDS when the block ends
-
-  // ---- epilogue: O = O^T / l, bf16 ------------------------------------------
+  if (n_tiles > 0 && !lag) lds_barrier();
+  // ---- epilogue: O = O^T / l, bf16, through LDS ------------------------------
+  // Once every wave's DMAs have landed and its reads returned, the ring is
+  // free: each wave stages its 32 x DV output tile there, then writes whole
+  // rows with 16-byte stores (a lane's registers hold 4-dim pieces of one row,
+  // and storing those directly splits every output row over 32 partial-line
+  // writes).
+  wait_vm<0>();
+  lds_barrier();
   // The partner lane (l ^ 32) summed the row's other 16 keys per tile under
   // the same running max.
   {
@@ -443,18 +509,39 @@ __global__ __launch_bounds__((Cfg<DK, DV, G, RCH>::NT), 1) void prefill_mfma_ker
                                                      __float_as_uint(l_run), false, false);
     l_run = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
   }
-  if (valid) {
-    const float inv = 1.f / l_run;
-    uint16_t* orow = (uint16_t*)a.o + (((int64_t)b * T + pos) * a.Hq + head) * DV + 4 * h;
-    // O^T element e of dim tile dt: dim 32dt + 8(e/4) + 4h + (e%4).
+  static_assert(C::ROWS * DV * 2 <= C::LDS_BYTES, "output staging fits the ring");
+  constexpr int ORB = DV * 2;     // bytes per staged row
+  constexpr int VCM = C::VC - 1;  // chunks per row - 1 (a power of two)
+  __attribute__((address_space(3))) unsigned char* ost =
+      (__attribute__((address_space(3))) unsigned char*)lds + wave * (RW * ORB);
+  {
+    const float inv = valid ? 1.f / l_run : 0.f;
+    // O^T element e of dim tile dt: dim 32dt + 8(e/4) + 4h + (e%4), i.e. half
+    // h of 16-byte chunk 4dt + e/4 of row r32; chunks XOR-swizzled by the row.
 #pragma unroll
     for (int dt = 0; dt < DV / 32; ++dt)
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
         const uint32_t w0 = pack_bf16x2(oacc[dt][4 * jj] * inv, oacc[dt][4 * jj + 1] * inv);
         const uint32_t w1 = pack_bf16x2(oacc[dt][4 * jj + 2] * inv, oacc[dt][4 * jj + 3] * inv);
-        *(u32x2*)(orow + 32 * dt + 8 * jj) = u32x2{w0, w1};
+        const int c = 4 * dt + jj;
+        *(__attribute__((address_space(3))) u32x2*)(ost + r32 * ORB + ((c ^ (r32 & VCM)) << 4) +
+                                                    8 * h) = u32x2{w0, w1};
       }
+  }
+  // A wave reads back only what it wrote; its LDS operations run in order.
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  {
+    constexpr int RPI = 64 / C::VC;  // rows per store instruction
+    const int c = lane % C::VC;
+#pragma unroll
+    for (int i = 0; i < RW / RPI; ++i) {
+      const int row = i * RPI + lane / C::VC;
+      const u32x4 val =
+          *(const __attribute__((address_space(3))) u32x4*)(ost + row * ORB + ((c ^ (row & VCM)) << 4));
+      const int p = wlo + row;
+      if (p < T) *(u32x4*)((uint16_t*)a.o + (((int64_t)b * T + p) * a.Hq + head) * DV + 8 * c) = val;
+    }
   }
 }
 
