@@ -319,7 +319,7 @@ __global__ __launch_bounds__((Cfg<DK, DV, G, RCH>::NT), 1) void prefill_mfma_ker
   // registers; the scheduling barriers keep the compiler from sinking each
   // read next to its MFMA (it would then wait out the full LDS latency
   // before every MFMA). Read i+OD-1 reuses the registers of MFMA i-1.
-  constexpr int OD = 3;
+  constexpr int OD = 4;
   constexpr int NS = DK / 16;                 // QK MFMAs per tile
   constexpr int NDT = DV / 32, NPV = 2 * NDT;  // P.V MFMAs per tile
   // Per-stage operand addressing: row bases for the stage and the lane masks,
@@ -359,12 +359,19 @@ __global__ __launch_bounds__((Cfg<DK, DV, G, RCH>::NT), 1) void prefill_mfma_ker
   // 0 .. NPV-1, V from stage sv) then QK of the next (ops NPV .. NPV+NS-1, K
   // from stage sk); either part may be absent (PV_, QK_ are compile-time
   // flags). The first OD-1 operands were read into the ring by stream_head.
-  auto mfma_stream = [&](auto PV_, auto QK_, const Addr& av, const Addr& ak) {
+  // `side` runs once, after the stream's second MFMA: work placed there
+  // (the next tile's DMA issue) fills issue slots while the matrix pipe is
+  // busy instead of delaying the first MFMA.
+  auto mfma_stream = [&](auto PV_, auto QK_, const Addr& av, const Addr& ak, auto&& side) {
     constexpr bool do_pv = decltype(PV_)::value, do_qk = decltype(QK_)::value;
     constexpr int lo = do_pv ? 0 : NPV, hi = do_qk ? NPV + NS : NPV;
     auto rd = [&](int i) { return i < NPV ? vread(av, i) : kread(ak, i - NPV); };
 #pragma unroll
     for (int i = lo; i < hi; ++i) {
+      if (i == lo + 2) {
+        side();
+        __builtin_amdgcn_sched_barrier(0);
+      }
       // ring slot of op i counts from the stream's first op
       if (i + OD - 1 < hi) ob[(i - lo + OD - 1) % OD] = rd(i + OD - 1);
       const bf16x8 op = ob[(i - lo) % OD];
@@ -385,21 +392,22 @@ __global__ __launch_bounds__((Cfg<DK, DV, G, RCH>::NT), 1) void prefill_mfma_ker
   // Softmax of the scores in sc (tile kb) into pop.
   auto softmax = [&](int kb) {
     const int j0 = kb * BN;
-    float sv[16];
-#pragma unroll
-    for (int e = 0; e < 16; ++e) sv[e] = sc[e];
     // Only tiles crossing the diagonal or a window edge of this wave's rows
     // pay for the per-score test; the empty asm keeps this a branch (the
-    // compiler would otherwise run the selects on every tile).
+    // compiler would otherwise run the selects on every tile). Scores are
+    // masked in place: a separate copy costs 16 moves per tile.
     if ((j0 + BN - 1 > wlo) || (W > 0 && j0 <= whi - W)) {
       asm volatile("");
       const int d0 = pos - j0 - 4 * h;
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const unsigned d = (unsigned)(d0 - (8 * (e / 4) + (e % 4)));  // pos - key
-        sv[e] = (d < wcap) ? sv[e] : -INFINITY;
+        sc[e] = (d < wcap) ? sc[e] : -INFINITY;
       }
     }
+    float sv[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) sv[e] = sc[e];
     float mx = sv[0];
 #pragma unroll
     for (int e = 1; e < 16; ++e) mx = fmaxf(mx, sv[e]);
@@ -458,7 +466,7 @@ __global__ __launch_bounds__((Cfg<DK, DV, G, RCH>::NT), 1) void prefill_mfma_ker
     if (live(kb_lo)) {
       const Addr a0 = addr(stage(0));
       stream_head(F_{}, a0, a0);
-      mfma_stream(F_{}, T_{}, a0, a0);
+      mfma_stream(F_{}, T_{}, a0, a0, [] {});
     }
     if (lag) {
       wait_vm<C::DMA_W>();
@@ -485,8 +493,11 @@ __global__ __launch_bounds__((Cfg<DK, DV, G, RCH>::NT), 1) void prefill_mfma_ker
     if (any) stream_head(T_{}, at, an);
     wait_vm<C::DMA_W>();
     lds_barrier();
-    dma_tile(kb + 3, (t + 3) & 3);
-    if (any) mfma_stream(T_{}, T_{}, at, an);
+    auto issue = [&] { dma_tile(kb + 3, (t + 3) & 3); };
+    if (any)
+      mfma_stream(T_{}, T_{}, at, an, issue);
+    else
+      issue();
     if (lag)
       wait_vm<C::DMA_W>();
     else
