@@ -36,9 +36,10 @@ struct PrefillArgs {
 // instantiation for; the caller then uses the general kernel. When K turns,
 // k_rot must hold K's rotary dims already turned (launch_rope_k_lead).
 hipError_t launch_prefill_mfma(const PrefillArgs& a, hipStream_t st);
-// The 16-row-wave variant for 512-dim keys (called by launch_prefill_mfma).
-hipError_t launch_prefill_mfma16(const PrefillArgs& a, hipStream_t st);
 bool prefill_mfma_supported(int Dk, int Dv, int G, float scale, int rotary_dims);
+// The variant for 512-dim keys (called by launch_prefill_mfma): 32-row
+// waves, one per SIMD, accumulators in AGPRs (prefill_mfma1w.hip).
+hipError_t launch_prefill_mfma1w(const PrefillArgs& a, hipStream_t st);
 
 // General kernel: any supported shape, fp32 or bf16.
 hipError_t launch_prefill_general(const PrefillArgs& a, bool bf16, hipStream_t st);

@@ -13,7 +13,7 @@
 // before the P.V product, and everything accumulates in fp32.
 //
 // Used for heads up to 256 dims; the 512-dim keys of the global layers go to
-// the 16-row kernel in prefill_mfma16.hip.
+// the one-wave-per-SIMD kernel in prefill_mfma1w.hip.
 //
 // Design for CDNA4:
 //  * A workgroup of 8 waves (two per SIMD) owns one (batch, KV head) and PW
@@ -68,7 +68,7 @@ struct Cfg {
   // Waves per workgroup: two per SIMD (a wave's registers fit in half the
   // file for heads up to 256 dims).
   static constexpr int NW = 8;
-  static_assert(DK <= 256 && DV <= 256, "larger heads use the 16-row kernel");
+  static_assert(DK <= 256 && DV <= 256, "larger heads use prefill_mfma1w.hip");
   static constexpr int NT = NW * 64;
   static constexpr int ROWS = NW * RW;        // (head, position) rows per WG
   static constexpr int PW = ROWS / G;         // query positions per WG
@@ -609,7 +609,7 @@ hipError_t launch_prefill_mfma(const PrefillArgs& a, hipStream_t st) {
   const int64_t per_b = (int64_t)a.T * a.Hkv * (a.Dk > a.Dv ? a.Dk : a.Dv) * 2;
   if (per_b >= (int64_t)1 << 31 || (int64_t)a.T * a.rot_pairs * 8 >= (int64_t)1 << 31)
     return hipErrorNotSupported;
-  if (a.Dk == 512 && a.Dv == 256) return launch_prefill_mfma16(a, st);
+  if (a.Dk == 512 && a.Dv == 256) return launch_prefill_mfma1w(a, st);
   if (a.Dk == 256 && a.Dv == 256) return dispatch_g<256, 256>(a, st);
   if (a.Dk == 128 && a.Dv == 128) return dispatch_g<128, 128>(a, st);
   return hipErrorNotSupported;

@@ -1,0 +1,637 @@
+// prefill_mfma1w.hip — flash-style causal / sliding-window GQA prefill on
+// gfx950 bf16 matrix cores (v_mfma_f32_32x32x16_bf16) with one wave per SIMD,
+// RoPE applied on the way in.
+//
+// What it computes (Gemma 4 pages): "Gemma 4: End-to-End Architecture
+// Walkthrough", Phase 3 — section 3a (local layers: query i sees the window of
+// keys i-W+1..i; global layers: keys 0..i), section 3b (grouped-query
+// attention, 2 or 8 query heads per KV head, widened global keys) and section
+// 3c (p-RoPE: only the leading quarter of the rotary pairs turn); "Gemma 4
+// Architecture Reference", "Positional Encoding: Proportional RoPE (p-RoPE)".
+// The result equals softmax(scale * rope(q) rope(k)^T + mask) v exactly in
+// exact arithmetic; here q/k are rounded to bf16 after rotation, P to bf16
+// before the P.V product, and everything accumulates in fp32.
+//
+// Design for CDNA4:
+//  * A workgroup of 4 waves, one per SIMD, owns one (batch, KV head) and PW
+//    consecutive query positions for all G query heads of that KV head: 128
+//    (head, position) rows. A wave holds 32 rows (two heads x 16 positions
+//    for G = 8, else one head x 32 positions) and so the whole register file
+//    of its SIMD: Q^T in VGPRs (DK/16 x 16 bytes per lane, 128 registers for
+//    the 512-dim global keys) and the O^T accumulator in AGPRs, which only
+//    MFMAs touch. 32-row waves use v_mfma_f32_32x32x16_bf16 for the widened
+//    keys too, where two waves per SIMD would not fit.
+//  * S^T = K Q^T (M = 32 keys, N = 32 rows) and O^T = V^T P^T as in the
+//    two-wave kernel: every lane holds 16 scores of one row, its partner lane
+//    (l ^ 32) the other 16, and the P^T operand is the lane's own scores.
+//  * Software pipeline: iteration t runs one stream of MFMAs, P.V of tile t-1
+//    and QK of tile t+1, and cuts the softmax of tile t into slices placed
+//    between those MFMAs, so the vector ALU works while the matrix pipe is
+//    busy. A dependent chain of these MFMAs issues every 32 cycles, so one
+//    wave keeps its SIMD's matrix pipe full.
+//  * K and V tiles (32 keys) move HBM -> LDS by direct DMA into two rings of
+//    3 stages each: iteration t issues K(t+3) and V(t+1), two iterations
+//    ahead of their use, with one barrier per iteration.
+//  * K and V rows are XOR-swizzled in 16-byte chunks (conflict-free operand
+//    reads); the output tile is staged in LDS and written as whole rows.
+//  * Only key tiles intersecting the workgroup's causal band / window are
+//    visited; a tile outside one wave's band is masked to -inf (no branch in
+//    the stream).
+//  * The running max is updated lazily: O is rescaled only when a row's block
+//    max exceeds the max in use by more than 2^8.
+#include <type_traits>
+
+#include "attn_common.h"
+#include "kernels.h"
+
+namespace attn {
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLazy = 8.0f;  // log2 headroom before the running max moves
+constexpr int RW = 32;         // query rows per wave
+constexpr int BN = 32;         // keys per tile
+constexpr int NW = 4;          // waves per workgroup (one per SIMD)
+constexpr int NT = NW * 64;
+
+template <int DK, int DV, int G, int RCH>
+struct Cfg1 {
+  static constexpr int HW = G >= 8 ? G / 4 : 1;  // heads per wave
+  static constexpr int PPW = RW / HW;            // positions per wave
+  static constexpr int NHG = G / HW;             // head groups across waves
+  static constexpr int NPB = NW / NHG;           // position blocks per workgroup
+  static constexpr int PW = NPB * PPW;           // positions per workgroup
+  static_assert(HW * NHG == G && NW % NHG == 0 && NPB * NHG == NW, "wave -> rows map");
+  static constexpr int NC = DK / 8;              // 16-byte chunks per K row
+  static constexpr int NP = NC - RCH;            // plain (unrotated) chunks per K row
+  static constexpr int KR_BYTES = BN * RCH * 16;  // K tile: rotated region, then plain
+  static constexpr int KT_BYTES = BN * NC * 16;
+  static constexpr int VC = DV / 8;
+  static constexpr int VT_BYTES = BN * VC * 16;
+  static constexpr int KS = 3, VS = 3;           // ring stages
+  static constexpr int V_OFF = KS * KT_BYTES;
+  static constexpr int LDS_BYTES = KS * KT_BYTES + VS * VT_BYTES;
+  static constexpr int KR_DMA = KR_BYTES / 1024;
+  static constexpr int KP_DMA = (KT_BYTES - KR_BYTES) / 1024;
+  static constexpr int K_DMA = KR_DMA + KP_DMA;
+  static constexpr int V_DMA = VT_BYTES / 1024;
+  static constexpr int KW = K_DMA / NW, VW = V_DMA / NW;  // DMAs per wave per tile
+  static constexpr bool ALIGNED = KR_DMA % NW == 0;
+  __host__ __device__ static constexpr int kregion(int n) { return n < KR_DMA ? 0 : 1; }
+  static_assert(KR_BYTES % 1024 == 0 && KT_BYTES % 1024 == 0 && VT_BYTES % 1024 == 0, "DMA blocks");
+  static_assert(K_DMA % NW == 0 && V_DMA % NW == 0, "even DMA split");
+  static_assert(KW + VW < 64, "vmcnt field");
+  static_assert(LDS_BYTES <= 160 * 1024, "LDS");
+  static_assert(NW * RW * DV * 2 <= LDS_BYTES, "output staging fits");
+  static_assert(DK % 16 == 0 && DV % 32 == 0 && RCH % 2 == 0 && VC >= 16, "tiling");
+};
+
+// XOR swizzle of 16-byte chunks inside a region row of `width` chunks, with
+// the largest power of two P <= 16 dividing the width.
+template <int width>
+struct Swz {
+  static constexpr int P = (width & 15) == 0 ? 16 : (width & 7) == 0 ? 8 : (width & 3) == 0 ? 4
+                           : (width & 1) == 0 ? 2 : 1;
+  static constexpr int M = P - 1;
+};
+template <int width>
+__device__ __forceinline__ int kswz(int r, int c) {
+  return c ^ (r & Swz<width>::M);
+}
+// V rows: chunk c of key row r sits at c ^ 4(r & 3) (transposing reads of 4
+// keys x 4 chunks per 32 lanes hit 16 distinct bank groups).
+__device__ __forceinline__ int vswz(int r, int c) { return c ^ ((r & 3) << 2); }
+
+__device__ __forceinline__ uint32_t rot_pair(uint32_t w, float c, float s) {
+  const float x0 = bf16_lo(w), x1 = bf16_hi(w);
+  return pack_bf16x2(x0 * c - x1 * s, x0 * s + x1 * c);
+}
+__device__ __forceinline__ u32x4 rotate4(u32x4 w, f32x4 t0, f32x4 t1) {
+  u32x4 r;
+  r[0] = rot_pair(w[0], t0[0], t0[1]);
+  r[1] = rot_pair(w[1], t0[2], t0[3]);
+  r[2] = rot_pair(w[2], t1[0], t1[1]);
+  r[3] = rot_pair(w[3], t1[2], t1[3]);
+  return r;
+}
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+template <int N>
+using IC = std::integral_constant<int, N>;
+
+// Calls f(IC<I>{}) for I = 0 .. N-1 at compile time.
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(IC<I>{});
+    static_for<I + 1, N>(f);
+  }
+}
+
+template <int DK, int DV, int G, int RCH>
+__global__ __launch_bounds__(NT, 1) void prefill_mfma1w_kernel(PrefillArgs a, int n_qt,
+                                                               int contig) {
+  using C = Cfg1<DK, DV, G, RCH>;
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[C::LDS_BYTES];
+  // Only MFMAs read or write the accumulators: this asm operand lets the
+  // compiler place them in AGPRs (the other half of the register file).
+  {
+    int z = 0;
+    asm volatile("; accumulators in AGPRs %0" : "+a"(z));
+  }
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int r32 = lane & 31, h = lane >> 5;  // this lane's row; half of the k range
+  const int T = a.T, W = a.window;
+  const int n_wg = n_qt * a.Hkv * a.B;
+  const int L = contig ? xcd_contiguous((int)blockIdx.x, n_wg) : (int)blockIdx.x;
+  const int grp = L / n_qt;
+  const int qt = n_qt - 1 - (L % n_qt);  // longest causal tiles first
+  const int kvh = grp % a.Hkv, b = grp / a.Hkv;
+  const int p0 = qt * C::PW;
+
+  // This lane's row: wave w takes head group w % NHG (HW heads) and position
+  // block w / NHG (PPW positions); row r32 is head r32 / PPW of the group at
+  // position r32 % PPW of the block.
+  const int hg = wave % C::NHG, pb = wave / C::NHG;
+  const int head = kvh * G + hg * C::HW + r32 / C::PPW;
+  const int wlo = p0 + pb * C::PPW;
+  const int pos = wlo + r32 % C::PPW;
+  const bool valid = pos < T;
+  const int whi = wlo + C::PPW - 1;
+
+  const int kv_lo = (W > 0) ? max(0, p0 - W + 1) : 0;
+  const int kv_hi = min(T, p0 + C::PW);
+  const int kb_lo = kv_lo / BN;
+  const int kb_hi = (kv_hi + BN - 1) / BN;
+  const int n_tiles = kb_hi - kb_lo;
+
+  // ---- DMA sources -------------------------------------------------------------
+  const int krow = a.Hkv * DK * 2, vrow = a.Hkv * DV * 2;  // bytes per token
+  const bool rot_q = RCH > 0 && a.rope_q;
+  const bool krot_ws = RCH > 0 && a.rope_k;  // rotated dims from the workspace
+  const int rrow = krot_ws ? a.Hkv * RCH * 16 : krow;
+  const u32x4 kdesc = buffer_desc((const char*)a.k + ((int64_t)b * T * a.Hkv + kvh) * DK * 2,
+                                  (T - 1) * krow + DK * 2);
+  const u32x4 vdesc = buffer_desc((const char*)a.v + ((int64_t)b * T * a.Hkv + kvh) * DV * 2,
+                                  (T - 1) * vrow + DV * 2);
+  const u32x4 rdesc =
+      krot_ws ? buffer_desc((const char*)a.k_rot + ((int64_t)b * T * a.Hkv + kvh) * RCH * 16,
+                            (T - 1) * rrow + RCH * 16)
+              : kdesc;
+
+  // Block n (n = i*NW + wave) of a tile covers 64 chunks; this lane's chunk
+  // offset inside tile row 0 is fixed, a tile adds j0 * row stride.
+  uint32_t koff[C::KW], voff[C::VW];
+#pragma unroll
+  for (int i = 0; i < C::KW; ++i) {
+    const int n = i * NW + wave;
+    if (n < C::KR_DMA) {
+      constexpr int RCHd = RCH > 0 ? RCH : 1;  // dead when RCH == 0
+      const int q = n * 64 + lane, r = q / RCHd;
+      koff[i] = r * rrow + kswz<RCHd>(r, q % RCHd) * 16;
+    } else {
+      constexpr int NPd = C::NP > 0 ? C::NP : 1;
+      const int q = (n - C::KR_DMA) * 64 + lane, r = q / NPd;
+      koff[i] = r * krow + (RCH + kswz<NPd>(r, q % NPd)) * 16;
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < C::VW; ++i) {
+    const int q = (i * NW + wave) * 64 + lane, r = q / C::VC;
+    voff[i] = r * vrow + vswz(r, q % C::VC) * 16;
+  }
+  // Tiles past the range go out at an offset past the descriptors' end: they
+  // return zeros without touching memory, so every iteration issues the same
+  // number of DMAs and one vmcnt value covers every wait.
+  auto dma_k = [&](int kb, int stage) {
+    const int j0 = kb * BN;
+    const uint32_t st = lds_addr(lds) + stage * C::KT_BYTES;
+    const uint32_t far = kb < kb_hi ? 0u : 0x80000000u;
+#pragma unroll
+    for (int i = 0; i < C::KW; ++i) {
+      const int n = i * NW + wave;
+      const int reg = C::ALIGNED ? C::kregion(i * NW) : C::kregion(n);
+      if (reg == 0)
+        dma16(rdesc, st + n * 1024, (koff[i] + j0 * rrow) | far);
+      else
+        dma16(kdesc, st + n * 1024, (koff[i] + j0 * krow) | far);
+    }
+  };
+  auto dma_k1 = [&](int kb, int stage, int i) {
+    const int j0 = kb * BN;
+    const uint32_t st = lds_addr(lds) + stage * C::KT_BYTES;
+    const uint32_t far = kb < kb_hi ? 0u : 0x80000000u;
+    const int n = i * NW + wave;
+    const int reg = C::ALIGNED ? C::kregion(i * NW) : C::kregion(n);
+    if (reg == 0)
+      dma16(rdesc, st + n * 1024, (koff[i] + j0 * rrow) | far);
+    else
+      dma16(kdesc, st + n * 1024, (koff[i] + j0 * krow) | far);
+  };
+  auto dma_v1 = [&](int kb, int stage, int i) {
+    const int j0 = kb * BN;
+    const uint32_t st = lds_addr(lds) + C::V_OFF + stage * C::VT_BYTES;
+    const uint32_t far = kb < kb_hi ? 0u : 0x80000000u;
+    dma16(vdesc, st + (i * NW + wave) * 1024, (voff[i] + j0 * vrow) | far);
+  };
+  auto dma_v = [&](int kb, int stage) {
+    const int j0 = kb * BN;
+    const uint32_t st = lds_addr(lds) + C::V_OFF + stage * C::VT_BYTES;
+    const uint32_t far = kb < kb_hi ? 0u : 0x80000000u;
+#pragma unroll
+    for (int i = 0; i < C::VW; ++i)
+      dma16(vdesc, st + (i * NW + wave) * 1024, (voff[i] + j0 * vrow) | far);
+  };
+
+  // ---- prologue: K(0), V(0) around the Q load, then K(1), K(2) ---------------
+  if (n_tiles > 0) {
+    dma_k(kb_lo, 0);
+    dma_v(kb_lo, 0);
+  }
+  bf16x8 qf[DK / 16];  // Q^T operand: step s covers dims 16s + 8h .. +7 of the row
+  {
+    const int tab_row = a.rot_pairs * 8;  // bytes per table row
+    const __amdgpu_buffer_rsrc_t tres = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)a.rope_tab, (short)0, rot_q ? T * tab_row : 0, 0x00020000);
+    const int prow = valid ? pos : T - 1;
+    const uint16_t* qrow =
+        (const uint16_t*)a.q + (((int64_t)b * T + prow) * a.Hq + head) * DK + 8 * h;
+    u32x4 qw[DK / 16];
+#pragma unroll
+    for (int s = 0; s < DK / 16; ++s) qw[s] = *(const u32x4*)(qrow + 16 * s);
+    if (rot_q) {
+      // rotated chunks 2s + h < RCH <=> s < RCH/2; all cos/sin loads at once
+      constexpr int NR = RCH / 2 > 0 ? RCH / 2 : 1;
+      f32x4 t[NR][2];
+#pragma unroll
+      for (int u = 0; u < RCH / 2; ++u) {
+        const int off = prow * tab_row + (16 * u + 8 * h) * 4;
+        t[u][0] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(tres, off, 0, 0));
+        t[u][1] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(tres, off + 16, 0, 0));
+      }
+#pragma unroll
+      for (int u = 0; u < RCH / 2; ++u) qw[u] = rotate4(qw[u], t[u][0], t[u][1]);
+    }
+#pragma unroll
+    for (int s = 0; s < DK / 16; ++s) {
+      qf[s] = __builtin_bit_cast(bf16x8, valid ? qw[s] : u32x4{});
+      asm volatile("" : "+v"(qf[s]));  // rotated before the next DMAs go out
+    }
+  }
+  if (n_tiles > 0) {
+    dma_k(kb_lo + 1, 1);
+    dma_k(kb_lo + 2, 2);
+    wait_vm<C::KW>();  // K(0), V(0), K(1) landed; K(2) may be in flight
+    lds_barrier();
+  }
+
+  // ---- operand addressing ----------------------------------------------------
+  // K operand of step s: key r32, chunk 2s + h of its region row, stored at
+  // chunk (2s + h) ^ x (x = r32 & M): byte 32s ^ 16(h ^ x) of the row.
+  constexpr int RW_ = RCH > 0 ? RCH : 16, PW_ = C::NP > 0 ? C::NP : 16;
+  const int kr_row = r32 * RW_ * 16, kp_row = C::KR_BYTES + r32 * PW_ * 16;
+  const int kxr = 16 * (h ^ (r32 & Swz<RW_>::M)), kxp = 16 * (h ^ (r32 & Swz<PW_>::M));
+  // V^T operand, transposing reads: in 16-lane group gi (h = gi >> 1, dim
+  // block db = gi & 1), lane 4r + c reads dims 32dt + 16db + 4c .. +3 of key
+  // 16j + 8hs + 4h + r, whose chunk 4dt + y (y = 2db + (c >> 1)) sits at
+  // 4(dt ^ r) + y: byte 64((dt & 3) ^ r) + 256(dt >> 2) + 16y + 8(c & 1).
+  int v_row, vx;
+  {
+    const int li = lane & 15, gi = lane >> 4, r = li >> 2, c = li & 3;
+    const int y = 2 * (gi & 1) + (c >> 1);
+    v_row = (4 * h + r) * C::VC * 16 + (y << 4) + ((c & 1) << 3);
+    vx = r << 6;
+  }
+  struct Addr {
+    const lds_u8 *kr, *kp, *v;
+    int kxr, kxp, vx;
+  };
+  // Row bases of K stage sk and V stage sv; the masks pass through an empty
+  // asm so the per-read XORs are neither hoisted nor folded into registers.
+  auto addr = [&](int sk, int sv) {
+    const lds_u8* kst =
+        (const lds_u8*)lds + __builtin_amdgcn_readfirstlane(sk * C::KT_BYTES);
+    const lds_u8* vst =
+        (const lds_u8*)lds + __builtin_amdgcn_readfirstlane(C::V_OFF + sv * C::VT_BYTES);
+    Addr ad{kst + kr_row, kst + kp_row, vst + v_row, kxr, kxp, vx};
+    asm volatile("" : "+v"(ad.kxr), "+v"(ad.kxp), "+v"(ad.vx));
+    return ad;
+  };
+  constexpr int NS = DK / 16;                 // QK MFMAs per tile
+  constexpr int NDT = DV / 32, NPV = 2 * NDT;  // P.V MFMAs per tile
+  auto kread = [&](const Addr& ad, int s) -> bf16x8 {
+    if (s < RCH / 2) return *(const lds_bf16x8*)(ad.kr + ((32 * s) ^ ad.kxr));
+    return *(const lds_bf16x8*)(ad.kp + ((32 * (s - RCH / 2)) ^ ad.kxp));
+  };
+  auto vread = [&](const Addr& ad, int i) -> bf16x8 {
+    const int j = i / NDT, dt = i % NDT;
+    const lds_u8* p = ad.v + (((dt & 3) << 6) ^ ad.vx) + (dt >> 2) * 256 + j * 16 * C::VC * 16;
+    const bf16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)p);
+    const bf16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p + 8 * C::VC * 16));
+    return __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+  };
+
+  // ---- state -------------------------------------------------------------------
+  // scores to log2 units; kept > 0 so a masked -inf score never meets a zero
+  // factor (scale 0 then acts as 1e-30: every visible key weighs the same)
+  const float c2 = fmaxf(a.scale * kLog2e, 1e-30f);
+  const unsigned wcap = (W > 0) ? (unsigned)W : 0x80000000u;
+  float m_run = -INFINITY, l_run = 0.f;
+  f32x16 oacc[NDT];
+#pragma unroll
+  for (int d = 0; d < NDT; ++d) oacc[d] = f32x16{};
+  // S^T of the tile whose softmax runs next (sc; element e holds key
+  // 8(e/4) + 4h + (e%4)) and of the tile whose QK runs in the current stream
+  // (sn). P^T operands of the tile whose P.V is in the stream (pop) and of the
+  // tile whose softmax is in the stream (pn).
+  f32x16 sc = f32x16{}, sn = f32x16{};
+  bf16x8 pop[2] = {bf16x8{}, bf16x8{}}, pn[2];
+  // softmax state of the tile in flight
+  float smx[4], sst[4], ssum = 0.f, salpha = 1.f, muse = 0.f, smc = 0.f, smn = 0.f;
+  float sp[16], stt[16];
+  int srv = 0;
+  bool sresc = false;
+
+  // Softmax of sc in NSL slices, laid out as a pipeline: every value a slice
+  // needs comes from an earlier slice, so no slice stalls the wave's
+  // in-order issue (and with it the next MFMA) on its own dependency chain.
+  //  0-3   partial maxima of 4 scores each
+  //  4     max of the partials; 5 the partner lane's half (row max)
+  //  6     scaled row max; 7 lazy-rescale vote; 8 new max, rescale factor
+  //  9     factor select, max in use
+  //  10-27 probability pipeline: slice 10+j scales score j, exponentiates
+  //        score j-1, adds probability j-2 to the row sum
+  //  28-29 bf16 P^T operands
+  constexpr int NSL = 30;
+  auto sm_slice = [&](auto K_) {
+    constexpr int k = decltype(K_)::value;
+    if constexpr (k < 4) {
+      smx[k] = fmaxf(fmaxf(sc[4 * k], sc[4 * k + 1]), fmaxf(sc[4 * k + 2], sc[4 * k + 3]));
+      asm volatile("" : "+v"(smx[k]));
+    } else if constexpr (k == 4) {
+      smx[0] = fmaxf(fmaxf(smx[0], smx[1]), fmaxf(smx[2], smx[3]));
+      asm volatile("" : "+v"(smx[0]));
+    } else if constexpr (k == 5) {
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(smx[0]),
+                                                       __float_as_uint(smx[0]), false, false);
+      smx[1] = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+      asm volatile("" : "+v"(smx[1]));
+    } else if constexpr (k == 6) {
+      smc = (smx[1] == -INFINITY) ? -INFINITY : smx[1] * c2;
+      asm volatile("" : "+v"(smc));
+    } else if constexpr (k == 7) {
+      sresc = __any(smc > m_run + kLazy);  // wave-uniform
+      // through a vector register, so the updates are selects, not a branch
+      srv = sresc;
+      asm volatile("" : "+v"(srv));
+    } else if constexpr (k == 8) {
+      smn = srv ? fmaxf(m_run, smc) : m_run;
+      sst[0] = fast_exp2(m_run - smn);
+      asm volatile("" : "+v"(smn), "+v"(sst[0]));
+    } else if constexpr (k == 9) {
+      salpha = srv ? ((m_run == -INFINITY) ? 0.f : sst[0]) : 1.f;
+      m_run = smn;
+      muse = (m_run == -INFINITY) ? 0.f : m_run;
+      ssum = 0.f;
+      asm volatile("" : "+v"(salpha), "+v"(muse), "+v"(ssum));
+    } else if constexpr (k < 28) {
+      constexpr int j = k - 10;
+      if constexpr (j < 16) {  // masked scores are -inf: exactly 0 after exp2
+        stt[j] = fmaf(sc[j], c2, -muse);
+        asm volatile("" : "+v"(stt[j]));
+      }
+      if constexpr (j >= 1 && j <= 16) {
+        sp[j - 1] = fast_exp2(stt[j - 1]);
+        asm volatile("" : "+v"(sp[j - 1]));
+      }
+      if constexpr (j >= 2) {
+        ssum += sp[j - 2];
+        asm volatile("" : "+v"(ssum));
+      }
+    } else {
+      constexpr int jj = k - 28;  // P^T operand of key step jj: elements 8jj .. 8jj+7
+      const f32x4 lo = {sp[8 * jj], sp[8 * jj + 1], sp[8 * jj + 2], sp[8 * jj + 3]};
+      const f32x4 hi = {sp[8 * jj + 4], sp[8 * jj + 5], sp[8 * jj + 6], sp[8 * jj + 7]};
+      pn[jj] = __builtin_shufflevector(__builtin_convertvector(lo, bf16x4),
+                                       __builtin_convertvector(hi, bf16x4), 0, 1, 2, 3, 4, 5, 6, 7);
+      asm volatile("" : "+v"(pn[jj]));
+    }
+  };
+
+  // One stream: P.V of the tile in pop (V at av) and QK of the next tile (K
+  // at ak, into sn), MFMAs interleaved (P.V first for PV_ ops, then QK), with
+  // the softmax slices of sc spread between them when SM_. Operand reads run
+  // OD-1 MFMAs ahead in a ring of OD registers; `side` runs after the second
+  // MFMA (the next tiles' DMA issue).
+  constexpr int OD = 4;
+  bf16x8 ob[OD];
+  // `side(j)` runs after MFMA j + 2 for j < NSIDE: the tile DMAs, one DMA
+  // group per MFMA so their issue never holds up the matrix pipe for long.
+  constexpr int NSIDE = C::KW + C::VW;
+  auto phase = [&](auto PV_, auto QK_, auto SM_, const Addr& av, const Addr& ak, auto&& side) {
+    constexpr bool do_pv = decltype(PV_)::value, do_qk = decltype(QK_)::value;
+    constexpr bool do_sm = decltype(SM_)::value;
+    constexpr int lo = do_pv ? 0 : NPV, hi = do_qk ? NPV + NS : NPV;
+    constexpr int nops = hi - lo;
+    auto rd = [&](int i) { return i < NPV ? vread(av, i) : kread(ak, i - NPV); };
+    if constexpr (nops == 0) {
+      static_for<0, NSIDE>([&](auto J_) { side(J_); });
+      if constexpr (do_sm) static_for<0, NSL>([&](auto K_) { sm_slice(K_); });
+    } else {
+#pragma unroll
+      for (int i = 0; i < OD - 1 && i < nops; ++i) ob[i] = rd(lo + i);
+      static_for<0, nops>([&](auto I_) {
+        constexpr int i = lo + decltype(I_)::value, n = decltype(I_)::value;
+        if constexpr (n >= 2 && n < 2 + NSIDE) side(IC<n - 2>{});
+        if constexpr (n + OD - 1 < nops) ob[(n + OD - 1) % OD] = rd(i + OD - 1);
+        const bf16x8 op = ob[n % OD];
+        if constexpr (i < NPV)
+          oacc[i % NDT] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op, pop[i / NDT], oacc[i % NDT], 0, 0, 0);
+        else
+          sn = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op, qf[i - NPV], i == NPV ? f32x16{} : sn, 0, 0, 0);
+        if constexpr (do_sm) {
+          // softmax slices k with k * nops / NSL landing on this MFMA
+          static_for<0, NSL>([&](auto K_) {
+            constexpr int k = decltype(K_)::value;
+            if constexpr ((k * nops) / NSL == n) sm_slice(K_);
+          });
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      });
+      static_for<(nops > 2 ? (nops - 2 < NSIDE ? nops - 2 : NSIDE) : 0), NSIDE>(
+          [&](auto J_) { side(J_); });
+    }
+  };
+  using T_ = std::true_type;
+  using F_ = std::false_type;
+  auto nothing = [](auto) {};
+
+  // Before the softmax of tile kb: tiles crossing this wave's diagonal or
+  // window edge (or outside its band) get the per-score mask.
+  auto mask = [&](int kb) {
+    const int j0 = kb * BN;
+    if ((j0 + BN - 1 > wlo) || (W > 0 && j0 <= whi - W)) {
+      asm volatile("");
+      const int d0 = pos - j0 - 4 * h;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const unsigned d = (unsigned)(d0 - (8 * (e / 4) + (e % 4)));  // pos - key
+        sc[e] = (d < wcap) ? sc[e] : -INFINITY;
+      }
+    }
+  };
+  // After a stream with a softmax: fold it into l and O, hand its P^T on.
+  auto settle = [&] {
+    l_run = l_run * salpha + ssum;
+    if (sresc) {
+#pragma unroll
+      for (int d = 0; d < NDT; ++d) oacc[d] *= salpha;
+    }
+    pop[0] = pn[0];
+    pop[1] = pn[1];
+  };
+
+  // ---- main loop ---------------------------------------------------------------
+  // Iteration t: mask S(t) | stream: P.V(t-1), QK(t+1), softmax(t) in slices |
+  // settle | wait, barrier. It issues K(t+3) and V(t+1): their stages held
+  // K(t) (read by QK(t) in iteration t-1) and V(t-2) (read in iteration t-1).
+  // Before its barrier a wave waits until all but its newest DMA group
+  // landed, so K(t+2) and V(t) are ready for iteration t+1.
+  // j-th DMA of iteration t's issue (K blocks first, then V).
+  auto issue = [&](int t, auto J_) {
+    constexpr int j = decltype(J_)::value;
+    if constexpr (j < C::KW)
+      dma_k1(kb_lo + t + 3, (t + 3) % 3, j);
+    else
+      dma_v1(kb_lo + t + 1, (t + 1) % 3, j - C::KW);
+  };
+  if (n_tiles > 0) {
+    {  // QK(0); iteration 0 refills its stage with K(3): all reads end first
+      const Addr a0 = addr(0, 0);
+      phase(F_{}, T_{}, F_{}, a0, a0, nothing);
+      sc = sn;
+      lds_barrier();
+    }
+    int t = 0;
+    // iteration 0: QK(1) and softmax(0), no P.V yet
+    mask(kb_lo);
+    if (n_tiles > 1)
+      phase(F_{}, T_{}, T_{}, addr(1, 0), addr(1, 0), [&](auto J_) { issue(0, J_); });
+    else
+      phase(F_{}, F_{}, T_{}, addr(0, 0), addr(0, 0), [&](auto J_) { issue(0, J_); });
+    settle();
+    sc = sn;
+    wait_vm<C::KW + C::VW>();
+    lds_barrier();
+    for (t = 1; t + 1 < n_tiles; ++t) {
+      mask(kb_lo + t);
+      phase(T_{}, T_{}, T_{}, addr((t + 1) % 3, (t - 1) % 3), addr((t + 1) % 3, (t - 1) % 3),
+            [&](auto J_) { issue(t, J_); });
+      settle();
+      sc = sn;
+      wait_vm<C::KW + C::VW>();
+      lds_barrier();
+    }
+    if (n_tiles > 1) {  // iteration n-1: P.V(n-2) and softmax(n-1)
+      t = n_tiles - 1;
+      mask(kb_lo + t);
+      phase(T_{}, F_{}, T_{}, addr(0, (t - 1) % 3), addr(0, (t - 1) % 3), [&](auto J_) { issue(t, J_); });
+      settle();
+      wait_vm<C::KW + C::VW>();
+      lds_barrier();
+    }
+    {  // P.V(n-1)
+      const Addr an = addr(0, (n_tiles - 1) % 3);
+      phase(T_{}, F_{}, F_{}, an, an, nothing);
+    }
+  }
+
+  // ---- epilogue: O = O^T / l, bf16, staged through LDS ---------------------------
+  wait_vm<0>();
+  lds_barrier();
+  {
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_run),
+                                                     __float_as_uint(l_run), false, false);
+    l_run = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+  }
+  constexpr int ORB = DV * 2;     // bytes per staged row
+  constexpr int VCM = C::VC - 1;  // chunks per row - 1 (a power of two)
+  __attribute__((address_space(3))) unsigned char* ost =
+      (__attribute__((address_space(3))) unsigned char*)lds + wave * (RW * ORB);
+  {
+    const float inv = valid ? 1.f / l_run : 0.f;
+    // O^T element e of dim tile dt: dim 32dt + 8(e/4) + 4h + (e%4), i.e. half
+    // h of 16-byte chunk 4dt + e/4 of row r32; chunks XOR-swizzled by the row.
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const uint32_t w0 = pack_bf16x2(oacc[dt][4 * jj] * inv, oacc[dt][4 * jj + 1] * inv);
+        const uint32_t w1 = pack_bf16x2(oacc[dt][4 * jj + 2] * inv, oacc[dt][4 * jj + 3] * inv);
+        const int c = 4 * dt + jj;
+        *(__attribute__((address_space(3))) u32x2*)(ost + r32 * ORB + ((c ^ (r32 & VCM)) << 4) +
+                                                    8 * h) = u32x2{w0, w1};
+      }
+  }
+  // A wave reads back only what it wrote; its LDS operations run in order.
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  {
+    constexpr int RPI = 64 / C::VC;  // rows per store instruction
+    const int c = lane % C::VC;
+#pragma unroll
+    for (int i = 0; i < RW / RPI; ++i) {
+      const int row = i * RPI + lane / C::VC;
+      const u32x4 val = *(const __attribute__((address_space(3))) u32x4*)(
+          ost + row * ORB + ((c ^ (row & VCM)) << 4));
+      const int p = wlo + row % C::PPW;
+      const int hd = kvh * G + hg * C::HW + row / C::PPW;
+      if (p < T) *(u32x4*)((uint16_t*)a.o + (((int64_t)b * T + p) * a.Hq + hd) * DV + 8 * c) = val;
+    }
+  }
+}
+
+template <int DK, int DV, int G, int RCH>
+hipError_t launch_one(const PrefillArgs& a, hipStream_t st) {
+  using C = Cfg1<DK, DV, G, RCH>;
+  const int n_qt = (a.T + C::PW - 1) / C::PW;
+  const int64_t n = (int64_t)n_qt * a.Hkv * a.B;
+  if (n == 0) return hipSuccess;
+  if (n > 0x7fffffff) return hipErrorInvalidValue;
+  // Sliding-window tiles reuse their neighbours' K/V: keep neighbours on one
+  // XCD. Causal tiles share the prefix of every key stream: interleave.
+  const int contig = (a.window > 0 && a.window < a.T) ? 1 : 0;
+  hipLaunchKernelGGL((prefill_mfma1w_kernel<DK, DV, G, RCH>), dim3((unsigned)n), dim3(NT), 0, st,
+                     a, n_qt, contig);
+  return hipGetLastError();
+}
+
+template <int DK, int DV, int G>
+hipError_t dispatch_rot(const PrefillArgs& a, hipStream_t st) {
+  const int rch = (a.rope_q || a.rope_k) ? (2 * a.rot_pairs) / 8 : 0;
+  if (rch == 0) return launch_one<DK, DV, G, 0>(a, st);
+  if (rch == DK / 32) return launch_one<DK, DV, G, DK / 32>(a, st);
+  if (rch == DK / 8) return launch_one<DK, DV, G, DK / 8>(a, st);
+  return hipErrorNotSupported;
+}
+
+template <int DK, int DV>
+hipError_t dispatch_g(const PrefillArgs& a, hipStream_t st) {
+  switch (a.Hq / a.Hkv) {
+    case 1: return dispatch_rot<DK, DV, 1>(a, st);
+    case 2: return dispatch_rot<DK, DV, 2>(a, st);
+    case 4: return dispatch_rot<DK, DV, 4>(a, st);
+    case 8: return dispatch_rot<DK, DV, 8>(a, st);
+    default: return hipErrorNotSupported;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_prefill_mfma1w(const PrefillArgs& a, hipStream_t st) {
+  if (a.Dk == 512 && a.Dv == 256) return dispatch_g<512, 256>(a, st);
+  return hipErrorNotSupported;
+}
+
+}  // namespace attn

@@ -351,8 +351,9 @@ def main():
             secondary[str(s)] = {"workload": sc["name"], "unit": "TFLOP/s",
                                  "value": round(rr["flops"] / rr["step_ms"] / 1e9, 3),
                                  "ms_per_step": round(rr["step_ms"], 4),
-                                 "roofline": roofline("mfma", tf, PEAK_BF16_TFLOPS, "TFLOP/s",
-                                                      _traffic("prefill_mfma", "global_prefill"))}
+                                 "roofline": dict(roofline("mfma", tf, PEAK_BF16_TFLOPS, "TFLOP/s",
+                                                           _traffic("prefill_mfma1w", "global_prefill")),
+                                                  kernel="prefill_mfma1w_kernel")}
             del rr
         elif sc["kind"] == "decode":
             rr = bench_decode(ar, torch, inputs, sc, max(3, args.steps // 4), 1)
