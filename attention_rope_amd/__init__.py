@@ -67,7 +67,7 @@ def load(path: str = LIB_PATH):
     lib.attn_prefill.argtypes = [vp, vp, vp, vp] + [i32] * 7 + [
         ctypes.c_float, _Rope, i32, vp, vp, sz, ctypes.c_int, vp]
     lib.attn_prefill.restype = ctypes.c_int
-    lib.attn_decode_workspace_bytes.argtypes = [i32] * 5
+    lib.attn_decode_workspace_bytes.argtypes = [i32] * 6
     lib.attn_decode_workspace_bytes.restype = sz
     lib.attn_decode.argtypes = [vp] * 6 + [i32] * 6 + [
         ctypes.c_float, _Rope, i32, vp, sz, ctypes.c_int, vp]
@@ -166,8 +166,9 @@ def prefill(q, k, v, *, window: int = 0, scale: float | None = None,
     return o
 
 
-def decode_workspace_bytes(B: int, Hq: int, Dv: int, max_kv_len: int, window: int) -> int:
-    return int(load().attn_decode_workspace_bytes(B, Hq, Dv, max_kv_len, window))
+def decode_workspace_bytes(B: int, Hq: int, Hkv: int, Dv: int, max_kv_len: int,
+                           window: int) -> int:
+    return int(load().attn_decode_workspace_bytes(B, Hq, Hkv, Dv, max_kv_len, window))
 
 
 def decode(q, k_cache, v_cache, row_offset, kv_len, *, window: int = 0,
@@ -182,7 +183,7 @@ def decode(q, k_cache, v_cache, row_offset, kv_len, *, window: int = 0,
     if scale is None:
         scale = Dk ** -0.5
     o = out if out is not None else torch.empty((B, Hq, Dv), dtype=q.dtype, device=q.device)
-    need = decode_workspace_bytes(B, Hq, Dv, max_kv_len, window)
+    need = decode_workspace_bytes(B, Hq, Hkv, Dv, max_kv_len, window)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
     _check(lib.attn_decode(_dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),

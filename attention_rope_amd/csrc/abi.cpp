@@ -189,9 +189,9 @@ attn_status_t attn_prefill(const void* q, const void* k, const void* v, void* o,
                        "prefill (general)");
 }
 
-size_t attn_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t Dv, int32_t max_kv_len,
-                                   int32_t window) {
-  return attn::decode_workspace_bytes(B, Hq, Dv, max_kv_len, window);
+size_t attn_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t Dv,
+                                   int32_t max_kv_len, int32_t window) {
+  return attn::decode_workspace_bytes(B, Hq, Hkv, Dv, max_kv_len, window);
 }
 
 attn_status_t attn_decode(const void* q, const void* k_cache, const void* v_cache,
@@ -207,19 +207,22 @@ attn_status_t attn_decode(const void* q, const void* k_cache, const void* v_cach
     return fail(ATTN_ERR_SHAPE, "Hq=%d must be a positive multiple of Hkv=%d", Hq, Hkv);
   if (!attn::decode_supported(Dk, Dv, Hq / Hkv))
     return fail(ATTN_ERR_UNSUPPORTED,
-                "decode supports Dk in {128,256,512}, Dv in {128,256}, Hq/Hkv <= 16 "
-                "(got Dk=%d Dv=%d G=%d)", Dk, Dv, Hq / Hkv);
+                "decode supports Dk in {128,256,512}, Dv in {128,256} (or 512 with "
+                "Dk=512), Hq/Hkv <= 16 (got Dk=%d Dv=%d G=%d)", Dk, Dv, Hq / Hkv);
   if (!std::isfinite(scale) || scale < 0.f)
     return fail(ATTN_ERR_UNSUPPORTED, "decode needs a finite scale >= 0");
   attn_status_t rs = check_rope(rope, Dk);
   if (rs != ATTN_OK) return rs;
   if (B == 0) return ok();
   if (max_kv_len < 1) return fail(ATTN_ERR_SHAPE, "max_kv_len=%d must be >= 1", max_kv_len);
+  if (!attn::decode_shape_fits(B, Hkv, Dk, Dv, max_kv_len, window))
+    return fail(ATTN_ERR_SHAPE, "cache too large for one call (max_kv_len=%d, Hkv=%d)",
+                max_kv_len, Hkv);
   if (!q || !k_cache || !v_cache || !row_offset || !kv_len || !o)
     return fail(ATTN_ERR_NULL, "q, caches, row_offset, kv_len and o must be non-NULL");
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o))
     return fail(ATTN_ERR_SHAPE, "q, caches and o must be 16-byte aligned");
-  const size_t need = attn::decode_workspace_bytes(B, Hq, Dv, max_kv_len, window);
+  const size_t need = attn::decode_workspace_bytes(B, Hq, Hkv, Dv, max_kv_len, window);
   if (!workspace || workspace_bytes < need)
     return fail(ATTN_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
                 workspace ? workspace_bytes : (size_t)0);

@@ -61,8 +61,9 @@ struct DecodeArgs {
   void* workspace;
 };
 
-size_t decode_workspace_bytes(int B, int Hq, int Dv, int max_kv_len, int window);
+size_t decode_workspace_bytes(int B, int Hq, int Hkv, int Dv, int max_kv_len, int window);
 bool decode_supported(int Dk, int Dv, int G);
+bool decode_shape_fits(int B, int Hkv, int Dk, int Dv, int max_kv_len, int window);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t st);
 
 }  // namespace attn

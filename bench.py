@@ -154,7 +154,7 @@ def bench_decode(ar, torch, inputs, cfg, steps, warmup):
                                                   device="cuda", kv_len=kvl)
         offd, kvld = off.cuda(), kvl.cuda()
         maxl = int(kvl.max())
-        ws = torch.empty(ar.decode_workspace_bytes(d.n_seq, d.Hq, d.Dv, maxl, d.window),
+        ws = torch.empty(ar.decode_workspace_bytes(d.n_seq, d.Hq, d.Hkv, d.Dv, maxl, d.window),
                          dtype=torch.uint8, device="cuda")
         o = torch.empty((d.n_seq, d.Hq, d.Dv), dtype=d.dtype, device="cuda")
         vis = [min(int(n), d.window) if d.window > 0 else int(n) for n in kvl.tolist()]
@@ -187,8 +187,35 @@ def bench_decode(ar, torch, inputs, cfg, steps, warmup):
     torch.cuda.synchronize()
     g_ms = sum(t.ms(i, 0, 1) for i in range(steps)) / steps
     l_ms = sum(t.ms(i, 1, 2) for i in range(steps)) / steps
+
+    # Keys as values (K = V) on the global shape: the global call's key cache
+    # passed as both caches (Dv = Dk = 512), so each row is read once.
+    g = calls[0]
+    d = g["d"]
+    o_kv = torch.empty((d.n_seq, d.Hq, d.Dk), dtype=d.dtype, device="cuda")
+    ws_kv = torch.empty(ar.decode_workspace_bytes(d.n_seq, d.Hq, d.Hkv, d.Dk, g["maxl"],
+                                                  d.window), dtype=torch.uint8, device="cuda")
+    vis = [min(int(n), d.window) if d.window > 0 else int(n) for n in g["kvl_host"].tolist()]
+    kv_bytes = sum(vis) * d.Hkv * d.Dk * 2 + d.n_seq * d.Hq * 2 * d.Dk * 2
+
+    def run_kv():
+        ar.decode(g["q"], g["kc"], g["kc"], g["off"], g["kvl"], window=d.window, scale=d.scale,
+                  rotary_dims=d.rotary_dims, theta=d.theta, max_kv_len=g["maxl"], out=o_kv,
+                  workspace=ws_kv)
+
+    for _ in range(warmup):
+        run_kv()
+    tk = Timer(torch, steps)
+    for i in range(steps):
+        flush.fill_(i & 0xff)
+        tk.mark(i, 0)
+        run_kv()
+        tk.mark(i, 1)
+    torch.cuda.synchronize()
+    kv_ms = sum(tk.ms(i, 0, 1) for i in range(steps)) / steps
     return dict(bytes=total_bytes, g_ms=g_ms, l_ms=l_ms, step_ms=g_ms + l_ms,
-                g_bytes=calls[0]["bytes"], l_bytes=calls[1]["bytes"], calls=calls)
+                g_bytes=calls[0]["bytes"], l_bytes=calls[1]["bytes"], calls=calls,
+                kv_ms=kv_ms, kv_bytes=kv_bytes, kv_out=o_kv)
 
 
 def bench_stack(ar, torch, inputs, cfg, steps, warmup):
@@ -366,6 +393,11 @@ def main():
                                                  "bytes": rr["g_bytes"]},
                                  "local_call": {"GB/s": round(l, 1), "ms": round(rr["l_ms"], 4),
                                                 "bytes": rr["l_bytes"]},
+                                 "keys_as_values_call": {
+                                     "GB/s": round(rr["kv_bytes"] / (rr["kv_ms"] * 1e-3) / 1e9, 1),
+                                     "ms": round(rr["kv_ms"], 4), "bytes": rr["kv_bytes"],
+                                     "what": "global shape with K = V: one 512-dim cache read "
+                                             "once for both products (Dv = Dk = 512)"},
                                  "roofline": roofline("hbm", g, PEAK_HBM_GBS, "GB/s",
                                                       _traffic("decode_ring", "global_decode"))}
             del rr

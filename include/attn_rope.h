@@ -124,6 +124,12 @@ attn_status_t attn_prefill(const void *q, const void *k, const void *v, void *o,
  *     already rotated) and values; sequence b owns rows
  *     row_offset[b] .. row_offset[b] + kv_len[b] - 1, the last one being the
  *     new token's own row (the caller appends it before the call).
+ *   Keys as values (K = V, the global-layer form of "Gemma 4: End-to-End
+ *     Architecture Walkthrough", Phase 3 section 3b, and of the "Gemma 4
+ *     Technical Report" reader, "Core Model Architecture"): pass the same
+ *     pointer as k_cache and v_cache with Dv == Dk. The attention weights then
+ *     multiply the cached (rotated) keys, and each cache row is read once for
+ *     both products.
  *   row_offset: device int64 [B]; kv_len: device int32 [B], 0 <= kv_len[b] <=
  *     max_kv_len. kv_len[b] == 0 gives o[b] = 0.
  *   window: <= 0: all rows; otherwise only the last `window` rows
@@ -131,11 +137,14 @@ attn_status_t attn_prefill(const void *q, const void *k, const void *v, void *o,
  *     they may hold anything).
  *   o [B, Hq, Dv] output.
  * Supported: Hq % Hkv == 0 with Hq / Hkv <= 16, Dk in {128, 256, 512},
- *   Dv in {128, 256}; max_kv_len >= 1.
+ *   Dv in {128, 256} (or 512 with Dk = 512); max_kv_len >= 1, and a cache
+ *   that fits one call (ATTN_ERR_SHAPE past about 5 * 10^8 rows per sequence,
+ *   or past 2 GB per 8192 rows of all KV heads).
  * Workspace: attn_decode_workspace_bytes() bytes of device memory for the
- *   split-K partial results; contents are scratch.
+ *   split-K partial results (the split depends on B, Hkv, max_kv_len and
+ *   window, so pass the same values to both calls); contents are scratch.
  */
-size_t attn_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t Dv,
+size_t attn_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t Dv,
                                    int32_t max_kv_len, int32_t window);
 
 attn_status_t attn_decode(const void *q, const void *k_cache, const void *v_cache,

@@ -131,6 +131,28 @@ def prefill(q, k, v, *, window: int, scale: float, rotary_dims: int = 0,
     return o
 
 
+def prefill_kv_shared(q, k, *, window: int, scale: float, rotary_dims: int = 0,
+                      theta: float = 10000.0, pos0: int = 0, rows=None,
+                      nthreads: int | None = None) -> np.ndarray:
+    """Attention with the keys reused as values (K = V), fp64.
+
+    Global layers drop the value projection and weight the key matrix itself,
+    so only keys are cached ("Gemma 4: End-to-End Architecture Walkthrough",
+    Phase 3 section 3b; "Gemma 4 Technical Report" reader, "Core Model
+    Architecture", worked example). The pages leave open whether the values
+    are the keys before or after RoPE. Reading taken: after -- the values are
+    the keys exactly as Q K^T uses them, which are the rows a decode cache
+    holds. q [B, n_rows, Hq, Dk], k [B, T, Hkv, Dk] (unrotated); returns
+    o [B, n_rows, Hq, Dk].
+    """
+    k = _f64(k)
+    B, T, Hkv, Dk = k.shape
+    pos = np.tile(np.arange(pos0, pos0 + T, dtype=np.int64), B)
+    kr = rope(k.reshape(B * T, Hkv, Dk), pos, rotary_dims, theta).reshape(B, T, Hkv, Dk)
+    return prefill(q, kr, kr, window=window, scale=scale, rotary_dims=rotary_dims,
+                   theta=theta, rope_mask=ROPE_Q, pos0=pos0, rows=rows, nthreads=nthreads)
+
+
 def decode_one(q, k_rows, v_rows, *, kv_len: int, row0: int = 0, window: int,
                scale: float, rotary_dims: int = 0, theta: float = 10000.0,
                nthreads: int | None = None) -> np.ndarray:

@@ -138,13 +138,21 @@ def test_decode_validation(lib):
     assert _decode(lib, ws=None) == 4
     assert _decode(lib, o=FAKE) == 6
     assert _decode(lib, B=0, q=None) == 0
+    assert _decode(lib, Dk=256, Dv=512) == 3        # 512-dim values need 512-dim keys
+    assert _decode(lib, B=1, max_kv_len=2**31 - 1) == 2   # > 65535 chunks of 8192 rows
+    assert b"too large" in lib.attn_last_error()
 
 
 def test_decode_workspace_bytes(lib):
-    # global: chunks of 1024 rows; local: chunks of 512 rows within the window
-    assert lib.attn_decode_workspace_bytes(64, 32, 256, 131073, 0) == 64 * 32 * 129 * 258 * 4
-    assert lib.attn_decode_workspace_bytes(64, 16, 256, 131073, 1024) == 64 * 16 * 2 * 258 * 4
-    assert lib.attn_decode_workspace_bytes(0, 16, 256, 10, 0) == 0
+    """Chunks: up to 4096 rows (global) or the whole window (local), halved
+    (down to 256) while B * Hkv * splits < 512."""
+    ws = lib.attn_decode_workspace_bytes
+    assert ws(64, 32, 4, 256, 131073, 0) == 64 * 32 * 33 * 258 * 4      # 4096-row chunks
+    assert ws(64, 16, 8, 256, 131073, 1024) == 64 * 16 * 1 * 258 * 4    # one 1024-row window
+    assert ws(1, 32, 4, 256, 131072, 0) == 1 * 32 * 128 * 258 * 4       # 1024-row chunks
+    assert ws(8, 16, 8, 256, 131073, 1024) == 8 * 16 * 4 * 258 * 4      # 256-row chunks
+    assert ws(1, 8, 1, 128, 300, 0) == 1 * 8 * 2 * 130 * 4              # floor of 256 rows
+    assert ws(0, 16, 8, 256, 10, 0) == 0
 
 
 def test_prope_validation(lib):

@@ -60,13 +60,18 @@ def test_config3_global_prefill():
     torch.cuda.empty_cache()
 
 
-@pytest.mark.parametrize("kind", ["glob", "loc"])
+@pytest.mark.parametrize("kind", ["glob", "loc", "glob_kv"])
 def test_config4_decode(kind):
+    """glob_kv: the global call with keys as values (its key cache passed as
+    both caches, Dv = Dk = 512), as the benchmark times it."""
     cfg = inputs.CONFIGS[4]
-    d = cfg["cases"][kind]
-    seed = cfg["seed"] + (0 if kind == "glob" else 100)
+    d = cfg["cases"]["loc" if kind == "loc" else "glob"]
+    seed = cfg["seed"] + (100 if kind == "loc" else 0)
     kvl = inputs.decode_lengths(d, cfg["seed"])
     q, kc, vc, off, kvl = inputs.decode_inputs(d, seed, device=DEV, kv_len=kvl)
+    if kind == "glob_kv":
+        del vc
+        vc = kc
     maxl = int(kvl.max())
     o = ar.decode(q, kc, vc, off.to(DEV), kvl.to(DEV), window=d.window, scale=d.scale,
                   rotary_dims=d.rotary_dims, theta=d.theta, max_kv_len=maxl)

@@ -12,13 +12,18 @@ DEV = "cuda:0"
 BF = torch.bfloat16
 
 
-def run(ar, Hq, Hkv, Dk, Dv, W, R, theta, lens, seed=3, poison=True):
+def run(ar, Hq, Hkv, Dk, Dv, W, R, theta, lens, seed=3, poison=True, shared=False):
+    """shared: one cache serves as keys and values (K = V), passed twice."""
     c = inputs.DecodeCase(len(lens), Hq, Hkv, Dk, Dv, window=W, rotary_dims=R, theta=theta,
                           len_lo=1, len_hi=1)
     kvl = torch.tensor(lens, dtype=torch.int32)
-    print(f"decode Hq={Hq} Hkv={Hkv} Dk={Dk} Dv={Dv} W={W} lens={lens}", flush=True)
+    print(f"decode Hq={Hq} Hkv={Hkv} Dk={Dk} Dv={Dv} W={W} shared={shared} lens={lens}",
+          flush=True)
     q, kc, vc, off, kvl = inputs.decode_inputs(c, seed, device=DEV, kv_len=kvl,
                                               poison_outside_window=poison)
+    if shared:
+        assert Dk == Dv
+        vc = kc
     o = ar.decode(q, kc, vc, off.to(DEV), kvl.to(DEV), window=W, scale=c.scale,
                   rotary_dims=R, theta=theta, max_kv_len=max(1, max(lens)))
     torch.cuda.synchronize()
@@ -47,8 +52,38 @@ def test_decode_shapes(gpu_lib, Hq, Hkv, Dk, Dv, R):
     run(gpu_lib, Hq, Hkv, Dk, Dv, 0, R, 1e4, [5, 64, 700, 2049])
 
 
+@pytest.mark.parametrize("Hq,Hkv,D,W,R,th", [(32, 4, 512, 0, 128, 1e6),
+                                             (16, 8, 256, 1024, 256, 1e4),
+                                             (8, 1, 128, 0, 32, 1e4)])
+def test_decode_keys_as_values(gpu_lib, Hq, Hkv, D, W, R, th):
+    """K = V: the same cache pointer as keys and values (tiles hold K only)."""
+    run(gpu_lib, Hq, Hkv, D, D, W, R, th, LENS, shared=True)
+
+
+def test_decode_512_dim_values(gpu_lib):
+    """Separate 512-dim values (one-wave ring) next to the shared form."""
+    run(gpu_lib, 32, 4, 512, 512, 0, 128, 1e6, [1, 17, 33, 700, 2049])
+    run(gpu_lib, 32, 4, 512, 512, 0, 128, 1e6, [1, 17, 33, 700, 2049], shared=True)
+
+
+def test_decode_long_chunks(gpu_lib):
+    """Enough sequences x KV heads that chunks stay 8192 rows long; lengths
+    straddle chunk boundaries, mixed with short sequences."""
+    lens = [8191, 8192, 8193, 16385] + [1 + 37 * i for i in range(28)]
+    run(gpu_lib, 16, 8, 256, 256, 0, 64, 1e6, lens)
+    run(gpu_lib, 16, 8, 256, 256, 0, 64, 1e6, lens, shared=True)
+
+
+@pytest.mark.parametrize("R", [4, 12, 36])
+def test_decode_rotary_dims_not_multiple_of_8(gpu_lib, R):
+    run(gpu_lib, 8, 2, 128, 128, 0, R, 1e4, [3, 40, 300])
+
+
 def test_decode_empty_sequence_is_zero(gpu_lib):
     o = run(gpu_lib, 32, 4, 512, 256, 0, 128, 1e6, [0, 10, 0, 300])
+    assert torch.all(o[0] == 0) and torch.all(o[2] == 0)
+    # one chunk per sequence (window 100): the streaming kernel writes o itself
+    o = run(gpu_lib, 16, 8, 256, 256, 100, 256, 1e4, [0, 10, 0, 300])
     assert torch.all(o[0] == 0) and torch.all(o[2] == 0)
 
 

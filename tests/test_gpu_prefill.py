@@ -175,3 +175,21 @@ def test_prefill_errors_raise(gpu_lib):
         gpu_lib.prefill(q, kv, kv, rotary_dims=66)
     with pytest.raises(ValueError):
         gpu_lib.prefill(q, q[:, :, :2], q[:, :, :2])  # non-contiguous views
+
+
+@pytest.mark.parametrize("T,Hq,Hkv,D,W,R,th", [(150, 16, 2, 512, 0, 128, 1e6),
+                                               (300, 16, 8, 256, 100, 256, 1e4)])
+def test_prefill_keys_as_values(gpu_lib, T, Hq, Hkv, D, W, R, th):
+    """K = V prefill: keys rotated once by prope_apply serve as keys (with
+    RoPE on q only) and as values; the oracle rotates them itself."""
+    c = inputs.PrefillCase(1, T, Hq, Hkv, D, D, window=W, rotary_dims=R, theta=th, dtype=BF)
+    q, k, _ = inputs.prefill_inputs(c, 21, device=DEV)
+    print(f"kv-shared prefill T={T} Hq={Hq} Hkv={Hkv} D={D} W={W}", flush=True)
+    pos = torch.arange(T, dtype=torch.int32, device=DEV)
+    kr = gpu_lib.prope(k[0], pos, rotary_dims=R, theta=th).unsqueeze(0)
+    o = gpu_lib.prefill(q, kr, kr, window=W, scale=c.scale, rotary_dims=R, theta=th,
+                        rope_mask=gpu_lib.ROPE_Q)
+    torch.cuda.synchronize()
+    ref = oracle.prefill_kv_shared(q.cpu(), k.cpu(), window=W, scale=c.scale, rotary_dims=R,
+                                   theta=th)
+    assert_close(o, ref, BF, "prefill K=V")

@@ -297,6 +297,82 @@ def test_row_subset_equals_full():
     np.testing.assert_array_equal(sub, full[:, rows])
 
 
+# ------------------------------------------------- K = V (keys as values) ----
+# Reading: the values are the keys after RoPE, the rows the cache holds.
+
+def test_kv_shared_first_token_returns_its_own_key():
+    """Token 0 sees only itself and RoPE at position 0 is the identity, so its
+    output is its own unrotated key (per KV head, for each of its G heads)."""
+    q = rng.standard_normal((2, 5, 8, 16))
+    k = rng.standard_normal((2, 5, 2, 16))
+    o = oracle.prefill_kv_shared(q, k, window=0, scale=0.3, rotary_dims=8, theta=1e4)
+    np.testing.assert_allclose(o[:, 0], np.repeat(k[:, 0], 4, axis=1), atol=1e-14)
+
+
+def test_kv_shared_two_token_closed_form():
+    """One rotary pair (D = 2): its frequency is 1 under any schedule, so
+    rope(x, pos) = x e^{i pos} as a complex number. Row 1 weights the rotated
+    keys r_0 = k_0, r_1 = k_1 e^{i}; scores are Re(q_1 e^{i} conj(r_j))."""
+    q1, k0, k1, s = complex(0.7, -1.1), complex(0.4, 0.9), complex(-1.3, 0.2), 0.8
+    q = np.array([[0.0, 0.0], [q1.real, q1.imag]]).reshape(1, 2, 1, 2)
+    k = np.array([[k0.real, k0.imag], [k1.real, k1.imag]]).reshape(1, 2, 1, 2)
+    o = oracle.prefill_kv_shared(q, k, window=0, scale=s, rotary_dims=2, theta=1e6)[0, 1, 0]
+    rot = cmath.exp(1j)
+    r0, r1, qr = k0, k1 * rot, q1 * rot
+    s0, s1 = s * (qr * r0.conjugate()).real, s * (qr * r1.conjugate()).real
+    e0, e1 = math.exp(s0), math.exp(s1)
+    want = (e0 * r0 + e1 * r1) / (e0 + e1)
+    assert abs(complex(o[0], o[1]) - want) < 1e-14
+
+
+def test_kv_shared_zero_scale_is_mean_of_visible_rotated_keys():
+    """Equal weights: o_i is the mean of the rotated keys i sees (window 3)."""
+    T, D, R, th = 9, 8, 4, 1e4
+    q = rng.standard_normal((1, T, 2, D))
+    k = rng.standard_normal((1, T, 1, D))
+    o = oracle.prefill_kv_shared(q, k, window=3, scale=0.0, rotary_dims=R, theta=th)
+    kr = oracle.rope(k[0], np.arange(T), R, th)[:, 0]
+    for i in range(T):
+        want = kr[max(0, i - 2):i + 1].mean(axis=0)
+        np.testing.assert_allclose(o[0, i, 0], want, atol=1e-14)
+        np.testing.assert_allclose(o[0, i, 1], want, atol=1e-14)
+
+
+def test_kv_shared_matches_torch_sdpa_with_rotated_keys_as_values():
+    B, T, Hq, Hkv, D, W, R, th = 2, 30, 8, 1, 16, 0, 4, 1e6
+    q = rng.standard_normal((B, T, Hq, D))
+    k = rng.standard_normal((B, T, Hkv, D))
+    pos = np.tile(np.arange(T), B)
+    qr = oracle.rope(q.reshape(B * T, Hq, D), pos, R, th).reshape(B, T, Hq, D)
+    kr = oracle.rope(k.reshape(B * T, Hkv, D), pos, R, th).reshape(B, T, Hkv, D)
+    o = oracle.prefill_kv_shared(q, k, window=W, scale=0.25, rotary_dims=R, theta=th)
+    np.testing.assert_allclose(o, _torch_sdpa(qr, kr, kr, W, 0.25, Hq // Hkv), atol=1e-12)
+
+
+def test_kv_shared_output_stays_in_the_keys_hull():
+    """A convex combination of rotated keys: no coordinate leaves the range the
+    visible keys span, and RoPE keeps key norms, so |o_i| <= max_j |k_j|."""
+    q = rng.standard_normal((1, 40, 4, 32)) * 3
+    k = rng.standard_normal((1, 40, 2, 32))
+    o = oracle.prefill_kv_shared(q, k, window=0, scale=1.0, rotary_dims=32, theta=1e4)
+    kmax = np.linalg.norm(k, axis=-1).max()
+    assert np.linalg.norm(o, axis=-1).max() <= kmax + 1e-12
+
+
+@pytest.mark.parametrize("W", [0, 7])
+def test_kv_shared_decode_equals_last_prefill_row(W):
+    """Decode with one cache passed as both K and V (rotated keys) equals the
+    last row of the K = V prefill over the same tokens."""
+    L, Hq, Hkv, D, R, th = 25, 8, 1, 16, 4, 1e6
+    q = rng.standard_normal((1, L + 1, Hq, D))
+    k = rng.standard_normal((1, L + 1, Hkv, D))
+    ref = oracle.prefill_kv_shared(q, k, window=W, scale=0.3, rotary_dims=R, theta=th)[0, L]
+    kr = oracle.rope(k[0], np.arange(L + 1), R, th)
+    out = oracle.decode(q[:, L], kr, kr, [0], [L + 1], window=W, scale=0.3,
+                        rotary_dims=R, theta=th)[0]
+    np.testing.assert_allclose(out, ref, rtol=1e-12, atol=1e-12)
+
+
 # -------------------------------------------------------------- decode ----
 
 @pytest.mark.parametrize("W", [0, 1, 5, 64])
