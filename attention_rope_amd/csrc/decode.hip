@@ -74,14 +74,15 @@ struct RCfg {
   static constexpr int KT = RBN * DK * 2, VT = SHARED ? 0 : RBN * DV * 2;
   static constexpr int V_OFF = SHARED ? 0 : KT;  // V rows' offset in a stage
   static constexpr int ST = KT + VT;
-  static constexpr int LDS = STAGES * ST;
+  static constexpr int RING = STAGES * ST;
+  static constexpr int RED = RW * 16 * (DV + 2) * 4;  // the wave merge reuses the ring
+  static constexpr int LDS = RING > RED ? RING : RED;
   static constexpr int K_DMA = KT / 1024, N_DMA = ST / 1024;
   static constexpr int DMA_W = N_DMA / RW;  // DMAs per wave per tile
   static_assert(KC >= 16 && VC >= 16, "row swizzle uses 16 chunk groups");
   static_assert(K_DMA % RW == 0 && N_DMA % RW == 0, "uniform DMA counts");
   static_assert(STAGES >= 2 && (AHEAD - 1) * DMA_W < 64 && LDS <= 160 * 1024,
                 "vmcnt / LDS limits");
-  static_assert(RW * 16 * (DV + 2) * 4 <= LDS, "the wave merge reuses the ring");
   static_assert(!SHARED || DK == DV, "shared K/V rows have one width");
 };
 
@@ -355,16 +356,18 @@ __global__ __launch_bounds__(DV) void decode_merge_kernel(DecodeArgs a, int ch, 
   o[d] = f32_to_bf16(num / den);
 }
 
-// Ring shapes. Separate K and V caches: 2 waves (32-row tiles), 3 stages;
-// 512-dim values (whose 32-row tiles would be 64 KB) and the local layers'
-// 256/256 heads take 1 wave with 16-row tiles, which for 256/256 lets three
-// workgroups share a CU (measured a few % faster on the local decode call).
-// One shared cache: a tile is K rows only, so 4 stages fit.
+// Ring shapes (measured on the decode workload). With one wave per SIMD a
+// workgroup's MFMA/LDS latency goes unhidden, so the heavier-per-byte cases
+// trade ring depth for more workgroups per CU:
+//  * separate 512/256 caches: 2 waves (32-row tiles), 3 stages;
+//  * local 256/256 heads: 1 wave (16-row tiles), 3 stages, three per CU;
+//  * one shared cache (K = V) and 512-dim values: 1 wave, 2 stages, so four
+//    (two) workgroups share a CU; 2 waves x 4 stages ran at 4.1 TB/s on the
+//    K = V global shape, this at 5.8.
 template <int DK, int DV, bool SHARED>
 using RingCfg = std::conditional_t<
-    SHARED, RCfg<DK, DV, 2, 4, true>,
-    std::conditional_t<(DK == 512 && DV == 512) || (DK == 256 && DV == 256),
-                       RCfg<DK, DV, 1, 3>, RCfg<DK, DV, 2, 3>>>;
+    SHARED || (DK == 512 && DV == 512), RCfg<DK, DV, 1, 2, SHARED>,
+    std::conditional_t<(DK == 256 && DV == 256), RCfg<DK, DV, 1, 3>, RCfg<DK, DV, 2, 3>>>;
 
 template <int DK, int DV, bool SHARED>
 hipError_t launch_ring(const DecodeArgs& a, const SplitPlan& pl, hipStream_t st) {

@@ -397,7 +397,11 @@ def main():
                                      "GB/s": round(rr["kv_bytes"] / (rr["kv_ms"] * 1e-3) / 1e9, 1),
                                      "ms": round(rr["kv_ms"], 4), "bytes": rr["kv_bytes"],
                                      "what": "global shape with K = V: one 512-dim cache read "
-                                             "once for both products (Dv = Dk = 512)"},
+                                             "once for both products (Dv = Dk = 512)",
+                                     "roofline": roofline(
+                                         "hbm", rr["kv_bytes"] / (rr["kv_ms"] * 1e-3) / 1e9,
+                                         PEAK_HBM_GBS, "GB/s",
+                                         _traffic("decode_ring", "kv_shared_global_decode"))},
                                  "roofline": roofline("hbm", g, PEAK_HBM_GBS, "GB/s",
                                                       _traffic("decode_ring", "global_decode"))}
             del rr
