@@ -31,8 +31,8 @@ STATUS = {0: "ok", 1: "null pointer", 2: "invalid shape or argument",
 # Every symbol the header declares (checked by the tests).
 EXPORTS = ("attn_rope_table", "attn_rope_table_bytes", "attn_prefill",
            "attn_prefill_workspace_bytes", "attn_decode",
-           "attn_decode_workspace_bytes", "prope_apply", "attn_status_string",
-           "attn_last_error")
+           "attn_decode_workspace_bytes", "attn_verify", "attn_verify_workspace_bytes",
+           "prope_apply", "attn_status_string", "attn_last_error")
 
 
 class AttnError(RuntimeError):
@@ -72,6 +72,11 @@ def load(path: str = LIB_PATH):
     lib.attn_decode.argtypes = [vp] * 6 + [i32] * 6 + [
         ctypes.c_float, _Rope, i32, vp, sz, ctypes.c_int, vp]
     lib.attn_decode.restype = ctypes.c_int
+    lib.attn_verify_workspace_bytes.argtypes = [i32] * 8
+    lib.attn_verify_workspace_bytes.restype = sz
+    lib.attn_verify.argtypes = [vp] * 6 + [i32] * 7 + [
+        ctypes.c_float, _Rope, i32, vp, sz, ctypes.c_int, vp]
+    lib.attn_verify.restype = ctypes.c_int
     lib.prope_apply.argtypes = [vp, vp, vp, i32, i32, i32, _Rope, ctypes.c_int, vp]
     lib.prope_apply.restype = ctypes.c_int
     lib.attn_status_string.argtypes = [ctypes.c_int]
@@ -189,6 +194,39 @@ def decode(q, k_cache, v_cache, row_offset, kv_len, *, window: int = 0,
     _check(lib.attn_decode(_dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
                            _dev(row_offset, "row_offset"), _dev(kv_len, "kv_len"),
                            _dev(o, "o"), B, Hq, Hkv, Dk, Dv, int(window), float(scale),
+                           _Rope(rotary_dims, theta), int(max_kv_len),
+                           ctypes.c_void_p(workspace.data_ptr()),
+                           workspace.numel() * workspace.element_size(),
+                           _dtype_code(q), _stream(q)))
+    return o
+
+
+def verify_workspace_bytes(B: int, n_q: int, Hq: int, Hkv: int, Dk: int, Dv: int,
+                           max_kv_len: int, window: int) -> int:
+    return int(load().attn_verify_workspace_bytes(B, n_q, Hq, Hkv, Dk, Dv, max_kv_len, window))
+
+
+def verify(q, k_cache, v_cache, row_offset, kv_len, *, window: int = 0,
+           scale: float | None = None, rotary_dims: int = 0, theta: float = 10000.0,
+           max_kv_len: int, out=None, workspace=None):
+    """q [B,n_q,Hq,Dk] (token j of sequence b at position kv_len[b]-n_q+j);
+    caches [rows,Hkv,Dk|Dv]; row_offset int64 [B]; kv_len int32 [B] ->
+    o [B,n_q,Hq,Dv]."""
+    lib = load()
+    B, n_q, Hq, Dk = q.shape
+    Hkv, Dv = k_cache.shape[1], v_cache.shape[2]
+    if row_offset.dtype != torch.int64 or kv_len.dtype != torch.int32:
+        raise TypeError("row_offset must be int64 and kv_len int32")
+    if scale is None:
+        scale = Dk ** -0.5
+    o = out if out is not None else torch.empty((B, n_q, Hq, Dv), dtype=q.dtype,
+                                                device=q.device)
+    need = verify_workspace_bytes(B, n_q, Hq, Hkv, Dk, Dv, max_kv_len, window)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    _check(lib.attn_verify(_dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
+                           _dev(row_offset, "row_offset"), _dev(kv_len, "kv_len"),
+                           _dev(o, "o"), B, n_q, Hq, Hkv, Dk, Dv, int(window), float(scale),
                            _Rope(rotary_dims, theta), int(max_kv_len),
                            ctypes.c_void_p(workspace.data_ptr()),
                            workspace.numel() * workspace.element_size(),

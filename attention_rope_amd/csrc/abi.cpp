@@ -67,6 +67,61 @@ bool prefill_turns_k_ahead(int32_t Dk, attn_rope_t rope, int32_t rope_mask) {
          (Dk == 128 || Dk == 256 || Dk == 512);
 }
 
+// attn_decode (n_q = 1) and attn_verify (n_q new tokens per sequence).
+attn_status_t decode_call(const char* what, const void* q, const void* k_cache,
+                          const void* v_cache, const int64_t* row_offset, const int32_t* kv_len,
+                          void* o, int32_t B, int32_t n_q, int32_t Hq, int32_t Hkv, int32_t Dk,
+                          int32_t Dv, int32_t window, float scale, attn_rope_t rope,
+                          int32_t max_kv_len, void* workspace, size_t workspace_bytes,
+                          attn_dtype_t dtype, void* stream) {
+  if (dtype != ATTN_BF16)
+    return fail(ATTN_ERR_UNSUPPORTED, "%s supports the ATTN_BF16 cache only", what);
+  if (B < 0 || B > 65535) return fail(ATTN_ERR_SHAPE, "B=%d must be in [0, 65535]", B);
+  if (n_q < 1 || n_q > 4096) return fail(ATTN_ERR_SHAPE, "n_q=%d must be in [1, 4096]", n_q);
+  if (Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0)
+    return fail(ATTN_ERR_SHAPE, "Hq=%d must be a positive multiple of Hkv=%d", Hq, Hkv);
+  if (!attn::decode_supported(Dk, Dv, Hq / Hkv))
+    return fail(ATTN_ERR_UNSUPPORTED,
+                "%s supports Dk in {128,256,512}, Dv in {128,256} (or 512 with "
+                "Dk=512), Hq/Hkv <= 16 (got Dk=%d Dv=%d G=%d)", what, Dk, Dv, Hq / Hkv);
+  if (!std::isfinite(scale) || scale < 0.f)
+    return fail(ATTN_ERR_UNSUPPORTED, "%s needs a finite scale >= 0", what);
+  attn_status_t rs = check_rope(rope, Dk);
+  if (rs != ATTN_OK) return rs;
+  if (B == 0) return ok();
+  if (max_kv_len < 1) return fail(ATTN_ERR_SHAPE, "max_kv_len=%d must be >= 1", max_kv_len);
+  if (!attn::decode_shape_fits(B, n_q, Hq, Hkv, Dk, Dv, max_kv_len, window))
+    return fail(ATTN_ERR_SHAPE, "cache too large for one call (max_kv_len=%d, Hkv=%d)",
+                max_kv_len, Hkv);
+  if (!q || !k_cache || !v_cache || !row_offset || !kv_len || !o)
+    return fail(ATTN_ERR_NULL, "q, caches, row_offset, kv_len and o must be non-NULL");
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o))
+    return fail(ATTN_ERR_SHAPE, "q, caches and o must be 16-byte aligned");
+  const size_t need =
+      attn::decode_workspace_bytes(B, n_q, Hq, Hkv, Dk, Dv, max_kv_len, window);
+  if (!workspace || workspace_bytes < need)
+    return fail(ATTN_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+                workspace ? workspace_bytes : (size_t)0);
+  if (!aligned16(workspace)) return fail(ATTN_ERR_WORKSPACE, "workspace must be 16-byte aligned");
+  const size_t no = (size_t)B * n_q * Hq * Dv * 2, nq = (size_t)B * n_q * Hq * Dk * 2;
+  if (overlap(o, no, q, nq) || overlap(workspace, need, o, no) || overlap(workspace, need, q, nq))
+    return fail(ATTN_ERR_ALIAS, "o / workspace must not overlap q or each other");
+
+  attn::DecodeArgs a{};
+  a.q = q; a.k_cache = k_cache; a.v_cache = v_cache;
+  a.row_offset = row_offset; a.kv_len = kv_len; a.o = o;
+  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.Dk = Dk; a.Dv = Dv;
+  a.window = window > 0 ? window : 0;
+  a.rot_pairs = rope.rotary_dims / 2;
+  a.theta = rope.rotary_dims > 0 ? rope.theta : 1.0;
+  a.scale = scale;
+  a.max_kv_len = max_kv_len;
+  a.workspace = workspace;
+  a.n_q = n_q;
+  return launch_status(attn::launch_decode(a, reinterpret_cast<hipStream_t>(stream)), what);
+}
+
+
 }  // namespace
 
 extern "C" {
@@ -191,7 +246,12 @@ attn_status_t attn_prefill(const void* q, const void* k, const void* v, void* o,
 
 size_t attn_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t Dv,
                                    int32_t max_kv_len, int32_t window) {
-  return attn::decode_workspace_bytes(B, Hq, Hkv, Dv, max_kv_len, window);
+  return attn::decode_workspace_bytes(B, 1, Hq, Hkv, 0, Dv, max_kv_len, window);
+}
+
+size_t attn_verify_workspace_bytes(int32_t B, int32_t n_q, int32_t Hq, int32_t Hkv, int32_t Dk,
+                                   int32_t Dv, int32_t max_kv_len, int32_t window) {
+  return attn::decode_workspace_bytes(B, n_q, Hq, Hkv, Dk, Dv, max_kv_len, window);
 }
 
 attn_status_t attn_decode(const void* q, const void* k_cache, const void* v_cache,
@@ -200,50 +260,20 @@ attn_status_t attn_decode(const void* q, const void* k_cache, const void* v_cach
                           int32_t window, float scale, attn_rope_t rope,
                           int32_t max_kv_len, void* workspace, size_t workspace_bytes,
                           attn_dtype_t dtype, void* stream) {
-  if (dtype != ATTN_BF16)
-    return fail(ATTN_ERR_UNSUPPORTED, "decode supports the ATTN_BF16 cache only");
-  if (B < 0 || B > 65535) return fail(ATTN_ERR_SHAPE, "B=%d must be in [0, 65535]", B);
-  if (Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0)
-    return fail(ATTN_ERR_SHAPE, "Hq=%d must be a positive multiple of Hkv=%d", Hq, Hkv);
-  if (!attn::decode_supported(Dk, Dv, Hq / Hkv))
-    return fail(ATTN_ERR_UNSUPPORTED,
-                "decode supports Dk in {128,256,512}, Dv in {128,256} (or 512 with "
-                "Dk=512), Hq/Hkv <= 16 (got Dk=%d Dv=%d G=%d)", Dk, Dv, Hq / Hkv);
-  if (!std::isfinite(scale) || scale < 0.f)
-    return fail(ATTN_ERR_UNSUPPORTED, "decode needs a finite scale >= 0");
-  attn_status_t rs = check_rope(rope, Dk);
-  if (rs != ATTN_OK) return rs;
-  if (B == 0) return ok();
-  if (max_kv_len < 1) return fail(ATTN_ERR_SHAPE, "max_kv_len=%d must be >= 1", max_kv_len);
-  if (!attn::decode_shape_fits(B, Hkv, Dk, Dv, max_kv_len, window))
-    return fail(ATTN_ERR_SHAPE, "cache too large for one call (max_kv_len=%d, Hkv=%d)",
-                max_kv_len, Hkv);
-  if (!q || !k_cache || !v_cache || !row_offset || !kv_len || !o)
-    return fail(ATTN_ERR_NULL, "q, caches, row_offset, kv_len and o must be non-NULL");
-  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o))
-    return fail(ATTN_ERR_SHAPE, "q, caches and o must be 16-byte aligned");
-  const size_t need = attn::decode_workspace_bytes(B, Hq, Hkv, Dv, max_kv_len, window);
-  if (!workspace || workspace_bytes < need)
-    return fail(ATTN_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
-                workspace ? workspace_bytes : (size_t)0);
-  if (!aligned16(workspace)) return fail(ATTN_ERR_WORKSPACE, "workspace must be 16-byte aligned");
-  const size_t no = (size_t)B * Hq * Dv * 2;
-  if (overlap(o, no, q, (size_t)B * Hq * Dk * 2) || overlap(workspace, need, o, no) ||
-      overlap(workspace, need, q, (size_t)B * Hq * Dk * 2))
-    return fail(ATTN_ERR_ALIAS, "o / workspace must not overlap q or each other");
+  return decode_call("decode", q, k_cache, v_cache, row_offset, kv_len, o, B, 1, Hq, Hkv, Dk,
+                     Dv, window, scale, rope, max_kv_len, workspace, workspace_bytes, dtype,
+                     stream);
+}
 
-  attn::DecodeArgs a{};
-  a.q = q; a.k_cache = k_cache; a.v_cache = v_cache;
-  a.row_offset = row_offset; a.kv_len = kv_len; a.o = o;
-  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.Dk = Dk; a.Dv = Dv;
-  a.window = window > 0 ? window : 0;
-  a.rot_pairs = rope.rotary_dims / 2;
-  a.theta = rope.rotary_dims > 0 ? rope.theta : 1.0;
-  a.scale = scale;
-  a.max_kv_len = max_kv_len;
-  a.workspace = workspace;
-  return launch_status(attn::launch_decode(a, reinterpret_cast<hipStream_t>(stream)),
-                       "decode");
+attn_status_t attn_verify(const void* q, const void* k_cache, const void* v_cache,
+                          const int64_t* row_offset, const int32_t* kv_len, void* o,
+                          int32_t B, int32_t n_q, int32_t Hq, int32_t Hkv, int32_t Dk,
+                          int32_t Dv, int32_t window, float scale, attn_rope_t rope,
+                          int32_t max_kv_len, void* workspace, size_t workspace_bytes,
+                          attn_dtype_t dtype, void* stream) {
+  return decode_call("verify", q, k_cache, v_cache, row_offset, kv_len, o, B, n_q, Hq, Hkv,
+                     Dk, Dv, window, scale, rope, max_kv_len, workspace, workspace_bytes,
+                     dtype, stream);
 }
 
 attn_status_t prope_apply(const void* x, void* y, const int32_t* positions, int32_t N,

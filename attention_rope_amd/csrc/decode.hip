@@ -22,6 +22,7 @@
 //  * With several chunks per sequence each writes an online-softmax partial
 //    (max, sum, acc) and a second kernel merges them; with one chunk the
 //    streaming kernel normalises and writes o itself.
+#include <algorithm>
 #include <type_traits>
 
 #include "attn_common.h"
@@ -43,12 +44,15 @@ struct SplitPlan {
   int ch, ns;  // rows per chunk, chunks per sequence (grid extent)
 };
 
-inline SplitPlan decode_plan(int B, int Hkv, int max_kv_len, int window) {
-  const int range = (window > 0 && window < max_kv_len) ? window : max_kv_len;
+// groups: workgroups per (sequence, chunk); n_q new tokens per sequence widen
+// a window's range by n_q - 1 rows.
+inline SplitPlan decode_plan(int B, int groups, int max_kv_len, int window, int n_q = 1) {
+  const int64_t wr = (int64_t)window + n_q - 1;
+  const int range = (window > 0 && wr < max_kv_len) ? (int)wr : max_kv_len;
   int ch = (window > 0) ? range : kMaxChunk;
   ch = ch > kMaxChunk ? kMaxChunk : (ch < 1 ? 1 : ch);
   auto splits = [&](int c) { return (int)(((int64_t)range + c - 1) / c); };
-  while (ch > kMinChunk && (int64_t)B * Hkv * splits(ch) < kMinGroups) ch = (ch + 1) / 2;
+  while (ch > kMinChunk && (int64_t)B * groups * splits(ch) < kMinGroups) ch = (ch + 1) / 2;
   return {ch, splits(ch)};
 }
 
@@ -92,24 +96,37 @@ __global__ __launch_bounds__(C::RW * 64, 1) void decode_ring_kernel(DecodeArgs a
   __shared__ __attribute__((aligned(1024))) unsigned char lds[C::LDS];
 
   // KV heads vary fastest in the grid, so the workgroups that share a chunk's
-  // cache rows run side by side.
-  const int kvh = blockIdx.x, split = blockIdx.y, b = blockIdx.z;
+  // cache rows run side by side. The MFMA's 16 columns are (token, head)
+  // pairs: column c of group cg is q = 16 cg + c, token q / G, head q % G.
+  const int cg = blockIdx.x / a.Hkv, kvh = blockIdx.x - cg * a.Hkv;
+  const int split = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 15, g = lane >> 4;
-  const int G = a.Hq / a.Hkv;
+  const int G = a.Hq / a.Hkv, n_q = a.n_q, ncol = n_q * G;
+  auto col_ok = [&](int c) { return 16 * cg + c < ncol; };
+  auto col_tok = [&](int c) { return (16 * cg + c) / G; };
+  auto col_row = [&](int c) -> int64_t {  // row of q and o: [B, n_q, Hq]
+    const int q = 16 * cg + c, j = q / G;
+    return ((int64_t)b * n_q + j) * a.Hq + kvh * G + (q - j * G);
+  };
 
   const int kv_len = a.kv_len[b];
-  if (kv_len <= 0 || kv_len > a.max_kv_len) {
-    // No rows: o = 0; kv_len past max_kv_len: poisoned (NaN). With several
-    // chunks the merge writes these rows.
+  if (kv_len <= 0 || kv_len > a.max_kv_len || kv_len < n_q) {
+    // No rows: o = 0; kv_len past max_kv_len or short of the new tokens:
+    // poisoned (NaN). With several chunks the merge writes these rows.
     if (n_split == 1) {
-      uint16_t* o = (uint16_t*)a.o + ((int64_t)b * a.Hq + kvh * G) * DV;
-      for (int idx = tid; idx < G * DV; idx += kRW * 64) o[idx] = kv_len == 0 ? 0 : 0x7fc0;
+      for (int idx = tid; idx < 16 * DV; idx += kRW * 64) {
+        const int c = idx / DV;
+        if (col_ok(c))
+          ((uint16_t*)a.o)[col_row(c) * DV + idx % DV] = kv_len == 0 ? 0 : 0x7fc0;
+      }
     }
     return;
   }
-  const int lo = (a.window > 0) ? max(0, kv_len - a.window) : 0;
+  // Token j (position kv_len - n_q + j) sees rows [lo_j, pos_j]; the chunks
+  // cover [lo_0, kv_len).
+  const int lo = (a.window > 0) ? max(0, kv_len - n_q + 1 - a.window) : 0;
   const int c0 = lo + split * ch;
   if (c0 >= kv_len) return;
   const int c1 = min(kv_len, c0 + ch);
@@ -162,7 +179,16 @@ __global__ __launch_bounds__(C::RW * 64, 1) void decode_ring_kernel(DecodeArgs a
   // fp64) into a small LDS table; every lane then reads the pairs it holds.
   __shared__ float2 cs_tab[kRW][DK / 2];
   bf16x8 qf[DK / 32];
-  {
+  if (a.q_rotated) {
+    const bool hv = col_ok(col);
+    const uint16_t* qrow = (const uint16_t*)a.q + col_row(hv ? col : 0) * DK;
+#pragma unroll
+    for (int s = 0; s < DK / 32; ++s) {
+      u32x4 w = *(const u32x4*)(qrow + 32 * s + 8 * g);
+      if (!hv) w = u32x4{0, 0, 0, 0};
+      qf[s] = __builtin_bit_cast(bf16x8, w);
+    }
+  } else {  // one token per sequence (n_q = 1), turned here at kv_len - 1
     const int qpos = kv_len - 1;
     const double l2t = log2(a.theta);
     for (int p = lane; p < a.rot_pairs; p += 64) {
@@ -173,9 +199,8 @@ __global__ __launch_bounds__(C::RW * 64, 1) void decode_ring_kernel(DecodeArgs a
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    const bool hv = col < G;
-    const int head = kvh * G + (hv ? col : 0);
-    const uint16_t* qrow = (const uint16_t*)a.q + ((int64_t)b * a.Hq + head) * DK;
+    const bool hv = col_ok(col);
+    const uint16_t* qrow = (const uint16_t*)a.q + col_row(hv ? col : 0) * DK;
 #pragma unroll
     for (int s = 0; s < DK / 32; ++s) {
       const int d0 = 32 * s + 8 * g;
@@ -196,6 +221,14 @@ __global__ __launch_bounds__(C::RW * 64, 1) void decode_ring_kernel(DecodeArgs a
   }
   wait_vm<(C::AHEAD - 1) * C::DMA_W>();
   lds_barrier();
+
+  // Visible keys of this lane's column, and the tile-uniform bounds inside
+  // which no column masks anything.
+  const int col_pos = kv_len - n_q + (col_ok(col) ? col_tok(col) : 0);
+  const int col_lo = (a.window > 0) ? max(0, col_pos + 1 - a.window) : 0;
+  const int col_hi = min(c1, col_pos + 1);
+  const int mask_lo = (a.window > 0) ? max(0, kv_len - a.window) : 0;
+  const int mask_hi = min(c1, kv_len - n_q + 1);
 
   // scores to log2 units; kept > 0 so a masked -inf never meets a zero factor
   const float c2 = fmaxf(a.scale * kLog2e, 1e-30f);
@@ -233,9 +266,11 @@ __global__ __launch_bounds__(C::RW * 64, 1) void decode_ring_kernel(DecodeArgs a
       s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, qf[k], s, 0, 0, 0);
     }
     const int key0 = c0 + t * kRBN + 16 * wave + 4 * g;
-    if (c0 + (t + 1) * kRBN > c1) {  // last tile of the chunk: mask rows >= c1
+    // Edge tiles only: the chunk's end, the new tokens' own rows (each sees
+    // the rows up to its own) and a window's start (later tokens start later).
+    if (c0 + t * kRBN < mask_lo || c0 + (t + 1) * kRBN > mask_hi) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) s[i] = (key0 + i < c1) ? s[i] : -INFINITY;
+      for (int i = 0; i < 4; ++i) s[i] = (key0 + i >= col_lo && key0 + i < col_hi) ? s[i] : -INFINITY;
     }
     float mx = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
     mx = xor32_16_max(mx);
@@ -289,9 +324,9 @@ __global__ __launch_bounds__(C::RW * 64, 1) void decode_ring_kernel(DecodeArgs a
   }
   __syncthreads();
   if (n_split == 1) {  // one chunk per sequence: normalise and write o here
-    uint16_t* o = (uint16_t*)a.o + ((int64_t)b * a.Hq + kvh * G) * DV;
-    for (int idx = tid; idx < G * DV; idx += kRW * 64) {
+    for (int idx = tid; idx < 16 * DV; idx += kRW * 64) {
       const int h = idx / DV, d = idx % DV;
+      if (!col_ok(h)) continue;
       float M = -INFINITY;
 #pragma unroll
       for (int w = 0; w < kRW; ++w) M = fmaxf(M, red[(w * 16 + h) * RS + DV]);
@@ -302,13 +337,14 @@ __global__ __launch_bounds__(C::RW * 64, 1) void decode_ring_kernel(DecodeArgs a
         num += f * red[(w * 16 + h) * RS + d];
         den += f * red[(w * 16 + h) * RS + DV + 1];
       }
-      o[idx] = f32_to_bf16(num / den);
+      ((uint16_t*)a.o)[col_row(h) * DV + d] = f32_to_bf16(num / den);
     }
     return;
   }
   float* part = reinterpret_cast<float*>(a.workspace);
-  for (int idx = tid; idx < G * (DV + 2); idx += kRW * 64) {
+  for (int idx = tid; idx < 16 * (DV + 2); idx += kRW * 64) {
     const int h = idx / (DV + 2), d = idx % (DV + 2);
+    if (!col_ok(h)) continue;
     float M = -INFINITY;
 #pragma unroll
     for (int w = 0; w < kRW; ++w) M = fmaxf(M, red[(w * 16 + h) * RS + DV]);
@@ -322,26 +358,28 @@ __global__ __launch_bounds__(C::RW * 64, 1) void decode_ring_kernel(DecodeArgs a
         val += f * red[(w * 16 + h) * RS + d];
       }
     }
-    const int64_t slot = ((int64_t)b * a.Hq + kvh * G + h) * n_split + split;
+    const int64_t slot = col_row(h) * n_split + split;
     part[slot * (DV + 2) + d] = val;  // d == DV+1 sums the l's by the same rule
   }
 }
 
-// Merge the splits of one (sequence, query head): O = sum_c f_c acc_c / sum_c f_c l_c.
+// Merge the splits of one (sequence, token, query head):
+// O = sum_c f_c acc_c / sum_c f_c l_c. A chunk with no row a token sees holds
+// m = -inf and adds nothing.
 template <int DV>
 __global__ __launch_bounds__(DV) void decode_merge_kernel(DecodeArgs a, int ch, int n_split) {
-  const int bh = blockIdx.x;
-  const int b = bh / a.Hq;
+  const int bh = blockIdx.x;  // (b * n_q + j) * Hq + h
+  const int b = bh / (a.n_q * a.Hq);
   const int kv_len = a.kv_len[b];
   uint16_t* o = (uint16_t*)a.o + (int64_t)bh * DV;
   const int d = threadIdx.x;
   if (d >= DV) return;
-  if (kv_len <= 0 || kv_len > a.max_kv_len) {
+  if (kv_len <= 0 || kv_len > a.max_kv_len || kv_len < a.n_q) {
     // kv_len == 0: no rows, o = 0. Out of range: poison the row (NaN).
     o[d] = (kv_len == 0) ? 0 : 0x7fc0;
     return;
   }
-  const int lo = (a.window > 0) ? max(0, kv_len - a.window) : 0;
+  const int lo = (a.window > 0) ? max(0, kv_len - a.n_q + 1 - a.window) : 0;
   const int n = (kv_len - lo + ch - 1) / ch;
   const float* part = reinterpret_cast<const float*>(a.workspace) + (int64_t)bh * n_split * (DV + 2);
   float M = -INFINITY;
@@ -370,46 +408,84 @@ using RingCfg = std::conditional_t<
     std::conditional_t<(DK == 256 && DV == 256), RCfg<DK, DV, 1, 3>, RCfg<DK, DV, 2, 3>>>;
 
 template <int DK, int DV, bool SHARED>
-hipError_t launch_ring(const DecodeArgs& a, const SplitPlan& pl, hipStream_t st) {
+hipError_t launch_ring(const DecodeArgs& a, const SplitPlan& pl, int ncg, hipStream_t st) {
   using C = RingCfg<DK, DV, SHARED>;
   // Chunk-relative 32-bit buffer offsets: ch rows plus the read-ahead tiles.
   const int64_t row = (int64_t)a.Hkv * (DK > DV ? DK : DV) * 2;
   static_assert((C::STAGES + 1) * C::RBN <= 192, "read-ahead bound of decode_shape_fits");
   if (((int64_t)pl.ch + (C::STAGES + 1) * C::RBN) * row >= ((int64_t)1 << 31))
     return hipErrorInvalidValue;
-  hipLaunchKernelGGL((decode_ring_kernel<C, DK, DV>), dim3(a.Hkv, pl.ns, a.B),
+  hipLaunchKernelGGL((decode_ring_kernel<C, DK, DV>), dim3(a.Hkv * ncg, pl.ns, a.B),
                      dim3(C::RW * 64), 0, st, a, pl.ch, pl.ns);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || pl.ns == 1) return e;  // one chunk: the ring kernel wrote o
-  hipLaunchKernelGGL((decode_merge_kernel<DV>), dim3(a.B * a.Hq), dim3(DV), 0, st, a, pl.ch,
-                     pl.ns);
+  hipLaunchKernelGGL((decode_merge_kernel<DV>), dim3(a.B * a.n_q * a.Hq), dim3(DV), 0, st, a,
+                     pl.ch, pl.ns);
   return hipGetLastError();
 }
 
+// 16-column groups of (token, head) pairs per KV head.
+inline int column_groups(int n_q, int G) { return (n_q * G + 15) / 16; }
+
 template <int DK, int DV>
 hipError_t launch_dk_dv(const DecodeArgs& a, hipStream_t st) {
-  const SplitPlan pl = decode_plan(a.B, a.Hkv, a.max_kv_len, a.window);
+  const int ncg = column_groups(a.n_q, a.Hq / a.Hkv);
+  const SplitPlan pl = decode_plan(a.B, a.Hkv * ncg, a.max_kv_len, a.window, a.n_q);
   if (pl.ns > 65535) return hipErrorInvalidValue;
   if constexpr (DK == DV) {
-    if (a.k_cache == a.v_cache) return launch_ring<DK, DV, true>(a, pl, st);
+    if (a.k_cache == a.v_cache) return launch_ring<DK, DV, true>(a, pl, ncg, st);
   }
-  return launch_ring<DK, DV, false>(a, pl, st);
+  return launch_ring<DK, DV, false>(a, pl, ncg, st);
+}
+
+// Several new tokens: turn every query once at its own position
+// (kv_len - n_q + j) into the workspace, in the arithmetic of the one-token
+// path (fp64 angle, fp32 rotation of the bf16 pair, bf16 result).
+__global__ __launch_bounds__(256) void verify_rotate_q_kernel(DecodeArgs a, uint32_t* out) {
+  const int P = a.Dk / 2;
+  const int64_t total = (int64_t)a.B * a.n_q * a.Hq * P;
+  const double l2t = log2(a.theta);
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total;
+       i += (int64_t)gridDim.x * 256) {
+    const int p = (int)(i % P);
+    const int64_t bj = i / P / a.Hq;  // b * n_q + j
+    const int b = (int)(bj / a.n_q), j = (int)(bj % a.n_q);
+    uint32_t w = reinterpret_cast<const uint32_t*>(a.q)[i];
+    if (p < a.rot_pairs) {
+      const int pos = max(0, a.kv_len[b] - a.n_q + j);
+      float c, sn;
+      rope_cos_sin(pos, rope_freq(p, a.Dk, l2t), &c, &sn);
+      const float x0 = bf16_lo(w), x1 = bf16_hi(w);
+      w = pack_bf16x2(x0 * c - x1 * sn, x0 * sn + x1 * c);
+    }
+    out[i] = w;
+  }
+}
+
+inline size_t rotated_q_bytes(int B, int n_q, int Hq, int Dk) {
+  if (n_q <= 1) return 0;
+  return ((size_t)B * n_q * Hq * Dk * 2 + 255) & ~(size_t)255;
 }
 
 }  // namespace
 
-size_t decode_workspace_bytes(int B, int Hq, int Hkv, int Dv, int max_kv_len, int window) {
-  if (B <= 0 || Hq <= 0 || Hkv <= 0 || Dv <= 0 || max_kv_len <= 0) return 0;
-  const int ns = decode_plan(B, Hkv, max_kv_len, window).ns;
-  return (size_t)B * Hq * ns * (Dv + 2) * sizeof(float);
+size_t decode_workspace_bytes(int B, int n_q, int Hq, int Hkv, int Dk, int Dv, int max_kv_len,
+                              int window) {
+  if (B <= 0 || n_q <= 0 || Hq <= 0 || Hkv <= 0 || Dv <= 0 || max_kv_len <= 0) return 0;
+  const int ncg = column_groups(n_q, Hq / Hkv);
+  const int ns = decode_plan(B, Hkv * ncg, max_kv_len, window, n_q).ns;
+  return rotated_q_bytes(B, n_q, Hq, Dk) + (size_t)B * n_q * Hq * ns * (Dv + 2) * sizeof(float);
 }
 
-bool decode_shape_fits(int B, int Hkv, int Dk, int Dv, int max_kv_len, int window) {
-  const SplitPlan pl = decode_plan(B, Hkv, max_kv_len, window);
+bool decode_shape_fits(int B, int n_q, int Hq, int Hkv, int Dk, int Dv, int max_kv_len,
+                       int window) {
+  const int ncg = column_groups(n_q, Hq / Hkv);
+  const SplitPlan pl = decode_plan(B, Hkv * ncg, max_kv_len, window, n_q);
   // 32-bit chunk-relative offsets (chunk plus the deepest read-ahead) and the
-  // grid's y extent.
+  // grid's x and y extents.
   const int64_t row = (int64_t)Hkv * (Dk > Dv ? Dk : Dv) * 2;
-  return pl.ns <= 65535 && ((int64_t)pl.ch + 192) * row < ((int64_t)1 << 31);
+  return pl.ns <= 65535 && (int64_t)Hkv * ncg < ((int64_t)1 << 31) &&
+         ((int64_t)pl.ch + 192) * row < ((int64_t)1 << 31);
 }
 
 bool decode_supported(int Dk, int Dv, int G) {
@@ -418,8 +494,20 @@ bool decode_supported(int Dk, int Dv, int G) {
   return kdim && vdim && G >= 1 && G <= 16;
 }
 
-hipError_t launch_decode(const DecodeArgs& a, hipStream_t st) {
-  if (a.B == 0) return hipSuccess;
+hipError_t launch_decode(const DecodeArgs& a0, hipStream_t st) {
+  if (a0.B == 0) return hipSuccess;
+  DecodeArgs a = a0;
+  if (a0.n_q > 1) {
+    uint32_t* qr = static_cast<uint32_t*>(a0.workspace);
+    const int64_t total = (int64_t)a0.B * a0.n_q * a0.Hq * (a0.Dk / 2);
+    const int blocks = (int)std::min<int64_t>((total + 255) / 256, 8192);
+    hipLaunchKernelGGL(verify_rotate_q_kernel, dim3(blocks), dim3(256), 0, st, a0, qr);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    a.q = qr;
+    a.q_rotated = 1;
+    a.workspace = static_cast<char*>(a0.workspace) + rotated_q_bytes(a0.B, a0.n_q, a0.Hq, a0.Dk);
+  }
 #define ATTN_DEC(DK, DV) \
   if (a.Dk == DK && a.Dv == DV) return launch_dk_dv<DK, DV>(a, st);
   ATTN_DEC(512, 256)

@@ -59,11 +59,20 @@ struct DecodeArgs {
   float scale;
   int max_kv_len;
   void* workspace;
+  // New tokens per sequence (1: decode). Token j of sequence b sits at
+  // position kv_len[b] - n_q + j and attends the rows up to its own; q and o
+  // are [B, n_q, Hq, D]. With q_rotated the queries are already turned.
+  int n_q = 1;
+  int q_rotated = 0;
 };
 
-size_t decode_workspace_bytes(int B, int Hq, int Hkv, int Dv, int max_kv_len, int window);
+// Workspace of a decode (n_q = 1) or verify (n_q > 1) call: the split-K
+// partials, and for n_q > 1 the turned queries ahead of them.
+size_t decode_workspace_bytes(int B, int n_q, int Hq, int Hkv, int Dk, int Dv, int max_kv_len,
+                              int window);
 bool decode_supported(int Dk, int Dv, int G);
-bool decode_shape_fits(int B, int Hkv, int Dk, int Dv, int max_kv_len, int window);
+bool decode_shape_fits(int B, int n_q, int Hq, int Hkv, int Dk, int Dv, int max_kv_len,
+                       int window);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t st);
 
 }  // namespace attn

@@ -213,9 +213,38 @@ def bench_decode(ar, torch, inputs, cfg, steps, warmup):
         tk.mark(i, 1)
     torch.cuda.synchronize()
     kv_ms = sum(tk.ms(i, 0, 1) for i in range(steps)) / steps
+
+    # Verify (speculative decoding): the global call with its last 2 cache
+    # rows taken as 2 new tokens per sequence (8 heads x 2 tokens fill the 16
+    # MFMA columns, so each row is still read once per KV head).
+    n_q = 2
+    q_v = inputs.normal((d.n_seq, n_q, d.Hq, d.Dk), seed, 90, d.dtype, "cuda")
+    o_v = torch.empty((d.n_seq, n_q, d.Hq, d.Dv), dtype=d.dtype, device="cuda")
+    ws_v = torch.empty(ar.verify_workspace_bytes(d.n_seq, n_q, d.Hq, d.Hkv, d.Dk, d.Dv,
+                                                 g["maxl"], d.window),
+                       dtype=torch.uint8, device="cuda")
+    v_bytes = (sum(vis) * d.Hkv * (d.Dk + d.Dv) * 2
+               + d.n_seq * n_q * d.Hq * (d.Dk + d.Dv) * 2)
+
+    def run_v():
+        ar.verify(q_v, g["kc"], g["vc"], g["off"], g["kvl"], window=d.window, scale=d.scale,
+                  rotary_dims=d.rotary_dims, theta=d.theta, max_kv_len=g["maxl"], out=o_v,
+                  workspace=ws_v)
+
+    for _ in range(warmup):
+        run_v()
+    tv = Timer(torch, steps)
+    for i in range(steps):
+        flush.fill_(i & 0xff)
+        tv.mark(i, 0)
+        run_v()
+        tv.mark(i, 1)
+    torch.cuda.synchronize()
+    v_ms = sum(tv.ms(i, 0, 1) for i in range(steps)) / steps
     return dict(bytes=total_bytes, g_ms=g_ms, l_ms=l_ms, step_ms=g_ms + l_ms,
                 g_bytes=calls[0]["bytes"], l_bytes=calls[1]["bytes"], calls=calls,
-                kv_ms=kv_ms, kv_bytes=kv_bytes, kv_out=o_kv)
+                kv_ms=kv_ms, kv_bytes=kv_bytes, kv_out=o_kv, v_ms=v_ms, v_bytes=v_bytes,
+                v_nq=n_q)
 
 
 def bench_stack(ar, torch, inputs, cfg, steps, warmup):
@@ -402,6 +431,11 @@ def main():
                                          "hbm", rr["kv_bytes"] / (rr["kv_ms"] * 1e-3) / 1e9,
                                          PEAK_HBM_GBS, "GB/s",
                                          _traffic("decode_ring", "kv_shared_global_decode"))},
+                                 "verify_call": {
+                                     "GB/s": round(rr["v_bytes"] / (rr["v_ms"] * 1e-3) / 1e9, 1),
+                                     "ms": round(rr["v_ms"], 4), "bytes": rr["v_bytes"],
+                                     "what": f"global call with {rr['v_nq']} new tokens per "
+                                             "sequence (speculative-decoding verify)"},
                                  "roofline": roofline("hbm", g, PEAK_HBM_GBS, "GB/s",
                                                       _traffic("decode_ring", "global_decode"))}
             del rr

@@ -156,6 +156,37 @@ attn_status_t attn_decode(const void *q, const void *k_cache, const void *v_cach
                           void *stream);
 
 /*
+ * Verify (speculative decoding) / append attention: n_q new tokens per
+ * sequence at once, as when a target model checks a drafter's proposals in one
+ * pass ("Gemma 4: End-to-End Architecture Walkthrough", Phase 4; "Gemma 4
+ * Technical Report" reader, "Speculative Decoding and Infrastructure").
+ *   Sequence b's last n_q cache rows are the new tokens (the caller appends
+ *   them, rotated keys, before the call). Token j sits at position
+ *   p_j = kv_len[b] - n_q + j and attends exactly what a one-token decode at
+ *   kv_len = p_j + 1 would: cache rows up to its own (causal within the
+ *   draft), or the last `window` of those.
+ *   q [B, n_q, Hq, Dk] unrotated (token j is turned at p_j);
+ *   o [B, n_q, Hq, Dv]. Caches, row_offset, window, rope, scale, K = V and
+ *   the supported shapes as for attn_decode; n_q in [1, 4096].
+ *   kv_len[b] == 0 gives o[b] = 0; 0 < kv_len[b] < n_q (tokens without
+ *   their rows) or kv_len[b] > max_kv_len poison o[b] with NaN.
+ *   n_q * (Hq / Hkv) <= 16 reads each cache row once per KV head; more
+ *   (token, head) pairs re-read it once per 16.
+ * Workspace: attn_verify_workspace_bytes() bytes (the turned queries and the
+ *   split-K partials); contents are scratch.
+ */
+size_t attn_verify_workspace_bytes(int32_t B, int32_t n_q, int32_t Hq, int32_t Hkv,
+                                   int32_t Dk, int32_t Dv, int32_t max_kv_len,
+                                   int32_t window);
+
+attn_status_t attn_verify(const void *q, const void *k_cache, const void *v_cache,
+                          const int64_t *row_offset, const int32_t *kv_len,
+                          void *o, int32_t B, int32_t n_q, int32_t Hq, int32_t Hkv,
+                          int32_t Dk, int32_t Dv, int32_t window, float scale,
+                          attn_rope_t rope, int32_t max_kv_len, void *workspace,
+                          size_t workspace_bytes, attn_dtype_t dtype, void *stream);
+
+/*
  * (p-)RoPE on its own: y[n, h, :] = rope(x[n, h, :], positions[n]).
  *   x, y [N, H, D]; positions: device int32 [N], each >= 0.
  *   y may equal x (in place: dims >= rotary_dims are then not touched);

@@ -202,3 +202,41 @@ def decode(q, k_cache, v_cache, row_offset, kv_len, *, window: int, scale: float
     Hq = q.shape[1]
     Dv = v_cache.shape[2]
     return np.stack(outs) if outs else np.zeros((0, Hq, Dv))
+
+
+def verify(q, k_cache, v_cache, row_offset, kv_len, *, window: int, scale: float,
+           rotary_dims: int = 0, theta: float = 10000.0, seqs=None,
+           nthreads: int | None = None) -> np.ndarray:
+    """Several new tokens per sequence checked in one pass (speculative
+    decoding's verify step: "Gemma 4: End-to-End Architecture Walkthrough",
+    Phase 4; "Gemma 4 Technical Report" reader, "Speculative Decoding and
+    Infrastructure"). q [B, n_q, Hq, Dk]; sequence b's last n_q cache rows are
+    the new tokens, token j at position kv_len[b] - n_q + j. By definition
+    each token is a one-token decode over the cache prefix that ends at its
+    own row (causal within the draft). Returns [len(seqs), n_q, Hq, Dv].
+    """
+    kv_len = [int(x) for x in (kv_len.tolist() if hasattr(kv_len, "tolist") else kv_len)]
+    row_offset = [int(x) for x in (row_offset.tolist() if hasattr(row_offset, "tolist") else row_offset)]
+    n_q, Hq = q.shape[1], q.shape[2]
+    Dv = v_cache.shape[2]
+    if seqs is None:
+        seqs = range(len(kv_len))
+    out = []
+    for b in seqs:
+        n = kv_len[b]
+        if n == 0:
+            out.append(np.zeros((n_q, Hq, Dv)))
+            continue
+        if n < n_q:
+            raise RuntimeError("verify: kv_len smaller than the number of new tokens")
+        rows = []
+        for j in range(n_q):
+            m = n - n_q + j + 1  # the prefix that token j sees ends at its own row
+            lo = max(0, m - window) if window > 0 else 0
+            off = row_offset[b]
+            rows.append(decode_one(q[b, j], k_cache[off + lo: off + m],
+                                   v_cache[off + lo: off + m], kv_len=m, row0=lo,
+                                   window=window, scale=scale, rotary_dims=rotary_dims,
+                                   theta=theta, nthreads=nthreads))
+        out.append(np.stack(rows))
+    return np.stack(out) if out else np.zeros((0, n_q, Hq, Dv))

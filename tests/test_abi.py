@@ -166,3 +166,29 @@ def test_prope_validation(lib):
     assert f(y=P(0x10000 + 64)) == 6                 # partial overlap
     assert f(dtype=5) == 3
     assert f(N=0) == 0
+
+
+def test_verify_validation_and_workspace(lib):
+    ws = lib.attn_verify_workspace_bytes
+    q_region = 64 * 2 * 32 * 512 * 2
+    assert ws(64, 2, 32, 4, 512, 256, 131073, 0) == q_region + 64 * 2 * 32 * 33 * 258 * 4
+    # 20 tokens x 1 head: two 16-column groups; 256-row chunks over 300 rows
+    assert ws(1, 20, 2, 2, 128, 128, 300, 0) == 10240 + 1 * 20 * 2 * 2 * 130 * 4
+    assert ws(0, 2, 32, 4, 512, 256, 10, 0) == 0
+
+    def verify(**kw):
+        a = dict(q=FAKE, k=FAKE, v=FAKE, off=FAKE, kvl=FAKE, o=FAKE2, B=2, n_q=3, Hq=8, Hkv=1,
+                 Dk=128, Dv=128, window=0, scale=0.1, rope=R(32, 1e6), max_kv_len=100,
+                 ws=P(0x40000000), ws_bytes=1 << 30, dtype=ar.ATTN_BF16, stream=None)
+        a.update(kw)
+        return lib.attn_verify(a["q"], a["k"], a["v"], a["off"], a["kvl"], a["o"], a["B"],
+                               a["n_q"], a["Hq"], a["Hkv"], a["Dk"], a["Dv"], a["window"],
+                               a["scale"], a["rope"], a["max_kv_len"], a["ws"], a["ws_bytes"],
+                               a["dtype"], a["stream"])
+    assert verify(n_q=0) == 2
+    assert verify(n_q=5000) == 2
+    assert verify(Dk=64) == 3
+    assert verify(kvl=None) == 1
+    assert verify(ws_bytes=16) == 4
+    assert verify(dtype=ar.ATTN_F32) == 3
+    assert verify(B=0, q=None) == 0

@@ -60,10 +60,11 @@ def test_config3_global_prefill():
     torch.cuda.empty_cache()
 
 
-@pytest.mark.parametrize("kind", ["glob", "loc", "glob_kv"])
+@pytest.mark.parametrize("kind", ["glob", "loc", "glob_kv", "glob_verify"])
 def test_config4_decode(kind):
     """glob_kv: the global call with keys as values (its key cache passed as
-    both caches, Dv = Dk = 512), as the benchmark times it."""
+    both caches, Dv = Dk = 512); glob_verify: the global call with its last 2
+    rows as 2 new tokens per sequence; both as the benchmark times them."""
     cfg = inputs.CONFIGS[4]
     d = cfg["cases"]["loc" if kind == "loc" else "glob"]
     seed = cfg["seed"] + (100 if kind == "loc" else 0)
@@ -73,6 +74,9 @@ def test_config4_decode(kind):
         del vc
         vc = kc
     maxl = int(kvl.max())
+    if kind == "glob_verify":
+        verify_case(d, q, kc, vc, off, kvl, maxl, cfg["seed"])
+        return
     o = ar.decode(q, kc, vc, off.to(DEV), kvl.to(DEV), window=d.window, scale=d.scale,
                   rotary_dims=d.rotary_dims, theta=d.theta, max_kv_len=maxl)
     torch.cuda.synchronize()
@@ -91,6 +95,25 @@ def test_config4_decode(kind):
         mx, rel = assert_close(o[b], ref, torch.bfloat16, f"config 4 {kind} seq {b} len {n}")
         print(f"config 4 {kind}: seq {b} kv_len={n} max_abs={mx:.3e} rel_rms={rel:.3e}",
               flush=True)
+    del kc, vc
+    torch.cuda.empty_cache()
+
+
+def verify_case(d, q1, kc, vc, off, kvl, maxl, seed, n_q=2):
+    q = inputs.normal((d.n_seq, n_q, d.Hq, d.Dk), seed, 90, d.dtype, DEV)
+    o = ar.verify(q, kc, vc, off.to(DEV), kvl.to(DEV), window=d.window, scale=d.scale,
+                  rotary_dims=d.rotary_dims, theta=d.theta, max_kv_len=maxl)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o.float()).all()
+    lens = kvl.tolist()
+    for b in sorted({int(np.argmin(lens)), int(np.argmax(lens)), 7, 40}):
+        n, a = lens[b], int(off[b])
+        ref = oracle.verify(q[b:b + 1].cpu(), kc[a:a + n].cpu(), vc[a:a + n].cpu(), [0], [n],
+                            window=d.window, scale=d.scale, rotary_dims=d.rotary_dims,
+                            theta=d.theta)
+        mx, rel = assert_close(o[b:b + 1], ref, torch.bfloat16, f"config 4 verify seq {b}")
+        print(f"config 4 verify n_q={n_q}: seq {b} kv_len={n} max_abs={mx:.3e} "
+              f"rel_rms={rel:.3e}", flush=True)
     del kc, vc
     torch.cuda.empty_cache()
 

@@ -412,3 +412,48 @@ def test_decode_rejects_visible_rows_before_row0():
     kc = rng.standard_normal((5, 1, 8))
     with pytest.raises(RuntimeError):
         oracle.decode_one(q, kc, kc, kv_len=10, row0=5, window=6, scale=1.0)
+
+
+# ------------------------------------------------ verify (several tokens) ----
+
+def test_verify_one_token_is_decode():
+    lens, Hq, Hkv, D = [3, 17, 40], 8, 2, 16
+    offs = np.concatenate([[0], np.cumsum(lens)[:-1]])
+    kc = rng.standard_normal((sum(lens), Hkv, D))
+    vc = rng.standard_normal((sum(lens), Hkv, D))
+    q = rng.standard_normal((3, Hq, D))
+    a = oracle.decode(q, kc, vc, offs, lens, window=5, scale=0.3, rotary_dims=8, theta=1e4)
+    b = oracle.verify(q[:, None], kc, vc, offs, lens, window=5, scale=0.3, rotary_dims=8,
+                      theta=1e4)
+    np.testing.assert_allclose(b[:, 0], a, rtol=0, atol=1e-14)
+
+
+@pytest.mark.parametrize("W", [0, 3, 9])
+def test_verify_rows_equal_the_last_prefill_rows(W):
+    """The n_q new tokens of a sequence are the last n_q rows of a prefill
+    over the whole sequence (keys cached rotated, queries unrotated)."""
+    T, n_q, Hq, Hkv, D, R, th = 30, 5, 4, 2, 16, 8, 1e6
+    q = rng.standard_normal((1, T, Hq, D))
+    k = rng.standard_normal((1, T, Hkv, D))
+    v = rng.standard_normal((1, T, Hkv, D))
+    ref = oracle.prefill(q, k, v, window=W, scale=0.25, rotary_dims=R, theta=th)[0, T - n_q:]
+    kr = oracle.rope(k[0], np.arange(T), R, th)
+    out = oracle.verify(q[:, T - n_q:], kr, v[0], [0], [T], window=W, scale=0.25,
+                        rotary_dims=R, theta=th)[0]
+    np.testing.assert_allclose(out, ref, rtol=1e-12, atol=1e-12)
+
+
+def test_verify_first_draft_token_ignores_later_ones():
+    """Causal within the draft: changing the rows of later new tokens leaves
+    token 0's output alone, and token n_q-1 sees them all."""
+    T, n_q, D = 12, 3, 8
+    kc = rng.standard_normal((T, 1, D))
+    vc = rng.standard_normal((T, 1, D))
+    q = rng.standard_normal((1, n_q, 2, D))
+    a = oracle.verify(q, kc, vc, [0], [T], window=0, scale=0.5)
+    kc2, vc2 = kc.copy(), vc.copy()
+    kc2[T - 2:] += 3.0
+    vc2[T - 2:] -= 5.0
+    b = oracle.verify(q, kc2, vc2, [0], [T], window=0, scale=0.5)
+    np.testing.assert_allclose(a[0, 0], b[0, 0], rtol=0, atol=1e-14)
+    assert np.abs(a[0, 1] - b[0, 1]).max() > 1e-3 and np.abs(a[0, 2] - b[0, 2]).max() > 1e-3
