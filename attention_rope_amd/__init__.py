@@ -32,7 +32,7 @@ STATUS = {0: "ok", 1: "null pointer", 2: "invalid shape or argument",
 EXPORTS = ("attn_rope_table", "attn_rope_table_bytes", "attn_prefill",
            "attn_prefill_workspace_bytes", "attn_decode",
            "attn_decode_workspace_bytes", "attn_verify", "attn_verify_workspace_bytes",
-           "prope_apply", "attn_status_string", "attn_last_error")
+           "prope_apply", "prope_apply_2d", "attn_status_string", "attn_last_error")
 
 
 class AttnError(RuntimeError):
@@ -79,6 +79,8 @@ def load(path: str = LIB_PATH):
     lib.attn_verify.restype = ctypes.c_int
     lib.prope_apply.argtypes = [vp, vp, vp, i32, i32, i32, _Rope, ctypes.c_int, vp]
     lib.prope_apply.restype = ctypes.c_int
+    lib.prope_apply_2d.argtypes = [vp, vp, vp, i32, i32, i32, _Rope, ctypes.c_int, vp]
+    lib.prope_apply_2d.restype = ctypes.c_int
     lib.attn_status_string.argtypes = [ctypes.c_int]
     lib.attn_status_string.restype = ctypes.c_char_p
     lib.attn_last_error.argtypes = []
@@ -243,4 +245,17 @@ def prope(x, positions, *, rotary_dims: int, theta: float, out=None):
     y = out if out is not None else torch.empty_like(x)
     _check(lib.prope_apply(_dev(x, "x"), _dev(y, "y"), _dev(positions, "positions"),
                            N, H, D, _Rope(rotary_dims, theta), _dtype_code(x), _stream(x)))
+    return y
+
+
+def prope_2d(x, positions_xy, *, rotary_dims: int, theta: float, out=None):
+    """x [N,H,D] -> 2-D RoPE copy (or in place when out is x); positions_xy
+    int32 [N,2] = (width, height) coordinates; each half of D turns by one."""
+    lib = load()
+    N, H, D = x.shape
+    if positions_xy.dtype != torch.int32 or tuple(positions_xy.shape) != (N, 2):
+        raise TypeError("positions_xy must be int32 [N, 2]")
+    y = out if out is not None else torch.empty_like(x)
+    _check(lib.prope_apply_2d(_dev(x, "x"), _dev(y, "y"), _dev(positions_xy, "positions_xy"),
+                              N, H, D, _Rope(rotary_dims, theta), _dtype_code(x), _stream(x)))
     return y

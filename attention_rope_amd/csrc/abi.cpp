@@ -122,6 +122,35 @@ attn_status_t decode_call(const char* what, const void* q, const void* k_cache,
 }
 
 
+// prope_apply (NH = 1) and prope_apply_2d (NH = 2 halves, positions [N, 2]).
+attn_status_t prope_call(const void* x, void* y, const int32_t* positions, int32_t N,
+                         int32_t H, int32_t D, int NH, attn_rope_t rope, attn_dtype_t dtype,
+                         void* stream) {
+  if (dtype != ATTN_F32 && dtype != ATTN_BF16)
+    return fail(ATTN_ERR_UNSUPPORTED, "dtype %d is not ATTN_F32 or ATTN_BF16", (int)dtype);
+  if (N < 0 || H < 0) return fail(ATTN_ERR_SHAPE, "N=%d and H=%d must be >= 0", N, H);
+  if (D < 2 || D > 1024 || D % 2) return fail(ATTN_ERR_SHAPE, "D=%d must be even, 2..1024", D);
+  attn_status_t rs = check_rope(rope, D / NH);
+  if (rs != ATTN_OK) return rs;
+  if (N == 0 || H == 0) return ok();
+  if (!x || !y || !positions) return fail(ATTN_ERR_NULL, "x, y and positions must be non-NULL");
+  const size_t es = elem_size(dtype);
+  if ((reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(y)) & (2 * es - 1))
+    return fail(ATTN_ERR_SHAPE, "x and y must be aligned to a pair of elements");
+  const size_t n = (size_t)N * H * D * es;
+  if (x != y && overlap(x, n, y, n)) return fail(ATTN_ERR_ALIAS, "y partially overlaps x");
+  if ((int64_t)N * NH * (rope.rotary_dims / 2) > (int64_t)INT32_MAX * 256)
+    return fail(ATTN_ERR_SHAPE, "N too large");
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  if (rope.rotary_dims == 0) {
+    if (x == y) return ok();
+    return launch_status(hipMemcpyAsync(y, x, n, hipMemcpyDeviceToDevice, st), "prope copy");
+  }
+  return launch_status(attn::launch_prope(x, y, positions, N, H, D, rope.rotary_dims / 2, NH,
+                                          rope.theta, dtype == ATTN_BF16, st),
+                       "prope");
+}
+
 }  // namespace
 
 extern "C" {
@@ -279,29 +308,14 @@ attn_status_t attn_verify(const void* q, const void* k_cache, const void* v_cach
 attn_status_t prope_apply(const void* x, void* y, const int32_t* positions, int32_t N,
                           int32_t H, int32_t D, attn_rope_t rope, attn_dtype_t dtype,
                           void* stream) {
-  if (dtype != ATTN_F32 && dtype != ATTN_BF16)
-    return fail(ATTN_ERR_UNSUPPORTED, "dtype %d is not ATTN_F32 or ATTN_BF16", (int)dtype);
-  if (N < 0 || H < 0) return fail(ATTN_ERR_SHAPE, "N=%d and H=%d must be >= 0", N, H);
-  if (D < 2 || D > 1024 || D % 2) return fail(ATTN_ERR_SHAPE, "D=%d must be even, 2..1024", D);
-  attn_status_t rs = check_rope(rope, D);
-  if (rs != ATTN_OK) return rs;
-  if (N == 0 || H == 0) return ok();
-  if (!x || !y || !positions) return fail(ATTN_ERR_NULL, "x, y and positions must be non-NULL");
-  const size_t es = elem_size(dtype);
-  if ((reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(y)) & (2 * es - 1))
-    return fail(ATTN_ERR_SHAPE, "x and y must be aligned to a pair of elements");
-  const size_t n = (size_t)N * H * D * es;
-  if (x != y && overlap(x, n, y, n)) return fail(ATTN_ERR_ALIAS, "y partially overlaps x");
-  if ((int64_t)N * (rope.rotary_dims / 2) > (int64_t)INT32_MAX * 256)
-    return fail(ATTN_ERR_SHAPE, "N too large");
-  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  if (rope.rotary_dims == 0) {
-    if (x == y) return ok();
-    return launch_status(hipMemcpyAsync(y, x, n, hipMemcpyDeviceToDevice, st), "prope copy");
-  }
-  return launch_status(attn::launch_prope(x, y, positions, N, H, D, rope.rotary_dims / 2,
-                                          rope.theta, dtype == ATTN_BF16, st),
-                       "prope");
+  return prope_call(x, y, positions, N, H, D, 1, rope, dtype, stream);
+}
+
+attn_status_t prope_apply_2d(const void* x, void* y, const int32_t* positions_xy, int32_t N,
+                             int32_t H, int32_t D, attn_rope_t rope, attn_dtype_t dtype,
+                             void* stream) {
+  if (D % 4) return fail(ATTN_ERR_SHAPE, "D=%d must be a multiple of 4 (two even halves)", D);
+  return prope_call(x, y, positions_xy, N, H, D, 2, rope, dtype, stream);
 }
 
 }  // extern "C"

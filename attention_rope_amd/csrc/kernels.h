@@ -10,8 +10,10 @@ namespace attn {
 // ---- RoPE -----------------------------------------------------------------
 hipError_t launch_rope_table(float2* tab, int T, int P, int D, int pos0,
                              double theta, hipStream_t st);
+// NH = 1: pos [N]; NH = 2 (2-D RoPE): pos [N, 2], each half of D turned by
+// its own coordinate. P = rotary pairs per half.
 hipError_t launch_prope(const void* x, void* y, const int32_t* pos, int N, int H,
-                        int D, int P, double theta, bool bf16, hipStream_t st);
+                        int D, int P, int NH, double theta, bool bf16, hipStream_t st);
 // out[b, t, h, 0:R] = rotation of the first R dims of k[b, t, h, :] (bf16) by
 // the table row of token t; R = 2 * table pairs, a multiple of 8.
 hipError_t launch_rope_k_lead(const void* k, void* out, const float2* tab, int B, int T,

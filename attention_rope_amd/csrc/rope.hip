@@ -24,21 +24,28 @@ __global__ void rope_table_kernel(float2* __restrict__ tab, int T, int P, int D,
   tab[idx] = make_float2(c, s);
 }
 
-// y[n, h, :] = rope(x[n, h, :], pos[n]). One thread per (n, pair) computes the
-// angle once and applies it to all H heads; a second grid dimension copies the
-// untouched dims when y != x.
+// y[n, h, :] = rope(x[n, h, :], pos[n]) with NH = 1 half, or 2-D RoPE with
+// NH = 2: each half of the D dims is a vector of its own, turned by its own
+// coordinate (pos[2n] the patch's width coordinate for the first half,
+// pos[2n + 1] its height coordinate for the second), pair p of a half by
+// coordinate * theta^(-2p/(D/2)) ("Gemma 4: End-to-End Architecture
+// Walkthrough", Phase 1 section 1b). One thread per (n, half, pair) forms the
+// angle once and applies it to all H heads; a second grid dimension copies
+// the untouched dims when y != x.
 template <typename T_>
 __global__ void prope_kernel(const T_* __restrict__ x, T_* __restrict__ y,
                              const int32_t* __restrict__ pos, int N, int H, int D,
-                             int P, double log2_theta, int in_place) {
+                             int P, int NH, double log2_theta, int in_place) {
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int DH = D / NH;  // dims per half
   if (blockIdx.y == 0) {
-    if (idx >= (int64_t)N * P) return;
-    const int n = (int)(idx / P), p = (int)(idx % P);
+    if (idx >= (int64_t)N * NH * P) return;
+    const int n = (int)(idx / (NH * P)), q = (int)(idx % (NH * P));
+    const int half = q / P, p = q - half * P;
     float c, s;
-    rope_cos_sin(pos[n], rope_freq(p, D, log2_theta), &c, &s);
+    rope_cos_sin(pos[(int64_t)n * NH + half], rope_freq(p, DH, log2_theta), &c, &s);
     for (int h = 0; h < H; ++h) {
-      const int64_t off = ((int64_t)n * H + h) * D + 2 * p;
+      const int64_t off = ((int64_t)n * H + h) * D + half * DH + 2 * p;
       float x0, x1;
       if constexpr (sizeof(T_) == 2) {
         x0 = bf16_to_f32(reinterpret_cast<const uint16_t*>(x)[off]);
@@ -56,15 +63,16 @@ __global__ void prope_kernel(const T_* __restrict__ x, T_* __restrict__ y,
       }
     }
   } else {
-    // Copy dims [2P, D) of every (n, h) when writing out of place.
+    // Copy dims [2P, DH) of every half of every (n, h) when writing out of place.
     if (in_place) return;
-    const int rest = D - 2 * P;
+    const int rest = DH - 2 * P;
     if (rest == 0) return;
-    const int64_t total = (int64_t)N * H * rest;
+    const int64_t total = (int64_t)N * H * NH * rest;
     for (int64_t i = idx; i < total; i += (int64_t)gridDim.x * blockDim.x) {
-      const int64_t nh = i / rest;
-      const int d = 2 * P + (int)(i % rest);
-      y[nh * D + d] = x[nh * D + d];
+      const int64_t nhh = i / rest;  // (n * H + h) * NH + half
+      const int d = (int)(nhh % NH) * DH + 2 * P + (int)(i % rest);
+      const int64_t base = (nhh / NH) * D;
+      y[base + d] = x[base + d];
     }
   }
 }
@@ -120,28 +128,29 @@ hipError_t launch_rope_table(float2* tab, int T, int P, int D, int pos0,
 }
 
 hipError_t launch_prope(const void* x, void* y, const int32_t* pos, int N, int H,
-                        int D, int P, double theta, bool bf16, hipStream_t st) {
-  const int64_t n = (int64_t)N * P;
+                        int D, int P, int NH, double theta, bool bf16, hipStream_t st) {
+  const int64_t n = (int64_t)N * NH * P;
   const int threads = 256;
-  int blocks = (int)((n + threads - 1) / threads);
+  int64_t blocks = (n + threads - 1) / threads;
   if (blocks < 1) blocks = 1;
+  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
   const int in_place = (x == y);
-  const int ydim = (in_place || D == 2 * P) ? 1 : 2;
-  int bx = blocks;
+  const int ydim = (in_place || D == 2 * P * NH) ? 1 : 2;
+  int bx = (int)blocks;
   if (ydim == 2) {
-    // The copy half needs enough blocks for N*H*(D-2P) elements as well.
-    const int64_t m = (int64_t)N * H * (D - 2 * P);
+    // The copy half needs enough blocks for the untouched elements as well.
+    const int64_t m = (int64_t)N * H * (D - 2 * P * NH);
     int64_t want = (m + threads - 1) / threads;
     if (want > 65536) want = 65536;
     if (want > bx) bx = (int)want;
   }
   if (bf16)
     hipLaunchKernelGGL(prope_kernel<uint16_t>, dim3(bx, ydim), dim3(threads), 0, st,
-                       (const uint16_t*)x, (uint16_t*)y, pos, N, H, D, P, log2(theta),
+                       (const uint16_t*)x, (uint16_t*)y, pos, N, H, D, P, NH, log2(theta),
                        in_place);
   else
     hipLaunchKernelGGL(prope_kernel<float>, dim3(bx, ydim), dim3(threads), 0, st,
-                       (const float*)x, (float*)y, pos, N, H, D, P, log2(theta),
+                       (const float*)x, (float*)y, pos, N, H, D, P, NH, log2(theta),
                        in_place);
   return hipGetLastError();
 }

@@ -196,6 +196,24 @@ attn_status_t prope_apply(const void *x, void *y, const int32_t *positions,
                           int32_t N, int32_t H, int32_t D, attn_rope_t rope,
                           attn_dtype_t dtype, void *stream);
 
+/*
+ * 2-D RoPE for image patches ("Gemma 4: End-to-End Architecture Walkthrough",
+ * Phase 1 section 1b; "Gemma 4 Architecture Reference", "Vision Encoder"):
+ * each patch vector is split in half and each half is turned like a
+ * D/2-dim RoPE vector, the first half by the patch's width (x) coordinate,
+ * the second by its height (y) coordinate.
+ *   y[n, h, 0:D/2] = rope(x[n, h, 0:D/2], positions_xy[n][0]),
+ *   y[n, h, D/2:D] = rope(x[n, h, D/2:D], positions_xy[n][1]),
+ *   with pair p of a half turned by coordinate * theta^(-2p/(D/2)) for the
+ *   first rope.rotary_dims dims of each half.
+ *   x, y [N, H, D], D a multiple of 4, 4 <= D <= 1024; positions_xy: device
+ *   int32 [N, 2], each >= 0; rope.rotary_dims even, <= D/2. In place and
+ *   overlap rules as for prope_apply.
+ */
+attn_status_t prope_apply_2d(const void *x, void *y, const int32_t *positions_xy,
+                             int32_t N, int32_t H, int32_t D, attn_rope_t rope,
+                             attn_dtype_t dtype, void *stream);
+
 /* Static text for a status code. */
 const char *attn_status_string(attn_status_t s);
 

@@ -96,6 +96,22 @@ def rope(x, positions, rotary_dims: int, theta: float) -> np.ndarray:
     return y
 
 
+def rope_2d(x, positions_xy, rotary_dims: int, theta: float) -> np.ndarray:
+    """2-D RoPE for image patches, fp64: each half of the D dims is a vector
+    of its own, turned like D/2-dim RoPE by one patch coordinate -- the first
+    half by the width (x) coordinate, the second by the height (y) coordinate
+    ("Gemma 4: End-to-End Architecture Walkthrough", Phase 1 section 1b).
+    rotary_dims applies within each half. x [N, H, D]; positions_xy [N, 2]."""
+    x = _f64(x)
+    N, H, D = x.shape
+    assert D % 4 == 0
+    pxy = np.asarray(positions_xy, dtype=np.int64).reshape(N, 2)
+    h = D // 2
+    first = rope(np.ascontiguousarray(x[:, :, :h]), pxy[:, 0], rotary_dims, theta)
+    second = rope(np.ascontiguousarray(x[:, :, h:]), pxy[:, 1], rotary_dims, theta)
+    return np.concatenate([first, second], axis=2)
+
+
 def prefill(q, k, v, *, window: int, scale: float, rotary_dims: int = 0,
             theta: float = 10000.0, rope_mask: int = ROPE_Q | ROPE_K,
             pos0: int = 0, rows=None, nthreads: int | None = None) -> np.ndarray:

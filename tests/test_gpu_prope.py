@@ -5,7 +5,7 @@ import torch
 
 import inputs
 import oracle
-from parity import to64
+from parity import assert_close, to64
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -52,3 +52,30 @@ def test_prope_errors(gpu_lib):
     pos = torch.zeros(4, dtype=torch.int32, device=DEV)
     with pytest.raises(gpu_lib.AttnError):
         gpu_lib.prope(x, pos, rotary_dims=10, theta=1e4)
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("N,H,D,R", [(300, 4, 64, 32), (2520, 2, 128, 32), (7, 1, 4, 2)])
+def test_prope_2d(gpu_lib, dtype, N, H, D, R):
+    """2-D RoPE (each half turned by one patch coordinate) vs the oracle; 2520
+    patches is the 280-token budget's patch count, coordinates on a 60 x 42 grid."""
+    g = torch.Generator().manual_seed(N + D)
+    x = torch.randn(N, H, D, generator=g).to(dtype)
+    pxy = torch.stack([torch.arange(N) % 60, torch.arange(N) // 60], 1).to(torch.int32)
+    print(f"prope_2d N={N} H={H} D={D} R={R} {dtype}", flush=True)
+    y = gpu_lib.prope_2d(x.to(DEV), pxy.to(DEV), rotary_dims=R, theta=1e4)
+    torch.cuda.synchronize()
+    ref = oracle.rope_2d(x, pxy.numpy(), R, 1e4)
+    assert_close(y, ref, dtype, "prope_2d")
+    # in place gives the same values
+    xi = x.to(DEV).clone()
+    gpu_lib.prope_2d(xi, pxy.to(DEV), rotary_dims=R, theta=1e4, out=xi)
+    torch.cuda.synchronize()
+    assert torch.equal(xi, y)
+
+
+def test_prope_2d_rejects_odd_halves(gpu_lib):
+    x = torch.zeros(4, 1, 6, dtype=torch.bfloat16, device=DEV)
+    pxy = torch.zeros(4, 2, dtype=torch.int32, device=DEV)
+    with pytest.raises(gpu_lib.AttnError):
+        gpu_lib.prope_2d(x, pxy, rotary_dims=2, theta=1e4)

@@ -457,3 +457,51 @@ def test_verify_first_draft_token_ignores_later_ones():
     b = oracle.verify(q, kc2, vc2, [0], [T], window=0, scale=0.5)
     np.testing.assert_allclose(a[0, 0], b[0, 0], rtol=0, atol=1e-14)
     assert np.abs(a[0, 1] - b[0, 1]).max() > 1e-3 and np.abs(a[0, 2] - b[0, 2]).max() > 1e-3
+
+
+# ----------------------------------------------------- 2-D RoPE (patches) ----
+
+def test_rope_2d_one_pair_per_half_closed_form():
+    """D = 4: pair 0 of each half turns by its coordinate in radians (pair 0
+    has frequency 1 under any schedule)."""
+    x = rng.standard_normal((3, 2, 4))
+    pxy = np.array([[0, 0], [3, 1], [7, 12]])
+    y = oracle.rope_2d(x, pxy, 2, 1e4)
+    for n in range(3):
+        for hh in range(2):
+            a = complex(x[n, hh, 0], x[n, hh, 1]) * cmath.exp(1j * pxy[n, 0])
+            b = complex(x[n, hh, 2], x[n, hh, 3]) * cmath.exp(1j * pxy[n, 1])
+            assert abs(complex(y[n, hh, 0], y[n, hh, 1]) - a) < 1e-13
+            assert abs(complex(y[n, hh, 2], y[n, hh, 3]) - b) < 1e-13
+
+
+def test_rope_2d_each_half_follows_its_own_coordinate():
+    x = rng.standard_normal((4, 3, 32))
+    pxy = np.array([[5, 9], [0, 4], [7, 0], [2, 2]])
+    y = oracle.rope_2d(x, pxy, 8, 1e4)                           # 8 of each half's 16 dims
+    np.testing.assert_array_equal(y[1, :, :16], x[1, :, :16])   # x = 0: first half still
+    np.testing.assert_array_equal(y[2, :, 16:], x[2, :, 16:])   # y = 0: second half still
+    pxy2 = pxy.copy()
+    pxy2[:, 1] += 6                                              # move y only
+    y2 = oracle.rope_2d(x, pxy2, 8, 1e4)
+    np.testing.assert_array_equal(y2[:, :, :16], y[:, :, :16])
+    assert np.abs(y2[:, :, 16:] - y[:, :, 16:]).max() > 1e-3
+    # dims past rotary_dims in each half are untouched, norms per half kept
+    np.testing.assert_array_equal(y[:, :, 8:16], x[:, :, 8:16])
+    np.testing.assert_array_equal(y[:, :, 24:], x[:, :, 24:])
+    for s0 in (slice(0, 16), slice(16, 32)):
+        np.testing.assert_allclose(np.linalg.norm(y[:, :, s0], axis=-1),
+                                   np.linalg.norm(x[:, :, s0], axis=-1), rtol=1e-13)
+
+
+def test_rope_2d_scores_depend_only_on_the_offset():
+    """<R(x1, y1) q, R(x2, y2) k> depends only on (x2 - x1, y2 - y1)."""
+    q = rng.standard_normal((1, 1, 64))
+    k = rng.standard_normal((1, 1, 64))
+    def score(a, b):
+        return float(np.sum(oracle.rope_2d(q, [a], 64 // 2, 100.0) *
+                            oracle.rope_2d(k, [b], 64 // 2, 100.0)))
+    s0 = score((3, 4), (10, 6))
+    for dx, dy in [(5, 0), (0, 9), (17, 23)]:
+        assert abs(score((3 + dx, 4 + dy), (10 + dx, 6 + dy)) - s0) < 1e-10
+    assert abs(score((3, 4), (10, 7)) - s0) > 1e-6
