@@ -32,6 +32,7 @@ STATUS = {0: "ok", 1: "null pointer", 2: "invalid shape or argument",
 EXPORTS = ("attn_rope_table", "attn_rope_table_bytes", "attn_prefill",
            "attn_prefill_workspace_bytes", "attn_decode",
            "attn_decode_workspace_bytes", "attn_verify", "attn_verify_workspace_bytes",
+           "attn_kv_quantize_int8", "attn_decode_int8", "attn_decode_int8_workspace_bytes",
            "prope_apply", "prope_apply_2d", "attn_status_string", "attn_last_error")
 
 
@@ -79,6 +80,13 @@ def load(path: str = LIB_PATH):
     lib.attn_verify.restype = ctypes.c_int
     lib.prope_apply.argtypes = [vp, vp, vp, i32, i32, i32, _Rope, ctypes.c_int, vp]
     lib.prope_apply.restype = ctypes.c_int
+    lib.attn_kv_quantize_int8.argtypes = [vp, vp, vp, i32, i32, i32, ctypes.c_int, vp]
+    lib.attn_kv_quantize_int8.restype = ctypes.c_int
+    lib.attn_decode_int8_workspace_bytes.argtypes = [i32] * 6
+    lib.attn_decode_int8_workspace_bytes.restype = sz
+    lib.attn_decode_int8.argtypes = [vp] * 8 + [i32] * 6 + [
+        ctypes.c_float, _Rope, i32, vp, sz, vp]
+    lib.attn_decode_int8.restype = ctypes.c_int
     lib.prope_apply_2d.argtypes = [vp, vp, vp, i32, i32, i32, _Rope, ctypes.c_int, vp]
     lib.prope_apply_2d.restype = ctypes.c_int
     lib.attn_status_string.argtypes = [ctypes.c_int]
@@ -259,3 +267,51 @@ def prope_2d(x, positions_xy, *, rotary_dims: int, theta: float, out=None):
     _check(lib.prope_apply_2d(_dev(x, "x"), _dev(y, "y"), _dev(positions_xy, "positions_xy"),
                               N, H, D, _Rope(rotary_dims, theta), _dtype_code(x), _stream(x)))
     return y
+
+
+def kv_quantize_int8(x, *, codes=None, scales=None):
+    """x [N,H,D] bf16 -> (codes int8 [N,H,D], scales float32 [N,H]); one
+    symmetric scale per (row, head), s = max|x| / 127."""
+    lib = load()
+    N, H, D = x.shape
+    c = codes if codes is not None else torch.empty((N, H, D), dtype=torch.int8, device=x.device)
+    sc = scales if scales is not None else torch.empty((N, H), dtype=torch.float32,
+                                                       device=x.device)
+    _check(lib.attn_kv_quantize_int8(_dev(x, "x"), _dev(c, "codes"), _dev(sc, "scales"), N, H, D,
+                                     _dtype_code(x), _stream(x)))
+    return c, sc
+
+
+def decode_int8_workspace_bytes(B: int, Hq: int, Hkv: int, Dv: int, max_kv_len: int,
+                                window: int) -> int:
+    return int(load().attn_decode_int8_workspace_bytes(B, Hq, Hkv, Dv, max_kv_len, window))
+
+
+def decode_int8(q, k_codes, k_scales, v_codes, v_scales, row_offset, kv_len, *,
+                window: int = 0, scale: float | None = None, rotary_dims: int = 0,
+                theta: float = 10000.0, max_kv_len: int, out=None, workspace=None):
+    """attn_decode over int8 caches: codes [rows,Hkv,D] int8, scales
+    [rows,Hkv] float32; q [B,Hq,Dk] bf16 -> o [B,Hq,Dv] bf16."""
+    lib = load()
+    B, Hq, Dk = q.shape
+    Hkv, Dv = k_codes.shape[1], v_codes.shape[2]
+    if row_offset.dtype != torch.int64 or kv_len.dtype != torch.int32:
+        raise TypeError("row_offset must be int64 and kv_len int32")
+    if k_codes.dtype != torch.int8 or v_codes.dtype != torch.int8:
+        raise TypeError("codes must be int8")
+    if k_scales.dtype != torch.float32 or v_scales.dtype != torch.float32:
+        raise TypeError("scales must be float32")
+    if scale is None:
+        scale = Dk ** -0.5
+    o = out if out is not None else torch.empty((B, Hq, Dv), dtype=q.dtype, device=q.device)
+    need = decode_int8_workspace_bytes(B, Hq, Hkv, Dv, max_kv_len, window)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    _check(lib.attn_decode_int8(_dev(q, "q"), _dev(k_codes, "k_codes"), _dev(k_scales, "k_scales"),
+                                _dev(v_codes, "v_codes"), _dev(v_scales, "v_scales"),
+                                _dev(row_offset, "row_offset"), _dev(kv_len, "kv_len"),
+                                _dev(o, "o"), B, Hq, Hkv, Dk, Dv, int(window), float(scale),
+                                _Rope(rotary_dims, theta), int(max_kv_len),
+                                ctypes.c_void_p(workspace.data_ptr()),
+                                workspace.numel() * workspace.element_size(), _stream(q)))
+    return o

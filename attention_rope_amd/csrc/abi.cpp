@@ -305,6 +305,80 @@ attn_status_t attn_verify(const void* q, const void* k_cache, const void* v_cach
                      dtype, stream);
 }
 
+attn_status_t attn_kv_quantize_int8(const void* x, int8_t* codes, float* scales, int32_t N,
+                                    int32_t H, int32_t D, attn_dtype_t dtype, void* stream) {
+  if (dtype != ATTN_BF16) return fail(ATTN_ERR_UNSUPPORTED, "int8 quantiser reads ATTN_BF16");
+  if (N < 0 || H < 0) return fail(ATTN_ERR_SHAPE, "N=%d and H=%d must be >= 0", N, H);
+  if (D != 128 && D != 256 && D != 512)
+    return fail(ATTN_ERR_UNSUPPORTED, "int8 quantiser supports D in {128,256,512}, got %d", D);
+  if (N == 0 || H == 0) return ok();
+  if (!x || !codes || !scales) return fail(ATTN_ERR_NULL, "x, codes and scales must be non-NULL");
+  if (!aligned16(x) || (reinterpret_cast<uintptr_t>(scales) & 3))
+    return fail(ATTN_ERR_SHAPE, "x must be 16-byte aligned, scales 4-byte aligned");
+  const size_t rows = (size_t)N * H;
+  if (overlap(x, rows * D * 2, codes, rows * D) || overlap(x, rows * D * 2, scales, rows * 4) ||
+      overlap(codes, rows * D, scales, rows * 4))
+    return fail(ATTN_ERR_ALIAS, "x, codes and scales must not overlap");
+  return launch_status(attn::launch_kv_quantize_int8(x, codes, scales, N, H, D,
+                                                     reinterpret_cast<hipStream_t>(stream)),
+                       "int8 quantiser");
+}
+
+size_t attn_decode_int8_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t Dv,
+                                        int32_t max_kv_len, int32_t window) {
+  return attn::decode_workspace_bytes(B, 1, Hq, Hkv, 0, Dv, max_kv_len, window);
+}
+
+attn_status_t attn_decode_int8(const void* q, const int8_t* k_codes, const float* k_scales,
+                               const int8_t* v_codes, const float* v_scales,
+                               const int64_t* row_offset, const int32_t* kv_len, void* o,
+                               int32_t B, int32_t Hq, int32_t Hkv, int32_t Dk, int32_t Dv,
+                               int32_t window, float scale, attn_rope_t rope,
+                               int32_t max_kv_len, void* workspace, size_t workspace_bytes,
+                               void* stream) {
+  if (B < 0 || B > 65535) return fail(ATTN_ERR_SHAPE, "B=%d must be in [0, 65535]", B);
+  if (Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0)
+    return fail(ATTN_ERR_SHAPE, "Hq=%d must be a positive multiple of Hkv=%d", Hq, Hkv);
+  if (!attn::decode_int8_supported(Dk, Dv, Hq / Hkv))
+    return fail(ATTN_ERR_UNSUPPORTED,
+                "int8 decode supports (Dk, Dv) in {(512,256), (256,256)}, Hq/Hkv <= 16 "
+                "(got Dk=%d Dv=%d G=%d)", Dk, Dv, Hq / Hkv);
+  if (!std::isfinite(scale) || scale < 0.f)
+    return fail(ATTN_ERR_UNSUPPORTED, "int8 decode needs a finite scale >= 0");
+  attn_status_t rs = check_rope(rope, Dk);
+  if (rs != ATTN_OK) return rs;
+  if (B == 0) return ok();
+  if (max_kv_len < 1) return fail(ATTN_ERR_SHAPE, "max_kv_len=%d must be >= 1", max_kv_len);
+  if (!attn::decode_shape_fits(B, 1, Hq, Hkv, Dk, Dv, max_kv_len, window))
+    return fail(ATTN_ERR_SHAPE, "cache too large for one call (max_kv_len=%d, Hkv=%d)",
+                max_kv_len, Hkv);
+  if (!q || !k_codes || !k_scales || !v_codes || !v_scales || !row_offset || !kv_len || !o)
+    return fail(ATTN_ERR_NULL, "q, codes, scales, row_offset, kv_len and o must be non-NULL");
+  if (!aligned16(q) || !aligned16(k_codes) || !aligned16(v_codes) || !aligned16(o) ||
+      ((reinterpret_cast<uintptr_t>(k_scales) | reinterpret_cast<uintptr_t>(v_scales)) & 3))
+    return fail(ATTN_ERR_SHAPE, "q, codes and o must be 16-byte aligned, scales 4-byte");
+  const size_t need = attn::decode_workspace_bytes(B, 1, Hq, Hkv, Dk, Dv, max_kv_len, window);
+  if (!workspace || workspace_bytes < need)
+    return fail(ATTN_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+                workspace ? workspace_bytes : (size_t)0);
+  if (!aligned16(workspace)) return fail(ATTN_ERR_WORKSPACE, "workspace must be 16-byte aligned");
+  const size_t no = (size_t)B * Hq * Dv * 2, nq = (size_t)B * Hq * Dk * 2;
+  if (overlap(o, no, q, nq) || overlap(workspace, need, o, no) || overlap(workspace, need, q, nq))
+    return fail(ATTN_ERR_ALIAS, "o / workspace must not overlap q or each other");
+  attn::DecodeArgs a{};
+  a.q = q; a.k_cache = k_codes; a.v_cache = v_codes; a.k_scale = k_scales;
+  a.v_scale = v_scales; a.row_offset = row_offset; a.kv_len = kv_len; a.o = o;
+  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.Dk = Dk; a.Dv = Dv;
+  a.window = window > 0 ? window : 0;
+  a.rot_pairs = rope.rotary_dims / 2;
+  a.theta = rope.rotary_dims > 0 ? rope.theta : 1.0;
+  a.scale = scale;
+  a.max_kv_len = max_kv_len;
+  a.workspace = workspace;
+  return launch_status(attn::launch_decode_int8(a, reinterpret_cast<hipStream_t>(stream)),
+                       "int8 decode");
+}
+
 attn_status_t prope_apply(const void* x, void* y, const int32_t* positions, int32_t N,
                           int32_t H, int32_t D, attn_rope_t rope, attn_dtype_t dtype,
                           void* stream) {

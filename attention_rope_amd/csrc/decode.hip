@@ -29,9 +29,7 @@
 #include "kernels.h"
 
 namespace attn {
-namespace {
 
-constexpr float kLog2e = 1.4426950408889634f;
 // Split-K plan: each workgroup streams `ch` consecutive visible rows of one
 // sequence for one KV head. A workgroup's start (locating its rows, turning
 // the query, filling the DMA ring) and end (draining, writing its partial)
@@ -40,13 +38,9 @@ constexpr float kLog2e = 1.4426950408889634f;
 // halved while the grid would hold fewer than kMinGroups workgroups.
 constexpr int kMaxChunk = 4096, kMinChunk = 256, kMinGroups = 512;
 
-struct SplitPlan {
-  int ch, ns;  // rows per chunk, chunks per sequence (grid extent)
-};
-
 // groups: workgroups per (sequence, chunk); n_q new tokens per sequence widen
 // a window's range by n_q - 1 rows.
-inline SplitPlan decode_plan(int B, int groups, int max_kv_len, int window, int n_q = 1) {
+SplitPlan decode_plan(int B, int groups, int max_kv_len, int window, int n_q) {
   const int64_t wr = (int64_t)window + n_q - 1;
   const int range = (window > 0 && wr < max_kv_len) ? (int)wr : max_kv_len;
   int ch = (window > 0) ? range : kMaxChunk;
@@ -55,6 +49,10 @@ inline SplitPlan decode_plan(int B, int groups, int max_kv_len, int window, int 
   while (ch > kMinChunk && (int64_t)B * groups * splits(ch) < kMinGroups) ch = (ch + 1) / 2;
   return {ch, splits(ch)};
 }
+
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
 
 // ---- streaming kernel: K/V tiles through an LDS DMA ring -------------------
 // Decode is bound by the bytes of the cache, and there is little arithmetic
@@ -407,6 +405,13 @@ using RingCfg = std::conditional_t<
     SHARED || (DK == 512 && DV == 512), RCfg<DK, DV, 1, 2, SHARED>,
     std::conditional_t<(DK == 256 && DV == 256), RCfg<DK, DV, 1, 3>, RCfg<DK, DV, 2, 3>>>;
 
+template <int DV>
+hipError_t launch_merge_dv(const DecodeArgs& a, const SplitPlan& pl, hipStream_t st) {
+  hipLaunchKernelGGL((decode_merge_kernel<DV>), dim3(a.B * a.n_q * a.Hq), dim3(DV), 0, st, a,
+                     pl.ch, pl.ns);
+  return hipGetLastError();
+}
+
 template <int DK, int DV, bool SHARED>
 hipError_t launch_ring(const DecodeArgs& a, const SplitPlan& pl, int ncg, hipStream_t st) {
   using C = RingCfg<DK, DV, SHARED>;
@@ -419,9 +424,7 @@ hipError_t launch_ring(const DecodeArgs& a, const SplitPlan& pl, int ncg, hipStr
                      dim3(C::RW * 64), 0, st, a, pl.ch, pl.ns);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || pl.ns == 1) return e;  // one chunk: the ring kernel wrote o
-  hipLaunchKernelGGL((decode_merge_kernel<DV>), dim3(a.B * a.n_q * a.Hq), dim3(DV), 0, st, a,
-                     pl.ch, pl.ns);
-  return hipGetLastError();
+  return launch_merge_dv<DV>(a, pl, st);
 }
 
 // 16-column groups of (token, head) pairs per KV head.
@@ -468,6 +471,15 @@ inline size_t rotated_q_bytes(int B, int n_q, int Hq, int Dk) {
 }
 
 }  // namespace
+
+hipError_t launch_decode_merge(const DecodeArgs& a, const SplitPlan& pl, hipStream_t st) {
+  switch (a.Dv) {
+    case 128: return launch_merge_dv<128>(a, pl, st);
+    case 256: return launch_merge_dv<256>(a, pl, st);
+    case 512: return launch_merge_dv<512>(a, pl, st);
+    default: return hipErrorNotSupported;
+  }
+}
 
 size_t decode_workspace_bytes(int B, int n_q, int Hq, int Hkv, int Dk, int Dv, int max_kv_len,
                               int window) {

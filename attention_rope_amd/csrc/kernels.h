@@ -66,7 +66,19 @@ struct DecodeArgs {
   // are [B, n_q, Hq, D]. With q_rotated the queries are already turned.
   int n_q = 1;
   int q_rotated = 0;
+  // int8 caches (attn_decode_int8): per (row, KV head) scales, fp32 [rows, Hkv].
+  const float* k_scale = nullptr;
+  const float* v_scale = nullptr;
 };
+
+// Split-K plan shared by the decode kernels: ch rows per chunk, ns chunks per
+// sequence. groups = workgroups per (sequence, chunk).
+struct SplitPlan {
+  int ch, ns;
+};
+SplitPlan decode_plan(int B, int groups, int max_kv_len, int window, int n_q = 1);
+// Merge of the chunk partials into o (any supported Dv).
+hipError_t launch_decode_merge(const DecodeArgs& a, const SplitPlan& pl, hipStream_t st);
 
 // Workspace of a decode (n_q = 1) or verify (n_q > 1) call: the split-K
 // partials, and for n_q > 1 the turned queries ahead of them.
@@ -76,5 +88,14 @@ bool decode_supported(int Dk, int Dv, int G);
 bool decode_shape_fits(int B, int n_q, int Hq, int Hkv, int Dk, int Dv, int max_kv_len,
                        int window);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t st);
+
+// ---- int8 KV cache -------------------------------------------------------------
+// codes[n, h, :] = round-half-even(x / s), s = max|x[n, h, :]| / 127 (fp32).
+hipError_t launch_kv_quantize_int8(const void* x, int8_t* codes, float* scales, int N, int H,
+                                   int D, hipStream_t st);
+// Decode over int8 caches (k_cache / v_cache hold the codes, k_scale / v_scale
+// the scales); (Dk, Dv) in {(512, 256), (256, 256)}.
+bool decode_int8_supported(int Dk, int Dv, int G);
+hipError_t launch_decode_int8(const DecodeArgs& a, hipStream_t st);
 
 }  // namespace attn

@@ -241,10 +241,38 @@ def bench_decode(ar, torch, inputs, cfg, steps, warmup):
         tv.mark(i, 1)
     torch.cuda.synchronize()
     v_ms = sum(tv.ms(i, 0, 1) for i in range(steps)) / steps
+
+    # int8 cache: the global call's caches quantised once (outside the timed
+    # region), one scale per (row, KV head); the decode reads codes + scales.
+    kq, ks = ar.kv_quantize_int8(g["kc"])
+    vq, vs = ar.kv_quantize_int8(g["vc"])
+    o_i8 = torch.empty((d.n_seq, d.Hq, d.Dv), dtype=d.dtype, device="cuda")
+    ws_i8 = torch.empty(ar.decode_int8_workspace_bytes(d.n_seq, d.Hq, d.Hkv, d.Dv, g["maxl"],
+                                                       d.window),
+                        dtype=torch.uint8, device="cuda")
+    i8_bytes = (sum(vis) * d.Hkv * (d.Dk + d.Dv + 8)
+                + d.n_seq * d.Hq * (d.Dk + d.Dv) * 2)
+
+    def run_i8():
+        ar.decode_int8(g["q"], kq, ks, vq, vs, g["off"], g["kvl"], window=d.window,
+                       scale=d.scale, rotary_dims=d.rotary_dims, theta=d.theta,
+                       max_kv_len=g["maxl"], out=o_i8, workspace=ws_i8)
+
+    for _ in range(warmup):
+        run_i8()
+    ti = Timer(torch, steps)
+    for i in range(steps):
+        flush.fill_(i & 0xff)
+        ti.mark(i, 0)
+        run_i8()
+        ti.mark(i, 1)
+    torch.cuda.synchronize()
+    i8_ms = sum(ti.ms(i, 0, 1) for i in range(steps)) / steps
+    del kq, vq
     return dict(bytes=total_bytes, g_ms=g_ms, l_ms=l_ms, step_ms=g_ms + l_ms,
                 g_bytes=calls[0]["bytes"], l_bytes=calls[1]["bytes"], calls=calls,
                 kv_ms=kv_ms, kv_bytes=kv_bytes, kv_out=o_kv, v_ms=v_ms, v_bytes=v_bytes,
-                v_nq=n_q)
+                v_nq=n_q, i8_ms=i8_ms, i8_bytes=i8_bytes)
 
 
 def bench_stack(ar, torch, inputs, cfg, steps, warmup):
@@ -436,6 +464,15 @@ def main():
                                      "ms": round(rr["v_ms"], 4), "bytes": rr["v_bytes"],
                                      "what": f"global call with {rr['v_nq']} new tokens per "
                                              "sequence (speculative-decoding verify)"},
+                                 "int8_cache_call": {
+                                     "GB/s": round(rr["i8_bytes"] / (rr["i8_ms"] * 1e-3) / 1e9, 1),
+                                     "ms": round(rr["i8_ms"], 4), "bytes": rr["i8_bytes"],
+                                     "what": "global call over int8 codes + fp32 per-row scales "
+                                             "(same tokens; bytes counted as read)",
+                                     "roofline": roofline(
+                                         "hbm", rr["i8_bytes"] / (rr["i8_ms"] * 1e-3) / 1e9,
+                                         PEAK_HBM_GBS, "GB/s",
+                                         _traffic("decode_i8", "int8_global_decode"))},
                                  "roofline": roofline("hbm", g, PEAK_HBM_GBS, "GB/s",
                                                       _traffic("decode_ring", "global_decode"))}
             del rr

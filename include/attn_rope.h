@@ -197,6 +197,36 @@ attn_status_t prope_apply(const void *x, void *y, const int32_t *positions,
                           attn_dtype_t dtype, void *stream);
 
 /*
+ * int8 KV cache ("Gemma 4 Technical Report" reader, "Quantization and
+ * Efficiency": int8 KV caching). The pages give no scheme; this library's:
+ * symmetric codes, one fp32 scale per (cache row, KV head):
+ *   s = max_d |x[n, h, d]| / 127, codes[n, h, d] = round-half-even(x / s)
+ *   (fp32, IEEE division; a row of zeros gets s = 0 and codes 0).
+ * attn_kv_quantize_int8: x [N, H, D] bf16 (16-byte aligned) -> codes int8
+ *   [N, H, D], scales float [N, H]; D in {128, 256, 512}; no overlaps.
+ * attn_decode_int8: attn_decode over such caches, attending the dequantised
+ *   rows code * s. k_codes [rows, Hkv, Dk] / k_scales [rows, Hkv] hold the
+ *   keys (already rotated before quantising), v_codes / v_scales the values;
+ *   other arguments as for attn_decode. (Dk, Dv) in {(512, 256), (256, 256)};
+ *   bf16 q and o. Reads half the bytes of the bf16 cache.
+ * Workspace: attn_decode_int8_workspace_bytes() bytes (split-K partials).
+ */
+attn_status_t attn_kv_quantize_int8(const void *x, int8_t *codes, float *scales,
+                                    int32_t N, int32_t H, int32_t D,
+                                    attn_dtype_t dtype, void *stream);
+
+size_t attn_decode_int8_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t Dv,
+                                        int32_t max_kv_len, int32_t window);
+
+attn_status_t attn_decode_int8(const void *q, const int8_t *k_codes, const float *k_scales,
+                               const int8_t *v_codes, const float *v_scales,
+                               const int64_t *row_offset, const int32_t *kv_len, void *o,
+                               int32_t B, int32_t Hq, int32_t Hkv, int32_t Dk, int32_t Dv,
+                               int32_t window, float scale, attn_rope_t rope,
+                               int32_t max_kv_len, void *workspace,
+                               size_t workspace_bytes, void *stream);
+
+/*
  * 2-D RoPE for image patches ("Gemma 4: End-to-End Architecture Walkthrough",
  * Phase 1 section 1b; "Gemma 4 Architecture Reference", "Vision Encoder"):
  * each patch vector is split in half and each half is turned like a

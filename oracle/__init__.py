@@ -256,3 +256,41 @@ def verify(q, k_cache, v_cache, row_offset, kv_len, *, window: int, scale: float
                                    theta=theta, nthreads=nthreads))
         out.append(np.stack(rows))
     return np.stack(out) if out else np.zeros((0, n_q, Hq, Dv))
+
+
+# ---- int8 KV cache --------------------------------------------------------
+# The pages name int8 KV caching ("Gemma 4 Technical Report" reader,
+# "Quantization and Efficiency", Table 3 caption) but give no scheme. Reading
+# taken: symmetric codes with one scale per (cache row, KV head),
+# s = max|x| / 127 and code = round-half-even(x / s). The codes are integers
+# that floating point decides, so this function takes those decisions in the
+# kernel's precision (fp32, IEEE division) rather than fp64; everything after
+# dequantisation is fp64.
+
+def kv_quantize_int8(x):
+    """x [N, H, D] (the stored values, e.g. bf16) -> (codes int8 [N, H, D],
+    scales float32 [N, H]). A row of zeros gets scale 0 and codes 0."""
+    x32 = np.asarray(x.float() if hasattr(x, "float") else x, dtype=np.float32)
+    amax = np.abs(x32).max(axis=-1)
+    s = (amax / np.float32(127.0)).astype(np.float32)
+    safe = np.where(s > 0, s, np.float32(1.0)).astype(np.float32)
+    code = np.rint(x32 / safe[..., None]).astype(np.float32)
+    code = np.where(s[..., None] > 0, code, np.float32(0.0))
+    return code.astype(np.int8), s
+
+
+def kv_dequantize_int8(codes, scales) -> np.ndarray:
+    """codes [N, H, D] int8, scales [N, H] -> fp64 values code * scale."""
+    c = np.asarray(codes.cpu() if hasattr(codes, "cpu") else codes).astype(np.float64)
+    s = np.asarray(scales.cpu() if hasattr(scales, "cpu") else scales).astype(np.float64)
+    return c * s[..., None]
+
+
+def decode_int8(q, k_codes, k_scales, v_codes, v_scales, row_offset, kv_len, *,
+                window: int, scale: float, rotary_dims: int = 0, theta: float = 10000.0,
+                seqs=None, nthreads: int | None = None) -> np.ndarray:
+    """Decode over an int8 cache: the plain decode of the dequantised rows."""
+    return decode(q, kv_dequantize_int8(k_codes, k_scales),
+                  kv_dequantize_int8(v_codes, v_scales), row_offset, kv_len, window=window,
+                  scale=scale, rotary_dims=rotary_dims, theta=theta, seqs=seqs,
+                  nthreads=nthreads)

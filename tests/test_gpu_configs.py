@@ -60,7 +60,7 @@ def test_config3_global_prefill():
     torch.cuda.empty_cache()
 
 
-@pytest.mark.parametrize("kind", ["glob", "loc", "glob_kv", "glob_verify"])
+@pytest.mark.parametrize("kind", ["glob", "loc", "glob_kv", "glob_verify", "glob_int8"])
 def test_config4_decode(kind):
     """glob_kv: the global call with keys as values (its key cache passed as
     both caches, Dv = Dk = 512); glob_verify: the global call with its last 2
@@ -76,6 +76,9 @@ def test_config4_decode(kind):
     maxl = int(kvl.max())
     if kind == "glob_verify":
         verify_case(d, q, kc, vc, off, kvl, maxl, cfg["seed"])
+        return
+    if kind == "glob_int8":
+        int8_case(d, q, kc, vc, off, kvl, maxl)
         return
     o = ar.decode(q, kc, vc, off.to(DEV), kvl.to(DEV), window=d.window, scale=d.scale,
                   rotary_dims=d.rotary_dims, theta=d.theta, max_kv_len=maxl)
@@ -115,6 +118,28 @@ def verify_case(d, q1, kc, vc, off, kvl, maxl, seed, n_q=2):
         print(f"config 4 verify n_q={n_q}: seq {b} kv_len={n} max_abs={mx:.3e} "
               f"rel_rms={rel:.3e}", flush=True)
     del kc, vc
+    torch.cuda.empty_cache()
+
+
+def int8_case(d, q, kc, vc, off, kvl, maxl):
+    kq, ks = ar.kv_quantize_int8(kc)
+    vq, vs = ar.kv_quantize_int8(vc)
+    del kc, vc
+    o = ar.decode_int8(q, kq, ks, vq, vs, off.to(DEV), kvl.to(DEV), window=d.window,
+                       scale=d.scale, rotary_dims=d.rotary_dims, theta=d.theta, max_kv_len=maxl)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o.float()).all()
+    lens = kvl.tolist()
+    for b in sorted({int(np.argmin(lens)), int(np.argmax(lens)), 3, 33}):
+        n, a = lens[b], int(off[b])
+        ref = oracle.decode_int8(q[b:b + 1].cpu(), kq[a:a + n].cpu(), ks[a:a + n].cpu(),
+                                 vq[a:a + n].cpu(), vs[a:a + n].cpu(), [0], [n],
+                                 window=d.window, scale=d.scale, rotary_dims=d.rotary_dims,
+                                 theta=d.theta)
+        mx, rel = assert_close(o[b:b + 1], ref, torch.bfloat16, f"config 4 int8 seq {b}")
+        print(f"config 4 int8: seq {b} kv_len={n} max_abs={mx:.3e} rel_rms={rel:.3e}",
+              flush=True)
+    del kq, vq
     torch.cuda.empty_cache()
 
 

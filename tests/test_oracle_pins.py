@@ -505,3 +505,59 @@ def test_rope_2d_scores_depend_only_on_the_offset():
     for dx, dy in [(5, 0), (0, 9), (17, 23)]:
         assert abs(score((3 + dx, 4 + dy), (10 + dx, 6 + dy)) - s0) < 1e-10
     assert abs(score((3, 4), (10, 7)) - s0) > 1e-6
+
+
+# ------------------------------------------------------------ int8 cache ----
+# The scheme (per row and head, symmetric, scale = max|x| / 127) is this
+# build's reading: the pages give none, so the scheme itself is parity unpinned;
+# these pins fix that the codes realise it.
+
+def test_kv_quantize_int8_bounds_and_extremes():
+    x = rng.standard_normal((50, 3, 64)).astype(np.float32) * rng.uniform(0.01, 50, (50, 3, 1)).astype(np.float32)
+    x[7, 1] = 0.0
+    codes, s = oracle.kv_quantize_int8(x)
+    assert codes.dtype == np.int8 and s.dtype == np.float32
+    assert np.abs(codes.astype(int)).max() <= 127
+    amax = np.abs(x).max(-1)
+    np.testing.assert_allclose(s, amax / 127, rtol=1e-7)
+    # the largest magnitude of each (row, head) lands on +-127 with its sign
+    idx = np.abs(x).argmax(-1)
+    top = np.take_along_axis(codes, idx[..., None], -1)[..., 0].astype(int)
+    sign = np.sign(np.take_along_axis(x, idx[..., None], -1)[..., 0]).astype(int)
+    ok = amax > 0
+    assert np.all(top[ok] == 127 * sign[ok])
+    # round to nearest: dequantised error at most half a step (+ fp32 slack)
+    err = np.abs(oracle.kv_dequantize_int8(codes, s) - x)
+    assert np.all(err <= s[..., None].astype(np.float64) * (0.5 + 1e-5))
+    assert np.all(codes[7, 1] == 0) and s[7, 1] == 0
+
+
+def test_kv_quantize_int8_exact_grid_and_ties():
+    """Values already on the grid come back exactly; exact half steps round
+    to even."""
+    s0 = np.float32(0.25)
+    k = np.arange(-127, 128, dtype=np.float32)
+    x = (k * s0).reshape(1, 1, -1)
+    codes, s = oracle.kv_quantize_int8(x)
+    assert s[0, 0] == np.float32(127 * 0.25 / 127)
+    np.testing.assert_array_equal(codes[0, 0].astype(int), k.astype(int))
+    x2 = np.array([[[127.0, 0.5, 1.5, 2.5, -0.5, -1.5]]], dtype=np.float32)  # s = 1
+    c2, _ = oracle.kv_quantize_int8(x2)
+    assert c2[0, 0].tolist() == [127, 0, 2, 2, 0, -2]
+
+
+def test_decode_int8_equals_decode_of_dequantised_cache():
+    lens, Hq, Hkv, D = [5, 40], 4, 2, 16
+    offs = [0, 5]
+    kc = rng.standard_normal((45, Hkv, D))
+    vc = rng.standard_normal((45, Hkv, D))
+    q = rng.standard_normal((2, Hq, D))
+    kq, ks = oracle.kv_quantize_int8(kc)
+    vq, vs = oracle.kv_quantize_int8(vc)
+    a = oracle.decode_int8(q, kq, ks, vq, vs, offs, lens, window=0, scale=0.3)
+    b = oracle.decode(q, kq.astype(np.float64) * ks[..., None], vq.astype(np.float64) * vs[..., None],
+                      offs, lens, window=0, scale=0.3)
+    np.testing.assert_allclose(a, b, rtol=0, atol=1e-14)
+    # and stays within the quantisation error of the unquantised decode
+    c = oracle.decode(q, kc, vc, offs, lens, window=0, scale=0.3)
+    assert np.abs(a - c).max() < 0.05
