@@ -15,14 +15,15 @@
 //    workgroups per CU, so four SIMDs share the conversion work.
 //  * Scales never touch the codes: the K scale multiplies the 16 scores of a
 //    tile after Q.K^T, the V scale multiplies the probabilities before P.V.
-//  * Codes are converted with a +128 bias: code ^ 0x80 is code + 128 as an
+//  * Q.K^T on v_mfma_i32_16x16x64_i8 straight from the K codes in LDS: the
+//    query is split into two int8 parts (a code and the code of its
+//    residual), so two exact int32 products replace any conversion of K.
+//  * V codes are converted once per tile into a bf16 tile in LDS, from which
+//    the transposing reads of the bf16 kernel build the P.V operand. They
+//    are converted with a +128 bias: code ^ 0x80 is code + 128 as an
 //    unsigned byte, which v_cvt_f32_ubyte turns into fp32 in one instruction
-//    and which bf16 holds exactly. The bias is removed afterwards from sums
-//    that are exact or nearly so: 128 * sum(q) per head from each score, and
-//    128 * sum(bf16 P') per head from the P.V accumulator.
-//  * K codes go from LDS straight into registers (8 bytes per lane per MFMA);
-//    V codes are converted once per tile into a bf16 tile in LDS, from which
-//    the transposing reads of the bf16 kernel build the P.V operand.
+//    and which bf16 holds exactly; 128 * sum(bf16 P') per head is removed
+//    from the P.V accumulator afterwards.
 #include <algorithm>
 
 #include "attn_common.h"
@@ -82,13 +83,7 @@ __device__ __forceinline__ f32x4 ubytes(uint32_t w) {
                (float)(w >> 24)};
 }
 
-// 8 codes (two dwords) -> bf16x8 of code + 128 (exact).
-__device__ __forceinline__ bf16x8 codes8_to_bf16(u32x2 w) {
-  const f32x4 a = ubytes(w[0]), b = ubytes(w[1]);
-  const u32x4 p = {pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]), pack_bf16x2(b[0], b[1]),
-                   pack_bf16x2(b[2], b[3])};
-  return __builtin_bit_cast(bf16x8, p);
-}
+typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 // Stage layout (bytes): K codes [16][DK] (16-byte chunks swizzled by row),
 // V codes [16][DV], then two 256-byte blocks of scales (lanes 0-15 of each
@@ -174,9 +169,15 @@ __global__ __launch_bounds__(64, 1) void decode_i8_kernel(DecodeArgs a, int ch, 
 #pragma unroll
   for (int i = 0; i < C::AHEAD; ++i) dma_tile(i, i);
 
-  // ---- rotated queries (bf16) as the B operand, and their per-head sums ----
-  bf16x8 qf[DK / 32];
-  float qsum = 0.f;
+  // ---- rotated queries as two int8 B operands -----------------------------
+  // Q.K^T runs on v_mfma_i32_16x16x64_i8 straight from the K codes. The bf16
+  // query of head `col` (lane holds dims 64s + 16g .. +15) is split as
+  // q = s1 q1 + s2 q2 + e: q1 = rint(q / s1) with s1 = max|q| / 127, q2 the
+  // same for the residual, so |e| <= max|q| / (4 * 127^2) -- far below the
+  // bf16 rounding the query already carries. Both int32 dot products are
+  // exact; the score is ks * (s1 S1 + s2 S2).
+  i32x4 q1[DK / 64], q2[DK / 64];
+  float qs1, qs2;
   {
     const int qpos = kv_len - 1;
     const double l2t = log2(a.theta);
@@ -191,26 +192,54 @@ __global__ __launch_bounds__(64, 1) void decode_i8_kernel(DecodeArgs a, int ch, 
     const bool hv = col < G;
     const uint16_t* qrow =
         (const uint16_t*)a.q + ((int64_t)b * a.Hq + kvh * G + (hv ? col : 0)) * DK;
+    float qv[DK / 4];  // this lane's 16 dims per 64-dim step, as fp32
+    float amax = 0.f;
 #pragma unroll
-    for (int s = 0; s < DK / 32; ++s) {
-      const int d0 = 32 * s + 8 * g;
-      u32x4 w = *(const u32x4*)(qrow + d0);
+    for (int s = 0; s < DK / 64; ++s) {
+      const int d0 = 64 * s + 16 * g;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        if (d0 / 2 + e < a.rot_pairs) {
-          const float2 t = cs_tab[d0 / 2 + e];
-          const float x0 = bf16_lo(w[e]), x1 = bf16_hi(w[e]);
-          w[e] = pack_bf16x2(x0 * t.x - x1 * t.y, x0 * t.y + x1 * t.x);
+      for (int h = 0; h < 2; ++h) {
+        u32x4 w = *(const u32x4*)(qrow + d0 + 8 * h);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int pr = d0 / 2 + 4 * h + e;
+          if (pr < a.rot_pairs) {
+            const float2 t = cs_tab[pr];
+            const float x0 = bf16_lo(w[e]), x1 = bf16_hi(w[e]);
+            w[e] = pack_bf16x2(x0 * t.x - x1 * t.y, x0 * t.y + x1 * t.x);
+          }
+          const float x0 = hv ? bf16_lo(w[e]) : 0.f, x1 = hv ? bf16_hi(w[e]) : 0.f;
+          qv[16 * s + 8 * h + 2 * e] = x0;
+          qv[16 * s + 8 * h + 2 * e + 1] = x1;
+          amax = fmaxf(amax, fmaxf(fabsf(x0), fabsf(x1)));
         }
       }
-      if (!hv) w = u32x4{0, 0, 0, 0};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) qsum += bf16_lo(w[e]) + bf16_hi(w[e]);
-      qf[s] = __builtin_bit_cast(bf16x8, w);
     }
-    qsum = xor32_16_sum(qsum);  // the head's sum over all DK dims
+    amax = xor32_16_max(amax);
+    qs1 = amax / 127.f;
+    const float r1 = amax > 0.f ? 127.f / amax : 0.f;
+    float rmax = 0.f;
+#pragma unroll
+    for (int i = 0; i < DK / 4; ++i) {
+      const float c = rintf(qv[i] * r1);
+      qv[i] = qv[i] - qs1 * c;  // residual
+      rmax = fmaxf(rmax, fabsf(qv[i]));
+      const int s = i / 16, e = i % 16;
+      const uint32_t byte = (uint32_t)(int)c & 0xffu;
+      if (e % 4 == 0) q1[s][e / 4] = (int)byte;
+      else q1[s][e / 4] |= (int)(byte << (8 * (e % 4)));
+    }
+    rmax = xor32_16_max(rmax);
+    qs2 = rmax / 127.f;
+    const float r2 = rmax > 0.f ? 127.f / rmax : 0.f;
+#pragma unroll
+    for (int i = 0; i < DK / 4; ++i) {
+      const int s = i / 16, e = i % 16;
+      const uint32_t byte = (uint32_t)(int)rintf(qv[i] * r2) & 0xffu;
+      if (e % 4 == 0) q2[s][e / 4] = (int)byte;
+      else q2[s][e / 4] |= (int)(byte << (8 * (e % 4)));
+    }
   }
-  const float qbias = 128.f * qsum;
   wait_vm<(C::AHEAD - 1) * C::N_DMA>();
   lds_barrier();
 
@@ -220,8 +249,8 @@ __global__ __launch_bounds__(64, 1) void decode_i8_kernel(DecodeArgs a, int ch, 
 #pragma unroll
   for (int d = 0; d < DV / 16; ++d) oacc[d] = f32x4{};
 
-  // K codes: row col, dims 32s + 8g .. +7 = chunk 2s + (g >> 1), half g & 1.
-  const int krd = col * DK + 8 * (g & 1);
+  // K codes: row col, dims 64s + 16g .. +15 = chunk 4s + g.
+  const int krd = col * DK;
   // V^T from the bf16 tile (layout of the bf16 kernel's V rows, one wave).
   int vo[8];
   {
@@ -251,18 +280,20 @@ __global__ __launch_bounds__(64, 1) void decode_i8_kernel(DecodeArgs a, int ch, 
       *(u32x4*)(rowp + (((2 * c) ^ (r & 15)) << 4)) = lo4;
       *(u32x4*)(rowp + (((2 * c + 1) ^ (r & 15)) << 4)) = hi4;
     }
-    // S^T[16 keys][16 heads] over code + 128, then the exact corrections.
-    f32x4 s = f32x4{};
+    // S^T[16 keys][16 heads] = ks * (s1 K.q1 + s2 K.q2), int32 dot products.
+    i32x4 S1 = i32x4{}, S2 = i32x4{};
 #pragma unroll
-    for (int k = 0; k < DK / 32; ++k) {
-      const int c = 2 * k + (g >> 1);
-      const u32x2 w = *(const __attribute__((address_space(3))) u32x2*)(st + krd + ((c ^ col) << 4));
-      s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(codes8_to_bf16(w), qf[k], s, 0, 0, 0);
+    for (int k = 0; k < DK / 64; ++k) {
+      const i32x4 kc = *(const __attribute__((address_space(3))) i32x4*)(
+          st + krd + (((4 * k + g) ^ col) << 4));
+      S1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(kc, q1[k], S1, 0, 0, 0);
+      S2 = __builtin_amdgcn_mfma_i32_16x16x64_i8(kc, q2[k], S2, 0, 0, 0);
     }
     const f32x4 ks = *(const __attribute__((address_space(3))) f32x4*)(st + C::KT + C::VT + 16 * g);
     const f32x4 vs = *(const __attribute__((address_space(3))) f32x4*)(st + C::KT + C::VT + 256 + 16 * g);
+    f32x4 s;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) s[i] = (s[i] - qbias) * ks[i];
+    for (int i = 0; i < 4; ++i) s[i] = (qs1 * (float)S1[i] + qs2 * (float)S2[i]) * ks[i];
     const int key0 = c0 + t * 16 + 4 * g;
     if (c0 + (t + 1) * 16 > c1) {
 #pragma unroll
