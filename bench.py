@@ -463,7 +463,11 @@ def main():
                                      "GB/s": round(rr["v_bytes"] / (rr["v_ms"] * 1e-3) / 1e9, 1),
                                      "ms": round(rr["v_ms"], 4), "bytes": rr["v_bytes"],
                                      "what": f"global call with {rr['v_nq']} new tokens per "
-                                             "sequence (speculative-decoding verify)"},
+                                             "sequence (speculative-decoding verify)",
+                                     "roofline": roofline(
+                                         "hbm", rr["v_bytes"] / (rr["v_ms"] * 1e-3) / 1e9,
+                                         PEAK_HBM_GBS, "GB/s",
+                                         _traffic("decode_ring", "verify_global_decode"))},
                                  "int8_cache_call": {
                                      "GB/s": round(rr["i8_bytes"] / (rr["i8_ms"] * 1e-3) / 1e9, 1),
                                      "ms": round(rr["i8_ms"], 4), "bytes": rr["i8_bytes"],
