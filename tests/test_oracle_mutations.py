@@ -51,3 +51,40 @@ def test_pins_catch_planted_mistake(name, tmp_path):
                         os.path.join(ROOT, "tests", "test_oracle_pins.py")],
                        capture_output=True, text=True, cwd=ROOT, env=env, timeout=600)
     assert r.returncode != 0, f"pins missed the planted mistake {name}:\n{r.stdout[-2000:]}"
+
+
+PY_SRC = os.path.join(ROOT, "oracle", "__init__.py")
+# Mistakes planted in the oracle's Python layer (K = V, verify, int8, 2-D RoPE).
+PY_MUTATIONS = {
+    "kv_shared_unrotated_values": ("return prefill(q, kr, kr,", "return prefill(q, kr, k,"),
+    "verify_not_causal_in_draft": ("m = n - n_q + j + 1", "m = n"),
+    "int8_round_half_away": ("code = np.rint(x32 / safe[..., None]).astype(np.float32)",
+                             "code = np.trunc(x32 / safe[..., None] + np.copysign(np.float32(0.5), x32)).astype(np.float32)"),
+    "int8_scale_128": ("s = (amax / np.float32(127.0)).astype(np.float32)",
+                       "s = (amax / np.float32(128.0)).astype(np.float32)"),
+    "rope_2d_coordinates_swapped": ("first = rope(np.ascontiguousarray(x[:, :, :h]), pxy[:, 0],",
+                                    "first = rope(np.ascontiguousarray(x[:, :, :h]), pxy[:, 1],"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(PY_MUTATIONS))
+def test_pins_catch_planted_python_mistake(name, tmp_path):
+    old, new = PY_MUTATIONS[name]
+    src = open(PY_SRC).read()
+    assert src.count(old) == 1, f"mutation site for {name} not found in the oracle"
+    pkg = tmp_path / "oracle"
+    pkg.mkdir()
+    (pkg / "__init__.py").write_text(src.replace(old, new))
+    lib = os.path.join(ROOT, "oracle", "liboracle.so")
+    env = dict(os.environ, ATTN_ORACLE_LIB=lib, OMP_NUM_THREADS="2")
+    # import the mutated copy first, so the pins (and conftest's path setup)
+    # find it already loaded
+    code = ("import sys; sys.path.insert(0, sys.argv[1]); import oracle; "
+            "assert oracle.__file__.startswith(sys.argv[1]), oracle.__file__; "
+            "import pytest; sys.exit(pytest.main(sys.argv[2:]))")
+    r = subprocess.run([sys.executable, "-c", code, str(tmp_path), "-x", "-q", "-p",
+                        "no:cacheprovider", "-k", "kv_shared or verify or int8 or rope_2d",
+                        os.path.join(ROOT, "tests", "test_oracle_pins.py")],
+                       capture_output=True, text=True, cwd=ROOT, env=env, timeout=600)
+    assert "AssertionError: /" not in r.stderr, r.stderr[-2000:]
+    assert r.returncode == 1, f"pins missed the planted mistake {name}:\n{r.stdout[-2000:]}"
