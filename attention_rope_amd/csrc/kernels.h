@@ -32,6 +32,10 @@ struct PrefillArgs {
   int rot_pairs;           // rotary pairs (0: none)
   int rope_q, rope_k;      // apply rotation to q / k
   float scale;
+  // Element strides of v and o per token and per head (0: dense, Hkv * Dv
+  // and Dv for v, Hq * Dv and Dv for o); the 512-dim value path runs as two
+  // 256-dim halves over strided views.
+  int64_t v_tok = 0, v_head = 0, o_tok = 0, o_head = 0;
 };
 
 // MFMA flash kernel (bf16). Returns hipErrorNotSupported for shapes it has no

@@ -595,7 +595,7 @@ hipError_t dispatch_g(const PrefillArgs& a, hipStream_t st) {
 
 bool prefill_mfma_supported(int Dk, int Dv, int G, float scale, int rotary_dims) {
   const bool shape = (Dk == 128 && Dv == 128) || (Dk == 256 && Dv == 256) ||
-                     (Dk == 512 && Dv == 256);
+                     (Dk == 512 && (Dv == 256 || Dv == 512));
   const bool rot = rotary_dims == 0 || rotary_dims == Dk / 4 || rotary_dims == Dk;
   return shape && rot && (G == 1 || G == 2 || G == 4 || G == 8) && scale >= 0.f;
 }
@@ -610,6 +610,25 @@ hipError_t launch_prefill_mfma(const PrefillArgs& a, hipStream_t st) {
   if (per_b >= (int64_t)1 << 31 || (int64_t)a.T * a.rot_pairs * 8 >= (int64_t)1 << 31)
     return hipErrorNotSupported;
   if (a.Dk == 512 && a.Dv == 256) return launch_prefill_mfma1w(a, st);
+  if (a.Dk == 512 && a.Dv == 512) {
+    // 512-dim values (a K = V layer, or separate ones) as two passes over
+    // 256-dim halves of v and o: the O accumulators of 512 dims would not fit
+    // beside the operands. Each pass recomputes Q.K^T (3/2 of the useful
+    // FLOPs in all).
+    PrefillArgs h = a;
+    h.Dv = 256;
+    h.v_tok = (int64_t)a.Hkv * 512;
+    h.v_head = 512;
+    h.o_tok = (int64_t)a.Hq * 512;
+    h.o_head = 512;
+    for (int half = 0; half < 2; ++half) {
+      h.v = static_cast<const uint16_t*>(a.v) + 256 * half;
+      h.o = static_cast<uint16_t*>(a.o) + 256 * half;
+      const hipError_t e = launch_prefill_mfma1w(h, st);
+      if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+  }
   if (a.Dk == 256 && a.Dv == 256) return dispatch_g<256, 256>(a, st);
   if (a.Dk == 128 && a.Dv == 128) return dispatch_g<128, 128>(a, st);
   return hipErrorNotSupported;

@@ -168,13 +168,15 @@ __global__ __launch_bounds__(NT, 1) void prefill_mfma1w_kernel(PrefillArgs a, in
   const int n_tiles = kb_hi - kb_lo;
 
   // ---- DMA sources -------------------------------------------------------------
-  const int krow = a.Hkv * DK * 2, vrow = a.Hkv * DV * 2;  // bytes per token
+  const int64_t v_tok = a.v_tok ? a.v_tok : (int64_t)a.Hkv * DV;
+  const int64_t v_head = a.v_head ? a.v_head : DV;
+  const int krow = a.Hkv * DK * 2, vrow = (int)(v_tok * 2);  // bytes per token
   const bool rot_q = RCH > 0 && a.rope_q;
   const bool krot_ws = RCH > 0 && a.rope_k;  // rotated dims from the workspace
   const int rrow = krot_ws ? a.Hkv * RCH * 16 : krow;
   const u32x4 kdesc = buffer_desc((const char*)a.k + ((int64_t)b * T * a.Hkv + kvh) * DK * 2,
                                   (T - 1) * krow + DK * 2);
-  const u32x4 vdesc = buffer_desc((const char*)a.v + ((int64_t)b * T * a.Hkv + kvh) * DV * 2,
+  const u32x4 vdesc = buffer_desc((const char*)a.v + ((int64_t)b * T * v_tok + kvh * v_head) * 2,
                                   (T - 1) * vrow + DV * 2);
   const u32x4 rdesc =
       krot_ws ? buffer_desc((const char*)a.k_rot + ((int64_t)b * T * a.Hkv + kvh) * RCH * 16,
@@ -575,6 +577,8 @@ __global__ __launch_bounds__(NT, 1) void prefill_mfma1w_kernel(PrefillArgs a, in
                                                     8 * h) = u32x2{w0, w1};
       }
   }
+  const int64_t o_tok = a.o_tok ? a.o_tok : (int64_t)a.Hq * DV;
+  const int64_t o_head = a.o_head ? a.o_head : DV;
   // A wave reads back only what it wrote; its LDS operations run in order.
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   {
@@ -587,7 +591,7 @@ __global__ __launch_bounds__(NT, 1) void prefill_mfma1w_kernel(PrefillArgs a, in
           ost + row * ORB + ((c ^ (row & VCM)) << 4));
       const int p = wlo + row % C::PPW;
       const int hd = kvh * G + hg * C::HW + row / C::PPW;
-      if (p < T) *(u32x4*)((uint16_t*)a.o + (((int64_t)b * T + p) * a.Hq + hd) * DV + 8 * c) = val;
+      if (p < T) *(u32x4*)((uint16_t*)a.o + ((int64_t)b * T + p) * o_tok + hd * o_head + 8 * c) = val;
     }
   }
 }

@@ -143,6 +143,38 @@ def bench_prefill(ar, torch, inputs, cfg, steps, warmup):
                 kern_ms=kern_ms, span_ms=span_ms, wall_s=wall, tensors=(q, k, v, o))
 
 
+def bench_prefill_kv_shared(ar, torch, inputs, cfg, steps, warmup):
+    """The global prefill shape as a K = V layer: keys turned once by
+    prope_apply and passed as both k and v (RoPE on q only), 512-dim values.
+    Times the attention call (two passes over 256-dim value halves)."""
+    c = cfg["case"]
+    q, k, _ = inputs.prefill_inputs(c, cfg["seed"], device="cuda")
+    pos = torch.arange(c.T, dtype=torch.int32, device="cuda").repeat(c.B)
+    kr = ar.prope(k.reshape(c.B * c.T, c.Hkv, c.Dk), pos, rotary_dims=c.rotary_dims,
+                  theta=c.theta).reshape(c.B, c.T, c.Hkv, c.Dk)
+    o = torch.empty((c.B, c.T, c.Hq, c.Dk), dtype=c.dtype, device="cuda")
+    tab = ar.rope_table(c.T, head_dim=c.Dk, rotary_dims=c.rotary_dims, theta=c.theta,
+                        pos0=c.pos0)
+
+    def call():
+        ar.prefill(q, kr, kr, window=c.window, scale=c.scale, rotary_dims=c.rotary_dims,
+                   theta=c.theta, pos0=c.pos0, out=o, table=tab, rope_mask=ar.ROPE_Q)
+
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    t = Timer(torch, steps)
+    for i in range(steps):
+        t.mark(i, 0)
+        call()
+        t.mark(i, 1)
+    torch.cuda.synchronize()
+    ms = sum(t.ms(i, 0, 1) for i in range(steps)) / steps
+    flops = float(c.B * c.Hq * pairs(c.T, c.window) * 2 * (c.Dk + c.Dk))
+    del q, k, kr, o
+    return dict(flops=flops, ms=ms)
+
+
 def bench_decode(ar, torch, inputs, cfg, steps, warmup):
     seed = cfg["seed"]
     calls = []
@@ -439,6 +471,13 @@ def main():
                                                            _traffic("prefill_mfma1w", "global_prefill")),
                                                   kernel="prefill_mfma1w_kernel")}
             del rr
+            torch.cuda.empty_cache()
+            kv = bench_prefill_kv_shared(ar, torch, inputs, sc, max(2, args.steps // 8), 1)
+            secondary[str(s)]["keys_as_values"] = {
+                "TFLOP/s": round(kv["flops"] / kv["ms"] / 1e9, 3), "ms": round(kv["ms"], 4),
+                "what": "same shape as a K = V layer: rotated keys as both k and v, 512-dim "
+                        "values, attention call only (two passes over 256-dim value halves; "
+                        "TFLOP/s counts the K = V layer's algorithmic FLOPs)"}
         elif sc["kind"] == "decode":
             rr = bench_decode(ar, torch, inputs, sc, max(3, args.steps // 4), 1)
             gbs = rr["bytes"] / (rr["step_ms"] * 1e-3) / 1e9

@@ -94,9 +94,13 @@ attn_status_t attn_rope_table(void *table, int32_t T, int32_t pos0, int32_t head
  *   scale: finite (1/sqrt(Dk) in the usual model).
  * Supported: B, T >= 0 (an empty problem is a no-op), Hq % Hkv == 0,
  *   Dk, Dv even and <= 512. bf16 with (Dk, Dv) in {(128,128), (256,256),
- *   (512,256)}, Hq/Hkv in {1, 2, 4, 8}, scale >= 0 and rotary_dims a multiple
- *   of 8 in {0, Dk/4, Dk} runs the MFMA flash kernel; every other supported
- *   case runs a slower general kernel with the same results.
+ *   (512,256), (512,512)}, Hq/Hkv in {1, 2, 4, 8}, scale >= 0 and
+ *   rotary_dims a multiple of 8 in {0, Dk/4, Dk} runs the MFMA flash kernel
+ *   ((512,512) as two passes over 256-dim halves of v and o); every other
+ *   supported case runs a slower general kernel with the same results.
+ *   Keys as values (K = V on a global layer): turn k once with prope_apply,
+ *   pass it as both k and v with rope_mask = ATTN_ROPE_Q; the values are
+ *   then the rotated keys, as a decode over that cache sees them.
  * Workspace: attn_prefill_workspace_bytes() bytes of device memory (0 when no
  *   workspace is needed, then workspace may be NULL). The bf16 path turns the
  *   rotary dims of every key once into it before attending; contents are

@@ -45,6 +45,9 @@ MFMA_CASES = [
     (1, 300, 32, 4, 512, 256, 0, 128, 1e6),
     (2, 45, 16, 2, 512, 256, 0, 128, 1e6),
     (1, 129, 8, 1, 512, 256, 100, 512, 1e6),
+    # 512-dim values: two passes over 256-dim halves of v and o
+    (1, 300, 32, 4, 512, 512, 0, 128, 1e6),
+    (2, 130, 16, 2, 512, 512, 100, 512, 1e6),
     # D=128 heads, every GQA ratio the kernel instantiates
     (1, 130, 8, 1, 128, 128, 0, 32, 1e6),
     (1, 65, 4, 4, 128, 128, 17, 0, 1e4),
