@@ -95,3 +95,20 @@ def test_decode_int8_close_to_bf16_decode(gpu_lib):
                             theta=1e6, max_kv_len=4000)
     torch.cuda.synchronize()
     assert (a.float() - b.float()).abs().max().item() < 0.05
+
+
+def test_decode_int8_empty_and_out_of_range(gpu_lib):
+    """kv_len 0 gives zeros, kv_len past max_kv_len poisons the row (NaN), with
+    one chunk (window 100) and with several (global, 4096-row chunks)."""
+    for W, Hq, Hkv, D in [(100, 16, 8, 256), (0, 32, 4, 512)]:
+        c = inputs.DecodeCase(3, Hq, Hkv, D, 256, window=W, rotary_dims=64, theta=1e4,
+                              len_lo=1, len_hi=1)
+        kvl = torch.tensor([0, 50, 9000], dtype=torch.int32)
+        print(f"int8 edge W={W} D={D}", flush=True)
+        q, kq, ks, vq, vs, off, kvl = _int8_caches(gpu_lib, c, 8, kvl, poison=False)
+        o = gpu_lib.decode_int8(q, kq, ks, vq, vs, off.to(DEV), kvl.to(DEV), window=W,
+                                rotary_dims=64, theta=1e4, max_kv_len=1000)
+        torch.cuda.synchronize()
+        assert torch.all(o[0] == 0)
+        assert torch.isfinite(o[1].float()).all()
+        assert torch.isnan(o[2].float()).all()
