@@ -46,6 +46,9 @@ bool prefill_mfma_supported(int Dk, int Dv, int G, float scale, int rotary_dims)
 // The variant for 512-dim keys (called by launch_prefill_mfma): 32-row
 // waves, one per SIMD, accumulators in AGPRs (prefill_mfma1w.hip).
 hipError_t launch_prefill_mfma1w(const PrefillArgs& a, hipStream_t st);
+// The local-layer shape (256-dim heads, G = 2) with 4-wave workgroups, two
+// per CU (prefill_mfma2g.hip); called by launch_prefill_mfma.
+hipError_t launch_prefill_mfma2g(const PrefillArgs& a, hipStream_t st);
 
 // General kernel: any supported shape, fp32 or bf16.
 hipError_t launch_prefill_general(const PrefillArgs& a, bool bf16, hipStream_t st);

@@ -13,7 +13,9 @@
 // before the P.V product, and everything accumulates in fp32.
 //
 // Used for heads up to 256 dims; the 512-dim keys of the global layers go to
-// the one-wave-per-SIMD kernel in prefill_mfma1w.hip.
+// the one-wave-per-SIMD kernel in prefill_mfma1w.hip, and the local layers'
+// shape (256-dim heads, 2 query heads per KV head) to the two-workgroups-per-
+// CU variant of this kernel in prefill_mfma2g.hip.
 //
 // Design for CDNA4:
 //  * A workgroup of 8 waves (two per SIMD) owns one (batch, KV head) and PW
@@ -54,6 +56,7 @@
 
 #include "attn_common.h"
 #include "kernels.h"
+#include "prefill_common.h"
 
 namespace attn {
 namespace {
@@ -107,42 +110,7 @@ struct Cfg {
   static_assert(VC >= 16, "V rows swizzle over 16 chunk groups");
 };
 
-// XOR swizzle of 16-byte chunks inside a region row of `width` chunks. The
-// mask P-1 uses the largest power of two P <= 16 dividing the width, so the
-// swizzled index stays inside the row.
-template <int width>
-struct Swz {
-  static constexpr int P = (width & 15) == 0 ? 16 : (width & 7) == 0 ? 8 : (width & 3) == 0 ? 4
-                           : (width & 1) == 0 ? 2 : 1;
-  static constexpr int M = P - 1;
-  static constexpr int HB = P >= 2 ? P / 2 : 1;  // distinct read bases (below)
-};
-template <int width>
-__device__ __forceinline__ int kswz(int r, int c) {
-  return c ^ (r & Swz<width>::M);
-}
-// V rows: chunk c of key row r sits at c ^ 4(r & 3). A transposing read of
-// the V^T operand takes 4 consecutive keys x 4 consecutive chunks (one
-// 32-dim tile) per 32 lanes; this swizzle puts the 16 pieces in 16 distinct
-// bank groups (an XOR by r & 15 would keep them in 4).
-__device__ __forceinline__ int vswz(int r, int c) { return c ^ ((r & 3) << 2); }
-
-__device__ __forceinline__ uint32_t rot_pair(uint32_t w, float c, float s) {
-  const float x0 = bf16_lo(w), x1 = bf16_hi(w);
-  return pack_bf16x2(x0 * c - x1 * s, x0 * s + x1 * c);
-}
-
-// Rotate 8 bf16 (4 pairs) with (c0 s0 c1 s1) (c2 s2 c3 s3).
-__device__ __forceinline__ u32x4 rotate4(u32x4 w, f32x4 t0, f32x4 t1) {
-  u32x4 r;
-  r[0] = rot_pair(w[0], t0[0], t0[1]);
-  r[1] = rot_pair(w[1], t0[2], t0[3]);
-  r[2] = rot_pair(w[2], t1[0], t1[1]);
-  r[3] = rot_pair(w[3], t1[2], t1[3]);
-  return r;
-}
-
-__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+using namespace prefill;
 
 template <int DK, int DV, int G, int RCH>
 __global__ __launch_bounds__((Cfg<DK, DV, G, RCH>::NT), 1) void prefill_mfma_kernel(
@@ -629,6 +597,7 @@ hipError_t launch_prefill_mfma(const PrefillArgs& a, hipStream_t st) {
     }
     return hipSuccess;
   }
+  if (a.Dk == 256 && a.Dv == 256 && a.Hq / a.Hkv == 2) return launch_prefill_mfma2g(a, st);
   if (a.Dk == 256 && a.Dv == 256) return dispatch_g<256, 256>(a, st);
   if (a.Dk == 128 && a.Dv == 128) return dispatch_g<128, 128>(a, st);
   return hipErrorNotSupported;
