@@ -256,6 +256,7 @@ attn_status_t attn_prefill(const void* q, const void* k, const void* v, void* o,
   a.rope_k = rot && (rope_mask & ATTN_ROPE_K);
   a.scale = scale;
   a.rope_tab = rot ? reinterpret_cast<const float2*>(rope_table) : nullptr;
+  a.rope_rho = rot ? std::pow(rope.theta, -2.0 / (double)Dk) : 1.0;
   if (dtype == ATTN_BF16 &&
       attn::prefill_mfma_supported(Dk, Dv, Hq / Hkv, scale, rot ? rope.rotary_dims : 0)) {
     if (a.rope_k) {

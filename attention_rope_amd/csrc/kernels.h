@@ -36,6 +36,10 @@ struct PrefillArgs {
   // and Dv for v, Hq * Dv and Dv for o); the 512-dim value path runs as two
   // 256-dim halves over strided views.
   int64_t v_tok = 0, v_head = 0, o_tok = 0, o_head = 0;
+  // theta^(-2/Dk): ratio of successive rotary frequencies of the table (row t
+  // of rope_tab turns pair p by (pos0 + t) * rope_rho^p). Kernels that turn a
+  // table row further by a small position offset use it.
+  double rope_rho = 1.0;
 };
 
 // MFMA flash kernel (bf16). Returns hipErrorNotSupported for shapes it has no

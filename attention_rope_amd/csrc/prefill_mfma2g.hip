@@ -164,10 +164,21 @@ __global__ __launch_bounds__((Cfg2<DK, DV, G, RCH>::NT), 2) void prefill_mfma2g_
 
   bf16x8 qf[DK / 16];
   {
-    const int tab_row = a.rot_pairs * 8;
-    const __amdgpu_buffer_rsrc_t tres = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)a.rope_tab, (short)0, rot_q ? T * tab_row : 0, 0x00020000);
+    const int tab_row = a.rot_pairs * 8;  // bytes per table row (<= 1 KB: rot_pairs <= 128)
     const int prow = valid ? pos : T - 1;
+    // Q's rotation by angle addition: the table row of the wave's first
+    // position (one DMA of 1 KB into this wave's slot of the second V stage,
+    // which iteration 0 refills from this same wave), turned further by the
+    // lane's offset d = prow - base (0..31) at the pair's frequency rho^i,
+    // i = 8u + 4h + j. The small angles d * rho^i need no memory: they go
+    // through the sine and cosine units (in revolutions) while Q is in flight.
+    // The frequencies come from an fp64 product chain; d = 0 keeps the table
+    // values.
+    const int base = min(wlo, T - 1);
+    const int tslot = C::V_BASE + C::VT_BYTES + wave * 1024;
+    if (rot_q)
+      dma16(buffer_desc(a.rope_tab, (uint32_t)(T * tab_row)), lds_addr(lds) + tslot,
+            base * tab_row + lane * 16);
     const uint16_t* qrow =
         (const uint16_t*)a.q + (((int64_t)b * T + prow) * a.Hq + head) * DK + 8 * h;
     u32x4 qw[DK / 16];
@@ -175,15 +186,36 @@ __global__ __launch_bounds__((Cfg2<DK, DV, G, RCH>::NT), 2) void prefill_mfma2g_
     for (int s = 0; s < DK / 16; ++s) qw[s] = *(const u32x4*)(qrow + 16 * s);
     if (rot_q) {
       constexpr int NR = RCH / 2 > 0 ? RCH / 2 : 1;
-      f32x4 t[NR][2];
+      float dcs[NR][8];  // (cos, sin) of d * rho^i, pairs j = 0..3 of chunk u
+      const double rho = a.rope_rho, rho2 = rho * rho, rho4 = rho2 * rho2, rho5 = rho4 * rho;
+      const double turns = (double)(prow - base) * 0.15915494309189535;  // d / (2 pi)
+      double w = h ? rho4 : 1.0;
+#pragma unroll
+      for (int u = 0; u < RCH / 2; ++u)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float x = __builtin_amdgcn_fractf((float)(turns * w));
+          dcs[u][2 * j] = __builtin_amdgcn_cosf(x);
+          dcs[u][2 * j + 1] = __builtin_amdgcn_sinf(x);
+          w *= (j == 3) ? rho5 : rho;
+        }
+      __builtin_amdgcn_sched_barrier(0);
+      wait_vm<0>();  // Q and the table row landed (and the K/V DMAs before them)
+      const __attribute__((address_space(3))) f32x4* trow =
+          (const __attribute__((address_space(3))) f32x4*)((const lds_u8*)lds + tslot);
 #pragma unroll
       for (int u = 0; u < RCH / 2; ++u) {
-        const int off = prow * tab_row + (16 * u + 8 * h) * 4;
-        t[u][0] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(tres, off, 0, 0));
-        t[u][1] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(tres, off + 16, 0, 0));
-      }
+        const f32x4 t0 = trow[4 * u + 2 * h], t1 = trow[4 * u + 2 * h + 1];
+        float cs[8];
 #pragma unroll
-      for (int u = 0; u < RCH / 2; ++u) qw[u] = rotate4(qw[u], t[u][0], t[u][1]);
+        for (int j = 0; j < 4; ++j) {
+          const float cb = (j < 2 ? t0 : t1)[2 * (j % 2)], sb = (j < 2 ? t0 : t1)[2 * (j % 2) + 1];
+          const float cd = dcs[u][2 * j], sd = dcs[u][2 * j + 1];
+          cs[2 * j] = cb * cd - sb * sd;
+          cs[2 * j + 1] = sb * cd + cb * sd;
+        }
+        qw[u] = rotate4(qw[u], f32x4{cs[0], cs[1], cs[2], cs[3]}, f32x4{cs[4], cs[5], cs[6], cs[7]});
+      }
     }
 #pragma unroll
     for (int s = 0; s < DK / 16; ++s) {

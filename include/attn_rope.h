@@ -86,9 +86,11 @@ attn_status_t attn_rope_table(void *table, int32_t T, int32_t pos0, int32_t head
  *   o [B, T, Hq, Dv] output; must not overlap q, k or v.
  *   Token t's rotation comes from row t of rope_table (made by attn_rope_table
  *   for the same T, head_dim = Dk and rope settings; the caller keeps them
- *   consistent). rope_mask: ATTN_ROPE_Q | ATTN_ROPE_K selects which of q and k
- *   are rotated; with rope.rotary_dims == 0 or rope_mask == 0 nothing turns
- *   and rope_table may be NULL.
+ *   consistent: some kernels read one row per 32 tokens and turn it further
+ *   by the token's offset at the frequencies theta^(-2p/Dk), so the rows must
+ *   be those of consecutive positions). rope_mask: ATTN_ROPE_Q | ATTN_ROPE_K
+ *   selects which of q and k are rotated; with rope.rotary_dims == 0 or
+ *   rope_mask == 0 nothing turns and rope_table may be NULL.
  *   window: <= 0 or >= T gives full causal attention; otherwise query i sees
  *   keys j with i - window < j <= i (the window includes the query itself).
  *   scale: finite (1/sqrt(Dk) in the usual model).

@@ -94,6 +94,16 @@ def test_prefill_pos0(gpu_lib, pos0):
     run_case(gpu_lib, 1, 77, 8, 1, 128, 128, 0, 32, 1e6, F32, pos0=pos0)
 
 
+@pytest.mark.parametrize("R", [64, 256])
+@pytest.mark.parametrize("pos0", [1, 1000, 131000])
+def test_prefill_local_pos0(gpu_lib, pos0, R):
+    # The local-layer kernel (256-dim heads, 2 q heads per KV head) turns q by
+    # the table row of its wave's first position and then by the lane's offset
+    # from it, so a table for positions pos0.. must still match the oracle.
+    run_case(gpu_lib, 1, 300, 16, 8, 256, 256, 128, R, 1e4, BF, rope_mask=1, pos0=pos0)
+    run_case(gpu_lib, 2, 97, 4, 2, 256, 256, 0, R, 1e6, BF, rope_mask=3, pos0=pos0)
+
+
 def test_prefill_uniform_values(gpu_lib):
     run_case(gpu_lib, 1, 200, 32, 4, 512, 256, 0, 128, 1e6, BF, v_dist="uniform")
 
