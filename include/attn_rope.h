@@ -142,6 +142,12 @@ attn_status_t attn_prefill(const void *q, const void *k, const void *v, void *o,
  *     [kv_len - window, kv_len) are read (rows before are never touched, so
  *     they may hold anything).
  *   o [B, Hq, Dv] output.
+ *   Drafter cross-attention (an MTP drafter attends the target model's cache,
+ *     "Gemma 4: End-to-End Architecture Walkthrough", Phase 4): for the
+ *     drafter's k-th proposal at position L + k over a target cache of L
+ *     rows, turn q there with prope_apply, then call attn_decode with
+ *     rope.rotary_dims = 0, kv_len = L and window = W - k - 1 (0 for global
+ *     layers).
  * Supported: Hq % Hkv == 0 with Hq / Hkv <= 16, Dk in {128, 256, 512},
  *   Dv in {128, 256} (or 512 with Dk = 512); max_kv_len >= 1, and a cache
  *   that fits one call (ATTN_ERR_SHAPE past about 5 * 10^8 rows per sequence,

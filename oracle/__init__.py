@@ -258,6 +258,46 @@ def verify(q, k_cache, v_cache, row_offset, kv_len, *, window: int, scale: float
     return np.stack(out) if out else np.zeros((0, n_q, Hq, Dv))
 
 
+def cross_attend(q, k_cache, v_cache, row_offset, kv_len, q_pos, *, window: int,
+                 scale: float, rotary_dims: int = 0, theta: float = 10000.0) -> np.ndarray:
+    """A drafter's attention into the target model's KV cache ("Gemma 4:
+    End-to-End Architecture Walkthrough", Phase 4: the MTP drafter attends the
+    target's already-computed cache instead of keeping one of its own), fp64.
+
+    q [B, Hq, Dk] unrotated; sequence b's query sits at position q_pos[b]
+    (>= kv_len[b] - 1: the drafted tokens lie past the cache) and is rotated
+    there. Cache rows row_offset[b] .. row_offset[b] + kv_len[b] - 1 hold the
+    target's keys (already rotated) and values for positions 0 .. kv_len[b]-1.
+    Row r is visible when r < kv_len[b] and, for window > 0, q_pos[b] - r <
+    window. KV head of query head h: h // (Hq / Hkv). With no visible row the
+    output is 0. Softmax in two passes (max, then exp and sums), plain numpy.
+    Returns [B, Hq, Dv].
+    """
+    q = _f64(q)
+    B, Hq, Dk = q.shape
+    Hkv, Dv = k_cache.shape[1], v_cache.shape[2]
+    G = Hq // Hkv
+    row_offset = [int(x) for x in (row_offset.tolist() if hasattr(row_offset, "tolist") else row_offset)]
+    kv_len = [int(x) for x in (kv_len.tolist() if hasattr(kv_len, "tolist") else kv_len)]
+    q_pos = [int(x) for x in (q_pos.tolist() if hasattr(q_pos, "tolist") else q_pos)]
+    qr = rope(q, q_pos, rotary_dims, theta)
+    out = np.zeros((B, Hq, Dv), dtype=np.float64)
+    for b in range(B):
+        n, off, p = kv_len[b], row_offset[b], q_pos[b]
+        assert p >= n - 1, "the query lies past the cache"
+        lo = max(0, p - window + 1) if window > 0 else 0
+        if lo >= n:
+            continue
+        K = _f64(k_cache[off + lo: off + n])
+        V = _f64(v_cache[off + lo: off + n])
+        for h in range(Hq):
+            g = h // G
+            s = scale * (K[:, g, :] @ qr[b, h])
+            e = np.exp(s - s.max())
+            out[b, h] = (e @ V[:, g, :]) / e.sum()
+    return out
+
+
 # ---- int8 KV cache --------------------------------------------------------
 # The pages name int8 KV caching ("Gemma 4 Technical Report" reader,
 # "Quantization and Efficiency", Table 3 caption) but give no scheme. Reading

@@ -43,6 +43,11 @@ def test_decode_global(gpu_lib):
 def test_decode_local_window(gpu_lib):
     # rows outside the window are NaN: reading any would poison the output
     run(gpu_lib, 16, 8, 256, 256, 1024, 256, 1e4, LENS)
+
+
+def test_decode_local_g8(gpu_lib):
+    # small-model local layer: window 512, 8 query heads per KV head
+    run(gpu_lib, 8, 1, 256, 256, 512, 256, 1e4, LENS)
     run(gpu_lib, 16, 8, 256, 256, 100, 256, 1e4, [1, 50, 99, 100, 101, 700])
 
 

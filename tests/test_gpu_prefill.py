@@ -57,6 +57,9 @@ MFMA_CASES = [
     (1, 64, 16, 8, 256, 256, 63, 256, 1e4),
     (1, 64, 16, 8, 256, 256, 64, 256, 1e4),
     (1, 64, 16, 8, 256, 256, 500, 256, 1e4),
+    # small-model local layers: window 512 with 8 or 4 query heads per KV head
+    (1, 300, 8, 1, 256, 256, 512, 256, 1e4),
+    (2, 100, 8, 2, 256, 256, 33, 256, 1e4),
 ]
 
 

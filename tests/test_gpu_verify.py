@@ -92,3 +92,35 @@ def test_verify_tokens_equal_separate_decodes(gpu_lib):
                            rotary_dims=128, theta=1e6, max_kv_len=max(lens))
         torch.cuda.synchronize()
         assert (o[:, j].float() - d.float()).abs().max().item() < 2e-2
+
+
+@pytest.mark.parametrize("shape", [
+    (32, 4, 512, 256, 0, 128, 1e6),    # global layer, p-RoPE
+    (16, 8, 256, 256, 512, 256, 1e4),  # local layer, window 512
+    (8, 1, 256, 256, 512, 256, 1e4),   # small-model local layer: 8 query heads per KV head
+], ids=["global", "local", "local-g8"])
+def test_drafter_cross_attention(gpu_lib, shape):
+    """An MTP drafter's queries attend the target model's cache, which holds
+    no rows of theirs: drafting step j puts its query at position L_b + j past
+    a cache of L_b rows. The entry points express it as prope_apply at L_b + j
+    followed by attn_decode with no rotation, kv_len = L_b and the window
+    narrowed by j + 1 (the rows a query at L_b + j may see). Rows outside the
+    decode window are NaN."""
+    Hq, Hkv, Dk, Dv, W, R, theta = shape
+    lens = [1, 40, 511, 512, 513, 3000]
+    c = inputs.DecodeCase(len(lens), Hq, Hkv, Dk, Dv, window=W, rotary_dims=R, theta=theta,
+                          len_lo=1, len_hi=1)
+    kvl = torch.tensor(lens, dtype=torch.int32)
+    _, kc, vc, off, kvl = inputs.decode_inputs(c, 11, device=DEV, kv_len=kvl)
+    q = inputs.normal((len(lens), Hq, Dk), 11, 79, torch.bfloat16, DEV)
+    for j in range(3):
+        print(f"drafter step {j} Hq={Hq} Hkv={Hkv} Dk={Dk} Dv={Dv} W={W}", flush=True)
+        qpos = (kvl + j).to(torch.int32)
+        qr = gpu_lib.prope(q, qpos.to(DEV), rotary_dims=R, theta=theta)
+        o = gpu_lib.decode(qr, kc, vc, off.to(DEV), kvl.to(DEV),
+                           window=(W - j - 1) if W else 0, scale=Dk ** -0.5, rotary_dims=0,
+                           max_kv_len=max(lens))
+        torch.cuda.synchronize()
+        ref = oracle.cross_attend(q.cpu(), kc.cpu(), vc.cpu(), off, kvl, qpos, window=W,
+                                  scale=Dk ** -0.5, rotary_dims=R, theta=theta)
+        assert_close(o, ref, torch.bfloat16, f"drafter step {j}")

@@ -459,6 +459,84 @@ def test_verify_first_draft_token_ignores_later_ones():
     assert np.abs(a[0, 1] - b[0, 1]).max() > 1e-3 and np.abs(a[0, 2] - b[0, 2]).max() > 1e-3
 
 
+# ------------------------------------- drafter cross-attention into a cache ----
+
+def _drafter_cache(T, Hkv, D, R, th):
+    """Cache rows 0..T-1 built from unrotated keys turned at their positions."""
+    k = rng.standard_normal((T, Hkv, D))
+    v = rng.standard_normal((T, Hkv, D))
+    return k, oracle.rope(k, np.arange(T), R, th), v
+
+
+def test_cross_attend_at_the_cache_end_is_decode():
+    """A query at position kv_len - 1 over the cache is a plain decode (the C
+    path), for every window."""
+    lens, Hq, Hkv, D = [3, 17, 40], 8, 2, 16
+    offs = np.concatenate([[0], np.cumsum(lens)[:-1]])
+    kc = rng.standard_normal((sum(lens), Hkv, D))
+    vc = rng.standard_normal((sum(lens), Hkv, D))
+    q = rng.standard_normal((3, Hq, D))
+    for W in (0, 1, 5, 100):
+        a = oracle.decode(q, kc, vc, offs, lens, window=W, scale=0.3, rotary_dims=8, theta=1e4)
+        b = oracle.cross_attend(q, kc, vc, offs, lens, [n - 1 for n in lens], window=W,
+                                scale=0.3, rotary_dims=8, theta=1e4)
+        np.testing.assert_allclose(b, a, rtol=0, atol=1e-12)
+
+
+def test_cross_attend_depends_on_relative_positions():
+    """Without a window only q_pos - (key position) enters: shifting the query
+    and every cached key by s leaves the output unchanged, and moving the
+    query alone changes it."""
+    T, Hq, Hkv, D, R, th, s = 20, 4, 2, 16, 16, 1e4, 37
+    k = rng.standard_normal((T, Hkv, D))
+    v = rng.standard_normal((T, Hkv, D))
+    q = rng.standard_normal((1, Hq, D))
+    a = oracle.cross_attend(q, oracle.rope(k, np.arange(T), R, th), v, [0], [T], [T + 2],
+                            window=0, scale=0.4, rotary_dims=R, theta=th)
+    b = oracle.cross_attend(q, oracle.rope(k, np.arange(T) + s, R, th), v, [0], [T], [T + 2 + s],
+                            window=0, scale=0.4, rotary_dims=R, theta=th)
+    c = oracle.cross_attend(q, oracle.rope(k, np.arange(T), R, th), v, [0], [T], [T + 5],
+                            window=0, scale=0.4, rotary_dims=R, theta=th)
+    np.testing.assert_allclose(a, b, rtol=0, atol=1e-12)
+    assert np.abs(a - c).max() > 1e-3
+
+
+def test_cross_attend_window_edge():
+    """Query at p past the cache, window W: row p - W + 1 is the first visible
+    one. Poisoning the rows before it (NaN) changes nothing; changing that row
+    changes the output."""
+    T, Hq, Hkv, D, R, th, W, p = 30, 2, 1, 8, 8, 1e4, 10, 31
+    _, kc, vc = _drafter_cache(T, Hkv, D, R, th)
+    q = rng.standard_normal((1, Hq, D))
+    kw = dict(window=W, scale=0.5, rotary_dims=R, theta=th)
+    a = oracle.cross_attend(q, kc, vc, [0], [T], [p], **kw)
+    kp, vp = kc.copy(), vc.copy()
+    kp[: p - W + 1] = np.nan
+    vp[: p - W + 1] = np.nan
+    b = oracle.cross_attend(q, kp, vp, [0], [T], [p], **kw)
+    np.testing.assert_allclose(a, b, rtol=0, atol=0)
+    vc2 = vc.copy()
+    vc2[p - W + 1] += 4.0
+    c = oracle.cross_attend(q, kc, vc2, [0], [T], [p], **kw)
+    assert np.abs(a - c).max() > 1e-3
+
+
+@pytest.mark.parametrize("W", [0, 7])
+def test_cross_attend_past_the_cache_is_a_narrower_decode(W):
+    """A query d positions past the cache end equals the decode (C path, no
+    rotation) of the query turned at its own position, with the window
+    narrowed by d: the rows it may see are the cache's last W - d."""
+    T, Hq, Hkv, D, R, th = 25, 4, 1, 16, 16, 1e6
+    _, kc, vc = _drafter_cache(T, Hkv, D, R, th)
+    q = rng.standard_normal((1, Hq, D))
+    for d in (1, 2, 3):
+        a = oracle.cross_attend(q, kc, vc, [0], [T], [T - 1 + d], window=W, scale=0.3,
+                                rotary_dims=R, theta=th)
+        qr = oracle.rope(q, [T - 1 + d], R, th)
+        b = oracle.decode(qr, kc, vc, [0], [T], window=(W - d if W > 0 else 0), scale=0.3)
+        np.testing.assert_allclose(a, b, rtol=0, atol=1e-12)
+
+
 # ----------------------------------------------------- 2-D RoPE (patches) ----
 
 def test_rope_2d_one_pair_per_half_closed_form():
