@@ -17,9 +17,9 @@
 //    consecutive query positions for all G query heads of that KV head: 128
 //    (head, position) rows. A wave holds 32 rows (two heads x 16 positions
 //    for G = 8, else one head x 32 positions) and so the whole register file
-//    of its SIMD: Q^T in VGPRs (DK/16 x 16 bytes per lane, 128 registers for
-//    the 512-dim global keys) and the O^T accumulator in AGPRs, which only
-//    MFMAs touch. 32-row waves use v_mfma_f32_32x32x16_bf16 for the widened
+//    of its SIMD: the O^T accumulator in AGPRs, which only MFMAs touch, and
+//    Q^T (DK/16 x 16 bytes per lane, 128 registers for the 512-dim global
+//    keys) in the AGPRs left over and the rest in VGPRs. 32-row waves use v_mfma_f32_32x32x16_bf16 for the widened
 //    keys too, where two waves per SIMD would not fit.
 //  * S^T = K Q^T (M = 32 keys, N = 32 rows) and O^T = V^T P^T as in the
 //    two-wave kernel: every lane holds 16 scores of one row, its partner lane
@@ -249,10 +249,23 @@ __global__ __launch_bounds__(NT, 1) void prefill_mfma1w_kernel(PrefillArgs a, in
 #pragma unroll
       for (int u = 0; u < RCH / 2; ++u) qw[u] = rotate4(qw[u], t[u][0], t[u][1]);
     }
+    // Q^T is only ever an MFMA operand, so it lives in the AGPRs the O
+    // accumulator (DV/2) and the QK result (16) leave free; the rest stays in
+    // VGPRs. Left to itself the allocator spreads Q over both files and copies
+    // each step's operand into place before its MFMA (~130 extra moves per
+    // tile on the 512-dim keys, in the wave's one issue stream). With every
+    // key dim rotated the extra K addressing leaves no VGPRs for that split:
+    // there Q stays in VGPRs.
+    constexpr int QA0 = (256 - DV / 2 - 16) / 4 < DK / 16 ? (256 - DV / 2 - 16) / 4 : DK / 16;
+    constexpr int QA = RCH == DK / 8 ? 0 : QA0;
 #pragma unroll
     for (int s = 0; s < DK / 16; ++s) {
       qf[s] = __builtin_bit_cast(bf16x8, valid ? qw[s] : u32x4{});
-      asm volatile("" : "+v"(qf[s]));  // rotated before the next DMAs go out
+      // rotated before the next DMAs go out
+      if (s < QA)
+        asm volatile("" : "+a"(qf[s]));
+      else
+        asm volatile("" : "+v"(qf[s]));
     }
   }
   if (n_tiles > 0) {
