@@ -79,3 +79,19 @@ def test_prope_2d_rejects_odd_halves(gpu_lib):
     pxy = torch.zeros(4, 2, dtype=torch.int32, device=DEV)
     with pytest.raises(gpu_lib.AttnError):
         gpu_lib.prope_2d(x, pxy, rotary_dims=2, theta=1e4)
+
+
+@pytest.mark.parametrize("T,pos0,D,R,theta", [(200, 0, 256, 256, 1e4), (150, 131000, 512, 128, 1e6),
+                                              (40, 2 ** 31 - 41, 128, 32, 1e6)])
+def test_rope_table_vs_oracle(gpu_lib, T, pos0, D, R, theta):
+    """attn_rope_table row t, pair p holds (cos, sin) of pair p's angle at
+    position pos0 + t: what the oracle's rotation does to the unit vector with
+    a 1 in the pair's first dim. Entries are fp32 roundings of fp64 values."""
+    tab = gpu_lib.rope_table(T, head_dim=D, rotary_dims=R, theta=theta, pos0=pos0)
+    torch.cuda.synchronize()
+    e = np.zeros((T, R // 2, D))
+    e[:, np.arange(R // 2), 2 * np.arange(R // 2)] = 1.0
+    rot = oracle.rope(e, np.arange(T) + pos0, R, theta)
+    ref = np.stack([rot[:, np.arange(R // 2), 2 * np.arange(R // 2)],
+                    rot[:, np.arange(R // 2), 2 * np.arange(R // 2) + 1]], axis=-1)
+    np.testing.assert_allclose(tab.cpu().double().numpy(), ref, rtol=0, atol=1.2e-7)
