@@ -1,7 +1,8 @@
 #!/usr/bin/env python3
 """Benchmark of the MI355X hybrid-attention hot path (one GPU).
 
-    python bench.py [--steps K] [--warmup W] [--workload N] [--secondary 3,4,5]
+    python bench.py [--steps K] [--warmup W] [--workload NAME]
+                    [--secondary global_prefill,decode,stack]
 
 Prints ONE JSON line. `value` is the throughput of the headline workload
 (default: the local sliding-window prefill, B=4 T=4096 16q/8kv D=256 W=512,
@@ -391,9 +392,10 @@ def main():
     # (0.27-0.28 ms against 0.23 ms once warm), so the default warm-up runs
     # ~0.15 s of untimed steps.
     ap.add_argument("--warmup", type=int, default=500)
-    ap.add_argument("--workload", type=int, default=2, choices=[2, 3, 5])
-    ap.add_argument("--secondary", default="3,4,5",
-                    help="other workloads measured in the same run ('' for none)")
+    ap.add_argument("--workload", default="local_prefill",
+                    choices=["local_prefill", "global_prefill", "stack"])
+    ap.add_argument("--secondary", default="global_prefill,decode,stack",
+                    help="other workloads measured in the same run, by name ('' for none)")
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -424,10 +426,10 @@ def main():
         print(json.dumps({"calibrate_copy_bytes": n, "launches": 3}), flush=True)
         return
 
-    cfg = inputs.CONFIGS[args.workload]
+    cfg = inputs.WORKLOADS[args.workload]
     # Steps of tens of milliseconds (global prefill, stack) warm the part in
     # a few steps; cap their warm-up so the default run stays short.
-    warmup = args.warmup if args.workload == 2 else min(args.warmup, 10)
+    warmup = args.warmup if args.workload == "local_prefill" else min(args.warmup, 10)
     if cfg["kind"] == "stack":
         r = bench_stack(ar, torch, inputs, cfg, args.steps, warmup)
         value, kern_ms = r["flops"] / r["step_ms"] / 1e9, r["step_ms"]
@@ -459,21 +461,23 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic (seeded N(0,1) / U(-1,1) inputs, no weights)",
-        "config": {"workload": cfg["name"], "config_id": args.workload,
+        "config": {"workload": cfg["name"], "workload_key": args.workload,
                    "seed": cfg["seed"], "parallelism": "none (1 GPU)"},
         "roofline": bound_rl,
     }
 
     secondary = {}
-    for s in [int(x) for x in args.secondary.split(",") if x.strip()]:
+    for s in [x.strip() for x in args.secondary.split(",") if x.strip()]:
         if s == args.workload:
             continue
-        sc = inputs.CONFIGS[s]
+        if s not in inputs.WORKLOADS or s == "small_global_fp32":
+            raise SystemExit(f"--secondary: unknown workload {s!r}")
+        sc = inputs.WORKLOADS[s]
         torch.cuda.empty_cache()
         if sc["kind"] == "prefill":
             rr = bench_prefill(ar, torch, inputs, sc, max(3, args.steps // 4), 1)
             tf = rr["flops"] / rr["kern_ms"] / 1e9
-            secondary[str(s)] = {"workload": sc["name"], "unit": "TFLOP/s",
+            secondary[s] = {"workload": sc["name"], "unit": "TFLOP/s",
                                  "value": round(rr["flops"] / rr["step_ms"] / 1e9, 3),
                                  "ms_per_step": round(rr["step_ms"], 4),
                                  "roofline": dict(roofline("mfma", tf, PEAK_BF16_TFLOPS, "TFLOP/s",
@@ -482,7 +486,7 @@ def main():
             del rr
             torch.cuda.empty_cache()
             kv = bench_prefill_kv_shared(ar, torch, inputs, sc, max(2, args.steps // 8), 1)
-            secondary[str(s)]["keys_as_values"] = {
+            secondary[s]["keys_as_values"] = {
                 "TFLOP/s": round(kv["flops"] / kv["ms"] / 1e9, 3), "ms": round(kv["ms"], 4),
                 "what": "same shape as a K = V layer: rotated keys as both k and v, 512-dim "
                         "values, attention call only (two passes over 256-dim value halves; "
@@ -492,7 +496,7 @@ def main():
             gbs = rr["bytes"] / (rr["step_ms"] * 1e-3) / 1e9
             g = rr["g_bytes"] / (rr["g_ms"] * 1e-3) / 1e9
             l = rr["l_bytes"] / (rr["l_ms"] * 1e-3) / 1e9
-            secondary[str(s)] = {"workload": sc["name"], "unit": "GB/s", "value": round(gbs, 1),
+            secondary[s] = {"workload": sc["name"], "unit": "GB/s", "value": round(gbs, 1),
                                  "ms_per_step": round(rr["step_ms"], 4),
                                  "global_call": {"GB/s": round(g, 1), "ms": round(rr["g_ms"], 4),
                                                  "bytes": rr["g_bytes"]},
@@ -531,7 +535,7 @@ def main():
         else:
             rr = bench_stack(ar, torch, inputs, sc, max(3, args.steps // 4), 1)
             tf = rr["flops"] / rr["step_ms"] / 1e9
-            secondary[str(s)] = {"workload": sc["name"], "unit": "TFLOP/s", "value": round(tf, 3),
+            secondary[s] = {"workload": sc["name"], "unit": "TFLOP/s", "value": round(tf, 3),
                                  "ms_per_step": round(rr["step_ms"], 4),
                                  "roofline": roofline("mfma", tf, PEAK_BF16_TFLOPS, "TFLOP/s",
                                                       None)}

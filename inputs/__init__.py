@@ -14,7 +14,7 @@ part of the definition and never depends on free memory.
 Workload shapes follow the configurations the pages' hybrid attention implies
 (local sliding-window layers with 2 query heads per KV head and 256-dim heads,
 global layers with 8 query heads per KV head, 512-dim keys and 256-dim values);
-see ``CONFIGS``.
+see ``WORKLOADS``.
 """
 from __future__ import annotations
 
@@ -195,25 +195,25 @@ class StackCase:
             self.layers = [(loc, None)] * self.n_local + [(glo, None), (glo, self.n_local)]
 
 
-CONFIGS = {
-    1: dict(kind="prefill", seed=SEED0 + 1,
+WORKLOADS = {
+    "small_global_fp32": dict(kind="prefill", seed=SEED0 + 1,
             case=PrefillCase(1, 256, 8, 1, 128, 128, window=0, rotary_dims=32,
                              theta=1e6, dtype=torch.float32),
             name="global prefill fp32 B=1 T=256 8q/1kv D=128 p-RoPE(32 of 128, 1e6)"),
-    2: dict(kind="prefill", seed=SEED0 + 2,
+    "local_prefill": dict(kind="prefill", seed=SEED0 + 2,
             case=PrefillCase(4, 4096, window=512, dtype=torch.bfloat16, **LOCAL),
             name="local sliding-window prefill bf16 B=4 T=4096 16q/8kv D=256 W=512 RoPE(1e4)"),
-    3: dict(kind="prefill", seed=SEED0 + 3,
+    "global_prefill": dict(kind="prefill", seed=SEED0 + 3,
             case=PrefillCase(1, 32768, window=0, dtype=torch.bfloat16,
                              v_dist="uniform", **GLOBAL),
             name="global prefill bf16 B=1 T=32768 32q/4kv Dk=512 Dv=256 p-RoPE(128 of 512, 1e6)"),
-    4: dict(kind="decode", seed=SEED0 + 4,
+    "decode": dict(kind="decode", seed=SEED0 + 4,
             cases=dict(
                 glob=DecodeCase(64, 32, 4, 512, 256, window=0, rotary_dims=128,
                                 theta=1e6, len_lo=1024, len_hi=131072),
                 loc=DecodeCase(64, 16, 8, 256, 256, window=1024, rotary_dims=256,
                                theta=1e4, len_lo=1024, len_hi=131072)),
             name="decode bf16 64 seqs L~U[1024,131072]: global 32q/4kv 512/256 + local 16q/8kv 256 W=1024"),
-    5: dict(kind="stack", seed=SEED0 + 5, case=StackCase(),
+    "stack": dict(kind="stack", seed=SEED0 + 5, case=StackCase(),
             name="stack bf16 B=2 T=16384: 5 local W=1024 + global + shared-KV global"),
 }

@@ -29,43 +29,43 @@ def sample_rows(T, W, n_random, seed):
     return np.array(sorted(r for r in rows if 0 <= r < T), dtype=np.int32)
 
 
-def prefill_case(cfg_id, rows_random):
-    cfg = inputs.CONFIGS[cfg_id]
+def prefill_case(name, rows_random):
+    cfg = inputs.WORKLOADS[name]
     c = cfg["case"]
     q, k, v = inputs.prefill_inputs(c, cfg["seed"], device=DEV)
     tab = ar.rope_table(c.T, head_dim=c.Dk, rotary_dims=c.rotary_dims, theta=c.theta)
     o = ar.prefill(q, k, v, window=c.window, scale=c.scale, rotary_dims=c.rotary_dims,
                    theta=c.theta, table=tab)
     torch.cuda.synchronize()
-    rows = None if rows_random is None else sample_rows(c.T, c.window, rows_random, cfg_id)
+    rows = None if rows_random is None else sample_rows(c.T, c.window, rows_random, cfg["seed"])
     qh = q.cpu() if rows is None else q.cpu()[:, rows]
     ref = oracle.prefill(qh, k.cpu(), v.cpu(), window=c.window, scale=c.scale,
                          rotary_dims=c.rotary_dims, theta=c.theta, rows=rows)
     got = o if rows is None else o[:, torch.as_tensor(rows, device=DEV, dtype=torch.long)]
-    mx, rel = assert_close(got, ref, c.dtype, f"config {cfg_id}")
-    print(f"config {cfg_id}: rows={'all' if rows is None else len(rows)} "
+    mx, rel = assert_close(got, ref, c.dtype, name)
+    print(f"{name}: rows={'all' if rows is None else len(rows)} "
           f"max_abs={mx:.3e} rel_rms={rel:.3e}", flush=True)
 
 
-def test_config1_fp32_global_full():
-    prefill_case(1, None)
+def test_small_global_fp32_full():
+    prefill_case("small_global_fp32", None)
 
 
-def test_config2_local_prefill():
-    prefill_case(2, 96)
+def test_local_prefill_full_size():
+    prefill_case("local_prefill", 96)
 
 
-def test_config3_global_prefill():
-    prefill_case(3, 40)
+def test_global_prefill_full_size():
+    prefill_case("global_prefill", 40)
     torch.cuda.empty_cache()
 
 
 @pytest.mark.parametrize("kind", ["glob", "loc", "glob_kv", "glob_verify", "glob_int8"])
-def test_config4_decode(kind):
+def test_decode_full_size(kind):
     """glob_kv: the global call with keys as values (its key cache passed as
     both caches, Dv = Dk = 512); glob_verify: the global call with its last 2
     rows as 2 new tokens per sequence; both as the benchmark times them."""
-    cfg = inputs.CONFIGS[4]
+    cfg = inputs.WORKLOADS["decode"]
     d = cfg["cases"]["loc" if kind == "loc" else "glob"]
     seed = cfg["seed"] + (100 if kind == "loc" else 0)
     kvl = inputs.decode_lengths(d, cfg["seed"])
@@ -95,8 +95,8 @@ def test_config4_decode(kind):
         ref = oracle.decode_one(q[b].cpu(), kc[a + lo:a + n].cpu(), vc[a + lo:a + n].cpu(),
                                 kv_len=n, row0=lo, window=d.window, scale=d.scale,
                                 rotary_dims=d.rotary_dims, theta=d.theta)
-        mx, rel = assert_close(o[b], ref, torch.bfloat16, f"config 4 {kind} seq {b} len {n}")
-        print(f"config 4 {kind}: seq {b} kv_len={n} max_abs={mx:.3e} rel_rms={rel:.3e}",
+        mx, rel = assert_close(o[b], ref, torch.bfloat16, f"decode {kind} seq {b} len {n}")
+        print(f"decode {kind}: seq {b} kv_len={n} max_abs={mx:.3e} rel_rms={rel:.3e}",
               flush=True)
     del kc, vc
     torch.cuda.empty_cache()
@@ -114,8 +114,8 @@ def verify_case(d, q1, kc, vc, off, kvl, maxl, seed, n_q=2):
         ref = oracle.verify(q[b:b + 1].cpu(), kc[a:a + n].cpu(), vc[a:a + n].cpu(), [0], [n],
                             window=d.window, scale=d.scale, rotary_dims=d.rotary_dims,
                             theta=d.theta)
-        mx, rel = assert_close(o[b:b + 1], ref, torch.bfloat16, f"config 4 verify seq {b}")
-        print(f"config 4 verify n_q={n_q}: seq {b} kv_len={n} max_abs={mx:.3e} "
+        mx, rel = assert_close(o[b:b + 1], ref, torch.bfloat16, f"decode verify seq {b}")
+        print(f"decode verify n_q={n_q}: seq {b} kv_len={n} max_abs={mx:.3e} "
               f"rel_rms={rel:.3e}", flush=True)
     del kc, vc
     torch.cuda.empty_cache()
@@ -136,15 +136,15 @@ def int8_case(d, q, kc, vc, off, kvl, maxl):
                                  vq[a:a + n].cpu(), vs[a:a + n].cpu(), [0], [n],
                                  window=d.window, scale=d.scale, rotary_dims=d.rotary_dims,
                                  theta=d.theta)
-        mx, rel = assert_close(o[b:b + 1], ref, torch.bfloat16, f"config 4 int8 seq {b}")
-        print(f"config 4 int8: seq {b} kv_len={n} max_abs={mx:.3e} rel_rms={rel:.3e}",
+        mx, rel = assert_close(o[b:b + 1], ref, torch.bfloat16, f"decode int8 seq {b}")
+        print(f"decode int8: seq {b} kv_len={n} max_abs={mx:.3e} rel_rms={rel:.3e}",
               flush=True)
     del kq, vq
     torch.cuda.empty_cache()
 
 
-def test_config5_stack():
-    cfg = inputs.CONFIGS[5]
+def test_stack_full_size():
+    cfg = inputs.WORKLOADS["stack"]
     sc = cfg["case"]
     layers = []
     tabs = {}
@@ -174,7 +174,7 @@ def test_config5_stack():
                              scale=c.scale, rotary_dims=c.rotary_dims, theta=c.theta,
                              rows=rows)
         got = o[:, torch.as_tensor(rows, device=DEV, dtype=torch.long)]
-        mx, rel = assert_close(got, ref, c.dtype, f"config 5 layer {li + 1}")
-        print(f"config 5 layer {li + 1}: max_abs={mx:.3e} rel_rms={rel:.3e}", flush=True)
+        mx, rel = assert_close(got, ref, c.dtype, f"stack layer {li + 1}")
+        print(f"stack layer {li + 1}: max_abs={mx:.3e} rel_rms={rel:.3e}", flush=True)
     del layers
     torch.cuda.empty_cache()
