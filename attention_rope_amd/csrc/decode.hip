@@ -397,13 +397,16 @@ __global__ __launch_bounds__(DV) void decode_merge_kernel(DecodeArgs a, int ch, 
 // trade ring depth for more workgroups per CU:
 //  * separate 512/256 caches: 2 waves (32-row tiles), 3 stages;
 //  * local 256/256 heads: 1 wave (16-row tiles), 3 stages, three per CU;
-//  * one shared cache (K = V) and 512-dim values: 1 wave, 2 stages, so four
-//    (two) workgroups share a CU; 2 waves x 4 stages ran at 4.1 TB/s on the
-//    K = V global shape, this at 5.8.
+//  * one shared cache (K = V): 2 waves (32-row tiles), 2 stages. On the
+//    K = V global shape this runs at 6.0 TB/s, 1 wave x 2 stages at 5.7 and
+//    2 waves x 4 stages at 4.1;
+//  * separate caches with 512-dim values: 1 wave, 2 stages, two workgroups
+//    per CU.
 template <int DK, int DV, bool SHARED>
 using RingCfg = std::conditional_t<
-    SHARED || (DK == 512 && DV == 512), RCfg<DK, DV, 1, 2, SHARED>,
-    std::conditional_t<(DK == 256 && DV == 256), RCfg<DK, DV, 1, 3>, RCfg<DK, DV, 2, 3>>>;
+    SHARED, RCfg<DK, DV, 2, 2, SHARED>,
+    std::conditional_t<(DK == 512 && DV == 512), RCfg<DK, DV, 1, 2, SHARED>,
+    std::conditional_t<(DK == 256 && DV == 256), RCfg<DK, DV, 1, 3>, RCfg<DK, DV, 2, 3>>>>;
 
 template <int DV>
 hipError_t launch_merge_dv(const DecodeArgs& a, const SplitPlan& pl, hipStream_t st) {
