@@ -5,6 +5,9 @@ kernels. torch provides device memory and the current stream. The entry
 points mirror the C ABI in include/attn_rope.h:
 
     prefill(q, k, v, *, window, scale, rotary_dims, theta, rope_mask, pos0)
+    verify(q, k_cache, v_cache, row_offset, kv_len, *, ...)
+    kv_quantize_int8(x), decode_int8(q, k_codes, k_scales, v_codes, v_scales, ...)
+    prope_2d(x, positions_xy, *, rotary_dims, theta)
     decode(q, k_cache, v_cache, row_offset, kv_len, *, window, scale,
            rotary_dims, theta, max_kv_len)
     prope(x, positions, *, rotary_dims, theta, out=None)
@@ -29,7 +32,7 @@ STATUS = {0: "ok", 1: "null pointer", 2: "invalid shape or argument",
           5: "kernel launch failed", 6: "output overlaps an input"}
 
 # Every symbol the header declares (checked by the tests).
-EXPORTS = ("attn_rope_table", "attn_rope_table_bytes", "attn_prefill",
+EXPORTS = ("attn_prefill",
            "attn_prefill_workspace_bytes", "attn_decode",
            "attn_decode_workspace_bytes", "attn_verify", "attn_verify_workspace_bytes",
            "attn_kv_quantize_int8", "attn_decode_int8", "attn_decode_int8_workspace_bytes",
@@ -59,14 +62,10 @@ def load(path: str = LIB_PATH):
                            "`python -c 'import __graft_entry__ as g; g.build()'`")
     lib = ctypes.CDLL(path)
     vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
-    lib.attn_rope_table_bytes.argtypes = [i32, i32]
-    lib.attn_rope_table_bytes.restype = sz
-    lib.attn_rope_table.argtypes = [vp, i32, i32, i32, _Rope, vp]
-    lib.attn_rope_table.restype = ctypes.c_int
     lib.attn_prefill_workspace_bytes.argtypes = [i32, i32, i32, i32, _Rope, i32, ctypes.c_int]
     lib.attn_prefill_workspace_bytes.restype = sz
     lib.attn_prefill.argtypes = [vp, vp, vp, vp] + [i32] * 7 + [
-        ctypes.c_float, _Rope, i32, vp, vp, sz, ctypes.c_int, vp]
+        ctypes.c_float, _Rope, i32, i32, vp, sz, ctypes.c_int, vp]
     lib.attn_prefill.restype = ctypes.c_int
     lib.attn_decode_workspace_bytes.argtypes = [i32] * 6
     lib.attn_decode_workspace_bytes.restype = sz
@@ -118,22 +117,36 @@ def _dev(t: torch.Tensor, name: str):
     return ctypes.c_void_p(t.data_ptr())
 
 
+def _nbytes(t: torch.Tensor) -> int:
+    return t.numel() * t.element_size()
+
+
+def _need_dims(t: torch.Tensor, n: int, name: str):
+    if t.dim() != n:
+        raise ValueError(f"{name} must have {n} dims, got shape {tuple(t.shape)}")
+
+
+def _need_shape(t: torch.Tensor, shape, name: str):
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _same_device(ref: torch.Tensor, ref_name: str, **others):
+    for name, t in others.items():
+        if t.device != ref.device:
+            raise ValueError(f"{name} is on {t.device}, {ref_name} on {ref.device}")
+
+
+def _same(ref: torch.Tensor, ref_name: str, **others):
+    """Same device, and for the float tensors the same dtype, as ``ref``."""
+    _same_device(ref, ref_name, **others)
+    for name, t in others.items():
+        if t.is_floating_point() and t.dtype != ref.dtype:
+            raise TypeError(f"{name} is {t.dtype}, {ref_name} is {ref.dtype}")
+
+
 def _stream(t: torch.Tensor):
     return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
-
-
-def rope_table(T: int, *, head_dim: int, rotary_dims: int, theta: float, pos0: int = 0,
-               device="cuda", out=None):
-    """cos/sin table [T, rotary_dims/2, 2] fp32 for positions pos0..pos0+T-1
-    (None when there is nothing to rotate)."""
-    lib = load()
-    if T == 0 or rotary_dims == 0:
-        return None
-    tab = out if out is not None else torch.empty((T, rotary_dims // 2, 2),
-                                                  dtype=torch.float32, device=device)
-    _check(lib.attn_rope_table(_dev(tab, "table"), T, pos0, head_dim,
-                               _Rope(rotary_dims, theta), _stream(tab)))
-    return tab
 
 
 def prefill_workspace_bytes(B: int, T: int, Hkv: int, Dk: int, *, rotary_dims: int,
@@ -146,39 +159,67 @@ def prefill_workspace_bytes(B: int, T: int, Hkv: int, Dk: int, *, rotary_dims: i
 
 def prefill(q, k, v, *, window: int = 0, scale: float | None = None,
             rotary_dims: int = 0, theta: float = 10000.0,
-            rope_mask: int = ROPE_Q | ROPE_K, pos0: int = 0, out=None,
-            table=None, workspace=None):
+            rope_mask: int = ROPE_Q | ROPE_K, pos0: int = 0, out=None, workspace=None):
     """q [B,T,Hq,Dk], k [B,T,Hkv,Dk], v [B,T,Hkv,Dv] -> o [B,T,Hq,Dv].
 
-    ``table`` is a cos/sin table from rope_table() for the same T, pos0 and
-    RoPE settings; it is built here when not given. ``workspace`` is a device
-    byte buffer of at least prefill_workspace_bytes(); allocated here when not
-    given."""
+    Token t sits at position pos0 + t. ``workspace`` is a device byte buffer
+    of at least prefill_workspace_bytes() (K's turned rotary dims); allocated
+    here when not given."""
     lib = load()
+    _need_dims(q, 4, "q")
+    _need_dims(k, 4, "k")
+    _need_dims(v, 4, "v")
     B, T, Hq, Dk = q.shape
     Hkv, Dv = k.shape[2], v.shape[3]
-    if k.shape != (B, T, Hkv, Dk) or v.shape != (B, T, Hkv, Dv):
-        raise ValueError("q/k/v shapes disagree")
-    if not (q.dtype == k.dtype == v.dtype):
-        raise TypeError("q, k, v must share a dtype")
+    if tuple(k.shape) != (B, T, Hkv, Dk) or tuple(v.shape) != (B, T, Hkv, Dv):
+        raise ValueError(f"q/k/v shapes disagree: {tuple(q.shape)} {tuple(k.shape)} "
+                         f"{tuple(v.shape)}")
+    _same(q, "q", k=k, v=v)
     if scale is None:
         scale = Dk ** -0.5
     o = out if out is not None else torch.empty((B, T, Hq, Dv), dtype=q.dtype, device=q.device)
-    if table is None and rotary_dims > 0 and rope_mask and T > 0:
-        table = rope_table(T, head_dim=Dk, rotary_dims=rotary_dims, theta=theta, pos0=pos0,
-                           device=q.device)
-    tab_ptr = _dev(table, "table") if table is not None else None
+    _need_shape(o, (B, T, Hq, Dv), "out")
+    _same(q, "q", out=o)
     need = int(lib.attn_prefill_workspace_bytes(B, T, Hkv, Dk, _Rope(rotary_dims, theta),
                                                 int(rope_mask), _dtype_code(q)))
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    if workspace is not None:
+        _same(q, "q", workspace=workspace)
     ws_ptr = _dev(workspace, "workspace") if workspace is not None else None
-    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    ws_bytes = _nbytes(workspace) if workspace is not None else 0
     _check(lib.attn_prefill(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(o, "o"),
                             B, T, Hq, Hkv, Dk, Dv, int(window), float(scale),
-                            _Rope(rotary_dims, theta), int(rope_mask), tab_ptr,
+                            _Rope(rotary_dims, theta), int(rope_mask), int(pos0),
                             ws_ptr, ws_bytes, _dtype_code(q), _stream(q)))
     return o
+
+
+def _cache_args(q, k_cache, v_cache, row_offset, kv_len, n_q=None):
+    """Shapes, dtypes and devices of a decode-style call, checked on the host
+    (the kernels build buffer descriptors from these sizes)."""
+    if n_q is None:
+        _need_dims(q, 3, "q")
+        B, Hq, Dk = q.shape
+    else:
+        _need_dims(q, 4, "q")
+        B, _, Hq, Dk = q.shape
+    _need_dims(k_cache, 3, "k_cache")
+    _need_dims(v_cache, 3, "v_cache")
+    rows, Hkv = k_cache.shape[0], k_cache.shape[1]
+    Dv = v_cache.shape[2]
+    if k_cache.shape[2] != Dk:
+        raise ValueError(f"k_cache head dim {k_cache.shape[2]} != q head dim {Dk}")
+    if tuple(v_cache.shape[:2]) != (rows, Hkv):
+        raise ValueError(f"v_cache {tuple(v_cache.shape)} does not match k_cache "
+                         f"{tuple(k_cache.shape)} in rows and KV heads")
+    if row_offset.dtype != torch.int64 or kv_len.dtype != torch.int32:
+        raise TypeError("row_offset must be int64 and kv_len int32")
+    if row_offset.numel() != B or kv_len.numel() != B:
+        raise ValueError(f"row_offset and kv_len need {B} entries "
+                         f"(got {row_offset.numel()}, {kv_len.numel()})")
+    _same(q, "q", row_offset=row_offset, kv_len=kv_len)
+    return B, Hq, Hkv, Dk, Dv
 
 
 def decode_workspace_bytes(B: int, Hq: int, Hkv: int, Dv: int, max_kv_len: int,
@@ -191,22 +232,22 @@ def decode(q, k_cache, v_cache, row_offset, kv_len, *, window: int = 0,
            max_kv_len: int, out=None, workspace=None):
     """q [B,Hq,Dk]; caches [rows,Hkv,Dk|Dv]; row_offset int64 [B]; kv_len int32 [B]."""
     lib = load()
-    B, Hq, Dk = q.shape
-    Hkv, Dv = k_cache.shape[1], v_cache.shape[2]
-    if row_offset.dtype != torch.int64 or kv_len.dtype != torch.int32:
-        raise TypeError("row_offset must be int64 and kv_len int32")
+    B, Hq, Hkv, Dk, Dv = _cache_args(q, k_cache, v_cache, row_offset, kv_len)
+    _same(q, "q", k_cache=k_cache, v_cache=v_cache)
     if scale is None:
         scale = Dk ** -0.5
     o = out if out is not None else torch.empty((B, Hq, Dv), dtype=q.dtype, device=q.device)
+    _need_shape(o, (B, Hq, Dv), "out")
+    _same(q, "q", out=o)
     need = decode_workspace_bytes(B, Hq, Hkv, Dv, max_kv_len, window)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    _same(q, "q", workspace=workspace)
     _check(lib.attn_decode(_dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
                            _dev(row_offset, "row_offset"), _dev(kv_len, "kv_len"),
                            _dev(o, "o"), B, Hq, Hkv, Dk, Dv, int(window), float(scale),
                            _Rope(rotary_dims, theta), int(max_kv_len),
-                           ctypes.c_void_p(workspace.data_ptr()),
-                           workspace.numel() * workspace.element_size(),
+                           _dev(workspace, "workspace"), _nbytes(workspace),
                            _dtype_code(q), _stream(q)))
     return o
 
@@ -223,23 +264,24 @@ def verify(q, k_cache, v_cache, row_offset, kv_len, *, window: int = 0,
     caches [rows,Hkv,Dk|Dv]; row_offset int64 [B]; kv_len int32 [B] ->
     o [B,n_q,Hq,Dv]."""
     lib = load()
-    B, n_q, Hq, Dk = q.shape
-    Hkv, Dv = k_cache.shape[1], v_cache.shape[2]
-    if row_offset.dtype != torch.int64 or kv_len.dtype != torch.int32:
-        raise TypeError("row_offset must be int64 and kv_len int32")
+    n_q = q.shape[1] if q.dim() == 4 else 0
+    B, Hq, Hkv, Dk, Dv = _cache_args(q, k_cache, v_cache, row_offset, kv_len, n_q=n_q)
+    _same(q, "q", k_cache=k_cache, v_cache=v_cache)
     if scale is None:
         scale = Dk ** -0.5
     o = out if out is not None else torch.empty((B, n_q, Hq, Dv), dtype=q.dtype,
                                                 device=q.device)
+    _need_shape(o, (B, n_q, Hq, Dv), "out")
+    _same(q, "q", out=o)
     need = verify_workspace_bytes(B, n_q, Hq, Hkv, Dk, Dv, max_kv_len, window)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    _same(q, "q", workspace=workspace)
     _check(lib.attn_verify(_dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
                            _dev(row_offset, "row_offset"), _dev(kv_len, "kv_len"),
                            _dev(o, "o"), B, n_q, Hq, Hkv, Dk, Dv, int(window), float(scale),
                            _Rope(rotary_dims, theta), int(max_kv_len),
-                           ctypes.c_void_p(workspace.data_ptr()),
-                           workspace.numel() * workspace.element_size(),
+                           _dev(workspace, "workspace"), _nbytes(workspace),
                            _dtype_code(q), _stream(q)))
     return o
 
@@ -293,25 +335,31 @@ def decode_int8(q, k_codes, k_scales, v_codes, v_scales, row_offset, kv_len, *,
     """attn_decode over int8 caches: codes [rows,Hkv,D] int8, scales
     [rows,Hkv] float32; q [B,Hq,Dk] bf16 -> o [B,Hq,Dv] bf16."""
     lib = load()
-    B, Hq, Dk = q.shape
-    Hkv, Dv = k_codes.shape[1], v_codes.shape[2]
-    if row_offset.dtype != torch.int64 or kv_len.dtype != torch.int32:
-        raise TypeError("row_offset must be int64 and kv_len int32")
+    B, Hq, Hkv, Dk, Dv = _cache_args(q, k_codes, v_codes, row_offset, kv_len)
+    if q.dtype != torch.bfloat16:
+        raise TypeError("q must be bfloat16")
     if k_codes.dtype != torch.int8 or v_codes.dtype != torch.int8:
         raise TypeError("codes must be int8")
     if k_scales.dtype != torch.float32 or v_scales.dtype != torch.float32:
         raise TypeError("scales must be float32")
+    rows = k_codes.shape[0]
+    _need_shape(k_scales, (rows, Hkv), "k_scales")
+    _need_shape(v_scales, (rows, Hkv), "v_scales")
+    _same_device(q, "q", k_codes=k_codes, v_codes=v_codes, k_scales=k_scales,
+                 v_scales=v_scales)
     if scale is None:
         scale = Dk ** -0.5
     o = out if out is not None else torch.empty((B, Hq, Dv), dtype=q.dtype, device=q.device)
+    _need_shape(o, (B, Hq, Dv), "out")
+    _same(q, "q", out=o)
     need = decode_int8_workspace_bytes(B, Hq, Hkv, Dv, max_kv_len, window)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    _same_device(q, "q", workspace=workspace)
     _check(lib.attn_decode_int8(_dev(q, "q"), _dev(k_codes, "k_codes"), _dev(k_scales, "k_scales"),
                                 _dev(v_codes, "v_codes"), _dev(v_scales, "v_scales"),
                                 _dev(row_offset, "row_offset"), _dev(kv_len, "kv_len"),
                                 _dev(o, "o"), B, Hq, Hkv, Dk, Dv, int(window), float(scale),
                                 _Rope(rotary_dims, theta), int(max_kv_len),
-                                ctypes.c_void_p(workspace.data_ptr()),
-                                workspace.numel() * workspace.element_size(), _stream(q)))
+                                _dev(workspace, "workspace"), _nbytes(workspace), _stream(q)))
     return o

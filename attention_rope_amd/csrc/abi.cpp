@@ -55,7 +55,7 @@ attn_status_t check_rope(attn_rope_t rope, int32_t D) {
   return ATTN_OK;
 }
 
-bool prefill_uses_table(attn_rope_t rope, int32_t rope_mask) {
+bool prefill_rotates(attn_rope_t rope, int32_t rope_mask) {
   return rope.rotary_dims > 0 && (rope_mask & (ATTN_ROPE_Q | ATTN_ROPE_K)) != 0;
 }
 
@@ -151,6 +151,7 @@ attn_status_t prope_call(const void* x, void* y, const int32_t* positions, int32
                        "prope");
 }
 
+
 }  // namespace
 
 extern "C" {
@@ -170,30 +171,6 @@ const char* attn_status_string(attn_status_t s) {
 
 const char* attn_last_error(void) { return g_last_error.c_str(); }
 
-size_t attn_rope_table_bytes(int32_t T, int32_t rotary_dims) {
-  if (T <= 0 || rotary_dims <= 0) return 0;
-  return (size_t)T * (size_t)(rotary_dims / 2) * sizeof(float2);
-}
-
-attn_status_t attn_rope_table(void* table, int32_t T, int32_t pos0, int32_t head_dim,
-                              attn_rope_t rope, void* stream) {
-  if (T < 0) return fail(ATTN_ERR_SHAPE, "T=%d must be >= 0", T);
-  if (head_dim < 2 || head_dim % 2)
-    return fail(ATTN_ERR_SHAPE, "head_dim=%d must be even and >= 2", head_dim);
-  attn_status_t rs = check_rope(rope, head_dim);
-  if (rs != ATTN_OK) return rs;
-  if (pos0 < 0 || (int64_t)pos0 + T > INT32_MAX)
-    return fail(ATTN_ERR_SHAPE, "positions pos0=%d .. pos0+T-1 must lie in [0, 2^31-1)", pos0);
-  if (T == 0 || rope.rotary_dims == 0) return ok();
-  if (!table) return fail(ATTN_ERR_NULL, "table must be non-NULL");
-  if (!aligned16(table)) return fail(ATTN_ERR_SHAPE, "table must be 16-byte aligned");
-  return launch_status(attn::launch_rope_table(reinterpret_cast<float2*>(table), T,
-                                               rope.rotary_dims / 2, head_dim, pos0,
-                                               rope.theta,
-                                               reinterpret_cast<hipStream_t>(stream)),
-                       "rope table");
-}
-
 size_t attn_prefill_workspace_bytes(int32_t B, int32_t T, int32_t Hkv, int32_t Dk,
                                     attn_rope_t rope, int32_t rope_mask, attn_dtype_t dtype) {
   if (B <= 0 || T <= 0 || Hkv <= 0 || dtype != ATTN_BF16) return 0;
@@ -204,7 +181,7 @@ size_t attn_prefill_workspace_bytes(int32_t B, int32_t T, int32_t Hkv, int32_t D
 attn_status_t attn_prefill(const void* q, const void* k, const void* v, void* o,
                            int32_t B, int32_t T, int32_t Hq, int32_t Hkv, int32_t Dk,
                            int32_t Dv, int32_t window, float scale, attn_rope_t rope,
-                           int32_t rope_mask, const void* rope_table, void* workspace,
+                           int32_t rope_mask, int32_t pos0, void* workspace,
                            size_t workspace_bytes, attn_dtype_t dtype, void* stream) {
   if (dtype != ATTN_F32 && dtype != ATTN_BF16)
     return fail(ATTN_ERR_UNSUPPORTED, "dtype %d is not ATTN_F32 or ATTN_BF16", (int)dtype);
@@ -218,22 +195,20 @@ attn_status_t attn_prefill(const void* q, const void* k, const void* v, void* o,
     return fail(ATTN_ERR_SHAPE, "rope_mask=%d has unknown bits", rope_mask);
   attn_status_t rs = check_rope(rope, Dk);
   if (rs != ATTN_OK) return rs;
+  if (pos0 < 0 || (int64_t)pos0 + T > INT32_MAX)
+    return fail(ATTN_ERR_SHAPE, "positions pos0=%d .. pos0+T-1 must lie in [0, 2^31-1)", pos0);
   if (B == 0 || T == 0) return ok();
   if (!q || !k || !v || !o) return fail(ATTN_ERR_NULL, "q, k, v and o must be non-NULL");
-  const bool rot = prefill_uses_table(rope, rope_mask);
-  if (rot && !rope_table)
-    return fail(ATTN_ERR_NULL, "rope_table must be non-NULL when a rotation applies");
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) ||
-      (rot && !aligned16(rope_table)))
-    return fail(ATTN_ERR_SHAPE, "q, k, v, o and rope_table must be 16-byte aligned");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
+    return fail(ATTN_ERR_SHAPE, "q, k, v and o must be 16-byte aligned");
   const size_t es = elem_size(dtype);
   const size_t nq = (size_t)B * T * Hq * Dk * es, nk = (size_t)B * T * Hkv * Dk * es;
   const size_t nv = (size_t)B * T * Hkv * Dv * es, no = (size_t)B * T * Hq * Dv * es;
-  if (overlap(o, no, q, nq) || overlap(o, no, k, nk) || overlap(o, no, v, nv) ||
-      (rot && overlap(o, no, rope_table, attn_rope_table_bytes(T, rope.rotary_dims))))
-    return fail(ATTN_ERR_ALIAS, "o must not overlap q, k, v or rope_table");
+  if (overlap(o, no, q, nq) || overlap(o, no, k, nk) || overlap(o, no, v, nv))
+    return fail(ATTN_ERR_ALIAS, "o must not overlap q, k or v");
   if ((int64_t)B * T * Hq / 4 + 1 > INT32_MAX)
     return fail(ATTN_ERR_SHAPE, "B*T*Hq too large");
+  const bool rot = prefill_rotates(rope, rope_mask);
   const size_t nws = attn_prefill_workspace_bytes(B, T, Hkv, Dk, rope, rope_mask, dtype);
   if (nws > 0) {
     if (!workspace || workspace_bytes < nws)
@@ -241,9 +216,8 @@ attn_status_t attn_prefill(const void* q, const void* k, const void* v, void* o,
                   workspace_bytes, workspace);
     if (!aligned16(workspace)) return fail(ATTN_ERR_SHAPE, "workspace must be 16-byte aligned");
     if (overlap(workspace, nws, q, nq) || overlap(workspace, nws, k, nk) ||
-        overlap(workspace, nws, v, nv) || overlap(workspace, nws, o, no) ||
-        overlap(workspace, nws, rope_table, attn_rope_table_bytes(T, rope.rotary_dims)))
-      return fail(ATTN_ERR_ALIAS, "workspace must not overlap q, k, v, o or rope_table");
+        overlap(workspace, nws, v, nv) || overlap(workspace, nws, o, no))
+      return fail(ATTN_ERR_ALIAS, "workspace must not overlap q, k, v or o");
   }
 
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
@@ -255,14 +229,18 @@ attn_status_t attn_prefill(const void* q, const void* k, const void* v, void* o,
   a.rope_q = rot && (rope_mask & ATTN_ROPE_Q);
   a.rope_k = rot && (rope_mask & ATTN_ROPE_K);
   a.scale = scale;
-  a.rope_tab = rot ? reinterpret_cast<const float2*>(rope_table) : nullptr;
+  // Every kernel forms its angles from these (fp64), so all of them rotate
+  // token t by position pos0 + t with this call's rope settings.
+  a.pos0 = pos0;
+  a.log2_theta = rot ? std::log2(rope.theta) : 0.0;
   a.rope_rho = rot ? std::pow(rope.theta, -2.0 / (double)Dk) : 1.0;
   if (dtype == ATTN_BF16 &&
       attn::prefill_mfma_supported(Dk, Dv, Hq / Hkv, scale, rot ? rope.rotary_dims : 0)) {
-    if (a.rope_k) {
+    if (a.rope_k && nws > 0) {
       // K's rotary dims turn once here, not once per query tile in the kernel.
       attn_status_t r = launch_status(
-          attn::launch_rope_k_lead(k, workspace, a.rope_tab, B, T, Hkv, Dk, rope.rotary_dims, st),
+          attn::launch_rope_k_lead(k, workspace, B, T, Hkv, Dk, rope.rotary_dims, pos0,
+                                   rope.theta, st),
           "prefill (K rotation)");
       if (r != ATTN_OK) return r;
       a.k_rot = workspace;

@@ -8,16 +8,14 @@
 namespace attn {
 
 // ---- RoPE -----------------------------------------------------------------
-hipError_t launch_rope_table(float2* tab, int T, int P, int D, int pos0,
-                             double theta, hipStream_t st);
 // NH = 1: pos [N]; NH = 2 (2-D RoPE): pos [N, 2], each half of D turned by
 // its own coordinate. P = rotary pairs per half.
 hipError_t launch_prope(const void* x, void* y, const int32_t* pos, int N, int H,
                         int D, int P, int NH, double theta, bool bf16, hipStream_t st);
-// out[b, t, h, 0:R] = rotation of the first R dims of k[b, t, h, :] (bf16) by
-// the table row of token t; R = 2 * table pairs, a multiple of 8.
-hipError_t launch_rope_k_lead(const void* k, void* out, const float2* tab, int B, int T,
-                              int H, int D, int R, hipStream_t st);
+// out[b, t, h, 0:R] = rotation of the first R dims of k[b, t, h, :] (bf16) at
+// position pos0 + t; R a multiple of 8.
+hipError_t launch_rope_k_lead(const void* k, void* out, int B, int T, int H, int D, int R,
+                              int pos0, double theta, hipStream_t st);
 
 // ---- prefill ----------------------------------------------------------------
 struct PrefillArgs {
@@ -25,7 +23,6 @@ struct PrefillArgs {
   const void* k;
   const void* v;
   void* o;
-  const float2* rope_tab;  // [T][rot_pairs] cos/sin, or nullptr
   const void* k_rot;       // [B][T][Hkv][2*rot_pairs] K's rotary dims, turned (bf16 MFMA path)
   int B, T, Hq, Hkv, Dk, Dv;
   int window;              // 0: full causal
@@ -36,9 +33,12 @@ struct PrefillArgs {
   // and Dv for v, Hq * Dv and Dv for o); the 512-dim value path runs as two
   // 256-dim halves over strided views.
   int64_t v_tok = 0, v_head = 0, o_tok = 0, o_head = 0;
-  // theta^(-2/Dk): ratio of successive rotary frequencies of the table (row t
-  // of rope_tab turns pair p by (pos0 + t) * rope_rho^p). Kernels that turn a
-  // table row further by a small position offset use it.
+  // Token t sits at position pos0 + t; pair p turns by (pos0 + t) *
+  // theta^(-2p/Dk). log2_theta = log2(theta); rope_rho = theta^(-2/Dk), the
+  // ratio of successive pair frequencies (kernels that turn a base row further
+  // by a small position offset use it).
+  int pos0 = 0;
+  double log2_theta = 0.0;
   double rope_rho = 1.0;
 };
 

@@ -41,5 +41,71 @@ __device__ __forceinline__ u32x4 rotate4(u32x4 w, f32x4 t0, f32x4 t1) {
 }
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+typedef __attribute__((address_space(3))) f32x2 lds_float2;
+typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
+
+// Base row of a wave's Q rotation: slot[p] = (cos, sin) of pair p at position
+// pos (p < P), the angle pos * theta^(-2p/D) formed and evaluated in fp64.
+// Lanes take pairs lane, lane + 64, ...; the caller reads the slot only after
+// the wave's LDS writes landed (rotate_q_chunks waits for them).
+__device__ __forceinline__ void rope_base_row(lds_float2* slot, int64_t pos, int P, int D,
+                                              double log2_theta, int lane) {
+  for (int p = lane; p < P; p += 64) {
+    float c, s;
+    rope_cos_sin(pos, rope_freq(p, D, log2_theta), &c, &s);
+    slot[p] = f32x2{c, s};
+  }
+}
+
+// The (cos, sin) of d * rho^i for the pairs i = 8u + 4h + j (u < NU, j < 4)
+// of this lane's rotated Q^T chunks 2u + h: the small angle that turns the
+// base row's pair i from the wave's base position to the lane's own (d
+// positions further). rho = theta^(-2/D), so rho^i is pair i's frequency;
+// the powers come from an fp64 product chain, d * rho^i / (2 pi) is formed in
+// fp64 and its fraction goes through the sine and cosine units (which take
+// revolutions). Issued before the wait for Q, so it runs under Q's latency.
+template <int NU>
+__device__ __forceinline__ void rope_offsets(float (&dcs)[NU > 0 ? NU : 1][8], int d,
+                                             double rho, int h) {
+  const double rho2 = rho * rho, rho4 = rho2 * rho2, rho5 = rho4 * rho;
+  const double turns = (double)d * 0.15915494309189535;  // d / (2 pi)
+  double w = h ? rho4 : 1.0;
+#pragma unroll
+  for (int u = 0; u < NU; ++u)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float x = __builtin_amdgcn_fractf((float)(turns * w));
+      dcs[u][2 * j] = __builtin_amdgcn_cosf(x);
+      dcs[u][2 * j + 1] = __builtin_amdgcn_sinf(x);
+      w *= (j == 3) ? rho5 : rho;
+    }
+}
+
+// Turn this lane's first NU Q^T chunks (qw[u] = dims 16u + 8h .. +7) by the
+// base row in `slot` combined with the offsets from rope_offsets: (c, s) of
+// base + offset by angle addition, then rotate4. Waits for the slot's LDS
+// writes first, and for the slot's reads before returning (the memory clobber
+// keeps later DMAs into the slot's region behind them).
+template <int NU>
+__device__ __forceinline__ void rotate_q_chunks(u32x4* qw, const lds_float2* slot,
+                                                const float (&dcs)[NU > 0 ? NU : 1][8], int h) {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  const lds_f32x4* trow = (const lds_f32x4*)slot;
+#pragma unroll
+  for (int u = 0; u < NU; ++u) {
+    const f32x4 t0 = trow[4 * u + 2 * h], t1 = trow[4 * u + 2 * h + 1];
+    float cs[8];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float cb = (j < 2 ? t0 : t1)[2 * (j % 2)], sb = (j < 2 ? t0 : t1)[2 * (j % 2) + 1];
+      const float cd = dcs[u][2 * j], sd = dcs[u][2 * j + 1];
+      cs[2 * j] = cb * cd - sb * sd;
+      cs[2 * j + 1] = sb * cd + cb * sd;
+    }
+    qw[u] = rotate4(qw[u], f32x4{cs[0], cs[1], cs[2], cs[3]}, f32x4{cs[4], cs[5], cs[6], cs[7]});
+  }
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+}
+
 }  // namespace prefill
 }  // namespace attn

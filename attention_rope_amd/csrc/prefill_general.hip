@@ -8,7 +8,8 @@
 // layer keys 0..i; query head h reads KV head h / (Hq/Hkv).
 //
 // One wavefront per (batch, query head, query row). Lane l owns dimension
-// pairs l, l+64, ... of q/k and of v/o, so RoPE pairs stay inside a lane.
+// pairs l, l+64, ... of q/k and of v/o, so RoPE pairs stay inside a lane; each
+// rotation angle is formed and evaluated in fp64 where it is used.
 // Keys stream in order with an online softmax (running max and sum in fp32).
 #include "attn_common.h"
 #include "kernels.h"
@@ -42,17 +43,21 @@ __global__ __launch_bounds__(256) void prefill_general_kernel(PrefillArgs a) {
   const int g = h / G;
   const int PK = a.Dk / 2, PV = a.Dv / 2;
 
-  // Query pairs owned by this lane, rotated at token i.
+  // Frequencies of the rotary pairs this lane owns (fp64), and the query
+  // pairs, rotated at position pos0 + i.
+  double freq[kMaxPairs];
   float2 q[kMaxPairs];
 #pragma unroll
   for (int e = 0; e < kMaxPairs; ++e) {
     const int p = lane + 64 * e;
+    freq[e] = p < a.rot_pairs ? rope_freq(p, a.Dk, a.log2_theta) : 0.0;
     q[e] = make_float2(0.f, 0.f);
     if (p < PK) {
       float2 x = load_pair<BF16>(a.q, (((int64_t)b * a.T + i) * a.Hq + h) * a.Dk + 2 * p);
       if (a.rope_q && p < a.rot_pairs) {
-        const float2 cs = a.rope_tab[(int64_t)i * a.rot_pairs + p];
-        x = make_float2(x.x * cs.x - x.y * cs.y, x.x * cs.y + x.y * cs.x);
+        float c, sn;
+        rope_cos_sin((int64_t)a.pos0 + i, freq[e], &c, &sn);
+        x = make_float2(x.x * c - x.y * sn, x.x * sn + x.y * c);
       }
       q[e] = x;
     }
@@ -73,8 +78,9 @@ __global__ __launch_bounds__(256) void prefill_general_kernel(PrefillArgs a) {
       if (p < PK) {
         float2 kx = load_pair<BF16>(a.k, kbase + 2 * p);
         if (a.rope_k && p < a.rot_pairs) {
-          const float2 cs = a.rope_tab[(int64_t)j * a.rot_pairs + p];
-          kx = make_float2(kx.x * cs.x - kx.y * cs.y, kx.x * cs.y + kx.y * cs.x);
+          float c, sn;
+          rope_cos_sin((int64_t)a.pos0 + j, freq[e], &c, &sn);
+          kx = make_float2(kx.x * c - kx.y * sn, kx.x * sn + kx.y * c);
         }
         part += q[e].x * kx.x + q[e].y * kx.y;
       }

@@ -210,29 +210,25 @@ __global__ __launch_bounds__((Cfg<DK, DV, G, RCH>::NT), 1) void prefill_mfma_ker
   // Q^T operand: step s covers dims 16s + 8h .. 16s + 8h + 7 of this row.
   bf16x8 qf[DK / 16];
   {
-    const int tab_row = a.rot_pairs * 8;  // bytes per table row
-    const __amdgpu_buffer_rsrc_t tres = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)a.rope_tab, (short)0, rot_q ? T * tab_row : 0, 0x00020000);
     const int prow = valid ? pos : T - 1;
+    // Q's rotation by angle addition: the wave builds the (cos, sin) row of
+    // its first position in fp64 in block `wave` of ring stage 1 (which only
+    // this wave's own DMA of tile 1 overwrites, after the rotation), and each
+    // lane turns that row further by its offset d = prow - wlo (0..31).
+    const int base = min(wlo, T - 1);
+    lds_float2* slot = (lds_float2*)((lds_u8*)lds + C::ST_BYTES + wave * 1024);
     const uint16_t* qrow =
         (const uint16_t*)a.q + (((int64_t)b * T + prow) * a.Hq + head) * DK + 8 * h;
     u32x4 qw[DK / 16];
 #pragma unroll
     for (int s = 0; s < DK / 16; ++s) qw[s] = *(const u32x4*)(qrow + 16 * s);
     if (rot_q) {
-      // rotated chunks: chunk 2s + h < RCH  <=>  s < RCH/2 (RCH is even).
-      // All cos/sin loads go out at once (one memory round trip): the O
-      // accumulators are not live yet, so their registers hold the table.
-      constexpr int NR = RCH / 2 > 0 ? RCH / 2 : 1;
-      f32x4 t[NR][2];
-#pragma unroll
-      for (int u = 0; u < RCH / 2; ++u) {
-        const int off = prow * tab_row + (16 * u + 8 * h) * 4;
-        t[u][0] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(tres, off, 0, 0));
-        t[u][1] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(tres, off + 16, 0, 0));
-      }
-#pragma unroll
-      for (int u = 0; u < RCH / 2; ++u) qw[u] = rotate4(qw[u], t[u][0], t[u][1]);
+      rope_base_row(slot, (int64_t)a.pos0 + base, a.rot_pairs, DK, a.log2_theta, lane);
+      float dcs[RCH / 2 > 0 ? RCH / 2 : 1][8];
+      rope_offsets<RCH / 2>(dcs, prow - base, a.rope_rho, h);
+      __builtin_amdgcn_sched_barrier(0);
+      wait_vm<0>();  // Q landed (and tile 0 before it)
+      rotate_q_chunks<RCH / 2>(qw, slot, dcs, h);
     }
 #pragma unroll
     for (int s = 0; s < DK / 16; ++s) {

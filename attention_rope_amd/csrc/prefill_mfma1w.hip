@@ -84,6 +84,7 @@ struct Cfg1 {
   static_assert(KW + VW < 64, "vmcnt field");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS");
   static_assert(NW * RW * DV * 2 <= LDS_BYTES, "output staging fits");
+  static_assert(NW * DK * 4 <= VT_BYTES, "Q rotation rows fit the third V stage");
   static_assert(DK % 16 == 0 && DV % 32 == 0 && RCH % 2 == 0 && VC >= 16, "tiling");
 };
 
@@ -227,27 +228,26 @@ __global__ __launch_bounds__(NT, 1) void prefill_mfma1w_kernel(PrefillArgs a, in
   }
   bf16x8 qf[DK / 16];  // Q^T operand: step s covers dims 16s + 8h .. +7 of the row
   {
-    const int tab_row = a.rot_pairs * 8;  // bytes per table row
-    const __amdgpu_buffer_rsrc_t tres = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)a.rope_tab, (short)0, rot_q ? T * tab_row : 0, 0x00020000);
     const int prow = valid ? pos : T - 1;
+    // Q's rotation by angle addition: the wave builds the (cos, sin) row of
+    // its first position in fp64 in its slot of the third V stage (first
+    // refilled in iteration 1, after barriers), and each lane turns that row
+    // further by its offset d = prow - base (< 32) from it.
+    const int base = min(wlo, T - 1);
+    lds_float2* slot =
+        (lds_float2*)((lds_u8*)lds + C::V_OFF + 2 * C::VT_BYTES + wave * 2048);
     const uint16_t* qrow =
         (const uint16_t*)a.q + (((int64_t)b * T + prow) * a.Hq + head) * DK + 8 * h;
     u32x4 qw[DK / 16];
 #pragma unroll
     for (int s = 0; s < DK / 16; ++s) qw[s] = *(const u32x4*)(qrow + 16 * s);
     if (rot_q) {
-      // rotated chunks 2s + h < RCH <=> s < RCH/2; all cos/sin loads at once
-      constexpr int NR = RCH / 2 > 0 ? RCH / 2 : 1;
-      f32x4 t[NR][2];
-#pragma unroll
-      for (int u = 0; u < RCH / 2; ++u) {
-        const int off = prow * tab_row + (16 * u + 8 * h) * 4;
-        t[u][0] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(tres, off, 0, 0));
-        t[u][1] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(tres, off + 16, 0, 0));
-      }
-#pragma unroll
-      for (int u = 0; u < RCH / 2; ++u) qw[u] = rotate4(qw[u], t[u][0], t[u][1]);
+      rope_base_row(slot, (int64_t)a.pos0 + base, a.rot_pairs, DK, a.log2_theta, lane);
+      float dcs[RCH / 2 > 0 ? RCH / 2 : 1][8];
+      rope_offsets<RCH / 2>(dcs, prow - base, a.rope_rho, h);
+      __builtin_amdgcn_sched_barrier(0);
+      wait_vm<0>();  // Q landed (and K(0), V(0) before it)
+      rotate_q_chunks<RCH / 2>(qw, slot, dcs, h);
     }
     // Q^T is only ever an MFMA operand, so it lives in the AGPRs the O
     // accumulator (DV/2) and the QK result (16) leave free; the rest stays in

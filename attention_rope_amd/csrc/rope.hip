@@ -12,18 +12,6 @@
 
 namespace attn {
 
-// Cos/sin table for tokens 0..T-1 at positions pos0 + t: tab[t * P + p] =
-// (cos, sin) of pair p, P = rotary pairs. One thread per (t, p).
-__global__ void rope_table_kernel(float2* __restrict__ tab, int T, int P, int D,
-                                  int pos0, double log2_theta) {
-  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= (int64_t)T * P) return;
-  const int t = (int)(idx / P), p = (int)(idx % P);
-  float c, s;
-  rope_cos_sin((int64_t)pos0 + t, rope_freq(p, D, log2_theta), &c, &s);
-  tab[idx] = make_float2(c, s);
-}
-
 // y[n, h, :] = rope(x[n, h, :], pos[n]) with NH = 1 half, or 2-D RoPE with
 // NH = 2: each half of the D dims is a vector of its own, turned by its own
 // coordinate (pos[2n] the patch's width coordinate for the first half,
@@ -78,52 +66,63 @@ __global__ void prope_kernel(const T_* __restrict__ x, T_* __restrict__ y,
 }
 
 // K's rotary dims, turned once per key for the MFMA prefill: one thread per
-// (token, head, 8-dim chunk c < R/8) turns 4 pairs with the table row of its
-// token and writes them to out[b, t, h, 8c .. 8c+7] (bf16, fp32 arithmetic).
+// (token t, 8-dim chunk c < R/8) forms the angles of its 4 pairs at position
+// pos0 + t in fp64 once, then turns that chunk of every (batch, head) row of
+// the token and writes it to out[b, t, h, 8c .. 8c+7] (bf16, fp32 arithmetic).
+// Consecutive threads take consecutive chunks of one token, so each (b, h)
+// step reads and writes R/8 contiguous 16-byte pieces.
 __global__ void rope_k_lead_kernel(const uint16_t* __restrict__ k, uint16_t* __restrict__ out,
-                                   const float2* __restrict__ tab, int64_t n_chunks, int T,
-                                   int H, int D, int RC) {
+                                   int B, int T, int H, int D, int RC, int pos0,
+                                   double log2_theta) {
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= n_chunks) return;
+  if (idx >= (int64_t)T * RC) return;
   const int c = (int)(idx % RC);
-  const int64_t nh = idx / RC;  // (b*T + t)*H + h
-  const int t = (int)((nh / H) % T);
-  const u32x4 w = *reinterpret_cast<const u32x4*>(k + nh * D + 8 * c);
-  const f32x4 t0 = *reinterpret_cast<const f32x4*>(tab + (int64_t)t * (4 * RC) + 4 * c);
-  const f32x4 t1 = *reinterpret_cast<const f32x4*>(tab + (int64_t)t * (4 * RC) + 4 * c + 2);
-  u32x4 r;
+  const int t = (int)(idx / RC);
+  float cs[4], sn[4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const float cs = (j < 2) ? t0[2 * j] : t1[2 * (j - 2)];
-    const float sn = (j < 2) ? t0[2 * j + 1] : t1[2 * (j - 2) + 1];
-    const float x0 = bf16_lo(w[j]), x1 = bf16_hi(w[j]);
-    r[j] = pack_bf16x2(x0 * cs - x1 * sn, x0 * sn + x1 * cs);
+  for (int j = 0; j < 4; ++j)
+    rope_cos_sin((int64_t)pos0 + t, rope_freq(4 * c + j, D, log2_theta), &cs[j], &sn[j]);
+  // (b, h) rows n = b * H + h of token t, 8 at a time: all loads first, so
+  // every thread keeps 8 reads in flight.
+  const int BH = B * H;
+  for (int n0 = 0; n0 < BH; n0 += 8) {
+    u32x4 w[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int n = n0 + u;
+      if (n < BH) {
+        const int64_t nh = ((int64_t)(n / H) * T + t) * H + n % H;
+        w[u] = *reinterpret_cast<const u32x4*>(k + nh * D + 8 * c);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int n = n0 + u;
+      if (n < BH) {
+        const int64_t nh = ((int64_t)(n / H) * T + t) * H + n % H;
+        u32x4 r;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float x0 = bf16_lo(w[u][j]), x1 = bf16_hi(w[u][j]);
+          r[j] = pack_bf16x2(x0 * cs[j] - x1 * sn[j], x0 * sn[j] + x1 * cs[j]);
+        }
+        *reinterpret_cast<u32x4*>(out + nh * (8 * RC) + 8 * c) = r;
+      }
+    }
   }
-  *reinterpret_cast<u32x4*>(out + nh * (8 * RC) + 8 * c) = r;
 }
 
-hipError_t launch_rope_k_lead(const void* k, void* out, const float2* tab, int B, int T,
-                              int H, int D, int R, hipStream_t st) {
+hipError_t launch_rope_k_lead(const void* k, void* out, int B, int T, int H, int D, int R,
+                              int pos0, double theta, hipStream_t st) {
   if (R % 8 != 0 || D % 8 != 0 || R > D) return hipErrorInvalidValue;
-  const int64_t n = (int64_t)B * T * H * (R / 8);
-  if (n == 0) return hipSuccess;
+  const int64_t n = (int64_t)T * (R / 8);
+  if (n == 0 || B == 0 || H == 0) return hipSuccess;
   const int threads = 256;
   const int64_t blocks = (n + threads - 1) / threads;
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
   hipLaunchKernelGGL(rope_k_lead_kernel, dim3((unsigned)blocks), dim3(threads), 0, st,
                      reinterpret_cast<const uint16_t*>(k), reinterpret_cast<uint16_t*>(out),
-                     tab, n, T, H, D, R / 8);
-  return hipGetLastError();
-}
-
-hipError_t launch_rope_table(float2* tab, int T, int P, int D, int pos0,
-                             double theta, hipStream_t st) {
-  if ((int64_t)T * P == 0) return hipSuccess;
-  const int64_t n = (int64_t)T * P;
-  const int threads = 256;
-  const int blocks = (int)((n + threads - 1) / threads);
-  hipLaunchKernelGGL(rope_table_kernel, dim3(blocks), dim3(threads), 0, st, tab, T,
-                     P, D, pos0, log2(theta));
+                     B, T, H, D, R / 8, pos0, log2(theta));
   return hipGetLastError();
 }
 

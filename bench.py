@@ -1,39 +1,51 @@
 #!/usr/bin/env python3
 """Benchmark of the MI355X hybrid-attention hot path (one GPU).
 
-    python bench.py [--steps K] [--warmup W] [--workload NAME]
-                    [--secondary global_prefill,decode,stack]
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--secondary a,b,...]
 
-Prints ONE JSON line. `value` is the throughput of the headline workload
-(default: the local sliding-window prefill, B=4 T=4096 16q/8kv D=256 W=512,
-RoPE theta=1e4), in algorithmic TFLOP/s: FLOPs of allowed (query, key) pairs
-only, B*Hq*pairs(T,W)*2*(Dk+Dv). A step is one pass of the hot path over that
-batch: the RoPE cos/sin table for the positions, then attn_prefill, which
-turns K's rotary dims once into a workspace and runs the flash prefill kernel
-(Q rotated on load, window-aware tile skipping, QK^T and PV on bf16 MFMA,
-online softmax). The roofline entry times the attention kernel alone. The other workloads (global prefill, batched
-decode, the 7-layer local/global/shared-KV stack) are measured in the same
-run and reported under "secondary", each with its own roofline.
+Prints ONE JSON line. `value` is the throughput of the headline workload in
+algorithmic TFLOP/s: FLOPs of allowed (query, key) pairs only,
+B*Hq*pairs(T,W)*2*(Dk+Dv) per layer. The default headline is the largest
+single-GPU workload, the 7-layer stack (B=2, T=16384): 5 sliding-window local
+layers (W=1024, 16q/8kv, D=256, RoPE theta=1e4), one global layer (32q/4kv,
+Dk=512, Dv=256, p-RoPE on 128 of 512 dims, theta=1e6) and one global layer
+that reuses the previous layer's K/V. A step is one pass of the whole path
+over that batch: seven attn_prefill calls on one stream, each building its
+cos/sin table, turning K's rotary dims once and running the flash kernel.
 
-Inputs are synthetic and seeded (inputs/), resident in HBM before timing.
-Kernel durations come from HIP events recorded on the stream the kernels run
-on. The CPU baseline is the fp64 oracle timed on a bounded row sample of the
-headline workload on this host.
+Timing: HIP events recorded on the stream the kernels run on; W untimed
+warm-up steps, then exactly K timed steps between two device
+synchronisations; `ms_per_step` is the median step. The roofline entry is
+for the dominant kernel (the global layers' flash kernel, ~91 % of the
+FLOPs): its algorithmic FLOPs per launch over the mean duration of the
+global-layer calls inside the timed steps. `traffic` comes from committed
+rocprofv3 FETCH_SIZE / WRITE_SIZE summaries, and is null once the kernel's
+source has changed since they were taken.
+
+Secondary workloads (local prefill, global prefill, the small fp32 call,
+batched decode, the small models' 4:1 stack) are measured in the same run,
+each with its own roofline. The CPU baseline is the fp64 oracle timed on a
+seeded row subset of every layer of the headline stack on this host.
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
+import statistics
 import sys
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA (AMD spec, no sparsity)
-PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
+# MI355X published dense peaks (AMD specification, no sparsity).
+PEAK_BF16_TFLOPS = 2500.0
+PEAK_FP32_TFLOPS = 157.3
+PEAK_HBM_GBS = 8000.0
 PROFILES = os.path.join(ROOT, "profiles")
+MIN_TIMED_MS = 200.0
 
 
 def pairs(T: int, W: int) -> int:
@@ -55,13 +67,12 @@ def prefill_bytes(c) -> float:
 def rows_flops(c, rows) -> float:
     """Algorithmic FLOPs of a subset of query rows (all batches and heads)."""
     W = c.window if 0 < c.window < c.T else c.T
-    return float(sum(min(i + 1, W) for i in rows) * c.B * c.Hq * 2 * (c.Dk + c.Dv))
+    return float(sum(min(int(i) + 1, W) for i in rows) * c.B * c.Hq * 2 * (c.Dk + c.Dv))
 
 
 def _traffic(kernel: str, workload: str):
     """HBM bytes per launch from a committed counter summary, if it was taken
     on the current kernel source (else None)."""
-    import hashlib
     path = os.path.join(PROFILES, f"traffic_{kernel}_{workload}.json")
     if not os.path.exists(path):
         return None
@@ -77,12 +88,12 @@ def _traffic(kernel: str, workload: str):
     return rec.get("bytes_per_launch")
 
 
-class Timer:
-    """Event pairs on the current stream, one per step."""
+class Events:
+    """n_marks events per iteration on the current stream."""
 
-    def __init__(self, torch, n):
-        self.torch = torch
-        self.ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n)]
+    def __init__(self, torch, iters, n_marks):
+        self.ev = [[torch.cuda.Event(enable_timing=True) for _ in range(n_marks)]
+                   for _ in range(iters)]
 
     def mark(self, i, j):
         self.ev[i][j].record()
@@ -90,96 +101,178 @@ class Timer:
     def ms(self, i, a, b):
         return self.ev[i][a].elapsed_time(self.ev[i][b])
 
+    def series(self, a, b):
+        return [self.ms(i, a, b) for i in range(len(self.ev))]
 
-def bench_prefill(ar, torch, inputs, cfg, steps, warmup):
-    """Time the step (cos/sin table, then attn_prefill: K rotation pre-pass and
-    the attention kernel) and, separately, the attention kernel alone."""
+
+def timed(torch, body, iters, warmup, n_marks):
+    """Run body(ev, i) for `warmup` untimed and `iters` timed iterations
+    (ev None while warming up), with a device synchronisation on both sides
+    of the timed ones. Returns (events, wall seconds of the timed ones)."""
+    for _ in range(warmup):
+        body(None, 0)
+    torch.cuda.synchronize()
+    ev = Events(torch, iters, n_marks)
+    t0 = time.perf_counter()
+    for i in range(iters):
+        body(ev, i)
+    torch.cuda.synchronize()
+    return ev, time.perf_counter() - t0
+
+
+def iters_for(torch, body, n_marks, min_iters=10, min_ms=MIN_TIMED_MS, cap=5000):
+    """Timed iterations needed to span >= min_ms (from a short probe)."""
+    ev, _ = timed(torch, body, 3, 1, n_marks)
+    per = max(statistics.median(ev.series(0, n_marks - 1)), 1e-3)
+    return int(min(cap, max(min_iters, -(-min_ms // per) + 1)))
+
+
+def stats(xs):
+    return {"median": statistics.median(xs), "mean": sum(xs) / len(xs), "min": min(xs),
+            "max": max(xs)}
+
+
+def roofline(bound, achieved, peak, unit, traffic):
+    return {"bound": bound, "achieved": round(achieved, 3), "peak": peak, "unit": unit,
+            "frac": round(achieved / peak, 4), "traffic": traffic}
+
+
+# ---------------------------------------------------------------------------
+# Prefill workloads
+# ---------------------------------------------------------------------------
+def prefill_ws(ar, torch, cases):
+    """One workspace large enough for every call of `cases` (reused)."""
+    n = max(ar.prefill_workspace_bytes(c.B, c.T, c.Hkv, c.Dk, rotary_dims=c.rotary_dims,
+                                       theta=c.theta, dtype=c.dtype) for c in cases)
+    return torch.empty(max(n, 256), dtype=torch.uint8, device="cuda")
+
+
+def bench_prefill(ar, torch, inputs, cfg, warmup, iters=None):
+    """The attn_prefill call (cos/sin table, K rotation pre-pass, flash
+    kernel) and, separately, the flash kernel alone: a call with Q-only
+    rotation launches the same kernel instantiation with the same DMA volume
+    (K's rotary dims then come from k itself), after only the table."""
     c = cfg["case"]
     q, k, v = inputs.prefill_inputs(c, cfg["seed"], device="cuda")
     o = torch.empty((c.B, c.T, c.Hq, c.Dv), dtype=c.dtype, device="cuda")
-    tab = torch.empty((c.T, max(c.rotary_dims // 2, 1), 2), dtype=torch.float32, device="cuda")
-    nws = ar.prefill_workspace_bytes(c.B, c.T, c.Hkv, c.Dk, rotary_dims=c.rotary_dims,
-                                     theta=c.theta, dtype=c.dtype)
-    ws = torch.empty(max(nws, 16), dtype=torch.uint8, device="cuda")
+    ws = prefill_ws(ar, torch, [c])
 
-    def step(t=None, i=0):
-        if t: t.mark(i, 0)
-        ar.rope_table(c.T, head_dim=c.Dk, rotary_dims=c.rotary_dims, theta=c.theta,
-                      pos0=c.pos0, out=tab)
-        if t: t.mark(i, 1)
+    def call(ev, i, mask=ar.ROPE_Q | ar.ROPE_K):
+        if ev: ev.mark(i, 0)
         ar.prefill(q, k, v, window=c.window, scale=c.scale, rotary_dims=c.rotary_dims,
-                   theta=c.theta, pos0=c.pos0, out=o, table=tab, workspace=ws)
-        if t: t.mark(i, 2)
+                   theta=c.theta, pos0=c.pos0, out=o, workspace=ws, rope_mask=mask)
+        if ev: ev.mark(i, 1)
 
-    def kernel_only(t, i):
-        # Q-only rotation: the same kernel instantiation and launch with the
-        # same DMA volume (K's rotary dims are then read from k itself), and
-        # no pre-pass, so the events bracket the attention kernel alone.
-        t.mark(i, 0)
-        ar.prefill(q, k, v, window=c.window, scale=c.scale, rotary_dims=c.rotary_dims,
-                   theta=c.theta, pos0=c.pos0, out=o, table=tab, workspace=ws,
-                   rope_mask=ar.ROPE_Q)
-        t.mark(i, 1)
-
-    for _ in range(warmup):
-        step()
+    n = iters or iters_for(torch, call, 2)
+    ev, wall = timed(torch, call, n, warmup, 2)
+    call_ms = ev.series(0, 1)
+    kernel_only = lambda e, i: call(e, i, ar.ROPE_Q)
+    evk, _ = timed(torch, kernel_only, n, 3, 2)
+    kern_ms = evk.series(0, 1)
+    call(None, 0)  # leave o holding the full result
     torch.cuda.synchronize()
-    t = Timer(torch, steps)
-    t0 = time.perf_counter()
-    for i in range(steps):
-        step(t, i)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    step_ms = sum(t.ms(i, 0, 2) for i in range(steps)) / steps
-    call_ms = sum(t.ms(i, 1, 2) for i in range(steps)) / steps
-    span_ms = t.ev[0][0].elapsed_time(t.ev[-1][2])
-    tk = Timer(torch, steps)
-    for i in range(steps):
-        kernel_only(tk, i)
-    torch.cuda.synchronize()
-    kern_ms = sum(tk.ms(i, 0, 1) for i in range(steps)) / steps
-    step()  # leave o holding the full result
-    flops = prefill_flops(c)
-    return dict(flops=flops, bytes=prefill_bytes(c), step_ms=step_ms, call_ms=call_ms,
-                kern_ms=kern_ms, span_ms=span_ms, wall_s=wall, tensors=(q, k, v, o))
+    return dict(flops=prefill_flops(c), bytes=prefill_bytes(c), call=stats(call_ms),
+                kern=stats(kern_ms), iters=n, wall_s=wall, tensors=(q, k, v, o))
 
 
-def bench_prefill_kv_shared(ar, torch, inputs, cfg, steps, warmup):
+def bench_prefill_kv_shared(ar, torch, inputs, cfg, warmup):
     """The global prefill shape as a K = V layer: keys turned once by
-    prope_apply and passed as both k and v (RoPE on q only), 512-dim values.
-    Times the attention call (two passes over 256-dim value halves)."""
+    prope_apply and passed as both k and v (RoPE on q only), 512-dim values."""
     c = cfg["case"]
     q, k, _ = inputs.prefill_inputs(c, cfg["seed"], device="cuda")
     pos = torch.arange(c.T, dtype=torch.int32, device="cuda").repeat(c.B)
     kr = ar.prope(k.reshape(c.B * c.T, c.Hkv, c.Dk), pos, rotary_dims=c.rotary_dims,
                   theta=c.theta).reshape(c.B, c.T, c.Hkv, c.Dk)
+    del k
     o = torch.empty((c.B, c.T, c.Hq, c.Dk), dtype=c.dtype, device="cuda")
-    tab = ar.rope_table(c.T, head_dim=c.Dk, rotary_dims=c.rotary_dims, theta=c.theta,
-                        pos0=c.pos0)
+    ws = prefill_ws(ar, torch, [c])
 
-    def call():
+    def call(ev, i):
+        if ev: ev.mark(i, 0)
         ar.prefill(q, kr, kr, window=c.window, scale=c.scale, rotary_dims=c.rotary_dims,
-                   theta=c.theta, pos0=c.pos0, out=o, table=tab, rope_mask=ar.ROPE_Q)
+                   theta=c.theta, pos0=c.pos0, out=o, rope_mask=ar.ROPE_Q, workspace=ws)
+        if ev: ev.mark(i, 1)
 
-    for _ in range(warmup):
-        call()
-    torch.cuda.synchronize()
-    t = Timer(torch, steps)
-    for i in range(steps):
-        t.mark(i, 0)
-        call()
-        t.mark(i, 1)
-    torch.cuda.synchronize()
-    ms = sum(t.ms(i, 0, 1) for i in range(steps)) / steps
+    ev, _ = timed(torch, call, 10, warmup, 2)
+    ms = statistics.median(ev.series(0, 1))
     flops = float(c.B * c.Hq * pairs(c.T, c.window) * 2 * (c.Dk + c.Dk))
-    del q, k, kr, o
+    del q, kr, o
     return dict(flops=flops, ms=ms)
 
 
-def bench_decode(ar, torch, inputs, cfg, steps, warmup):
+def build_stack(ar, torch, inputs, cfg):
+    sc = cfg["case"]
+    layers = []
+    for li, (c, kv_from) in enumerate(sc.layers):
+        q, k, v = inputs.prefill_inputs(c, cfg["seed"], device="cuda", layer=li,
+                                        draw_kv=kv_from is None)
+        if kv_from is not None:
+            k, v = layers[kv_from]["k"], layers[kv_from]["v"]
+        o = torch.empty((c.B, c.T, c.Hq, c.Dv), dtype=c.dtype, device="cuda")
+        layers.append(dict(c=c, q=q, k=k, v=v, o=o, kv_from=kv_from, li=li))
+    return layers
+
+
+def bench_stack(ar, torch, inputs, cfg, steps, warmup):
+    """Steps over every layer of the stack on one stream, with an event
+    between consecutive layers (per-layer durations come out of the same
+    timed steps)."""
+    layers = build_stack(ar, torch, inputs, cfg)
+    ws = prefill_ws(ar, torch, [L["c"] for L in layers])
+    n = len(layers)
+
+    def step(ev, i):
+        for li, L in enumerate(layers):
+            c = L["c"]
+            if ev: ev.mark(i, li)
+            ar.prefill(L["q"], L["k"], L["v"], window=c.window, scale=c.scale,
+                       rotary_dims=c.rotary_dims, theta=c.theta, pos0=c.pos0, out=L["o"],
+                       workspace=ws)
+        if ev: ev.mark(i, n)
+
+    ev, wall = timed(torch, step, steps, warmup, n + 1)
+    step_ms = ev.series(0, n)
+    per_layer = [ev.series(li, li + 1) for li in range(n)]
+    flops = [prefill_flops(L["c"]) for L in layers]
+    return dict(flops=sum(flops), layer_flops=flops, step=stats(step_ms), step_series=step_ms,
+                layer_ms=per_layer, wall_s=wall, layers=layers)
+
+
+def stack_record(cfg, r):
+    """Per-layer detail of a stack run (median call time, TFLOP/s)."""
+    out = []
+    for L, fl, ms in zip(r["layers"], r["layer_flops"], r["layer_ms"]):
+        c = L["c"]
+        kind = "local" if c.window else ("global (shared K/V)" if L["kv_from"] is not None
+                                        else "global")
+        med = statistics.median(ms)
+        out.append({"layer": L["li"] + 1, "kind": kind, "ms": round(med, 4),
+                    "TFLOP/s": round(fl / med / 1e9, 2)})
+    return out
+
+
+def global_layer_roofline(r, traffic_workload):
+    """Dominant kernel of a stack: the global layers' flash kernel. Achieved =
+    a global layer's algorithmic FLOPs over the mean duration of the global
+    layers' calls in the timed steps (each call also builds its cos/sin
+    table and turns K's 128 rotary dims, ~0.1 % of the call)."""
+    g = [i for i, L in enumerate(r["layers"]) if not L["c"].window]
+    ms = [x for i in g for x in r["layer_ms"][i]]
+    mean_ms = sum(ms) / len(ms)
+    fl = r["layer_flops"][g[0]]
+    rl = roofline("mfma", fl / mean_ms / 1e9, PEAK_BF16_TFLOPS, "TFLOP/s",
+                  _traffic("prefill_mfma1w", traffic_workload))
+    rl.update(kernel="prefill_mfma1w_kernel", launches_per_step=len(g),
+              flops_per_launch=fl, launch_ms_mean=round(mean_ms, 4))
+    return rl
+
+
+# ---------------------------------------------------------------------------
+# Decode
+# ---------------------------------------------------------------------------
+def bench_decode(ar, torch, inputs, cfg, warmup):
     seed = cfg["seed"]
     calls = []
-    total_bytes = 0.0
     for name in ("glob", "loc"):
         d = cfg["cases"][name]
         kvl = inputs.decode_lengths(d, seed)          # same lengths for both calls
@@ -192,11 +285,10 @@ def bench_decode(ar, torch, inputs, cfg, steps, warmup):
         o = torch.empty((d.n_seq, d.Hq, d.Dv), dtype=d.dtype, device="cuda")
         vis = [min(int(n), d.window) if d.window > 0 else int(n) for n in kvl.tolist()]
         nbytes = sum(vis) * d.Hkv * (d.Dk + d.Dv) * 2 + d.n_seq * d.Hq * (d.Dk + d.Dv) * 2
-        total_bytes += nbytes
         calls.append(dict(name=name, d=d, q=q, kc=kc, vc=vc, off=offd, kvl=kvld, maxl=maxl,
-                          ws=ws, o=o, bytes=nbytes, kvl_host=kvl, off_host=off))
-    # A write larger than the 256 MB last-level (MALL) cache between steps, so
-    # no step reads cache lines a previous step left behind.
+                          ws=ws, o=o, bytes=nbytes, kvl_host=kvl, vis=vis))
+    # A write larger than the 256 MB last-level (MALL) cache before each timed
+    # call, so no call reads cache lines a previous one left behind.
     flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
 
     def run(cl):
@@ -205,47 +297,30 @@ def bench_decode(ar, torch, inputs, cfg, steps, warmup):
                   scale=d.scale, rotary_dims=d.rotary_dims, theta=d.theta,
                   max_kv_len=cl["maxl"], out=cl["o"], workspace=cl["ws"])
 
-    for _ in range(warmup):
-        for cl in calls:
-            run(cl)
-    torch.cuda.synchronize()
-    t = Timer(torch, steps)
-    for i in range(steps):
-        flush.fill_(i & 0xff)
-        t.mark(i, 0)
-        run(calls[0])
-        t.mark(i, 1)
-        run(calls[1])
-        t.mark(i, 2)
-    torch.cuda.synchronize()
-    g_ms = sum(t.ms(i, 0, 1) for i in range(steps)) / steps
-    l_ms = sum(t.ms(i, 1, 2) for i in range(steps)) / steps
+    def time_call(fn, n=10):
+        def body(ev, i):
+            flush.fill_(i & 0xff)
+            if ev: ev.mark(i, 0)
+            fn()
+            if ev: ev.mark(i, 1)
+        ev, _ = timed(torch, body, n, warmup, 2)
+        return statistics.median(ev.series(0, 1))
+
+    g_ms = time_call(lambda: run(calls[0]))
+    l_ms = time_call(lambda: run(calls[1]), n=40)
+    g = calls[0]
+    d = g["d"]
 
     # Keys as values (K = V) on the global shape: the global call's key cache
     # passed as both caches (Dv = Dk = 512), so each row is read once.
-    g = calls[0]
-    d = g["d"]
     o_kv = torch.empty((d.n_seq, d.Hq, d.Dk), dtype=d.dtype, device="cuda")
     ws_kv = torch.empty(ar.decode_workspace_bytes(d.n_seq, d.Hq, d.Hkv, d.Dk, g["maxl"],
                                                   d.window), dtype=torch.uint8, device="cuda")
-    vis = [min(int(n), d.window) if d.window > 0 else int(n) for n in g["kvl_host"].tolist()]
-    kv_bytes = sum(vis) * d.Hkv * d.Dk * 2 + d.n_seq * d.Hq * 2 * d.Dk * 2
-
-    def run_kv():
-        ar.decode(g["q"], g["kc"], g["kc"], g["off"], g["kvl"], window=d.window, scale=d.scale,
-                  rotary_dims=d.rotary_dims, theta=d.theta, max_kv_len=g["maxl"], out=o_kv,
-                  workspace=ws_kv)
-
-    for _ in range(warmup):
-        run_kv()
-    tk = Timer(torch, steps)
-    for i in range(steps):
-        flush.fill_(i & 0xff)
-        tk.mark(i, 0)
-        run_kv()
-        tk.mark(i, 1)
-    torch.cuda.synchronize()
-    kv_ms = sum(tk.ms(i, 0, 1) for i in range(steps)) / steps
+    kv_bytes = sum(g["vis"]) * d.Hkv * d.Dk * 2 + d.n_seq * d.Hq * 2 * d.Dk * 2
+    kv_ms = time_call(lambda: ar.decode(g["q"], g["kc"], g["kc"], g["off"], g["kvl"],
+                                        window=d.window, scale=d.scale,
+                                        rotary_dims=d.rotary_dims, theta=d.theta,
+                                        max_kv_len=g["maxl"], out=o_kv, workspace=ws_kv))
 
     # Verify (speculative decoding): the global call with its last 2 cache
     # rows taken as 2 new tokens per sequence (8 heads x 2 tokens fill the 16
@@ -256,24 +331,12 @@ def bench_decode(ar, torch, inputs, cfg, steps, warmup):
     ws_v = torch.empty(ar.verify_workspace_bytes(d.n_seq, n_q, d.Hq, d.Hkv, d.Dk, d.Dv,
                                                  g["maxl"], d.window),
                        dtype=torch.uint8, device="cuda")
-    v_bytes = (sum(vis) * d.Hkv * (d.Dk + d.Dv) * 2
+    v_bytes = (sum(g["vis"]) * d.Hkv * (d.Dk + d.Dv) * 2
                + d.n_seq * n_q * d.Hq * (d.Dk + d.Dv) * 2)
-
-    def run_v():
-        ar.verify(q_v, g["kc"], g["vc"], g["off"], g["kvl"], window=d.window, scale=d.scale,
-                  rotary_dims=d.rotary_dims, theta=d.theta, max_kv_len=g["maxl"], out=o_v,
-                  workspace=ws_v)
-
-    for _ in range(warmup):
-        run_v()
-    tv = Timer(torch, steps)
-    for i in range(steps):
-        flush.fill_(i & 0xff)
-        tv.mark(i, 0)
-        run_v()
-        tv.mark(i, 1)
-    torch.cuda.synchronize()
-    v_ms = sum(tv.ms(i, 0, 1) for i in range(steps)) / steps
+    v_ms = time_call(lambda: ar.verify(q_v, g["kc"], g["vc"], g["off"], g["kvl"],
+                                       window=d.window, scale=d.scale,
+                                       rotary_dims=d.rotary_dims, theta=d.theta,
+                                       max_kv_len=g["maxl"], out=o_v, workspace=ws_v))
 
     # int8 cache: the global call's caches quantised once (outside the timed
     # region), one scale per (row, KV head); the decode reads codes + scales.
@@ -283,78 +346,62 @@ def bench_decode(ar, torch, inputs, cfg, steps, warmup):
     ws_i8 = torch.empty(ar.decode_int8_workspace_bytes(d.n_seq, d.Hq, d.Hkv, d.Dv, g["maxl"],
                                                        d.window),
                         dtype=torch.uint8, device="cuda")
-    i8_bytes = (sum(vis) * d.Hkv * (d.Dk + d.Dv + 8)
+    i8_bytes = (sum(g["vis"]) * d.Hkv * (d.Dk + d.Dv + 8)
                 + d.n_seq * d.Hq * (d.Dk + d.Dv) * 2)
-
-    def run_i8():
-        ar.decode_int8(g["q"], kq, ks, vq, vs, g["off"], g["kvl"], window=d.window,
-                       scale=d.scale, rotary_dims=d.rotary_dims, theta=d.theta,
-                       max_kv_len=g["maxl"], out=o_i8, workspace=ws_i8)
-
-    for _ in range(warmup):
-        run_i8()
-    ti = Timer(torch, steps)
-    for i in range(steps):
-        flush.fill_(i & 0xff)
-        ti.mark(i, 0)
-        run_i8()
-        ti.mark(i, 1)
-    torch.cuda.synchronize()
-    i8_ms = sum(ti.ms(i, 0, 1) for i in range(steps)) / steps
-    del kq, vq
-    return dict(bytes=total_bytes, g_ms=g_ms, l_ms=l_ms, step_ms=g_ms + l_ms,
-                g_bytes=calls[0]["bytes"], l_bytes=calls[1]["bytes"], calls=calls,
-                kv_ms=kv_ms, kv_bytes=kv_bytes, kv_out=o_kv, v_ms=v_ms, v_bytes=v_bytes,
-                v_nq=n_q, i8_ms=i8_ms, i8_bytes=i8_bytes)
+    i8_ms = time_call(lambda: ar.decode_int8(g["q"], kq, ks, vq, vs, g["off"], g["kvl"],
+                                             window=d.window, scale=d.scale,
+                                             rotary_dims=d.rotary_dims, theta=d.theta,
+                                             max_kv_len=g["maxl"], out=o_i8, workspace=ws_i8))
+    del kq, vq, flush
+    return dict(g_ms=g_ms, l_ms=l_ms, g_bytes=g["bytes"], l_bytes=calls[1]["bytes"],
+                kv_ms=kv_ms, kv_bytes=kv_bytes, v_ms=v_ms, v_bytes=v_bytes, v_nq=n_q,
+                i8_ms=i8_ms, i8_bytes=i8_bytes)
 
 
-def bench_stack(ar, torch, inputs, cfg, steps, warmup):
-    sc = cfg["case"]
-    seed = cfg["seed"]
-    layers = []
-    for li, (c, kv_from) in enumerate(sc.layers):
-        q, k, v = inputs.prefill_inputs(c, seed, device="cuda", layer=li,
-                                        draw_kv=kv_from is None)
-        if kv_from is not None:
-            k, v = layers[kv_from]["k"], layers[kv_from]["v"]
-        o = torch.empty((c.B, c.T, c.Hq, c.Dv), dtype=c.dtype, device="cuda")
-        layers.append(dict(c=c, q=q, k=k, v=v, o=o, kv_from=kv_from))
-    loc, glo = sc.layers[0][0], sc.layers[sc.n_local][0]
-    tabs = {}
-    for c in (loc, glo):
-        tabs[id(c)] = torch.empty((c.T, c.rotary_dims // 2, 2), dtype=torch.float32,
-                                  device="cuda")
-    nws = max(ar.prefill_workspace_bytes(c.B, c.T, c.Hkv, c.Dk, rotary_dims=c.rotary_dims,
-                                         theta=c.theta, dtype=c.dtype) for c in (loc, glo))
-    ws = torch.empty(max(nws, 16), dtype=torch.uint8, device="cuda")  # reused layer by layer
-
-    def step(t=None, i=0):
-        if t: t.mark(i, 0)
-        for c in (loc, glo):  # one table per layer type, shared by its layers
-            ar.rope_table(c.T, head_dim=c.Dk, rotary_dims=c.rotary_dims, theta=c.theta,
-                          out=tabs[id(c)])
-        for L in layers:
-            c = L["c"]
-            ar.prefill(L["q"], L["k"], L["v"], window=c.window, scale=c.scale,
-                       rotary_dims=c.rotary_dims, theta=c.theta, out=L["o"],
-                       table=tabs[id(c)], workspace=ws)
-        if t: t.mark(i, 2)
-
-    for _ in range(warmup):
-        step()
-    torch.cuda.synchronize()
-    t = Timer(torch, steps)
-    for i in range(steps):
-        step(t, i)
-    torch.cuda.synchronize()
-    step_ms = sum(t.ms(i, 0, 2) for i in range(steps)) / steps
-    flops = sum(prefill_flops(L["c"]) for L in layers)
-    return dict(flops=flops, step_ms=step_ms, layers=layers)
+# ---------------------------------------------------------------------------
+# CPU baseline: the fp64 oracle on a seeded row subset of the stack
+# ---------------------------------------------------------------------------
+def cpu_baseline_stack(oracle, cfg, r, target_s):
+    """Time the oracle on every layer of the stack, on seeded query rows
+    (the first rows, window and tile edges, the last rows, plus random rows);
+    report algorithmic FLOP/s over the rows computed and the time the whole
+    stack would take at that rate."""
+    import numpy as np
+    import torch
+    n_rand = max(16, int(280 * target_s / 20.0))
+    rng = np.random.default_rng(cfg["seed"])
+    tot_fl, tot_s, rows_done, rows_all = 0.0, 0.0, 0, 0
+    for L in r["layers"]:
+        c = L["c"]
+        fixed = {0, 1, 2, 31, 32, 63, 64, c.T - 2, c.T - 1}
+        if c.window:
+            fixed |= {c.window - 1, c.window, c.window + 1}
+        rows = np.array(sorted(fixed | set(rng.choice(c.T, size=n_rand, replace=False)
+                                           .tolist())), dtype=np.int32)
+        idx = torch.as_tensor(rows, dtype=torch.long, device=L["q"].device)
+        qh = L["q"][:, idx].cpu()
+        kh, vh = L["k"].cpu(), L["v"].cpu()
+        t0 = time.perf_counter()
+        oracle.prefill(qh, kh, vh, window=c.window, scale=c.scale,
+                       rotary_dims=c.rotary_dims, theta=c.theta, rows=rows)
+        tot_s += time.perf_counter() - t0
+        tot_fl += rows_flops(c, rows)
+        rows_done += len(rows)
+        rows_all += c.T
+        del qh, kh, vh
+    rate = tot_fl / tot_s
+    return {"value": rate / 1e12, "unit": "TFLOP/s", "cores": oracle.max_threads(),
+            "kind": "oracle",
+            "sample": (f"{rows_done} of {rows_all} query rows over the 7 layers "
+                       f"(~{n_rand} seeded random rows per layer plus first/last/window-edge "
+                       f"rows), x B={r['layers'][0]['c'].B} x all heads; fp64 incl. K "
+                       f"rotation and KV replication per layer; {tot_s:.1f} s for "
+                       f"{tot_fl:.3e} FLOP; the full stack ({r['flops']:.3e} FLOP) "
+                       f"would take ~{r['flops'] / rate / 3600:.1f} h at this rate")}
 
 
-def cpu_baseline(oracle, inputs, cfg, res, target_s):
-    """Time the fp64 oracle on a growing sample of query rows (all batches and
-    heads) of the headline workload until one run takes >= target_s/4."""
+def cpu_baseline_prefill(oracle, cfg, res, target_s):
+    """The oracle on a seeded row sample of one prefill workload."""
     import numpy as np
     c = cfg["case"]
     q, k, v, _ = res["tensors"]
@@ -378,23 +425,95 @@ def cpu_baseline(oracle, inputs, cfg, res, target_s):
                       f"{dt:.1f} s"}
 
 
-def roofline(bound, achieved, peak, unit, traffic):
-    return {"bound": bound, "achieved": round(achieved, 3), "peak": peak, "unit": unit,
-            "frac": round(achieved / peak, 4), "traffic": traffic}
+# ---------------------------------------------------------------------------
+def secondary_prefill(ar, torch, inputs, name, sc):
+    fp32 = not str(sc["case"].dtype).endswith("bfloat16")
+    peak = PEAK_FP32_TFLOPS if fp32 else PEAK_BF16_TFLOPS
+    warm = 200 if name == "local_prefill" else (3 if name == "global_prefill" else 50)
+    rr = bench_prefill(ar, torch, inputs, sc, warm,
+                       iters=10 if name == "global_prefill" else None)
+    c = sc["case"]
+    kname = ("prefill_general" if fp32 else "prefill_mfma2g" if c.window and c.Hq // c.Hkv == 2
+             else "prefill_mfma1w" if c.Dk == 512 else "prefill_mfma")
+    tf_k = rr["flops"] / rr["kern"]["median"] / 1e9
+    rec = {"workload": sc["name"], "unit": "TFLOP/s",
+           "value": round(rr["flops"] / rr["call"]["median"] / 1e9, 3),
+           "ms_per_call": round(rr["call"]["median"], 5), "timed_calls": rr["iters"],
+           "what": "attn_prefill call: cos/sin table, K rotation pre-pass, flash kernel",
+           "roofline": dict(roofline("mfma", tf_k, peak, "TFLOP/s", _traffic(kname, name)),
+                            kernel=kname + "_kernel",
+                            kernel_ms=round(rr["kern"]["median"], 5),
+                            flops_per_launch=rr["flops"])}
+    if not fp32:
+        rec["roofline"]["hbm_frac_at_algorithmic_bytes"] = round(
+            rr["bytes"] / (rr["kern"]["median"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)
+    del rr
+    torch.cuda.empty_cache()
+    if name == "global_prefill":
+        kv = bench_prefill_kv_shared(ar, torch, inputs, sc, 1)
+        rec["keys_as_values"] = {
+            "TFLOP/s": round(kv["flops"] / kv["ms"] / 1e9, 3), "ms": round(kv["ms"], 4),
+            "what": "same shape as a K = V layer: rotated keys as both k and v, 512-dim "
+                    "values, attention call only (TFLOP/s counts the K = V layer's "
+                    "algorithmic FLOPs)"}
+    return rec
+
+
+def secondary_decode(ar, torch, inputs, sc):
+    rr = bench_decode(ar, torch, inputs, sc, 1)
+    g = rr["g_bytes"] / (rr["g_ms"] * 1e-3) / 1e9
+    l = rr["l_bytes"] / (rr["l_ms"] * 1e-3) / 1e9
+    step_ms = rr["g_ms"] + rr["l_ms"]
+
+    def leg(ms, nbytes, what, prof):
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        return {"GB/s": round(gbs, 1), "ms": round(ms, 4), "bytes": nbytes, "what": what,
+                "roofline": roofline("hbm", gbs, PEAK_HBM_GBS, "GB/s", _traffic(*prof))}
+
+    return {"workload": sc["name"], "unit": "GB/s",
+            "value": round((rr["g_bytes"] + rr["l_bytes"]) / (step_ms * 1e-3) / 1e9, 1),
+            "ms_per_step": round(step_ms, 4),
+            "global_call": {"GB/s": round(g, 1), "ms": round(rr["g_ms"], 4),
+                            "bytes": rr["g_bytes"]},
+            "local_call": {"GB/s": round(l, 1), "ms": round(rr["l_ms"], 4),
+                           "bytes": rr["l_bytes"],
+                           "roofline": roofline("hbm", l, PEAK_HBM_GBS, "GB/s", None)},
+            "keys_as_values_call": leg(rr["kv_ms"], rr["kv_bytes"],
+                                       "global shape with K = V: one 512-dim cache read "
+                                       "once for both products (Dv = Dk = 512)",
+                                       ("decode_ring", "kv_shared_global_decode")),
+            "verify_call": leg(rr["v_ms"], rr["v_bytes"],
+                               f"global call with {rr['v_nq']} new tokens per sequence "
+                               "(speculative-decoding verify)",
+                               ("decode_ring", "verify_global_decode")),
+            "int8_cache_call": leg(rr["i8_ms"], rr["i8_bytes"],
+                                   "global call over int8 codes + fp32 per-row scales "
+                                   "(same tokens; bytes counted as read)",
+                                   ("decode_i8", "int8_global_decode")),
+            "roofline": roofline("hbm", g, PEAK_HBM_GBS, "GB/s",
+                                 _traffic("decode_ring", "global_decode")),
+            "timing": "median of 10 calls (local: 40), 1 GiB MALL-evicting write before each"}
+
+
+def secondary_stack(ar, torch, inputs, name, sc):
+    rr = bench_stack(ar, torch, inputs, sc, 10, 2)
+    tf = rr["flops"] / rr["step"]["median"] / 1e9
+    rec = {"workload": sc["name"], "unit": "TFLOP/s", "value": round(tf, 3),
+           "ms_per_step": round(rr["step"]["median"], 4), "timed_steps": 10,
+           "layers": stack_record(sc, rr),
+           "roofline": global_layer_roofline(rr, name)}
+    del rr
+    return rec
 
 
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    # The GPU's clocks ramp up over the first tens of milliseconds of work: a
-    # few warm-up steps leave the headline step measured on a cold part
-    # (0.27-0.28 ms against 0.23 ms once warm), so the default warm-up runs
-    # ~0.15 s of untimed steps.
-    ap.add_argument("--warmup", type=int, default=500)
-    ap.add_argument("--workload", default="local_prefill",
-                    choices=["local_prefill", "global_prefill", "stack"])
-    ap.add_argument("--secondary", default="global_prefill,decode,stack",
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="stack", choices=["stack", "small_stack"])
+    ap.add_argument("--secondary",
+                    default="local_prefill,global_prefill,small_global_fp32,decode,small_stack",
                     help="other workloads measured in the same run, by name ('' for none)")
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -427,126 +546,60 @@ def main():
         return
 
     cfg = inputs.WORKLOADS[args.workload]
-    # Steps of tens of milliseconds (global prefill, stack) warm the part in
-    # a few steps; cap their warm-up so the default run stays short.
-    warmup = args.warmup if args.workload == "local_prefill" else min(args.warmup, 10)
-    if cfg["kind"] == "stack":
-        r = bench_stack(ar, torch, inputs, cfg, args.steps, warmup)
-        value, kern_ms = r["flops"] / r["step_ms"] / 1e9, r["step_ms"]
-        bound_rl = roofline("mfma", value, PEAK_BF16_TFLOPS, "TFLOP/s", None)
-    else:
-        r = bench_prefill(ar, torch, inputs, cfg, args.steps, warmup)
-        value = r["flops"] / r["step_ms"] / 1e9
-        kern = r["flops"] / r["kern_ms"] / 1e9
-        # the local layers' kernel (two workgroups per CU); the global shape
-        # runs the one-wave kernel
-        kname = "prefill_mfma2g" if cfg["case"].window else "prefill_mfma1w"
-        wl = "local_prefill" if cfg["case"].window else "global_prefill"
-        bound_rl = roofline("mfma", kern, PEAK_BF16_TFLOPS, "TFLOP/s", _traffic(kname, wl))
-        bound_rl["kernel"] = kname + "_kernel"
-        bound_rl["kernel_ms"] = round(r["kern_ms"], 5)
-        bound_rl["prefill_call_ms"] = round(r["call_ms"], 5)  # K rotation + kernel
-        bound_rl["hbm_frac_at_algorithmic_bytes"] = round(
-            r["bytes"] / (r["kern_ms"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)
+    r = bench_stack(ar, torch, inputs, cfg, args.steps, args.warmup)
+    med = r["step"]["median"]
+    value = r["flops"] / med / 1e9
+    timed_ms = sum(r["step_series"])
     out = {
         "metric": "prefill attn TFLOP/s & decode KV GB/s, as % of MI355X MFMA/HBM peak",
         "value": round(value, 3),
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
-        "warmup": warmup,
-        "ms_per_step": round(r["step_ms"], 5),
+        "warmup": args.warmup,
+        "ms_per_step": round(med, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
-        "data": "synthetic (seeded N(0,1) / U(-1,1) inputs, no weights)",
+        "data": "synthetic (seeded N(0,1) inputs, no weights)",
         "config": {"workload": cfg["name"], "workload_key": args.workload,
-                   "seed": cfg["seed"], "parallelism": "none (1 GPU)"},
-        "roofline": bound_rl,
+                   "seed": cfg["seed"], "flops_per_step": r["flops"],
+                   "parallelism": "none (1 GPU)"},
+        "roofline": global_layer_roofline(r, args.workload),
+        "timing": {"ms_per_step_median": round(med, 4),
+                   "ms_per_step_mean": round(r["step"]["mean"], 4),
+                   "ms_per_step_min": round(r["step"]["min"], 4),
+                   "ms_per_step_max": round(r["step"]["max"], 4),
+                   "timed_gpu_ms": round(timed_ms, 2),
+                   "timed_wall_ms": round(r["wall_s"] * 1e3, 2),
+                   "how": "HIP events on the kernels' stream, one pair per step and per "
+                          "layer; median of the timed steps"},
+        "layers": stack_record(cfg, r),
     }
+    if not args.no_cpu_baseline:
+        import oracle
+        out["cpu_baseline"] = cpu_baseline_stack(oracle, cfg, r, args.cpu_seconds)
+    del r
+    torch.cuda.empty_cache()
 
     secondary = {}
     for s in [x.strip() for x in args.secondary.split(",") if x.strip()]:
         if s == args.workload:
             continue
-        if s not in inputs.WORKLOADS or s == "small_global_fp32":
+        if s not in inputs.WORKLOADS:
             raise SystemExit(f"--secondary: unknown workload {s!r}")
         sc = inputs.WORKLOADS[s]
-        torch.cuda.empty_cache()
         if sc["kind"] == "prefill":
-            rr = bench_prefill(ar, torch, inputs, sc, max(3, args.steps // 4), 1)
-            tf = rr["flops"] / rr["kern_ms"] / 1e9
-            secondary[s] = {"workload": sc["name"], "unit": "TFLOP/s",
-                                 "value": round(rr["flops"] / rr["step_ms"] / 1e9, 3),
-                                 "ms_per_step": round(rr["step_ms"], 4),
-                                 "roofline": dict(roofline("mfma", tf, PEAK_BF16_TFLOPS, "TFLOP/s",
-                                                           _traffic("prefill_mfma1w", "global_prefill")),
-                                                  kernel="prefill_mfma1w_kernel")}
-            del rr
-            torch.cuda.empty_cache()
-            kv = bench_prefill_kv_shared(ar, torch, inputs, sc, max(2, args.steps // 8), 1)
-            secondary[s]["keys_as_values"] = {
-                "TFLOP/s": round(kv["flops"] / kv["ms"] / 1e9, 3), "ms": round(kv["ms"], 4),
-                "what": "same shape as a K = V layer: rotated keys as both k and v, 512-dim "
-                        "values, attention call only (two passes over 256-dim value halves; "
-                        "TFLOP/s counts the K = V layer's algorithmic FLOPs)"}
+            secondary[s] = secondary_prefill(ar, torch, inputs, s, sc)
         elif sc["kind"] == "decode":
-            rr = bench_decode(ar, torch, inputs, sc, max(3, args.steps // 4), 1)
-            gbs = rr["bytes"] / (rr["step_ms"] * 1e-3) / 1e9
-            g = rr["g_bytes"] / (rr["g_ms"] * 1e-3) / 1e9
-            l = rr["l_bytes"] / (rr["l_ms"] * 1e-3) / 1e9
-            secondary[s] = {"workload": sc["name"], "unit": "GB/s", "value": round(gbs, 1),
-                                 "ms_per_step": round(rr["step_ms"], 4),
-                                 "global_call": {"GB/s": round(g, 1), "ms": round(rr["g_ms"], 4),
-                                                 "bytes": rr["g_bytes"]},
-                                 "local_call": {"GB/s": round(l, 1), "ms": round(rr["l_ms"], 4),
-                                                "bytes": rr["l_bytes"]},
-                                 "keys_as_values_call": {
-                                     "GB/s": round(rr["kv_bytes"] / (rr["kv_ms"] * 1e-3) / 1e9, 1),
-                                     "ms": round(rr["kv_ms"], 4), "bytes": rr["kv_bytes"],
-                                     "what": "global shape with K = V: one 512-dim cache read "
-                                             "once for both products (Dv = Dk = 512)",
-                                     "roofline": roofline(
-                                         "hbm", rr["kv_bytes"] / (rr["kv_ms"] * 1e-3) / 1e9,
-                                         PEAK_HBM_GBS, "GB/s",
-                                         _traffic("decode_ring", "kv_shared_global_decode"))},
-                                 "verify_call": {
-                                     "GB/s": round(rr["v_bytes"] / (rr["v_ms"] * 1e-3) / 1e9, 1),
-                                     "ms": round(rr["v_ms"], 4), "bytes": rr["v_bytes"],
-                                     "what": f"global call with {rr['v_nq']} new tokens per "
-                                             "sequence (speculative-decoding verify)",
-                                     "roofline": roofline(
-                                         "hbm", rr["v_bytes"] / (rr["v_ms"] * 1e-3) / 1e9,
-                                         PEAK_HBM_GBS, "GB/s",
-                                         _traffic("decode_ring", "verify_global_decode"))},
-                                 "int8_cache_call": {
-                                     "GB/s": round(rr["i8_bytes"] / (rr["i8_ms"] * 1e-3) / 1e9, 1),
-                                     "ms": round(rr["i8_ms"], 4), "bytes": rr["i8_bytes"],
-                                     "what": "global call over int8 codes + fp32 per-row scales "
-                                             "(same tokens; bytes counted as read)",
-                                     "roofline": roofline(
-                                         "hbm", rr["i8_bytes"] / (rr["i8_ms"] * 1e-3) / 1e9,
-                                         PEAK_HBM_GBS, "GB/s",
-                                         _traffic("decode_i8", "int8_global_decode"))},
-                                 "roofline": roofline("hbm", g, PEAK_HBM_GBS, "GB/s",
-                                                      _traffic("decode_ring", "global_decode"))}
-            del rr
+            secondary[s] = secondary_decode(ar, torch, inputs, sc)
         else:
-            rr = bench_stack(ar, torch, inputs, sc, max(3, args.steps // 4), 1)
-            tf = rr["flops"] / rr["step_ms"] / 1e9
-            secondary[s] = {"workload": sc["name"], "unit": "TFLOP/s", "value": round(tf, 3),
-                                 "ms_per_step": round(rr["step_ms"], 4),
-                                 "roofline": roofline("mfma", tf, PEAK_BF16_TFLOPS, "TFLOP/s",
-                                                      None)}
-            del rr
+            secondary[s] = secondary_stack(ar, torch, inputs, s, sc)
         torch.cuda.synchronize()
+        torch.cuda.empty_cache()
     if secondary:
         out["secondary"] = secondary
-
-    if not args.no_cpu_baseline and cfg["kind"] == "prefill":
-        import oracle
-        out["cpu_baseline"] = cpu_baseline(oracle, inputs, cfg, r, args.cpu_seconds)
     print(json.dumps(out), flush=True)
 
 

@@ -65,32 +65,20 @@ typedef struct {
 enum { ATTN_ROPE_Q = 1, ATTN_ROPE_K = 2 };
 
 /*
- * RoPE cos/sin table for token positions pos0 .. pos0 + T - 1:
- * table[t][p] = (cos, sin) of (pos0 + t) * theta^(-2p/head_dim) as two fp32,
- * for pairs p < rope.rotary_dims / 2 (angles formed and evaluated in fp64).
- * It depends on positions and RoPE settings only, so one table serves every
- * layer of a type (and every batch row) that shares them.
- *   table: device buffer of attn_rope_table_bytes(T, rope.rotary_dims) bytes,
- *   16-byte aligned. head_dim even, rotary_dims <= head_dim, T >= 0,
- *   pos0 >= 0, pos0 + T <= 2^31 - 1.
- */
-size_t attn_rope_table_bytes(int32_t T, int32_t rotary_dims);
-
-attn_status_t attn_rope_table(void *table, int32_t T, int32_t pos0, int32_t head_dim,
-                              attn_rope_t rope, void *stream);
-
-/*
  * Prefill: o = softmax(scale * rope(q) rope(k)^T + mask) v for every query
  * row, per batch b and query head h, with KV head h / (Hq / Hkv).
+ * Source: "Gemma 4: End-to-End Architecture Walkthrough", Phase 3 section 3a
+ * (a local layer's query sees a fixed window of recent keys, a global layer's
+ * every earlier key), section 3b (grouped-query attention: 2 query heads per
+ * KV head on local layers, 8 on global ones, with wider global keys) and
+ * section 3c (p-RoPE turns only the leading rotary pairs; the angle is the
+ * token position times the pair's frequency).
  *   q [B, T, Hq, Dk], k [B, T, Hkv, Dk], v [B, T, Hkv, Dv]: unrotated inputs;
  *   o [B, T, Hq, Dv] output; must not overlap q, k or v.
- *   Token t's rotation comes from row t of rope_table (made by attn_rope_table
- *   for the same T, head_dim = Dk and rope settings; the caller keeps them
- *   consistent: some kernels read one row per 32 tokens and turn it further
- *   by the token's offset at the frequencies theta^(-2p/Dk), so the rows must
- *   be those of consecutive positions). rope_mask: ATTN_ROPE_Q | ATTN_ROPE_K
- *   selects which of q and k are rotated; with rope.rotary_dims == 0 or
- *   rope_mask == 0 nothing turns and rope_table may be NULL.
+ *   Token t of every batch row sits at position pos0 + t (pos0 >= 0,
+ *   pos0 + T <= 2^31 - 1); rope_mask: ATTN_ROPE_Q | ATTN_ROPE_K selects which
+ *   of q and k are rotated there. rope.rotary_dims == 0 or rope_mask == 0:
+ *   nothing turns.
  *   window: <= 0 or >= T gives full causal attention; otherwise query i sees
  *   keys j with i - window < j <= i (the window includes the query itself).
  *   scale: finite (1/sqrt(Dk) in the usual model).
@@ -103,11 +91,18 @@ attn_status_t attn_rope_table(void *table, int32_t T, int32_t pos0, int32_t head
  *   Keys as values (K = V on a global layer): turn k once with prope_apply,
  *   pass it as both k and v with rope_mask = ATTN_ROPE_Q; the values are
  *   then the rotated keys, as a decode over that cache sees them.
- * Workspace: attn_prefill_workspace_bytes() bytes of device memory (0 when no
- *   workspace is needed, then workspace may be NULL). The bf16 path turns the
- *   rotary dims of every key once into it before attending; contents are
- *   scratch, owned by the caller, and must not overlap any other argument.
- *   Too small or NULL when needed: ATTN_ERR_WORKSPACE.
+ *   Every rotation angle is (pos0 + t) * theta^(-2p/Dk), formed from this
+ *   call's own pos0 and rope arguments in fp64 inside the kernels.
+ * Workspace: attn_prefill_workspace_bytes() bytes of device memory, 16-byte
+ *   aligned (0 when nothing needs it: workspace may then be NULL). On the
+ *   bf16 path the call turns K's rotary dims once into it before attending.
+ *   Contents are scratch, owned by the caller; the workspace must not overlap
+ *   any tensor argument.
+ * Errors (nothing is launched): NULL tensors -> ATTN_ERR_NULL; bad sizes,
+ *   rope settings, pos0 or alignment -> ATTN_ERR_SHAPE; an unknown dtype ->
+ *   ATTN_ERR_UNSUPPORTED; workspace missing or too small ->
+ *   ATTN_ERR_WORKSPACE; overlaps -> ATTN_ERR_ALIAS; a refused launch ->
+ *   ATTN_ERR_LAUNCH.
  * All tensor pointers must be 16-byte aligned.
  */
 size_t attn_prefill_workspace_bytes(int32_t B, int32_t T, int32_t Hkv, int32_t Dk,
@@ -117,13 +112,17 @@ size_t attn_prefill_workspace_bytes(int32_t B, int32_t T, int32_t Hkv, int32_t D
 attn_status_t attn_prefill(const void *q, const void *k, const void *v, void *o,
                            int32_t B, int32_t T, int32_t Hq, int32_t Hkv,
                            int32_t Dk, int32_t Dv, int32_t window, float scale,
-                           attn_rope_t rope, int32_t rope_mask,
-                           const void *rope_table, void *workspace,
-                           size_t workspace_bytes, attn_dtype_t dtype,
-                           void *stream);
+                           attn_rope_t rope, int32_t rope_mask, int32_t pos0,
+                           void *workspace, size_t workspace_bytes,
+                           attn_dtype_t dtype, void *stream);
 
 /*
  * Decode: one new token per sequence over a ragged KV cache (bf16 only).
+ * Source: "Gemma 4: End-to-End Architecture Walkthrough", Phase 3 section 3b
+ * (global layers must keep the keys and values of the whole context; local
+ * layers only their window) and "Gemma 4 Architecture Reference", "Shared KV
+ * Cache"; the new token attends the cache exactly as its row of a prefill
+ * over the whole sequence would.
  *   q [B, Hq, Dk]: the new tokens' queries, unrotated; sequence b's query sits
  *     at position kv_len[b] - 1 and is rotated there (rope applies to q only).
  *   k_cache [rows, Hkv, Dk], v_cache [rows, Hkv, Dv]: cached keys (stored
@@ -147,7 +146,9 @@ attn_status_t attn_prefill(const void *q, const void *k, const void *v, void *o,
  *     drafter's k-th proposal at position L + k over a target cache of L
  *     rows, turn q there with prope_apply, then call attn_decode with
  *     rope.rotary_dims = 0, kv_len = L and window = W - k - 1 (0 for global
- *     layers).
+ *     layers). On a local layer this holds for k < W - 1; from k = W - 1 on
+ *     no target row lies inside the proposal's window, so there is nothing to
+ *     attend (the result is the empty-row 0) and no call is made.
  * Supported: Hq % Hkv == 0 with Hq / Hkv <= 16, Dk in {128, 256, 512},
  *   Dv in {128, 256} (or 512 with Dk = 512); max_kv_len >= 1, and a cache
  *   that fits one call (ATTN_ERR_SHAPE past about 5 * 10^8 rows per sequence,
@@ -200,9 +201,15 @@ attn_status_t attn_verify(const void *q, const void *k_cache, const void *v_cach
 
 /*
  * (p-)RoPE on its own: y[n, h, :] = rope(x[n, h, :], positions[n]).
+ * Source: "Gemma 4: End-to-End Architecture Walkthrough", Phase 3 section 3c
+ * (pair p of a head vector turns by position * theta^(-2p/D); p-RoPE keeps
+ * only the leading quarter of the pairs turning) and "Gemma 4 Architecture
+ * Reference", "Positional Encoding: Proportional RoPE (p-RoPE)" (p = 0.25,
+ * theta = 1e6 on global layers).
  *   x, y [N, H, D]; positions: device int32 [N], each >= 0.
  *   y may equal x (in place: dims >= rotary_dims are then not touched);
- *   partial overlap is rejected. D even, 2 <= D <= 1024.
+ *   partial overlap is rejected (ATTN_ERR_ALIAS). D even, 2 <= D <= 1024;
+ *   bad sizes or rope settings -> ATTN_ERR_SHAPE; NULL -> ATTN_ERR_NULL.
  */
 attn_status_t prope_apply(const void *x, void *y, const int32_t *positions,
                           int32_t N, int32_t H, int32_t D, attn_rope_t rope,

@@ -176,23 +176,35 @@ LOCAL = dict(Hq=16, Hkv=8, Dk=256, Dv=256, rotary_dims=256, theta=1e4)
 GLOBAL = dict(Hq=32, Hkv=4, Dk=512, Dv=256, rotary_dims=128, theta=1e6)
 
 
+# The small models' layer shapes: 8 query heads share one KV head on both
+# layer types, 256-dim local heads, 512-dim global keys, window 512.
+SMALL_LOCAL = dict(Hq=8, Hkv=1, Dk=256, Dv=256, rotary_dims=256, theta=1e4)
+SMALL_GLOBAL = dict(Hq=8, Hkv=1, Dk=512, Dv=256, rotary_dims=128, theta=1e6)
+
+
 @dataclass
 class StackCase:
-    """Layers 1-5 local (window 1024), layer 6 global, layer 7 global reusing
-    layer 6's K/V (only a new Q is drawn)."""
+    """n_local local layers (sliding window), then one global layer, then (with
+    shared_kv) a global layer reusing the previous global layer's K/V (only a
+    new Q is drawn). The default is the 5:1 stack with a shared-KV layer."""
     B: int = 2
     T: int = 16384
     n_local: int = 5
     window: int = 1024
     dtype: torch.dtype = torch.bfloat16
+    local: dict = field(default_factory=lambda: dict(LOCAL))
+    glob: dict = field(default_factory=lambda: dict(GLOBAL))
+    shared_kv: bool = True
     layers: list = field(default_factory=list)
 
     def __post_init__(self):
         if not self.layers:
-            loc = PrefillCase(self.B, self.T, window=self.window, dtype=self.dtype, **LOCAL)
-            glo = PrefillCase(self.B, self.T, window=0, dtype=self.dtype, **GLOBAL)
+            loc = PrefillCase(self.B, self.T, window=self.window, dtype=self.dtype, **self.local)
+            glo = PrefillCase(self.B, self.T, window=0, dtype=self.dtype, **self.glob)
             # (case, kv_from_layer): kv_from_layer is None when the layer owns K/V.
-            self.layers = [(loc, None)] * self.n_local + [(glo, None), (glo, self.n_local)]
+            self.layers = [(loc, None)] * self.n_local + [(glo, None)]
+            if self.shared_kv:
+                self.layers.append((glo, self.n_local))
 
 
 WORKLOADS = {
@@ -216,4 +228,12 @@ WORKLOADS = {
             name="decode bf16 64 seqs L~U[1024,131072]: global 32q/4kv 512/256 + local 16q/8kv 256 W=1024"),
     "stack": dict(kind="stack", seed=SEED0 + 5, case=StackCase(),
             name="stack bf16 B=2 T=16384: 5 local W=1024 + global + shared-KV global"),
+    # The small models' 4:1 pattern (4 local layers of window 512, then one
+    # global layer), 8 query heads per KV head throughout; same batch and
+    # length as the 5:1 stack.
+    "small_stack": dict(kind="stack", seed=SEED0 + 6,
+            case=StackCase(n_local=4, window=512, local=dict(SMALL_LOCAL),
+                           glob=dict(SMALL_GLOBAL), shared_kv=False),
+            name="small-model stack bf16 B=2 T=16384: 4 local W=512 8q/1kv D=256 + "
+                 "global 8q/1kv Dk=512 Dv=256"),
 }

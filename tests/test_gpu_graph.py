@@ -17,7 +17,6 @@ def test_graph_replays_match_eager(gpu_lib):
                            dtype=BF)
     q, k, v = inputs.prefill_inputs(c, 31, device=DEV)
     o = torch.empty((1, 640, 16, 256), dtype=BF, device=DEV)
-    tab = torch.empty((640, 128, 2), dtype=torch.float32, device=DEV)
     ws = torch.empty(ar.prefill_workspace_bytes(1, 640, 8, 256, rotary_dims=256, theta=1e4),
                      dtype=torch.uint8, device=DEV)
     d = inputs.DecodeCase(3, 32, 4, 512, 256, window=0, rotary_dims=128, theta=1e6,
@@ -30,9 +29,8 @@ def test_graph_replays_match_eager(gpu_lib):
                       device=DEV)
 
     def step():
-        ar.rope_table(640, head_dim=256, rotary_dims=256, theta=1e4, out=tab)
         ar.prefill(q, k, v, window=128, scale=c.scale, rotary_dims=256, theta=1e4, out=o,
-                   table=tab, workspace=ws)
+                   pos0=17, workspace=ws)
         ar.decode(dq, kc, vc, off, kvl, rotary_dims=128, theta=1e6, max_kv_len=3000, out=do,
                   workspace=dws)
 
@@ -45,7 +43,6 @@ def test_graph_replays_match_eager(gpu_lib):
     for r in range(3):
         o.zero_()
         do.zero_()
-        tab.zero_()
         ws.zero_()
         # unrelated eager work between replays
         ar.prefill(q[:, :64].contiguous(), k[:, :64].contiguous(), v[:, :64].contiguous(),

@@ -91,18 +91,23 @@ def test_prefill_rope_mask(gpu_lib, rope_mask):
     run_case(gpu_lib, 1, 90, 4, 2, 256, 256, 40, 256, 1e4, BF, rope_mask=rope_mask)
 
 
-@pytest.mark.parametrize("pos0", [1, 1000, 131000])
+@pytest.mark.parametrize("pos0", [1, 1000, 131000, 2 ** 31 - 78])
 def test_prefill_pos0(gpu_lib, pos0):
+    """Token t at position pos0 + t, up to the largest position the ABI takes
+    (2^31 - 2): the 512-dim-key kernel, the 8-wave kernel (8 q heads per KV
+    head, 128- and 256-dim heads), the K pre-pass, and the fp32 general kernel."""
     run_case(gpu_lib, 1, 77, 16, 2, 512, 256, 0, 128, 1e6, BF, pos0=pos0)
+    run_case(gpu_lib, 1, 77, 8, 1, 128, 128, 0, 32, 1e6, BF, pos0=pos0)
+    run_case(gpu_lib, 1, 77, 8, 1, 256, 256, 30, 256, 1e4, BF, pos0=pos0)
     run_case(gpu_lib, 1, 77, 8, 1, 128, 128, 0, 32, 1e6, F32, pos0=pos0)
 
 
 @pytest.mark.parametrize("R", [64, 256])
-@pytest.mark.parametrize("pos0", [1, 1000, 131000])
+@pytest.mark.parametrize("pos0", [1, 1000, 131000, 2 ** 31 - 301])
 def test_prefill_local_pos0(gpu_lib, pos0, R):
-    # The local-layer kernel (256-dim heads, 2 q heads per KV head) turns q by
-    # the table row of its wave's first position and then by the lane's offset
-    # from it, so a table for positions pos0.. must still match the oracle.
+    # Each kernel turns q by the (cos, sin) row of its wave's first position
+    # (fp64) and then by the lane's offset from it; both must give what the
+    # oracle's direct rotation at pos0 + t gives.
     run_case(gpu_lib, 1, 300, 16, 8, 256, 256, 128, R, 1e4, BF, rope_mask=1, pos0=pos0)
     run_case(gpu_lib, 2, 97, 4, 2, 256, 256, 0, R, 1e6, BF, rope_mask=3, pos0=pos0)
 

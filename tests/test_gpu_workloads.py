@@ -33,9 +33,8 @@ def prefill_case(name, rows_random):
     cfg = inputs.WORKLOADS[name]
     c = cfg["case"]
     q, k, v = inputs.prefill_inputs(c, cfg["seed"], device=DEV)
-    tab = ar.rope_table(c.T, head_dim=c.Dk, rotary_dims=c.rotary_dims, theta=c.theta)
     o = ar.prefill(q, k, v, window=c.window, scale=c.scale, rotary_dims=c.rotary_dims,
-                   theta=c.theta, table=tab)
+                   theta=c.theta)
     torch.cuda.synchronize()
     rows = None if rows_random is None else sample_rows(c.T, c.window, rows_random, cfg["seed"])
     qh = q.cpu() if rows is None else q.cpu()[:, rows]
@@ -147,18 +146,13 @@ def test_stack_full_size():
     cfg = inputs.WORKLOADS["stack"]
     sc = cfg["case"]
     layers = []
-    tabs = {}
     for li, (c, kv_from) in enumerate(sc.layers):
         q, k, v = inputs.prefill_inputs(c, cfg["seed"], device=DEV, layer=li,
                                         draw_kv=kv_from is None)
         if kv_from is not None:
             k, v = layers[kv_from][1], layers[kv_from][2]
-        key = (c.Dk, c.rotary_dims, c.theta)
-        if key not in tabs:
-            tabs[key] = ar.rope_table(c.T, head_dim=c.Dk, rotary_dims=c.rotary_dims,
-                                      theta=c.theta)
         o = ar.prefill(q, k, v, window=c.window, scale=c.scale, rotary_dims=c.rotary_dims,
-                       theta=c.theta, table=tabs[key])
+                       theta=c.theta)
         layers.append((q, k, v, o, c))
     torch.cuda.synchronize()
     # the shared-KV layer equals a standalone call on layer 6's K/V, bit for bit
