@@ -59,12 +59,10 @@ bool prefill_rotates(attn_rope_t rope, int32_t rope_mask) {
   return rope.rotary_dims > 0 && (rope_mask & (ATTN_ROPE_Q | ATTN_ROPE_K)) != 0;
 }
 
-// The bf16 MFMA path turns K's rotary dims ahead of the attention kernel, into
-// the workspace, for the rotary widths it is built for.
-bool prefill_turns_k_ahead(int32_t Dk, attn_rope_t rope, int32_t rope_mask) {
-  const int r = rope.rotary_dims;
-  return (rope_mask & ATTN_ROPE_K) && r > 0 && (r == Dk || r == Dk / 4) && r % 8 == 0 &&
-         (Dk == 128 || Dk == 256 || Dk == 512);
+// Whenever K turns, its rotary dims turn once ahead of the attention kernel,
+// into the workspace ([B, T, Hkv, rotary_dims] in the call's element type).
+bool prefill_turns_k_ahead(attn_rope_t rope, int32_t rope_mask) {
+  return (rope_mask & ATTN_ROPE_K) && rope.rotary_dims > 0;
 }
 
 // attn_decode (n_q = 1) and attn_verify (n_q new tokens per sequence).
@@ -173,9 +171,9 @@ const char* attn_last_error(void) { return g_last_error.c_str(); }
 
 size_t attn_prefill_workspace_bytes(int32_t B, int32_t T, int32_t Hkv, int32_t Dk,
                                     attn_rope_t rope, int32_t rope_mask, attn_dtype_t dtype) {
-  if (B <= 0 || T <= 0 || Hkv <= 0 || dtype != ATTN_BF16) return 0;
-  if (!prefill_turns_k_ahead(Dk, rope, rope_mask)) return 0;
-  return (size_t)B * T * Hkv * rope.rotary_dims * 2;
+  if (B <= 0 || T <= 0 || Hkv <= 0 || (dtype != ATTN_BF16 && dtype != ATTN_F32)) return 0;
+  if (rope.rotary_dims > Dk || !prefill_turns_k_ahead(rope, rope_mask)) return 0;
+  return (size_t)B * T * Hkv * rope.rotary_dims * elem_size(dtype);
 }
 
 attn_status_t attn_prefill(const void* q, const void* k, const void* v, void* o,
@@ -234,17 +232,17 @@ attn_status_t attn_prefill(const void* q, const void* k, const void* v, void* o,
   a.pos0 = pos0;
   a.log2_theta = rot ? std::log2(rope.theta) : 0.0;
   a.rope_rho = rot ? std::pow(rope.theta, -2.0 / (double)Dk) : 1.0;
+  if (a.rope_k && nws > 0) {
+    // K's rotary dims turn once here, not once per query tile in the kernel.
+    attn_status_t r = launch_status(
+        attn::launch_rope_k_lead(k, workspace, B, T, Hkv, Dk, rope.rotary_dims, pos0,
+                                 rope.theta, dtype == ATTN_BF16, st),
+        "prefill (K rotation)");
+    if (r != ATTN_OK) return r;
+    a.k_rot = workspace;
+  }
   if (dtype == ATTN_BF16 &&
       attn::prefill_mfma_supported(Dk, Dv, Hq / Hkv, scale, rot ? rope.rotary_dims : 0)) {
-    if (a.rope_k && nws > 0) {
-      // K's rotary dims turn once here, not once per query tile in the kernel.
-      attn_status_t r = launch_status(
-          attn::launch_rope_k_lead(k, workspace, B, T, Hkv, Dk, rope.rotary_dims, pos0,
-                                   rope.theta, st),
-          "prefill (K rotation)");
-      if (r != ATTN_OK) return r;
-      a.k_rot = workspace;
-    }
     hipError_t e = attn::launch_prefill_mfma(a, st);
     if (e != hipErrorNotSupported) return launch_status(e, "prefill (mfma)");
   }

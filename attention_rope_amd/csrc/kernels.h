@@ -12,10 +12,10 @@ namespace attn {
 // its own coordinate. P = rotary pairs per half.
 hipError_t launch_prope(const void* x, void* y, const int32_t* pos, int N, int H,
                         int D, int P, int NH, double theta, bool bf16, hipStream_t st);
-// out[b, t, h, 0:R] = rotation of the first R dims of k[b, t, h, :] (bf16) at
-// position pos0 + t; R a multiple of 8.
+// out[b, t, h, 0:R] = rotation of the first R dims of k[b, t, h, :] at
+// position pos0 + t (bf16 or fp32 elements, R even).
 hipError_t launch_rope_k_lead(const void* k, void* out, int B, int T, int H, int D, int R,
-                              int pos0, double theta, hipStream_t st);
+                              int pos0, double theta, bool bf16, hipStream_t st);
 
 // ---- prefill ----------------------------------------------------------------
 struct PrefillArgs {
@@ -23,7 +23,7 @@ struct PrefillArgs {
   const void* k;
   const void* v;
   void* o;
-  const void* k_rot;       // [B][T][Hkv][2*rot_pairs] K's rotary dims, turned (bf16 MFMA path)
+  const void* k_rot;       // [B][T][Hkv][2*rot_pairs] K's rotary dims, turned (when K turns)
   int B, T, Hq, Hkv, Dk, Dv;
   int window;              // 0: full causal
   int rot_pairs;           // rotary pairs (0: none)

@@ -8,8 +8,9 @@
 // layer keys 0..i; query head h reads KV head h / (Hq/Hkv).
 //
 // One wavefront per (batch, query head, query row). Lane l owns dimension
-// pairs l, l+64, ... of q/k and of v/o, so RoPE pairs stay inside a lane; each
-// rotation angle is formed and evaluated in fp64 where it is used.
+// pairs l, l+64, ... of q/k and of v/o, so RoPE pairs stay inside a lane. The
+// query's angles are formed in fp64 here; K's rotary pairs arrive turned by
+// the pre-pass (k_rot).
 // Keys stream in order with an online softmax (running max and sum in fp32).
 #include "attn_common.h"
 #include "kernels.h"
@@ -43,20 +44,18 @@ __global__ __launch_bounds__(256) void prefill_general_kernel(PrefillArgs a) {
   const int g = h / G;
   const int PK = a.Dk / 2, PV = a.Dv / 2;
 
-  // Frequencies of the rotary pairs this lane owns (fp64), and the query
-  // pairs, rotated at position pos0 + i.
-  double freq[kMaxPairs];
+  // The query pairs this lane owns, rotated at position pos0 + i (angles in
+  // fp64).
   float2 q[kMaxPairs];
 #pragma unroll
   for (int e = 0; e < kMaxPairs; ++e) {
     const int p = lane + 64 * e;
-    freq[e] = p < a.rot_pairs ? rope_freq(p, a.Dk, a.log2_theta) : 0.0;
     q[e] = make_float2(0.f, 0.f);
     if (p < PK) {
       float2 x = load_pair<BF16>(a.q, (((int64_t)b * a.T + i) * a.Hq + h) * a.Dk + 2 * p);
       if (a.rope_q && p < a.rot_pairs) {
         float c, sn;
-        rope_cos_sin((int64_t)a.pos0 + i, freq[e], &c, &sn);
+        rope_cos_sin((int64_t)a.pos0 + i, rope_freq(p, a.Dk, a.log2_theta), &c, &sn);
         x = make_float2(x.x * c - x.y * sn, x.x * sn + x.y * c);
       }
       q[e] = x;
@@ -71,17 +70,16 @@ __global__ __launch_bounds__(256) void prefill_general_kernel(PrefillArgs a) {
   const int lo = (a.window > 0) ? max(0, i - a.window + 1) : 0;
   for (int j = lo; j <= i; ++j) {
     const int64_t kbase = (((int64_t)b * a.T + j) * a.Hkv + g) * a.Dk;
+    const int64_t krbase = (((int64_t)b * a.T + j) * a.Hkv + g) * (2 * a.rot_pairs);
     float part = 0.f;
 #pragma unroll
     for (int e = 0; e < kMaxPairs; ++e) {
       const int p = lane + 64 * e;
       if (p < PK) {
-        float2 kx = load_pair<BF16>(a.k, kbase + 2 * p);
-        if (a.rope_k && p < a.rot_pairs) {
-          float c, sn;
-          rope_cos_sin((int64_t)a.pos0 + j, freq[e], &c, &sn);
-          kx = make_float2(kx.x * c - kx.y * sn, kx.x * sn + kx.y * c);
-        }
+        // K's rotary pairs come turned from the pre-pass (k_rot).
+        const float2 kx = (a.rope_k && p < a.rot_pairs)
+                              ? load_pair<BF16>(a.k_rot, krbase + 2 * p)
+                              : load_pair<BF16>(a.k, kbase + 2 * p);
         part += q[e].x * kx.x + q[e].y * kx.y;
       }
     }

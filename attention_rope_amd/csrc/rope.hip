@@ -112,8 +112,75 @@ __global__ void rope_k_lead_kernel(const uint16_t* __restrict__ k, uint16_t* __r
   }
 }
 
+hipError_t launch_rope_k_chunks(const void* k, void* out, int B, int T, int H, int D, int R,
+                                int pos0, double theta, hipStream_t st);
+
+// The same for any even R and either element type (the general prefill path):
+// one thread per (token t, pair p) forms the angle once and turns pair p of
+// every (batch, head) row of the token into out[b, t, h, 2p .. 2p+1].
+template <typename T_>
+__global__ void rope_k_pairs_kernel(const T_* __restrict__ k, T_* __restrict__ out, int B,
+                                    int T, int H, int D, int P, int pos0, double log2_theta) {
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= (int64_t)T * P) return;
+  const int p = (int)(idx % P);
+  const int t = (int)(idx / P);
+  float c, sn;
+  rope_cos_sin((int64_t)pos0 + t, rope_freq(p, D, log2_theta), &c, &sn);
+  const int BH = B * H;
+  for (int n0 = 0; n0 < BH; n0 += 8) {
+    float2 x[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int n = n0 + u;
+      if (n < BH) {
+        const int64_t nh = ((int64_t)(n / H) * T + t) * H + n % H;
+        if constexpr (sizeof(T_) == 2) {
+          const uint32_t w = reinterpret_cast<const uint32_t*>(k + nh * D)[p];
+          x[u] = make_float2(bf16_lo(w), bf16_hi(w));
+        } else {
+          x[u] = reinterpret_cast<const float2*>(k + nh * D)[p];
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int n = n0 + u;
+      if (n < BH) {
+        const int64_t nh = ((int64_t)(n / H) * T + t) * H + n % H;
+        const float y0 = x[u].x * c - x[u].y * sn, y1 = x[u].x * sn + x[u].y * c;
+        if constexpr (sizeof(T_) == 2)
+          reinterpret_cast<uint32_t*>(out + nh * (2 * P))[p] = pack_bf16x2(y0, y1);
+        else
+          reinterpret_cast<float2*>(out + nh * (2 * P))[p] = make_float2(y0, y1);
+      }
+    }
+  }
+}
+
 hipError_t launch_rope_k_lead(const void* k, void* out, int B, int T, int H, int D, int R,
-                              int pos0, double theta, hipStream_t st) {
+                              int pos0, double theta, bool bf16, hipStream_t st) {
+  if (R % 2 != 0 || R > D || D % 2 != 0) return hipErrorInvalidValue;
+  if ((int64_t)T * R == 0 || B == 0 || H == 0) return hipSuccess;
+  const int threads = 256;
+  if (!bf16 || R % 8 != 0 || D % 8 != 0) {
+    const int64_t blocks = ((int64_t)T * (R / 2) + threads - 1) / threads;
+    if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+    if (bf16)
+      hipLaunchKernelGGL(rope_k_pairs_kernel<uint16_t>, dim3((unsigned)blocks), dim3(threads), 0,
+                         st, (const uint16_t*)k, (uint16_t*)out, B, T, H, D, R / 2, pos0,
+                         log2(theta));
+    else
+      hipLaunchKernelGGL(rope_k_pairs_kernel<float>, dim3((unsigned)blocks), dim3(threads), 0,
+                         st, (const float*)k, (float*)out, B, T, H, D, R / 2, pos0,
+                         log2(theta));
+    return hipGetLastError();
+  }
+  return launch_rope_k_chunks(k, out, B, T, H, D, R, pos0, theta, st);
+}
+
+hipError_t launch_rope_k_chunks(const void* k, void* out, int B, int T, int H, int D, int R,
+                                int pos0, double theta, hipStream_t st) {
   if (R % 8 != 0 || D % 8 != 0 || R > D) return hipErrorInvalidValue;
   const int64_t n = (int64_t)T * (R / 8);
   if (n == 0 || B == 0 || H == 0) return hipSuccess;

@@ -83,17 +83,19 @@ def test_prefill_validation(lib):
 
 
 def test_prefill_workspace(lib):
-    """bf16 with K turning at a width the MFMA path serves: K's rotary dims
-    [B, T, Hkv, R] bf16; nothing otherwise (angles are formed in-kernel)."""
+    """Whenever K turns, its rotary dims [B, T, Hkv, R] in the call's element
+    type; nothing otherwise (every angle is formed in-kernel)."""
     ws = lib.attn_prefill_workspace_bytes
     assert ws(2, 8, 4, 128, R(32, 1e6), 3, ar.ATTN_BF16) == 2 * 8 * 4 * 32 * 2
     assert ws(2, 8, 4, 256, R(256, 1e4), 2, ar.ATTN_BF16) == 2 * 8 * 4 * 256 * 2
-    # nothing to turn ahead: q only, no rope, fp32, or a width the general path serves
+    assert ws(2, 8, 4, 128, R(32, 1e6), 3, ar.ATTN_F32) == 2 * 8 * 4 * 32 * 4
+    assert ws(2, 8, 4, 128, R(6, 1e6), 2, ar.ATTN_BF16) == 2 * 8 * 4 * 6 * 2
+    # nothing to turn ahead: q only, no rope, empty, bad dtype or width
     assert ws(2, 8, 4, 128, R(32, 1e6), 1, ar.ATTN_BF16) == 0
     assert ws(2, 8, 4, 128, R(0, 1e6), 3, ar.ATTN_BF16) == 0
-    assert ws(2, 8, 4, 128, R(32, 1e6), 3, ar.ATTN_F32) == 0
-    assert ws(2, 8, 4, 128, R(64, 1e6), 3, ar.ATTN_BF16) == 0
     assert ws(0, 8, 4, 128, R(32, 1e6), 3, ar.ATTN_BF16) == 0
+    assert ws(2, 8, 4, 128, R(32, 1e6), 3, 9) == 0
+    assert ws(2, 8, 4, 128, R(130, 1e6), 3, ar.ATTN_BF16) == 0
     kw = dict(Dk=128, Dv=128, rope=R(32, 1e6))
     need = 1 * 8 * 2 * 32 * 2
     assert _prefill(lib, **kw) == 4                                   # missing
@@ -102,8 +104,8 @@ def test_prefill_workspace(lib):
     assert _prefill(lib, ws=P(0x50000008), ws_bytes=need, **kw) == 2    # misaligned
     assert _prefill(lib, ws=FAKE, ws_bytes=need, **kw) == 6             # overlaps q/k/v
     assert _prefill(lib, ws=FAKE2, ws_bytes=need, **kw) == 6            # overlaps o
-    # rotation on a path that needs no workspace: fp32, or q only
-    assert _prefill(lib, rope=R(32, 1e4), dtype=ar.ATTN_F32, q=None) == 1
+    assert _prefill(lib, dtype=ar.ATTN_F32, **kw) == 4                  # fp32 turns K too
+    # q-only rotation needs no workspace (the NULL q is what fails)
     assert _prefill(lib, rope=R(32, 1e4), rope_mask=1, q=None) == 1
 
 

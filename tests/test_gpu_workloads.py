@@ -142,8 +142,11 @@ def int8_case(d, q, kc, vc, off, kvl, maxl):
     torch.cuda.empty_cache()
 
 
-def test_stack_full_size():
-    cfg = inputs.WORKLOADS["stack"]
+def stack_case(name, rows_random):
+    """Every layer of a stack workload as the benchmark runs it (one
+    attn_prefill call per layer, shared-KV layers handed the earlier layer's
+    K/V), each against the oracle on sampled rows."""
+    cfg = inputs.WORKLOADS[name]
     sc = cfg["case"]
     layers = []
     for li, (c, kv_from) in enumerate(sc.layers):
@@ -153,22 +156,55 @@ def test_stack_full_size():
             k, v = layers[kv_from][1], layers[kv_from][2]
         o = ar.prefill(q, k, v, window=c.window, scale=c.scale, rotary_dims=c.rotary_dims,
                        theta=c.theta)
-        layers.append((q, k, v, o, c))
+        layers.append((q, k, v, o, c, kv_from))
     torch.cuda.synchronize()
-    # the shared-KV layer equals a standalone call on layer 6's K/V, bit for bit
-    q7, k6, v6, o7, c7 = layers[-1]
-    assert k6.data_ptr() == layers[-2][1].data_ptr()
-    alone = ar.prefill(q7, k6.clone(), v6.clone(), window=0, scale=c7.scale,
-                       rotary_dims=c7.rotary_dims, theta=c7.theta)
-    torch.cuda.synchronize()
-    assert torch.equal(alone, o7)
-    for li, (q, k, v, o, c) in enumerate(layers):
-        rows = sample_rows(c.T, c.window, 12, 50 + li)
+    for li, (q, k, v, o, c, kv_from) in enumerate(layers):
+        if kv_from is None:
+            continue
+        # a shared-KV layer equals a standalone call on the earlier layer's K/V, bit for bit
+        assert k.data_ptr() == layers[kv_from][1].data_ptr()
+        alone = ar.prefill(q, k.clone(), v.clone(), window=c.window, scale=c.scale,
+                           rotary_dims=c.rotary_dims, theta=c.theta)
+        torch.cuda.synchronize()
+        assert torch.equal(alone, o)
+    for li, (q, k, v, o, c, _) in enumerate(layers):
+        rows = sample_rows(c.T, c.window, rows_random, 50 + li)
         ref = oracle.prefill(q.cpu()[:, rows], k.cpu(), v.cpu(), window=c.window,
                              scale=c.scale, rotary_dims=c.rotary_dims, theta=c.theta,
                              rows=rows)
         got = o[:, torch.as_tensor(rows, device=DEV, dtype=torch.long)]
-        mx, rel = assert_close(got, ref, c.dtype, f"stack layer {li + 1}")
-        print(f"stack layer {li + 1}: max_abs={mx:.3e} rel_rms={rel:.3e}", flush=True)
+        mx, rel = assert_close(got, ref, c.dtype, f"{name} layer {li + 1}")
+        print(f"{name} layer {li + 1}: rows={len(rows)} max_abs={mx:.3e} rel_rms={rel:.3e}",
+              flush=True)
     del layers
     torch.cuda.empty_cache()
+
+
+def test_stack_full_size():
+    stack_case("stack", 12)
+
+
+def test_small_stack_full_size():
+    """The small models' 4:1 stack (window 512, 8 query heads per KV head)."""
+    stack_case("small_stack", 12)
+
+
+@pytest.mark.parametrize("shape", ["global", "local_w512", "local_w1024", "small_local_w512"])
+def test_full_tensor_T2048(shape):
+    """Every output element at T = 2048 against the oracle, in the head shapes
+    of the workloads: global (32q/4kv, 512-dim keys, 256-dim values, p-RoPE),
+    local (16q/8kv, 256-dim heads, full RoPE) at both windows, and the small
+    models' local layer (8q/1kv)."""
+    shapes = {"global": (inputs.GLOBAL, 0), "local_w512": (inputs.LOCAL, 512),
+              "local_w1024": (inputs.LOCAL, 1024), "small_local_w512": (inputs.SMALL_LOCAL, 512)}
+    kw, W = shapes[shape]
+    c = inputs.PrefillCase(1, 2048, window=W, dtype=torch.bfloat16, **kw)
+    q, k, v = inputs.prefill_inputs(c, 77, device=DEV)
+    print(f"T=2048 {shape}", flush=True)
+    o = ar.prefill(q, k, v, window=c.window, scale=c.scale, rotary_dims=c.rotary_dims,
+                   theta=c.theta)
+    torch.cuda.synchronize()
+    ref = oracle.prefill(q.cpu(), k.cpu(), v.cpu(), window=c.window, scale=c.scale,
+                         rotary_dims=c.rotary_dims, theta=c.theta)
+    mx, rel = assert_close(o, ref, c.dtype, f"T=2048 {shape}")
+    print(f"T=2048 {shape}: max_abs={mx:.3e} rel_rms={rel:.3e}", flush=True)

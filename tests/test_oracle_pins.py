@@ -20,6 +20,7 @@ import numpy as np
 import pytest
 import torch
 
+import inputs
 import oracle
 
 GOLD = os.path.join(os.path.dirname(__file__), "golden")
@@ -639,3 +640,26 @@ def test_decode_int8_equals_decode_of_dequantised_cache():
     # and stays within the quantisation error of the unquantised decode
     c = oracle.decode(q, kc, vc, offs, lens, window=0, scale=0.3)
     assert np.abs(a - c).max() < 0.05
+
+
+def test_workload_shapes_follow_the_pages():
+    """Head ratios, head dims, windows and the local:global layer pattern of
+    every workload match what the pages state (tests/golden/gqa_ratios.json)."""
+    g = json.load(open(os.path.join(GOLD, "gqa_ratios.json")))
+    loc, glo = inputs.LOCAL, inputs.GLOBAL
+    assert loc["Hq"] // loc["Hkv"] == g["local"]["q_per_kv"]
+    assert loc["Dk"] == loc["Dv"] == g["local"]["head_dim"]
+    assert glo["Hq"] // glo["Hkv"] == g["global"]["q_per_kv"]
+    assert glo["Dk"] == g["global"]["key_dim"]
+    sm = g["small_model"]
+    for shape, key in ((inputs.SMALL_LOCAL, "local_head_dim"), (inputs.SMALL_GLOBAL, "global_key_dim")):
+        assert (shape["Hq"], shape["Hkv"]) == (sm["q_heads"], sm["kv_heads"])
+        assert shape["Dk"] == sm[key]
+    wl = inputs.WORKLOADS
+    assert wl["local_prefill"]["case"].window in g["local"]["windows"]
+    big, small = wl["stack"]["case"], wl["small_stack"]["case"]
+    for st, ref in ((big, g["large_model"]), (small, sm)):
+        kinds = [c.window > 0 for c, _ in st.layers]
+        assert kinds[:st.n_local] == [True] * st.n_local and not kinds[st.n_local]
+        assert st.n_local == ref["local_per_global"]
+        assert st.window == ref["window"]
