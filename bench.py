@@ -70,20 +70,27 @@ def rows_flops(c, rows) -> float:
     return float(sum(min(int(i) + 1, W) for i in rows) * c.B * c.Hq * 2 * (c.Dk + c.Dv))
 
 
+def _digest(paths):
+    """sha256[:16] over the given source files, in order."""
+    h = hashlib.sha256()
+    for rel in paths:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
 def _traffic(kernel: str, workload: str):
     """HBM bytes per launch from a committed counter summary, if it was taken
-    on the current kernel source (else None)."""
+    on the current kernel sources (else None)."""
     path = os.path.join(PROFILES, f"traffic_{kernel}_{workload}.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
-    src = os.path.join(ROOT, rec.get("source", ""))
-    if not os.path.exists(src):
+    srcs = rec.get("sources") or [rec.get("source", "")]
+    if not all(os.path.exists(os.path.join(ROOT, s)) for s in srcs):
         return None
-    with open(src, "rb") as f:
-        digest = hashlib.sha256(f.read()).hexdigest()[:16]
-    if digest != rec.get("source_sha256_16"):
+    if _digest(srcs) != rec.get("sources_sha256_16", rec.get("source_sha256_16")):
         return None
     return rec.get("bytes_per_launch")
 
