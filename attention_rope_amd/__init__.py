@@ -34,7 +34,8 @@ STATUS = {0: "ok", 1: "null pointer", 2: "invalid shape or argument",
 # Every symbol the header declares (checked by the tests).
 EXPORTS = ("attn_prefill",
            "attn_prefill_workspace_bytes", "attn_decode",
-           "attn_decode_workspace_bytes", "attn_verify", "attn_verify_workspace_bytes",
+           "attn_decode_workspace_bytes", "attn_decode_noalloc", "attn_decode_noalloc_max_bytes",
+           "attn_verify", "attn_verify_workspace_bytes",
            "attn_kv_quantize_int8", "attn_decode_int8", "attn_decode_int8_workspace_bytes",
            "prope_apply", "prope_apply_2d", "attn_status_string", "attn_last_error")
 
@@ -72,6 +73,11 @@ def load(path: str = LIB_PATH):
     lib.attn_decode.argtypes = [vp] * 6 + [i32] * 6 + [
         ctypes.c_float, _Rope, i32, vp, sz, ctypes.c_int, vp]
     lib.attn_decode.restype = ctypes.c_int
+    lib.attn_decode_noalloc_max_bytes.argtypes = []
+    lib.attn_decode_noalloc_max_bytes.restype = sz
+    lib.attn_decode_noalloc.argtypes = [vp] * 6 + [i32] * 6 + [
+        ctypes.c_float, _Rope, i32, ctypes.c_int, vp]
+    lib.attn_decode_noalloc.restype = ctypes.c_int
     lib.attn_verify_workspace_bytes.argtypes = [i32] * 8
     lib.attn_verify_workspace_bytes.restype = sz
     lib.attn_verify.argtypes = [vp] * 6 + [i32] * 7 + [
@@ -250,6 +256,30 @@ def decode(q, k_cache, v_cache, row_offset, kv_len, *, window: int = 0,
                            _dev(workspace, "workspace"), _nbytes(workspace),
                            _dtype_code(q), _stream(q)))
     return o
+
+
+def decode_noalloc(q, k_cache, v_cache, row_offset, kv_len, *, window: int = 0,
+                   scale: float | None = None, rotary_dims: int = 0, theta: float = 10000.0,
+                   max_kv_len: int, out):
+    """decode() through the entry point that allocates nothing: the split-K
+    partials live in the library's static device scratch. ``out`` [B,Hq,Dv]
+    is required (this call allocates no tensor either)."""
+    lib = load()
+    B, Hq, Hkv, Dk, Dv = _cache_args(q, k_cache, v_cache, row_offset, kv_len)
+    _same(q, "q", k_cache=k_cache, v_cache=v_cache, out=out)
+    _need_shape(out, (B, Hq, Dv), "out")
+    if scale is None:
+        scale = Dk ** -0.5
+    _check(lib.attn_decode_noalloc(_dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
+                                   _dev(row_offset, "row_offset"), _dev(kv_len, "kv_len"),
+                                   _dev(out, "o"), B, Hq, Hkv, Dk, Dv, int(window), float(scale),
+                                   _Rope(rotary_dims, theta), int(max_kv_len), _dtype_code(q),
+                                   _stream(q)))
+    return out
+
+
+def decode_noalloc_max_bytes() -> int:
+    return int(load().attn_decode_noalloc_max_bytes())
 
 
 def verify_workspace_bytes(B: int, n_q: int, Hq: int, Hkv: int, Dk: int, Dv: int,

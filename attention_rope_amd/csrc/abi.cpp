@@ -71,7 +71,7 @@ attn_status_t decode_call(const char* what, const void* q, const void* k_cache,
                           void* o, int32_t B, int32_t n_q, int32_t Hq, int32_t Hkv, int32_t Dk,
                           int32_t Dv, int32_t window, float scale, attn_rope_t rope,
                           int32_t max_kv_len, void* workspace, size_t workspace_bytes,
-                          attn_dtype_t dtype, void* stream) {
+                          attn_dtype_t dtype, void* stream, bool dry = false) {
   if (dtype != ATTN_BF16)
     return fail(ATTN_ERR_UNSUPPORTED, "%s supports the ATTN_BF16 cache only", what);
   if (B < 0 || B > 65535) return fail(ATTN_ERR_SHAPE, "B=%d must be in [0, 65535]", B);
@@ -95,6 +95,7 @@ attn_status_t decode_call(const char* what, const void* q, const void* k_cache,
     return fail(ATTN_ERR_NULL, "q, caches, row_offset, kv_len and o must be non-NULL");
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o))
     return fail(ATTN_ERR_SHAPE, "q, caches and o must be 16-byte aligned");
+  if (dry) return ok();
   const size_t need =
       attn::decode_workspace_bytes(B, n_q, Hq, Hkv, Dk, Dv, max_kv_len, window);
   if (!workspace || workspace_bytes < need)
@@ -269,6 +270,38 @@ attn_status_t attn_decode(const void* q, const void* k_cache, const void* v_cach
   return decode_call("decode", q, k_cache, v_cache, row_offset, kv_len, o, B, 1, Hq, Hkv, Dk,
                      Dv, window, scale, rope, max_kv_len, workspace, workspace_bytes, dtype,
                      stream);
+}
+
+size_t attn_decode_noalloc_max_bytes(void) { return attn::kDecodeScratchBytes; }
+
+attn_status_t attn_decode_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                                  const int64_t* row_offset, const int32_t* kv_len, void* o,
+                                  int32_t B, int32_t Hq, int32_t Hkv, int32_t Dk, int32_t Dv,
+                                  int32_t window, float scale, attn_rope_t rope,
+                                  int32_t max_kv_len, attn_dtype_t dtype, void* stream) {
+  // The same partials attn_decode keeps in its workspace; checked against the
+  // static scratch before anything touches the GPU.
+  if (B > 0 && Hq > 0 && Hkv > 0 && Hq % Hkv == 0 && max_kv_len >= 1) {
+    const size_t need = attn::decode_workspace_bytes(B, 1, Hq, Hkv, Dk, Dv, max_kv_len, window);
+    if (need > attn::kDecodeScratchBytes)
+      return fail(ATTN_ERR_WORKSPACE,
+                  "decode_noalloc: this call needs %zu bytes of split-K scratch, the static "
+                  "scratch holds %zu (use attn_decode with a workspace)",
+                  need, attn::kDecodeScratchBytes);
+  }
+  // Everything but the scratch is validated by the shared path; an empty
+  // batch or an invalid argument returns before the scratch is looked up.
+  const size_t zero_ws = 0;
+  attn_status_t pre = decode_call("decode_noalloc", q, k_cache, v_cache, row_offset, kv_len, o,
+                                  B, 1, Hq, Hkv, Dk, Dv, window, scale, rope, max_kv_len,
+                                  nullptr, zero_ws, dtype, nullptr, /*dry=*/true);
+  if (pre != ATTN_OK || B == 0) return pre;
+  void* ws = nullptr;
+  attn_status_t r = launch_status(attn::decode_scratch(&ws), "decode_noalloc (scratch)");
+  if (r != ATTN_OK) return r;
+  return decode_call("decode_noalloc", q, k_cache, v_cache, row_offset, kv_len, o, B, 1, Hq, Hkv,
+                     Dk, Dv, window, scale, rope, max_kv_len, ws, attn::kDecodeScratchBytes,
+                     dtype, stream);
 }
 
 attn_status_t attn_verify(const void* q, const void* k_cache, const void* v_cache,

@@ -28,6 +28,8 @@
 #include "attn_common.h"
 #include "kernels.h"
 
+#include <mutex>
+
 namespace attn {
 
 // Split-K plan: each workgroup streams `ch` consecutive visible rows of one
@@ -509,6 +511,36 @@ bool decode_supported(int Dk, int Dv, int G) {
   const bool kdim = Dk == 128 || Dk == 256 || Dk == 512;
   const bool vdim = Dv == 128 || Dv == 256 || (Dv == 512 && Dk == 512);
   return kdim && vdim && G >= 1 && G <= 16;
+}
+
+// Scratch of the decode entry point that allocates nothing: the split-K
+// partials live in this file-scope device array, one copy per GPU, held until
+// the process ends. Host code must never pass the array's name to a kernel
+// (on the host it is only a stand-in for the symbol): the device address of
+// each GPU's copy comes from hipGetSymbolAddress, taken once per device with
+// that device current, and is cached here.
+static __device__ __align__(256) unsigned char scratch[kDecodeScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+hipError_t decode_scratch(void** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_decode(const DecodeArgs& a0, hipStream_t st) {

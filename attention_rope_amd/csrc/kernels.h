@@ -96,6 +96,11 @@ hipError_t launch_decode_merge(const DecodeArgs& a, const SplitPlan& pl, hipStre
 size_t decode_workspace_bytes(int B, int n_q, int Hq, int Hkv, int Dk, int Dv, int max_kv_len,
                               int window);
 bool decode_supported(int Dk, int Dv, int G);
+// Device scratch of attn_decode_noalloc: a file-scope array of this many
+// bytes in decode.hip, one per GPU; decode_scratch returns the current
+// device's copy (its address taken once per device, nothing allocated).
+constexpr size_t kDecodeScratchBytes = (size_t)32 << 20;
+hipError_t decode_scratch(void** ptr);
 bool decode_shape_fits(int B, int n_q, int Hq, int Hkv, int Dk, int Dv, int max_kv_len,
                        int window);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t st);

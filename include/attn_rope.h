@@ -169,6 +169,28 @@ attn_status_t attn_decode(const void *q, const void *k_cache, const void *v_cach
                           void *stream);
 
 /*
+ * Decode that allocates nothing, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation): attn_decode's arguments and results without the
+ * workspace. The split-K partials live in a static device array of
+ * attn_decode_noalloc_max_bytes() bytes (32 MiB) inside the library, one
+ * copy per GPU, held until the process ends. A call whose partials need more
+ * (attn_decode_workspace_bytes() of the same arguments above that size)
+ * returns ATTN_ERR_WORKSPACE and launches nothing. Every call on a GPU uses
+ * that GPU's one array: calls that overlap on one GPU (other streams, or host
+ * threads without ordering) race on it. Nothing in it needs clearing between
+ * calls: a call reads only partials it wrote itself.
+ */
+size_t attn_decode_noalloc_max_bytes(void);
+
+attn_status_t attn_decode_noalloc(const void *q, const void *k_cache, const void *v_cache,
+                                  const int64_t *row_offset, const int32_t *kv_len,
+                                  void *o, int32_t B, int32_t Hq, int32_t Hkv,
+                                  int32_t Dk, int32_t Dv, int32_t window, float scale,
+                                  attn_rope_t rope, int32_t max_kv_len, attn_dtype_t dtype,
+                                  void *stream);
+
+/*
  * Verify (speculative decoding) / append attention: n_q new tokens per
  * sequence at once, as when a target model checks a drafter's proposals in one
  * pass ("Gemma 4: End-to-End Architecture Walkthrough", Phase 4; "Gemma 4

@@ -186,3 +186,22 @@ def test_verify_validation_and_workspace(lib):
     assert verify(ws_bytes=16) == 4
     assert verify(dtype=ar.ATTN_F32) == 3
     assert verify(B=0, q=None) == 0
+
+
+def test_decode_noalloc_validation(lib):
+    """The entry point that allocates nothing rejects, before touching the GPU,
+    a call whose split-K partials exceed its static scratch, and validates the
+    other arguments as attn_decode does."""
+    assert lib.attn_decode_noalloc_max_bytes() == 32 << 20
+    f = lambda **kw: lib.attn_decode_noalloc(
+        kw.get("q", FAKE), FAKE, FAKE, FAKE, kw.get("kvl", FAKE), kw.get("o", FAKE2),
+        kw.get("B", 64), 32, 4, 512, 256, 0, 0.05, R(128, 1e6), kw.get("max_kv_len", 131073),
+        kw.get("dtype", ar.ATTN_BF16), None)
+    # 64 sequences up to 131073 rows: 33 chunks of 4096 rows -> ~70 MB of partials
+    assert f() == 4
+    assert b"scratch" in lib.attn_last_error()
+    assert lib.attn_decode_workspace_bytes(64, 32, 4, 256, 131073, 0) > 32 << 20
+    assert f(B=1, kvl=None) == 1                      # fits; a NULL kv_len is caught first
+    assert f(B=1, dtype=ar.ATTN_F32) == 3
+    assert f(B=1, max_kv_len=0) == 2
+    assert f(B=0, q=None) == 0                        # empty batch: no-op
