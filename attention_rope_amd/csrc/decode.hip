@@ -32,26 +32,6 @@
 
 namespace attn {
 
-// Split-K plan: each workgroup streams `ch` consecutive visible rows of one
-// sequence for one KV head. A workgroup's start (locating its rows, turning
-// the query, filling the DMA ring) and end (draining, writing its partial)
-// leave its CU's memory pipe idle, so chunks are made as long as possible:
-// up to kMaxChunk rows (global layers) or the whole window (local layers),
-// halved while the grid would hold fewer than kMinGroups workgroups.
-constexpr int kMaxChunk = 4096, kMinChunk = 256, kMinGroups = 512;
-
-// groups: workgroups per (sequence, chunk); n_q new tokens per sequence widen
-// a window's range by n_q - 1 rows.
-SplitPlan decode_plan(int B, int groups, int max_kv_len, int window, int n_q) {
-  const int64_t wr = (int64_t)window + n_q - 1;
-  const int range = (window > 0 && wr < max_kv_len) ? (int)wr : max_kv_len;
-  int ch = (window > 0) ? range : kMaxChunk;
-  ch = ch > kMaxChunk ? kMaxChunk : (ch < 1 ? 1 : ch);
-  auto splits = [&](int c) { return (int)(((int64_t)range + c - 1) / c); };
-  while (ch > kMinChunk && (int64_t)B * groups * splits(ch) < kMinGroups) ch = (ch + 1) / 2;
-  return {ch, splits(ch)};
-}
-
 namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
@@ -434,12 +414,9 @@ hipError_t launch_ring(const DecodeArgs& a, const SplitPlan& pl, int ncg, hipStr
   return launch_merge_dv<DV>(a, pl, st);
 }
 
-// 16-column groups of (token, head) pairs per KV head.
-inline int column_groups(int n_q, int G) { return (n_q * G + 15) / 16; }
-
 template <int DK, int DV>
 hipError_t launch_dk_dv(const DecodeArgs& a, hipStream_t st) {
-  const int ncg = column_groups(a.n_q, a.Hq / a.Hkv);
+  const int ncg = decode_column_groups(a.n_q, a.Hq / a.Hkv);
   const SplitPlan pl = decode_plan(a.B, a.Hkv * ncg, a.max_kv_len, a.window, a.n_q);
   if (pl.ns > 65535) return hipErrorInvalidValue;
   if constexpr (DK == DV) {
@@ -472,11 +449,6 @@ __global__ __launch_bounds__(256) void verify_rotate_q_kernel(DecodeArgs a, uint
   }
 }
 
-inline size_t rotated_q_bytes(int B, int n_q, int Hq, int Dk) {
-  if (n_q <= 1) return 0;
-  return ((size_t)B * n_q * Hq * Dk * 2 + 255) & ~(size_t)255;
-}
-
 }  // namespace
 
 hipError_t launch_decode_merge(const DecodeArgs& a, const SplitPlan& pl, hipStream_t st) {
@@ -486,31 +458,6 @@ hipError_t launch_decode_merge(const DecodeArgs& a, const SplitPlan& pl, hipStre
     case 512: return launch_merge_dv<512>(a, pl, st);
     default: return hipErrorNotSupported;
   }
-}
-
-size_t decode_workspace_bytes(int B, int n_q, int Hq, int Hkv, int Dk, int Dv, int max_kv_len,
-                              int window) {
-  if (B <= 0 || n_q <= 0 || Hq <= 0 || Hkv <= 0 || Dv <= 0 || max_kv_len <= 0) return 0;
-  const int ncg = column_groups(n_q, Hq / Hkv);
-  const int ns = decode_plan(B, Hkv * ncg, max_kv_len, window, n_q).ns;
-  return rotated_q_bytes(B, n_q, Hq, Dk) + (size_t)B * n_q * Hq * ns * (Dv + 2) * sizeof(float);
-}
-
-bool decode_shape_fits(int B, int n_q, int Hq, int Hkv, int Dk, int Dv, int max_kv_len,
-                       int window) {
-  const int ncg = column_groups(n_q, Hq / Hkv);
-  const SplitPlan pl = decode_plan(B, Hkv * ncg, max_kv_len, window, n_q);
-  // 32-bit chunk-relative offsets (chunk plus the deepest read-ahead) and the
-  // grid's x and y extents.
-  const int64_t row = (int64_t)Hkv * (Dk > Dv ? Dk : Dv) * 2;
-  return pl.ns <= 65535 && (int64_t)Hkv * ncg < ((int64_t)1 << 31) &&
-         ((int64_t)pl.ch + 192) * row < ((int64_t)1 << 31);
-}
-
-bool decode_supported(int Dk, int Dv, int G) {
-  const bool kdim = Dk == 128 || Dk == 256 || Dk == 512;
-  const bool vdim = Dv == 128 || Dv == 256 || (Dv == 512 && Dk == 512);
-  return kdim && vdim && G >= 1 && G <= 16;
 }
 
 // Scratch of the decode entry point that allocates nothing: the split-K
@@ -555,7 +502,7 @@ hipError_t launch_decode(const DecodeArgs& a0, hipStream_t st) {
     if (e != hipSuccess) return e;
     a.q = qr;
     a.q_rotated = 1;
-    a.workspace = static_cast<char*>(a0.workspace) + rotated_q_bytes(a0.B, a0.n_q, a0.Hq, a0.Dk);
+    a.workspace = static_cast<char*>(a0.workspace) + decode_rotated_q_bytes(a0.B, a0.n_q, a0.Hq, a0.Dk);
   }
 #define ATTN_DEC(DK, DV) \
   if (a.Dk == DK && a.Dv == DV) return launch_dk_dv<DK, DV>(a, st);

@@ -417,10 +417,6 @@ hipError_t launch_kv_quantize_int8(const void* x, int8_t* codes, float* scales, 
   return hipGetLastError();
 }
 
-bool decode_int8_supported(int Dk, int Dv, int G) {
-  return (Dk == 512 || Dk == 256) && Dv == 256 && G >= 1 && G <= 16;
-}
-
 hipError_t launch_decode_int8(const DecodeArgs& a, hipStream_t st) {
   if (a.B == 0) return hipSuccess;
   if (a.Dk == 512 && a.Dv == 256) return launch_i8<512, 256>(a, st);

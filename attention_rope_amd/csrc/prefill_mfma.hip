@@ -557,13 +557,6 @@ hipError_t dispatch_g(const PrefillArgs& a, hipStream_t st) {
 
 }  // namespace
 
-bool prefill_mfma_supported(int Dk, int Dv, int G, float scale, int rotary_dims) {
-  const bool shape = (Dk == 128 && Dv == 128) || (Dk == 256 && Dv == 256) ||
-                     (Dk == 512 && (Dv == 256 || Dv == 512));
-  const bool rot = rotary_dims == 0 || rotary_dims == Dk / 4 || rotary_dims == Dk;
-  return shape && rot && (G == 1 || G == 2 || G == 4 || G == 8) && scale >= 0.f;
-}
-
 hipError_t launch_prefill_mfma(const PrefillArgs& a, hipStream_t st) {
   const int rdims = (a.rope_q || a.rope_k) ? 2 * a.rot_pairs : 0;
   if (!prefill_mfma_supported(a.Dk, a.Dv, a.Hq / a.Hkv, a.scale, rdims))

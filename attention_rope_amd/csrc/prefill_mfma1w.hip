@@ -178,47 +178,41 @@ __global__ __launch_bounds__(NT, 1) void prefill_mfma1w_kernel(PrefillArgs a, in
     const int q = (i * NW + wave) * 64 + lane, r = q / C::VC;
     voff[i] = r * vrow + vswz(r, q % C::VC) * 16;
   }
-  // Tiles past the range go out at an offset past the descriptors' end: they
-  // return zeros without touching memory, so every iteration issues the same
-  // number of DMAs and one vmcnt value covers every wait.
-  auto dma_k = [&](int kb, int stage) {
-    const int j0 = kb * BN;
-    const uint32_t st = lds_addr(lds) + stage * C::KT_BYTES;
-    const uint32_t far = kb < kb_hi ? 0u : 0x80000000u;
-#pragma unroll
-    for (int i = 0; i < C::KW; ++i) {
-      const int n = i * NW + wave;
-      const int reg = C::ALIGNED ? C::kregion(i * NW) : C::kregion(n);
-      if (reg == 0)
-        dma16(rdesc, st + n * 1024, (koff[i] + j0 * rrow) | far);
-      else
-        dma16(kdesc, st + n * 1024, (koff[i] + j0 * krow) | far);
-    }
+  // Tiles past the range go out with a descriptor of 0 records: they return
+  // zeros without touching memory, so every iteration issues the same number
+  // of DMAs and one vmcnt value covers every wait.
+  // Per-tile descriptors: the tile's first row becomes the base, so each DMA
+  // takes the lane's fixed offset; a tile past the range gets 0 records.
+  const uint32_t ktot = (T - 1) * krow + DK * 2, rtot = (T - 1) * rrow + RCH * 16;
+  const uint32_t vtot = (T - 1) * vrow + DV * 2;
+  auto tdesc = [&](u32x4 d, uint32_t off, uint32_t total, bool in) -> u32x4 {
+    const uint64_t base = (((uint64_t)(d[1] & 0xffffu) << 32) | d[0]) + off;
+    return u32x4{(uint32_t)base, (uint32_t)(base >> 32) & 0xffffu, in ? total - off : 0u, d[3]};
   };
   auto dma_k1 = [&](int kb, int stage, int i) {
     const int j0 = kb * BN;
     const uint32_t st = lds_addr(lds) + stage * C::KT_BYTES;
-    const uint32_t far = kb < kb_hi ? 0u : 0x80000000u;
+    const bool in = kb < kb_hi;
     const int n = i * NW + wave;
     const int reg = C::ALIGNED ? C::kregion(i * NW) : C::kregion(n);
     if (reg == 0)
-      dma16(rdesc, st + n * 1024, (koff[i] + j0 * rrow) | far);
+      dma16(tdesc(rdesc, in ? j0 * rrow : 0u, rtot, in), st + n * 1024, koff[i]);
     else
-      dma16(kdesc, st + n * 1024, (koff[i] + j0 * krow) | far);
+      dma16(tdesc(kdesc, in ? j0 * krow : 0u, ktot, in), st + n * 1024, koff[i]);
   };
   auto dma_v1 = [&](int kb, int stage, int i) {
     const int j0 = kb * BN;
     const uint32_t st = lds_addr(lds) + C::V_OFF + stage * C::VT_BYTES;
-    const uint32_t far = kb < kb_hi ? 0u : 0x80000000u;
-    dma16(vdesc, st + (i * NW + wave) * 1024, (voff[i] + j0 * vrow) | far);
+    const bool in = kb < kb_hi;
+    dma16(tdesc(vdesc, in ? j0 * vrow : 0u, vtot, in), st + (i * NW + wave) * 1024, voff[i]);
+  };
+  auto dma_k = [&](int kb, int stage) {
+#pragma unroll
+    for (int i = 0; i < C::KW; ++i) dma_k1(kb, stage, i);
   };
   auto dma_v = [&](int kb, int stage) {
-    const int j0 = kb * BN;
-    const uint32_t st = lds_addr(lds) + C::V_OFF + stage * C::VT_BYTES;
-    const uint32_t far = kb < kb_hi ? 0u : 0x80000000u;
 #pragma unroll
-    for (int i = 0; i < C::VW; ++i)
-      dma16(vdesc, st + (i * NW + wave) * 1024, (voff[i] + j0 * vrow) | far);
+    for (int i = 0; i < C::VW; ++i) dma_v1(kb, stage, i);
   };
 
   // ---- prologue: K(0), V(0) around the Q load, then K(1), K(2) ---------------

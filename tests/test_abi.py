@@ -205,3 +205,19 @@ def test_decode_noalloc_validation(lib):
     assert f(B=1, dtype=ar.ATTN_F32) == 3
     assert f(B=1, max_kv_len=0) == 2
     assert f(B=0, q=None) == 0                        # empty batch: no-op
+
+
+def test_no_device_is_a_launch_error(lib):
+    """With no GPU present, a call that passes validation reaches the HIP
+    runtime, which refuses it: ATTN_ERR_LAUNCH with the runtime's message, no
+    crash. (Skipped where a GPU is visible: the pointers here are fake.)"""
+    import torch
+    if torch.cuda.device_count() > 0:
+        pytest.skip("a GPU is visible")
+    rc = _prefill(lib, q=P(0x10000), k=P(0x20000), v=P(0x30000), o=P(0x40000))
+    assert rc == 5
+    assert b"HIP error" in lib.attn_last_error()
+    rc = lib.attn_decode_noalloc(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE2, 1, 8, 1, 128, 128, 0, 0.1,
+                                 R(0, 1e4), 10, ar.ATTN_BF16, None)
+    assert rc == 5
+    assert lib.attn_status_string(rc) == b"kernel launch failed"

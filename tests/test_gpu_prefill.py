@@ -214,3 +214,21 @@ def test_prefill_keys_as_values(gpu_lib, T, Hq, Hkv, D, W, R, th):
     ref = oracle.prefill_kv_shared(q.cpu(), k.cpu(), window=W, scale=c.scale, rotary_dims=R,
                                    theta=th)
     assert_close(o, ref, BF, "prefill K=V")
+
+
+@pytest.mark.parametrize("shape", ["local", "global", "small_local"])
+def test_grid_order_independent(gpu_lib, shape):
+    """A sequence's output does not depend on where and when its workgroups
+    run: computed alone (B=1) and as the second row of a batch (B=2, so the
+    grid and the block-to-tile mapping change), its rows are the same bits."""
+    kw = {"local": (inputs.LOCAL, 512), "global": (inputs.GLOBAL, 0),
+          "small_local": (inputs.SMALL_LOCAL, 512)}[shape]
+    c = inputs.PrefillCase(2, 1100, window=kw[1], dtype=BF, **kw[0])
+    q, k, v = inputs.prefill_inputs(c, 13, device=DEV)
+    both = gpu_lib.prefill(q, k, v, window=c.window, scale=c.scale, rotary_dims=c.rotary_dims,
+                           theta=c.theta)
+    alone = gpu_lib.prefill(q[1:].contiguous(), k[1:].contiguous(), v[1:].contiguous(),
+                            window=c.window, scale=c.scale, rotary_dims=c.rotary_dims,
+                            theta=c.theta)
+    torch.cuda.synchronize()
+    assert torch.equal(both[1:], alone)
