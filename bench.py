@@ -10,8 +10,9 @@ single-GPU workload, the 7-layer stack (B=2, T=16384): 5 sliding-window local
 layers (W=1024, 16q/8kv, D=256, RoPE theta=1e4), one global layer (32q/4kv,
 Dk=512, Dv=256, p-RoPE on 128 of 512 dims, theta=1e6) and one global layer
 that reuses the previous layer's K/V. A step is one pass of the whole path
-over that batch: seven attn_prefill calls on one stream, each building its
-cos/sin table, turning K's rotary dims once and running the flash kernel.
+over that batch: seven attn_prefill calls on one stream, each turning K's
+rotary dims once (a pre-pass) and running the flash kernel, which forms the
+rotation angles of Q itself from pos0.
 
 Timing: HIP events recorded on the stream the kernels run on; W untimed
 warm-up steps, then exactly K timed steps between two device
@@ -155,10 +156,10 @@ def prefill_ws(ar, torch, cases):
 
 
 def bench_prefill(ar, torch, inputs, cfg, warmup, iters=None):
-    """The attn_prefill call (cos/sin table, K rotation pre-pass, flash
-    kernel) and, separately, the flash kernel alone: a call with Q-only
-    rotation launches the same kernel instantiation with the same DMA volume
-    (K's rotary dims then come from k itself), after only the table."""
+    """The attn_prefill call (K rotation pre-pass, flash kernel) and,
+    separately, the flash kernel alone: a call with Q-only rotation launches
+    the same kernel instantiation with the same DMA volume (K's rotary dims
+    then come from k itself) and nothing else."""
     c = cfg["case"]
     q, k, v = inputs.prefill_inputs(c, cfg["seed"], device="cuda")
     o = torch.empty((c.B, c.T, c.Hq, c.Dv), dtype=c.dtype, device="cuda")
@@ -261,8 +262,8 @@ def stack_record(cfg, r):
 def global_layer_roofline(r, traffic_workload):
     """Dominant kernel of a stack: the global layers' flash kernel. Achieved =
     a global layer's algorithmic FLOPs over the mean duration of the global
-    layers' calls in the timed steps (each call also builds its cos/sin
-    table and turns K's 128 rotary dims, ~0.1 % of the call)."""
+    layers' calls in the timed steps (each call also turns K's 128 rotary
+    dims in a pre-pass, ~0.1 % of the call)."""
     g = [i for i, L in enumerate(r["layers"]) if not L["c"].window]
     ms = [x for i in g for x in r["layer_ms"][i]]
     mean_ms = sum(ms) / len(ms)
@@ -446,7 +447,7 @@ def secondary_prefill(ar, torch, inputs, name, sc):
     rec = {"workload": sc["name"], "unit": "TFLOP/s",
            "value": round(rr["flops"] / rr["call"]["median"] / 1e9, 3),
            "ms_per_call": round(rr["call"]["median"], 5), "timed_calls": rr["iters"],
-           "what": "attn_prefill call: cos/sin table, K rotation pre-pass, flash kernel",
+           "what": "attn_prefill call: K rotation pre-pass, flash kernel",
            "roofline": dict(roofline("mfma", tf_k, peak, "TFLOP/s", _traffic(kname, name)),
                             kernel=kname + "_kernel",
                             kernel_ms=round(rr["kern"]["median"], 5),
@@ -484,7 +485,8 @@ def secondary_decode(ar, torch, inputs, sc):
                             "bytes": rr["g_bytes"]},
             "local_call": {"GB/s": round(l, 1), "ms": round(rr["l_ms"], 4),
                            "bytes": rr["l_bytes"],
-                           "roofline": roofline("hbm", l, PEAK_HBM_GBS, "GB/s", None)},
+                           "roofline": roofline("hbm", l, PEAK_HBM_GBS, "GB/s",
+                                                _traffic("decode_ring", "local_decode"))},
             "keys_as_values_call": leg(rr["kv_ms"], rr["kv_bytes"],
                                        "global shape with K = V: one 512-dim cache read "
                                        "once for both products (Dv = Dk = 512)",
@@ -511,6 +513,11 @@ def secondary_stack(ar, torch, inputs, name, sc):
            "roofline": global_layer_roofline(rr, name)}
     del rr
     return rec
+
+
+def progress(msg):
+    """One line per finished leg on stderr (the JSON line stays alone on stdout)."""
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
 def main():
@@ -555,6 +562,7 @@ def main():
     cfg = inputs.WORKLOADS[args.workload]
     r = bench_stack(ar, torch, inputs, cfg, args.steps, args.warmup)
     med = r["step"]["median"]
+    progress(f"{args.workload}: {med:.3f} ms per step")
     value = r["flops"] / med / 1e9
     timed_ms = sum(r["step_series"])
     out = {
@@ -587,6 +595,7 @@ def main():
     if not args.no_cpu_baseline:
         import oracle
         out["cpu_baseline"] = cpu_baseline_stack(oracle, cfg, r, args.cpu_seconds)
+        progress("cpu baseline done")
     del r
     torch.cuda.empty_cache()
 
@@ -605,6 +614,7 @@ def main():
             secondary[s] = secondary_stack(ar, torch, inputs, s, sc)
         torch.cuda.synchronize()
         torch.cuda.empty_cache()
+        progress(f"{s} done")
     if secondary:
         out["secondary"] = secondary
     print(json.dumps(out), flush=True)

@@ -94,8 +94,10 @@ enum { ATTN_ROPE_Q = 1, ATTN_ROPE_K = 2 };
  *   Every rotation angle is (pos0 + t) * theta^(-2p/Dk), formed from this
  *   call's own pos0 and rope arguments in fp64 inside the kernels.
  * Workspace: attn_prefill_workspace_bytes() bytes of device memory, 16-byte
- *   aligned (0 when nothing needs it: workspace may then be NULL). On the
- *   bf16 path the call turns K's rotary dims once into it before attending.
+ *   aligned (0 when nothing needs it: workspace may then be NULL). When K
+ *   turns (ATTN_ROPE_K with rotary_dims > 0), the call first turns K's rotary
+ *   dims once into it, [B, T, Hkv, rotary_dims] in the element type, and the
+ *   attention kernel reads them from there.
  *   Contents are scratch, owned by the caller; the workspace must not overlap
  *   any tensor argument.
  * Errors (nothing is launched): NULL tensors -> ATTN_ERR_NULL; bad sizes,
