@@ -11,16 +11,19 @@
 // Design for CDNA4: the cache bytes halve, so the kernel must turn twice as
 // many rows per second into MFMA operands without adding HBM traffic.
 //  * Same split-K plan, DMA ring, MFMA layout and output path as the bf16
-//    streaming kernel; one wave per workgroup (16-row tiles), four
-//    workgroups per CU, so four SIMDs share the conversion work.
+//    streaming kernel; one wave per workgroup (16-row tiles, a 2-stage ring
+//    of 25 KB) and at most 256 registers per wave, so six workgroups share
+//    a CU. The bytes a CU keeps in flight grow with the workgroups resident,
+//    and with one tile ahead per wave those bytes set the read rate.
 //  * Scales never touch the codes: the K scale multiplies the 16 scores of a
 //    tile after Q.K^T, the V scale multiplies the probabilities before P.V.
 //  * Q.K^T on v_mfma_i32_16x16x64_i8 straight from the K codes in LDS: the
 //    query is split into two int8 parts (a code and the code of its
 //    residual), so two exact int32 products replace any conversion of K.
-//  * V codes are converted once per tile into a bf16 tile in LDS, from which
-//    the transposing reads of the bf16 kernel build the P.V operand. They
-//    are converted with a +128 bias: code ^ 0x80 is code + 128 as an
+//  * V codes are converted once per tile into a bf16 tile in LDS, written
+//    over the stage's own codes once Q.K^T has read them, from which the
+//    transposing reads of the bf16 kernel build the P.V operand. They are
+//    converted with a +128 bias: code ^ 0x80 is code + 128 as an
 //    unsigned byte, which v_cvt_f32_ubyte turns into fp32 in one instruction
 //    and which bf16 holds exactly; 128 * sum(bf16 P') per head is removed
 //    from the P.V accumulator afterwards.
@@ -87,7 +90,9 @@ typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 // Stage layout (bytes): K codes [16][DK] (16-byte chunks swizzled by row),
 // V codes [16][DV], then two 256-byte blocks of scales (lanes 0-15 of each
-// scale DMA hold rows 0-15; the other lanes read zeros).
+// scale DMA hold rows 0-15; the other lanes read zeros). Once Q.K^T has read
+// the K codes and the V codes are in registers, the tile's V as bf16 (+128),
+// [16][DV] rows of 2 DV bytes, is written over the stage's codes.
 template <int DK, int DV, int STAGES_>
 struct I8Cfg {
   static constexpr int STAGES = STAGES_, AHEAD = STAGES - 1;
@@ -98,17 +103,20 @@ struct I8Cfg {
   static constexpr int N_DMA = K_DMA + V_DMA + 2;
   static constexpr int VB = 16 * DV * 2;  // the tile's V as bf16 (+128)
   static constexpr int RING = STAGES * ST, RED = 16 * (DV + 2) * 4;
-  static constexpr int LDS = (RING > RED ? RING : RED) + VB;
+  static constexpr int LDS = RING > RED ? RING : RED;
   static_assert(KC >= 16 && VC >= 16, "row swizzle uses 16 chunk groups");
   static_assert(KT % 1024 == 0 && VT % 1024 == 0, "whole DMA blocks");
+  static_assert(VB <= KT + VT, "the bf16 V tile fits over the codes");
+  static_assert(DK / 2 * 8 <= ST, "the query's cos/sin rows fit a stage");
   static_assert((AHEAD - 1) * N_DMA < 64 && LDS <= 160 * 1024, "vmcnt / LDS limits");
 };
 
 template <class C, int DK, int DV>
-__global__ __launch_bounds__(64, 1) void decode_i8_kernel(DecodeArgs a, int ch, int n_split) {
+__global__ __launch_bounds__(64, 2) void decode_i8_kernel(DecodeArgs a, int ch, int n_split) {
   __shared__ __attribute__((aligned(1024))) unsigned char lds[C::LDS];
-  __shared__ float2 cs_tab[DK / 2];
-  unsigned char* vb = lds + (C::RING > C::RED ? C::RING : C::RED);
+  // The query's (cos, sin) rows live in stage AHEAD, which the prologue's
+  // DMAs leave free and the loop first refills after the query is turned.
+  float2* cs_tab = reinterpret_cast<float2*>(lds + C::AHEAD * C::ST);
 
   const int kvh = blockIdx.x, split = blockIdx.y, b = blockIdx.z;
   const int lane = threadIdx.x;
@@ -192,7 +200,10 @@ __global__ __launch_bounds__(64, 1) void decode_i8_kernel(DecodeArgs a, int ch, 
     const bool hv = col < G;
     const uint16_t* qrow =
         (const uint16_t*)a.q + ((int64_t)b * a.Hq + kvh * G + (hv ? col : 0)) * DK;
-    float qv[DK / 4];  // this lane's 16 dims per 64-dim step, as fp32
+    // This lane's 16 dims per 64-dim step, turned and kept as packed bf16
+    // (the query's own precision); the split below reads them three times
+    // rather than holding them as fp32.
+    uint32_t qw[DK / 8];
     float amax = 0.f;
 #pragma unroll
     for (int s = 0; s < DK / 64; ++s) {
@@ -208,22 +219,31 @@ __global__ __launch_bounds__(64, 1) void decode_i8_kernel(DecodeArgs a, int ch, 
             const float x0 = bf16_lo(w[e]), x1 = bf16_hi(w[e]);
             w[e] = pack_bf16x2(x0 * t.x - x1 * t.y, x0 * t.y + x1 * t.x);
           }
-          const float x0 = hv ? bf16_lo(w[e]) : 0.f, x1 = hv ? bf16_hi(w[e]) : 0.f;
-          qv[16 * s + 8 * h + 2 * e] = x0;
-          qv[16 * s + 8 * h + 2 * e + 1] = x1;
-          amax = fmaxf(amax, fmaxf(fabsf(x0), fabsf(x1)));
+          qw[8 * s + 4 * h + e] = hv ? w[e] : 0u;
+          amax = fmaxf(amax, fmaxf(fabsf(bf16_lo(qw[8 * s + 4 * h + e])),
+                                   fabsf(bf16_hi(qw[8 * s + 4 * h + e]))));
         }
       }
     }
     amax = xor32_16_max(amax);
     qs1 = amax / 127.f;
     const float r1 = amax > 0.f ? 127.f / amax : 0.f;
+    // element i (i < DK/4) of this lane: dim pair i/2 of the packed words
+    auto elem = [&](int i) {
+      const uint32_t w = qw[i / 2];
+      return (i & 1) ? bf16_hi(w) : bf16_lo(w);
+    };
+    auto residual = [&](int i, float* c) {
+      const float x = elem(i);
+      *c = rintf(x * r1);
+      return x - qs1 * *c;
+    };
     float rmax = 0.f;
 #pragma unroll
     for (int i = 0; i < DK / 4; ++i) {
-      const float c = rintf(qv[i] * r1);
-      qv[i] = qv[i] - qs1 * c;  // residual
-      rmax = fmaxf(rmax, fabsf(qv[i]));
+      float c;
+      const float r = residual(i, &c);
+      rmax = fmaxf(rmax, fabsf(r));
       const int s = i / 16, e = i % 16;
       const uint32_t byte = (uint32_t)(int)c & 0xffu;
       if (e % 4 == 0) q1[s][e / 4] = (int)byte;
@@ -234,8 +254,10 @@ __global__ __launch_bounds__(64, 1) void decode_i8_kernel(DecodeArgs a, int ch, 
     const float r2 = rmax > 0.f ? 127.f / rmax : 0.f;
 #pragma unroll
     for (int i = 0; i < DK / 4; ++i) {
+      float c;
+      const float r = residual(i, &c);
       const int s = i / 16, e = i % 16;
-      const uint32_t byte = (uint32_t)(int)rintf(qv[i] * r2) & 0xffu;
+      const uint32_t byte = (uint32_t)(int)rintf(r * r2) & 0xffu;
       if (e % 4 == 0) q2[s][e / 4] = (int)byte;
       else q2[s][e / 4] |= (int)(byte << (8 * (e % 4)));
     }
@@ -264,22 +286,6 @@ __global__ __launch_bounds__(64, 1) void decode_i8_kernel(DecodeArgs a, int ch, 
   for (int t = 0; t < n_tiles; ++t) {
     dma_tile(t + C::AHEAD, cur == 0 ? C::AHEAD : cur - 1);
     const lds_u8* st = (const lds_u8*)lds + __builtin_amdgcn_readfirstlane(cur * C::ST);
-    // V codes of this tile -> bf16 (+128) rows in vb: 4 chunks of 16 codes
-    // per lane, each into two 8-element bf16 chunks (same row swizzle).
-#pragma unroll
-    for (int i = 0; i < 16 * C::VC / 64; ++i) {
-      const int q = i * 64 + lane, r = q / C::VC, c = q % C::VC;
-      const u32x4 w = *(const __attribute__((address_space(3))) u32x4*)(st + C::KT + r * DV +
-                                                                     ((c ^ (r & 15)) << 4));
-      const f32x4 f0 = ubytes(w[0]), f1 = ubytes(w[1]), f2 = ubytes(w[2]), f3 = ubytes(w[3]);
-      const u32x4 lo4 = {pack_bf16x2(f0[0], f0[1]), pack_bf16x2(f0[2], f0[3]),
-                         pack_bf16x2(f1[0], f1[1]), pack_bf16x2(f1[2], f1[3])};
-      const u32x4 hi4 = {pack_bf16x2(f2[0], f2[1]), pack_bf16x2(f2[2], f2[3]),
-                         pack_bf16x2(f3[0], f3[1]), pack_bf16x2(f3[2], f3[3])};
-      unsigned char* rowp = vb + r * DV * 2;
-      *(u32x4*)(rowp + (((2 * c) ^ (r & 15)) << 4)) = lo4;
-      *(u32x4*)(rowp + (((2 * c + 1) ^ (r & 15)) << 4)) = hi4;
-    }
     // S^T[16 keys][16 heads] = ks * (s1 K.q1 + s2 K.q2), int32 dot products.
     i32x4 S1 = i32x4{}, S2 = i32x4{};
 #pragma unroll
@@ -288,6 +294,32 @@ __global__ __launch_bounds__(64, 1) void decode_i8_kernel(DecodeArgs a, int ch, 
           st + krd + (((4 * k + g) ^ col) << 4));
       S1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(kc, q1[k], S1, 0, 0, 0);
       S2 = __builtin_amdgcn_mfma_i32_16x16x64_i8(kc, q2[k], S2, 0, 0, 0);
+    }
+    // V codes of this tile -> bf16 (+128) rows written over the stage's codes
+    // from its base: 4 chunks of 16 codes per lane, each into two 8-element
+    // bf16 chunks (same row swizzle). Every code and K operand is read before
+    // the first write (one wave: its LDS operations complete in order).
+    u32x4 vw[16 * C::VC / 64];
+#pragma unroll
+    for (int i = 0; i < 16 * C::VC / 64; ++i) {
+      const int q = i * 64 + lane, r = q / C::VC, c = q % C::VC;
+      vw[i] = *(const __attribute__((address_space(3))) u32x4*)(st + C::KT + r * DV +
+                                                                ((c ^ (r & 15)) << 4));
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    unsigned char* vb = (unsigned char*)lds + __builtin_amdgcn_readfirstlane(cur * C::ST);
+#pragma unroll
+    for (int i = 0; i < 16 * C::VC / 64; ++i) {
+      const int q = i * 64 + lane, r = q / C::VC, c = q % C::VC;
+      const u32x4 w = vw[i];
+      const f32x4 f0 = ubytes(w[0]), f1 = ubytes(w[1]), f2 = ubytes(w[2]), f3 = ubytes(w[3]);
+      const u32x4 lo4 = {pack_bf16x2(f0[0], f0[1]), pack_bf16x2(f0[2], f0[3]),
+                         pack_bf16x2(f1[0], f1[1]), pack_bf16x2(f1[2], f1[3])};
+      const u32x4 hi4 = {pack_bf16x2(f2[0], f2[1]), pack_bf16x2(f2[2], f2[3]),
+                         pack_bf16x2(f3[0], f3[1]), pack_bf16x2(f3[2], f3[3])};
+      unsigned char* rowp = vb + r * DV * 2;
+      *(u32x4*)(rowp + (((2 * c) ^ (r & 15)) << 4)) = lo4;
+      *(u32x4*)(rowp + (((2 * c + 1) ^ (r & 15)) << 4)) = hi4;
     }
     const f32x4 ks = *(const __attribute__((address_space(3))) f32x4*)(st + C::KT + C::VT + 16 * g);
     const f32x4 vs = *(const __attribute__((address_space(3))) f32x4*)(st + C::KT + C::VT + 256 + 16 * g);
@@ -329,7 +361,7 @@ __global__ __launch_bounds__(64, 1) void decode_i8_kernel(DecodeArgs a, int ch, 
 #pragma unroll
     for (int d = 0; d < DV / 16; ++d) {
       const bf16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-          (lds_bf16x4*)((const lds_u8*)vb + vo[d % 8] + (d / 8) * 256));
+          (lds_bf16x4*)(st + vo[d % 8] + (d / 8) * 256));
       oacc[d] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, v), pb,
                                                           oacc[d], 0, 0, 0);
     }
