@@ -11,7 +11,8 @@
 // pairs l, l+64, ... of q/k and of v/o, so RoPE pairs stay inside a lane. The
 // query's angles are formed in fp64 here; K's rotary pairs arrive turned by
 // the pre-pass (k_rot).
-// Keys stream in order with an online softmax (running max and sum in fp32).
+// Keys stream in order, 8 at a time, with an online softmax (running max and
+// sum in fp32).
 #include "attn_common.h"
 #include "kernels.h"
 
@@ -31,7 +32,10 @@ __device__ __forceinline__ float2 load_pair(const void* base, int64_t elem) {
   }
 }
 
-template <bool BF16>
+// NE: dimension pairs per lane (ceil(max(Dk, Dv) / 128)). Lanes whose pair
+// is past the head read pair 0 and weigh it by 0 (a select, not a branch), so
+// every load of a key block goes out before the first is waited on.
+template <bool BF16, int NE>
 __global__ __launch_bounds__(256) void prefill_general_kernel(PrefillArgs a) {
   const int lane = threadIdx.x & 63;
   const int64_t row_id = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -46,9 +50,9 @@ __global__ __launch_bounds__(256) void prefill_general_kernel(PrefillArgs a) {
 
   // The query pairs this lane owns, rotated at position pos0 + i (angles in
   // fp64).
-  float2 q[kMaxPairs];
+  float2 q[NE];
 #pragma unroll
-  for (int e = 0; e < kMaxPairs; ++e) {
+  for (int e = 0; e < NE; ++e) {
     const int p = lane + 64 * e;
     q[e] = make_float2(0.f, 0.f);
     if (p < PK) {
@@ -63,42 +67,106 @@ __global__ __launch_bounds__(256) void prefill_general_kernel(PrefillArgs a) {
   }
 
   float m = -INFINITY, l = 0.f;
-  float2 acc[kMaxPairs];
+  float2 acc[NE];
 #pragma unroll
-  for (int e = 0; e < kMaxPairs; ++e) acc[e] = make_float2(0.f, 0.f);
+  for (int e = 0; e < NE; ++e) acc[e] = make_float2(0.f, 0.f);
 
+  // Keys in blocks of KB: the block's loads and reductions are independent,
+  // so they overlap; one online-softmax update per block. Keys past i (the
+  // last block's tail) are read at i and masked out.
+  // Keys per block: 8, which the reduction below assumes (16 measured
+  // slower).
+  constexpr int KB = 8;
   const int lo = (a.window > 0) ? max(0, i - a.window + 1) : 0;
-  for (int j = lo; j <= i; ++j) {
-    const int64_t kbase = (((int64_t)b * a.T + j) * a.Hkv + g) * a.Dk;
-    const int64_t krbase = (((int64_t)b * a.T + j) * a.Hkv + g) * (2 * a.rot_pairs);
-    float part = 0.f;
+  for (int j0 = lo; j0 <= i; j0 += KB) {
+    float s[KB];
 #pragma unroll
-    for (int e = 0; e < kMaxPairs; ++e) {
-      const int p = lane + 64 * e;
-      if (p < PK) {
+    for (int u = 0; u < KB; ++u) {
+      const int j = min(j0 + u, i);
+      const int64_t kbase = (((int64_t)b * a.T + j) * a.Hkv + g) * a.Dk;
+      const int64_t krbase = (((int64_t)b * a.T + j) * a.Hkv + g) * (2 * a.rot_pairs);
+      float part = 0.f;
+#pragma unroll
+      for (int e = 0; e < NE; ++e) {
+        const int p = lane + 64 * e;
+        const bool in = p < PK;
+        const int pc = in ? p : 0;
         // K's rotary pairs come turned from the pre-pass (k_rot).
-        const float2 kx = (a.rope_k && p < a.rot_pairs)
-                              ? load_pair<BF16>(a.k_rot, krbase + 2 * p)
-                              : load_pair<BF16>(a.k, kbase + 2 * p);
-        part += q[e].x * kx.x + q[e].y * kx.y;
+        const bool rot = a.rope_k && pc < a.rot_pairs;
+        const float2 kx = load_pair<BF16>(rot ? a.k_rot : a.k,
+                                          (rot ? krbase : kbase) + 2 * pc);
+        part += in ? q[e].x * kx.x + q[e].y * kx.y : 0.f;
+      }
+      s[u] = part;
+    }
+    // The block's V rows, loaded before the scores are reduced (they do not
+    // depend on them), so their latency runs under the reduction.
+    float2 vx[KB][NE];
+#pragma unroll
+    for (int u = 0; u < KB; ++u) {
+      const int j = min(j0 + u, i);
+      const int64_t vbase = (((int64_t)b * a.T + j) * a.Hkv + g) * a.Dv;
+#pragma unroll
+      for (int e = 0; e < NE; ++e) {
+        const int pp = lane + 64 * e;
+        vx[u][e] = load_pair<BF16>(a.v, vbase + 2 * (pp < PV ? pp : 0));
       }
     }
+    // Sum each key's partial over the 64 lanes by reduce-scatter: halving
+    // the keys a lane keeps at lane distances 32, 16 and 8 leaves lane l with
+    // key (l >> 3) & 7 summed over 8 lanes; three more steps finish the sum,
+    // and lane 8u then holds key u's score (10 exchanges instead of 48).
+    {
+      const bool b5 = lane & 32, b4 = lane & 16, b3 = lane & 8;
+      float t[4];
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) part += __shfl_xor(part, off);
-    const float s = part * a.scale;
-    const float m_new = fmaxf(m, s);
+      for (int k = 0; k < 4; ++k) {
+        const float give = b5 ? s[k] : s[k + 4];
+        t[k] = (b5 ? s[k + 4] : s[k]) + __shfl_xor(give, 32);
+      }
+      float w[2];
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const float give = b4 ? t[k] : t[k + 2];
+        w[k] = (b4 ? t[k + 2] : t[k]) + __shfl_xor(give, 16);
+      }
+      float x = (b3 ? w[1] : w[0]) + __shfl_xor(b3 ? w[0] : w[1], 8);
+      x += __shfl_xor(x, 4);
+      x += __shfl_xor(x, 2);
+      x += __shfl_xor(x, 1);
+#pragma unroll
+      for (int u = 0; u < KB; ++u)
+        s[u] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 8 * u));
+    }
+    float m_blk = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < KB; ++u) {
+      s[u] = (j0 + u <= i) ? s[u] * a.scale : -INFINITY;
+      m_blk = fmaxf(m_blk, s[u]);
+    }
+    const float m_new = fmaxf(m, m_blk);
     const float alpha = __expf(m - m_new);
-    const float p = __expf(s - m_new);
-    l = l * alpha + p;
-    m = m_new;
-    const int64_t vbase = (((int64_t)b * a.T + j) * a.Hkv + g) * a.Dv;
+    float pr[KB];
+    float psum = 0.f;
 #pragma unroll
-    for (int e = 0; e < kMaxPairs; ++e) {
-      const int pp = lane + 64 * e;
-      if (pp < PV) {
-        const float2 vx = load_pair<BF16>(a.v, vbase + 2 * pp);
-        acc[e].x = acc[e].x * alpha + p * vx.x;
-        acc[e].y = acc[e].y * alpha + p * vx.y;
+    for (int u = 0; u < KB; ++u) {
+      pr[u] = __expf(s[u] - m_new);
+      psum += pr[u];
+    }
+    l = l * alpha + psum;
+    m = m_new;
+#pragma unroll
+    for (int e = 0; e < NE; ++e) {
+      acc[e].x *= alpha;
+      acc[e].y *= alpha;
+    }
+#pragma unroll
+    for (int u = 0; u < KB; ++u) {
+#pragma unroll
+      for (int e = 0; e < NE; ++e) {
+        const float w = (lane + 64 * e < PV) ? pr[u] : 0.f;
+        acc[e].x += w * vx[u][e].x;
+        acc[e].y += w * vx[u][e].y;
       }
     }
   }
@@ -106,7 +174,7 @@ __global__ __launch_bounds__(256) void prefill_general_kernel(PrefillArgs a) {
   const float inv = 1.f / l;
   const int64_t obase = (((int64_t)b * a.T + i) * a.Hq + h) * a.Dv;
 #pragma unroll
-  for (int e = 0; e < kMaxPairs; ++e) {
+  for (int e = 0; e < NE; ++e) {
     const int pp = lane + 64 * e;
     if (pp < PV) {
       const float y0 = acc[e].x * inv, y1 = acc[e].y * inv;
@@ -125,12 +193,22 @@ hipError_t launch_prefill_general(const PrefillArgs& a, bool bf16, hipStream_t s
   const int64_t blocks = (rows + 3) / 4;
   if (blocks == 0) return hipSuccess;
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
-  if (bf16)
-    hipLaunchKernelGGL(prefill_general_kernel<true>, dim3((unsigned)blocks), dim3(256),
-                       0, st, a);
-  else
-    hipLaunchKernelGGL(prefill_general_kernel<false>, dim3((unsigned)blocks), dim3(256),
-                       0, st, a);
+  const int ne = ((a.Dk > a.Dv ? a.Dk : a.Dv) / 2 + 63) / 64;
+  if (ne < 1 || ne > kMaxPairs) return hipErrorInvalidValue;
+  auto go = [&](auto kern) {
+    hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(256), 0, st, a);
+  };
+  if (bf16) {
+    if (ne == 1) go(prefill_general_kernel<true, 1>);
+    else if (ne == 2) go(prefill_general_kernel<true, 2>);
+    else if (ne == 3) go(prefill_general_kernel<true, 3>);
+    else go(prefill_general_kernel<true, 4>);
+  } else {
+    if (ne == 1) go(prefill_general_kernel<false, 1>);
+    else if (ne == 2) go(prefill_general_kernel<false, 2>);
+    else if (ne == 3) go(prefill_general_kernel<false, 3>);
+    else go(prefill_general_kernel<false, 4>);
+  }
   return hipGetLastError();
 }
 

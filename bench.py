@@ -408,31 +408,6 @@ def cpu_baseline_stack(oracle, cfg, r, target_s):
                        f"would take ~{r['flops'] / rate / 3600:.1f} h at this rate")}
 
 
-def cpu_baseline_prefill(oracle, cfg, res, target_s):
-    """The oracle on a seeded row sample of one prefill workload."""
-    import numpy as np
-    c = cfg["case"]
-    q, k, v, _ = res["tensors"]
-    qh, kh, vh = q.cpu(), k.cpu(), v.cpu()
-    rng = np.random.default_rng(0)
-    n = 16
-    while True:
-        rows = np.sort(rng.choice(c.T, size=min(n, c.T), replace=False)).astype(np.int32)
-        t0 = time.perf_counter()
-        oracle.prefill(qh[:, rows], kh, vh, window=c.window, scale=c.scale,
-                       rotary_dims=c.rotary_dims, theta=c.theta, rows=rows)
-        dt = time.perf_counter() - t0
-        if dt >= target_s / 4 or n >= c.T:
-            break
-        n = min(c.T, max(2 * n, int(n * target_s / max(dt, 1e-3))))
-    fl = rows_flops(c, rows.tolist())
-    return {"value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.max_threads(),
-            "kind": "oracle",
-            "sample": f"{len(rows)} of {c.T} query rows x B={c.B} x Hq={c.Hq} "
-                      f"(seeded random rows; fp64, incl. K rotation and KV replication), "
-                      f"{dt:.1f} s"}
-
-
 # ---------------------------------------------------------------------------
 def secondary_prefill(ar, torch, inputs, name, sc):
     fp32 = not str(sc["case"].dtype).endswith("bfloat16")
@@ -448,7 +423,8 @@ def secondary_prefill(ar, torch, inputs, name, sc):
            "value": round(rr["flops"] / rr["call"]["median"] / 1e9, 3),
            "ms_per_call": round(rr["call"]["median"], 5), "timed_calls": rr["iters"],
            "what": "attn_prefill call: K rotation pre-pass, flash kernel",
-           "roofline": dict(roofline("mfma", tf_k, peak, "TFLOP/s", _traffic(kname, name)),
+           "roofline": dict(roofline("alu" if fp32 else "mfma", tf_k, peak, "TFLOP/s",
+                                     _traffic(kname, name)),
                             kernel=kname + "_kernel",
                             kernel_ms=round(rr["kern"]["median"], 5),
                             flops_per_launch=rr["flops"])}
