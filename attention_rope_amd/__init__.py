@@ -32,7 +32,7 @@ STATUS = {0: "ok", 1: "null pointer", 2: "invalid shape or argument",
           5: "kernel launch failed", 6: "output overlaps an input"}
 
 # Every symbol the header declares (checked by the tests).
-EXPORTS = ("attn_prefill",
+EXPORTS = ("attn_prefill", "attn_prefill_into_cache",
            "attn_prefill_workspace_bytes", "attn_decode",
            "attn_decode_workspace_bytes", "attn_decode_noalloc", "attn_decode_noalloc_max_bytes",
            "attn_verify", "attn_verify_workspace_bytes",
@@ -68,6 +68,9 @@ def load(path: str = LIB_PATH):
     lib.attn_prefill.argtypes = [vp, vp, vp, vp] + [i32] * 7 + [
         ctypes.c_float, _Rope, i32, i32, vp, sz, ctypes.c_int, vp]
     lib.attn_prefill.restype = ctypes.c_int
+    lib.attn_prefill_into_cache.argtypes = [vp, vp, vp, vp] + [i32] * 7 + [
+        ctypes.c_float, _Rope, i32, vp, vp, vp, ctypes.c_int64, vp, sz, ctypes.c_int, vp]
+    lib.attn_prefill_into_cache.restype = ctypes.c_int
     lib.attn_decode_workspace_bytes.argtypes = [i32] * 6
     lib.attn_decode_workspace_bytes.restype = sz
     lib.attn_decode.argtypes = [vp] * 6 + [i32] * 6 + [
@@ -198,6 +201,52 @@ def prefill(q, k, v, *, window: int = 0, scale: float | None = None,
                             B, T, Hq, Hkv, Dk, Dv, int(window), float(scale),
                             _Rope(rotary_dims, theta), int(rope_mask), int(pos0),
                             ws_ptr, ws_bytes, _dtype_code(q), _stream(q)))
+    return o
+
+
+def prefill_into_cache(q, k, v, k_cache, v_cache, row_offset, *, window: int = 0,
+                       scale: float | None = None, rotary_dims: int = 0,
+                       theta: float = 10000.0, pos0: int = 0, out=None, workspace=None):
+    """prefill() with RoPE on q and k that also writes the decode cache:
+    k_cache[row_offset[b] + t] = rope(k[b, t]) at position pos0 + t,
+    v_cache[row_offset[b] + t] = v[b, t]. k_cache [rows, Hkv, Dk], v_cache
+    [rows, Hkv, Dv], row_offset int64 [B] on the device. Returns o."""
+    lib = load()
+    _need_dims(q, 4, "q")
+    _need_dims(k, 4, "k")
+    _need_dims(v, 4, "v")
+    B, T, Hq, Dk = q.shape
+    Hkv, Dv = k.shape[2], v.shape[3]
+    if tuple(k.shape) != (B, T, Hkv, Dk) or tuple(v.shape) != (B, T, Hkv, Dv):
+        raise ValueError(f"q/k/v shapes disagree: {tuple(q.shape)} {tuple(k.shape)} "
+                         f"{tuple(v.shape)}")
+    _need_dims(k_cache, 3, "k_cache")
+    _need_dims(v_cache, 3, "v_cache")
+    rows = k_cache.shape[0]
+    _need_shape(k_cache, (rows, Hkv, Dk), "k_cache")
+    _need_shape(v_cache, (rows, Hkv, Dv), "v_cache")
+    if row_offset.dtype != torch.int64 or row_offset.numel() != B:
+        raise ValueError(f"row_offset must be int64 with {B} entries")
+    _same(q, "q", k=k, v=v, k_cache=k_cache, v_cache=v_cache)
+    _same_device(q, "q", row_offset=row_offset)
+    if scale is None:
+        scale = Dk ** -0.5
+    o = out if out is not None else torch.empty((B, T, Hq, Dv), dtype=q.dtype, device=q.device)
+    _need_shape(o, (B, T, Hq, Dv), "out")
+    _same(q, "q", out=o)
+    need = int(lib.attn_prefill_workspace_bytes(B, T, Hkv, Dk, _Rope(rotary_dims, theta),
+                                                ROPE_Q | ROPE_K, _dtype_code(q)))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    if workspace is not None:
+        _same(q, "q", workspace=workspace)
+    ws_ptr = _dev(workspace, "workspace") if workspace is not None else None
+    ws_bytes = _nbytes(workspace) if workspace is not None else 0
+    _check(lib.attn_prefill_into_cache(
+        _dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(o, "o"), B, T, Hq, Hkv, Dk, Dv,
+        int(window), float(scale), _Rope(rotary_dims, theta), int(pos0),
+        _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), _dev(row_offset, "row_offset"),
+        int(rows), ws_ptr, ws_bytes, _dtype_code(q), _stream(q)))
     return o
 
 

@@ -177,11 +177,22 @@ size_t attn_prefill_workspace_bytes(int32_t B, int32_t T, int32_t Hkv, int32_t D
   return (size_t)B * T * Hkv * rope.rotary_dims * elem_size(dtype);
 }
 
-attn_status_t attn_prefill(const void* q, const void* k, const void* v, void* o,
-                           int32_t B, int32_t T, int32_t Hq, int32_t Hkv, int32_t Dk,
+namespace {
+
+// Decode-cache outputs of attn_prefill_into_cache (k_cache == nullptr: none).
+struct CacheOut {
+  void* k_cache = nullptr;
+  void* v_cache = nullptr;
+  const int64_t* row_offset = nullptr;
+  int64_t cache_rows = 0;
+};
+
+attn_status_t prefill_call(const char* what, const void* q, const void* k, const void* v,
+                           void* o, int32_t B, int32_t T, int32_t Hq, int32_t Hkv, int32_t Dk,
                            int32_t Dv, int32_t window, float scale, attn_rope_t rope,
                            int32_t rope_mask, int32_t pos0, void* workspace,
-                           size_t workspace_bytes, attn_dtype_t dtype, void* stream) {
+                           size_t workspace_bytes, attn_dtype_t dtype, void* stream,
+                           const CacheOut& cache) {
   if (dtype != ATTN_F32 && dtype != ATTN_BF16)
     return fail(ATTN_ERR_UNSUPPORTED, "dtype %d is not ATTN_F32 or ATTN_BF16", (int)dtype);
   if (B < 0 || T < 0) return fail(ATTN_ERR_SHAPE, "B=%d and T=%d must be >= 0", B, T);
@@ -197,7 +208,8 @@ attn_status_t attn_prefill(const void* q, const void* k, const void* v, void* o,
   if (pos0 < 0 || (int64_t)pos0 + T > INT32_MAX)
     return fail(ATTN_ERR_SHAPE, "positions pos0=%d .. pos0+T-1 must lie in [0, 2^31-1)", pos0);
   if (B == 0 || T == 0) return ok();
-  if (!q || !k || !v || !o) return fail(ATTN_ERR_NULL, "q, k, v and o must be non-NULL");
+  if (!q || !k || !v || !o)
+    return fail(ATTN_ERR_NULL, "%s: q, k, v and o must be non-NULL", what);
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
     return fail(ATTN_ERR_SHAPE, "q, k, v and o must be 16-byte aligned");
   const size_t es = elem_size(dtype);
@@ -219,6 +231,34 @@ attn_status_t attn_prefill(const void* q, const void* k, const void* v, void* o,
       return fail(ATTN_ERR_ALIAS, "workspace must not overlap q, k, v or o");
   }
 
+  const bool fill = cache.k_cache != nullptr;
+  if (fill) {
+    if (!cache.v_cache || !cache.row_offset)
+      return fail(ATTN_ERR_NULL, "%s: k_cache, v_cache and row_offset must be non-NULL", what);
+    if (Dk % 8 || Dv % 8 || rope.rotary_dims % 8)
+      return fail(ATTN_ERR_SHAPE, "%s: Dk=%d, Dv=%d and rotary_dims=%d must be multiples of 8",
+                  what, Dk, Dv, rope.rotary_dims);
+    if (cache.cache_rows < T || cache.cache_rows > ((int64_t)1 << 40))
+      return fail(ATTN_ERR_SHAPE, "%s: cache_rows=%lld must be in [T, 2^40]", what,
+                  (long long)cache.cache_rows);
+    if (!aligned16(cache.k_cache) || !aligned16(cache.v_cache) ||
+        (reinterpret_cast<uintptr_t>(cache.row_offset) & 7u))
+      return fail(ATTN_ERR_SHAPE, "%s: caches must be 16-byte and row_offset 8-byte aligned",
+                  what);
+    const size_t nkc = (size_t)cache.cache_rows * Hkv * Dk * es;
+    const size_t nvc = (size_t)cache.cache_rows * Hkv * Dv * es;
+    const size_t nro = (size_t)B * sizeof(int64_t);
+    const void* ins[] = {q, k, v, o, workspace, cache.row_offset};
+    const size_t ns[] = {nq, nk, nv, no, nws, nro};
+    for (int i = 0; i < 6; ++i)
+      if (overlap(cache.k_cache, nkc, ins[i], ns[i]) || overlap(cache.v_cache, nvc, ins[i], ns[i]))
+        return fail(ATTN_ERR_ALIAS,
+                    "%s: the caches must not overlap q, k, v, o, the workspace or row_offset",
+                    what);
+    if (overlap(cache.k_cache, nkc, cache.v_cache, nvc))
+      return fail(ATTN_ERR_ALIAS, "%s: k_cache and v_cache must not overlap", what);
+  }
+
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   attn::PrefillArgs a{};
   a.q = q; a.k = k; a.v = v; a.o = o;
@@ -233,7 +273,19 @@ attn_status_t attn_prefill(const void* q, const void* k, const void* v, void* o,
   a.pos0 = pos0;
   a.log2_theta = rot ? std::log2(rope.theta) : 0.0;
   a.rope_rho = rot ? std::pow(rope.theta, -2.0 / (double)Dk) : 1.0;
-  if (a.rope_k && nws > 0) {
+  if (fill) {
+    // One pass over K and V: K's rotary dims turn once into the workspace
+    // (as below) and whole turned key rows and value rows go to the cache.
+    attn_status_t r = launch_status(
+        attn::launch_prefill_cache_fill(k, v, cache.k_cache, cache.v_cache,
+                                        nws > 0 ? workspace : nullptr, cache.row_offset,
+                                        cache.cache_rows, B, T, Hkv, Dk, Dv,
+                                        a.rope_k ? rope.rotary_dims : 0, pos0, rope.theta,
+                                        dtype == ATTN_BF16, st),
+        "prefill (cache fill)");
+    if (r != ATTN_OK) return r;
+    if (a.rope_k && nws > 0) a.k_rot = workspace;
+  } else if (a.rope_k && nws > 0) {
     // K's rotary dims turn once here, not once per query tile in the kernel.
     attn_status_t r = launch_status(
         attn::launch_rope_k_lead(k, workspace, B, T, Hkv, Dk, rope.rotary_dims, pos0,
@@ -249,6 +301,37 @@ attn_status_t attn_prefill(const void* q, const void* k, const void* v, void* o,
   }
   return launch_status(attn::launch_prefill_general(a, dtype == ATTN_BF16, st),
                        "prefill (general)");
+}
+
+}  // namespace
+
+attn_status_t attn_prefill(const void* q, const void* k, const void* v, void* o,
+                           int32_t B, int32_t T, int32_t Hq, int32_t Hkv, int32_t Dk,
+                           int32_t Dv, int32_t window, float scale, attn_rope_t rope,
+                           int32_t rope_mask, int32_t pos0, void* workspace,
+                           size_t workspace_bytes, attn_dtype_t dtype, void* stream) {
+  return prefill_call("prefill", q, k, v, o, B, T, Hq, Hkv, Dk, Dv, window, scale, rope,
+                      rope_mask, pos0, workspace, workspace_bytes, dtype, stream, CacheOut{});
+}
+
+attn_status_t attn_prefill_into_cache(const void* q, const void* k, const void* v, void* o,
+                                      int32_t B, int32_t T, int32_t Hq, int32_t Hkv,
+                                      int32_t Dk, int32_t Dv, int32_t window, float scale,
+                                      attn_rope_t rope, int32_t pos0, void* k_cache,
+                                      void* v_cache, const int64_t* row_offset,
+                                      int64_t cache_rows, void* workspace,
+                                      size_t workspace_bytes, attn_dtype_t dtype,
+                                      void* stream) {
+  CacheOut c;
+  c.k_cache = k_cache;
+  c.v_cache = v_cache;
+  c.row_offset = row_offset;
+  c.cache_rows = cache_rows;
+  if (B > 0 && T > 0 && !k_cache)
+    return fail(ATTN_ERR_NULL, "prefill_into_cache: k_cache must be non-NULL");
+  return prefill_call("prefill_into_cache", q, k, v, o, B, T, Hq, Hkv, Dk, Dv, window, scale,
+                      rope, ATTN_ROPE_Q | ATTN_ROPE_K, pos0, workspace, workspace_bytes, dtype,
+                      stream, c);
 }
 
 size_t attn_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t Dv,

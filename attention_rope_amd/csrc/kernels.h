@@ -16,6 +16,12 @@ hipError_t launch_prope(const void* x, void* y, const int32_t* pos, int N, int H
 // position pos0 + t (bf16 or fp32 elements, R even).
 hipError_t launch_rope_k_lead(const void* k, void* out, int B, int T, int H, int D, int R,
                               int pos0, double theta, bool bf16, hipStream_t st);
+// K turned into the workspace (as launch_rope_k_lead) and into k_cache rows
+// row_offset[b] + t, V copied into v_cache rows, in one pass (rope.hip).
+hipError_t launch_prefill_cache_fill(const void* k, const void* v, void* k_cache, void* v_cache,
+                                     void* k_rot, const int64_t* row_offset, int64_t cache_rows,
+                                     int B, int T, int H, int Dk, int Dv, int R, int pos0,
+                                     double theta, bool bf16, hipStream_t st);
 
 // ---- prefill ----------------------------------------------------------------
 struct PrefillArgs {

@@ -12,6 +12,36 @@
 
 namespace attn {
 
+// Pair (x0, x1) turned by the angle with cosine c and sine s, in fp32. Every
+// kernel here that turns K goes through this and turn_chunk, so a key turned
+// by any of them has the same bits.
+__device__ __forceinline__ float2 turn_pair(float x0, float x1, float c, float s) {
+  return make_float2(x0 * c - x1 * s, x0 * s + x1 * c);
+}
+
+// A 16-byte chunk of E = 16 / sizeof(T_) elements (E / 2 adjacent pairs)
+// turned by the pairs' (cos, sin).
+template <typename T_>
+__device__ __forceinline__ u32x4 turn_chunk(u32x4 w, const float* cs, const float* sn) {
+  u32x4 r;
+  if constexpr (sizeof(T_) == 2) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float2 y = turn_pair(bf16_lo(w[j]), bf16_hi(w[j]), cs[j], sn[j]);
+      r[j] = pack_bf16x2(y.x, y.y);
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const float2 y = turn_pair(__uint_as_float(w[2 * j]), __uint_as_float(w[2 * j + 1]),
+                                 cs[j], sn[j]);
+      r[2 * j] = __float_as_uint(y.x);
+      r[2 * j + 1] = __float_as_uint(y.y);
+    }
+  }
+  return r;
+}
+
 // y[n, h, :] = rope(x[n, h, :], pos[n]) with NH = 1 half, or 2-D RoPE with
 // NH = 2: each half of the D dims is a vector of its own, turned by its own
 // coordinate (pos[2n] the patch's width coordinate for the first half,
@@ -100,13 +130,8 @@ __global__ void rope_k_lead_kernel(const uint16_t* __restrict__ k, uint16_t* __r
       const int n = n0 + u;
       if (n < BH) {
         const int64_t nh = ((int64_t)(n / H) * T + t) * H + n % H;
-        u32x4 r;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const float x0 = bf16_lo(w[u][j]), x1 = bf16_hi(w[u][j]);
-          r[j] = pack_bf16x2(x0 * cs[j] - x1 * sn[j], x0 * sn[j] + x1 * cs[j]);
-        }
-        *reinterpret_cast<u32x4*>(out + nh * (8 * RC) + 8 * c) = r;
+        *reinterpret_cast<u32x4*>(out + nh * (8 * RC) + 8 * c) =
+            turn_chunk<uint16_t>(w[u], cs, sn);
       }
     }
   }
@@ -148,11 +173,11 @@ __global__ void rope_k_pairs_kernel(const T_* __restrict__ k, T_* __restrict__ o
       const int n = n0 + u;
       if (n < BH) {
         const int64_t nh = ((int64_t)(n / H) * T + t) * H + n % H;
-        const float y0 = x[u].x * c - x[u].y * sn, y1 = x[u].x * sn + x[u].y * c;
+        const float2 y = turn_pair(x[u].x, x[u].y, c, sn);
         if constexpr (sizeof(T_) == 2)
-          reinterpret_cast<uint32_t*>(out + nh * (2 * P))[p] = pack_bf16x2(y0, y1);
+          reinterpret_cast<uint32_t*>(out + nh * (2 * P))[p] = pack_bf16x2(y.x, y.y);
         else
-          reinterpret_cast<float2*>(out + nh * (2 * P))[p] = make_float2(y0, y1);
+          reinterpret_cast<float2*>(out + nh * (2 * P))[p] = y;
       }
     }
   }
@@ -190,6 +215,77 @@ hipError_t launch_rope_k_chunks(const void* k, void* out, int B, int T, int H, i
   hipLaunchKernelGGL(rope_k_lead_kernel, dim3((unsigned)blocks), dim3(threads), 0, st,
                      reinterpret_cast<const uint16_t*>(k), reinterpret_cast<uint16_t*>(out),
                      B, T, H, D, R / 8, pos0, log2(theta));
+  return hipGetLastError();
+}
+
+// Prefill's K/V pass that also fills a decode cache. Grid y = 0: one thread
+// per (token t, 16-byte chunk c of a key row) forms the angles of the chunk's
+// pairs at pos0 + t once (fp64), then for every (b, h) turns the chunk if it
+// lies in the leading R dims, writes it to the cache row row_offset[b] + t
+// and, if turned, to the workspace the attention kernel reads (the layout of
+// launch_rope_k_lead). Grid y = 1: the same for value rows, copied unchanged.
+// A batch row whose cache rows would leave [0, cache_rows) is not written to
+// the cache (its workspace rows still are).
+template <typename T_>
+__global__ void prefill_cache_fill_kernel(const T_* __restrict__ k, const T_* __restrict__ v,
+                                          T_* __restrict__ k_cache, T_* __restrict__ v_cache,
+                                          T_* __restrict__ k_rot,
+                                          const int64_t* __restrict__ row_offset,
+                                          int64_t cache_rows, int B, int T, int H, int Dk,
+                                          int Dv, int R, int pos0, double log2_theta) {
+  constexpr int E = 16 / sizeof(T_), NP = E / 2;  // elements, pairs per chunk
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const bool keys = blockIdx.y == 0;
+  const int D = keys ? Dk : Dv, NC = D / E;
+  if (idx >= (int64_t)T * NC) return;
+  const int c = (int)(idx % NC), t = (int)(idx / NC);
+  const bool turn = keys && c * E < R;
+  float cs[NP], sn[NP];
+#pragma unroll
+  for (int j = 0; j < NP; ++j) {
+    cs[j] = 1.f;
+    sn[j] = 0.f;
+    if (turn) rope_cos_sin((int64_t)pos0 + t, rope_freq(c * NP + j, Dk, log2_theta), &cs[j], &sn[j]);
+  }
+  const T_* src = keys ? k : v;
+  T_* dst = keys ? k_cache : v_cache;
+  for (int b = 0; b < B; ++b) {
+    const int64_t r0 = row_offset[b];
+    const bool in = r0 >= 0 && r0 <= cache_rows - T;
+    for (int h = 0; h < H; ++h) {
+      const int64_t n = ((int64_t)b * T + t) * H + h;
+      u32x4 w = *reinterpret_cast<const u32x4*>(src + n * D + c * E);
+      if (turn) {
+        w = turn_chunk<T_>(w, cs, sn);
+        *reinterpret_cast<u32x4*>(k_rot + n * R + c * E) = w;
+      }
+      if (in) *reinterpret_cast<u32x4*>(dst + ((r0 + t) * H + h) * D + c * E) = w;
+    }
+  }
+}
+
+hipError_t launch_prefill_cache_fill(const void* k, const void* v, void* k_cache, void* v_cache,
+                                     void* k_rot, const int64_t* row_offset, int64_t cache_rows,
+                                     int B, int T, int H, int Dk, int Dv, int R, int pos0,
+                                     double theta, bool bf16, hipStream_t st) {
+  const int E = bf16 ? 8 : 4;
+  if (Dk % E || Dv % E || R % E || R > Dk || (R > 0 && !k_rot)) return hipErrorInvalidValue;
+  const int64_t n = (int64_t)T * ((Dk > Dv ? Dk : Dv) / E);
+  if (n == 0 || B == 0 || H == 0) return hipSuccess;
+  const int threads = 256;
+  const int64_t blocks = (n + threads - 1) / threads;
+  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+  const double l2t = R > 0 ? log2(theta) : 0.0;
+  if (bf16)
+    hipLaunchKernelGGL(prefill_cache_fill_kernel<uint16_t>, dim3((unsigned)blocks, 2),
+                       dim3(threads), 0, st, (const uint16_t*)k, (const uint16_t*)v,
+                       (uint16_t*)k_cache, (uint16_t*)v_cache, (uint16_t*)k_rot, row_offset,
+                       cache_rows, B, T, H, Dk, Dv, R, pos0, l2t);
+  else
+    hipLaunchKernelGGL(prefill_cache_fill_kernel<float>, dim3((unsigned)blocks, 2),
+                       dim3(threads), 0, st, (const float*)k, (const float*)v,
+                       (float*)k_cache, (float*)v_cache, (float*)k_rot, row_offset, cache_rows,
+                       B, T, H, Dk, Dv, R, pos0, l2t);
   return hipGetLastError();
 }
 

@@ -119,6 +119,41 @@ attn_status_t attn_prefill(const void *q, const void *k, const void *v, void *o,
                            attn_dtype_t dtype, void *stream);
 
 /*
+ * Prefill that also fills the decode cache: attn_prefill with rope_mask =
+ * ATTN_ROPE_Q | ATTN_ROPE_K, whose K/V pass additionally writes every key,
+ * turned at its position, and every value into the caches a later
+ * attn_decode / attn_verify reads.
+ * Source: "Gemma 4: End-to-End Architecture Walkthrough", Phase 3 section 3b
+ * (the keys and values of the context are kept for the layers that attend
+ * them) and Phase 4 (the draft model attends the cache the target model has
+ * filled); the cached keys carry their rotation, as attn_decode expects.
+ *   q, k, v, o, B, T, Hq, Hkv, Dk, Dv, window, scale, rope, pos0: as for
+ *     attn_prefill (o is the same output).
+ *   k_cache [cache_rows, Hkv, Dk], v_cache [cache_rows, Hkv, Dv]: written at
+ *     rows row_offset[b] + t for t < T: k_cache gets rope(k[b, t]) at position
+ *     pos0 + t (all Dk dims, the leading rotary_dims turned), v_cache gets
+ *     v[b, t]. Other rows are not touched. Caller-owned device buffers.
+ *   row_offset: device int64 [B], 8-byte aligned. A batch row with
+ *     row_offset[b] < 0 or row_offset[b] + T > cache_rows is not written to
+ *     the cache (its o still is).
+ * Supported: Dk, Dv and rotary_dims multiples of 8; otherwise as attn_prefill.
+ *   Keys-as-values layers fill their one cache with prope_apply instead.
+ * Workspace: attn_prefill_workspace_bytes(B, T, Hkv, Dk, rope,
+ *   ATTN_ROPE_Q | ATTN_ROPE_K, dtype) bytes.
+ * Errors: as attn_prefill; NULL caches or row_offset -> ATTN_ERR_NULL;
+ *   caches overlapping each other, q, k, v, o, the workspace or row_offset ->
+ *   ATTN_ERR_ALIAS; cache_rows < T -> ATTN_ERR_SHAPE.
+ */
+attn_status_t attn_prefill_into_cache(const void *q, const void *k, const void *v, void *o,
+                                      int32_t B, int32_t T, int32_t Hq, int32_t Hkv,
+                                      int32_t Dk, int32_t Dv, int32_t window, float scale,
+                                      attn_rope_t rope, int32_t pos0, void *k_cache,
+                                      void *v_cache, const int64_t *row_offset,
+                                      int64_t cache_rows, void *workspace,
+                                      size_t workspace_bytes, attn_dtype_t dtype,
+                                      void *stream);
+
+/*
  * Decode: one new token per sequence over a ragged KV cache (bf16 only).
  * Source: "Gemma 4: End-to-End Architecture Walkthrough", Phase 3 section 3b
  * (global layers must keep the keys and values of the whole context; local
@@ -128,7 +163,8 @@ attn_status_t attn_prefill(const void *q, const void *k, const void *v, void *o,
  *   q [B, Hq, Dk]: the new tokens' queries, unrotated; sequence b's query sits
  *     at position kv_len[b] - 1 and is rotated there (rope applies to q only).
  *   k_cache [rows, Hkv, Dk], v_cache [rows, Hkv, Dv]: cached keys (stored
- *     already rotated) and values; sequence b owns rows
+ *     already rotated; attn_prefill_into_cache writes a prompt's rows) and
+ *     values; sequence b owns rows
  *     row_offset[b] .. row_offset[b] + kv_len[b] - 1, the last one being the
  *     new token's own row (the caller appends it before the call).
  *   Keys as values (K = V, the global-layer form of "Gemma 4: End-to-End

@@ -12,6 +12,11 @@ hipError_t launch_prope(const void*, void*, const int32_t*, int, int, int, int, 
                         hipStream_t) { ++g_launches; return hipSuccess; }
 hipError_t launch_rope_k_lead(const void*, void*, int, int, int, int, int, int, double, bool,
                               hipStream_t) { ++g_launches; return hipSuccess; }
+hipError_t launch_prefill_cache_fill(const void*, const void*, void*, void*, void*,
+                                     const int64_t*, int64_t, int, int, int, int, int, int, int,
+                                     double, bool, hipStream_t) {
+  ++g_launches; return hipSuccess;
+}
 hipError_t launch_prefill_mfma(const PrefillArgs&, hipStream_t) { ++g_launches; return hipSuccess; }
 hipError_t launch_prefill_mfma1w(const PrefillArgs&, hipStream_t) { ++g_launches; return hipSuccess; }
 hipError_t launch_prefill_mfma2g(const PrefillArgs&, hipStream_t) { ++g_launches; return hipSuccess; }

@@ -109,6 +109,42 @@ def test_prefill_workspace(lib):
     assert _prefill(lib, rope=R(32, 1e4), rope_mask=1, q=None) == 1
 
 
+def _into_cache(lib, **kw):
+    a = dict(q=P(0x10000), k=P(0x20000), v=P(0x30000), o=P(0x40000), B=2, T=8, Hq=4, Hkv=2,
+             Dk=64, Dv=64, window=0, scale=0.125, rope=R(16, 1e4), pos0=0,
+             kc=P(0x1000000), vc=P(0x2000000), off=P(0x3000000), rows=100,
+             ws=P(0x4000000), ws_bytes=1 << 20, dtype=ar.ATTN_BF16, stream=None)
+    a.update(kw)
+    return lib.attn_prefill_into_cache(a["q"], a["k"], a["v"], a["o"], a["B"], a["T"], a["Hq"],
+                                       a["Hkv"], a["Dk"], a["Dv"], a["window"], a["scale"],
+                                       a["rope"], a["pos0"], a["kc"], a["vc"], a["off"],
+                                       a["rows"], a["ws"], a["ws_bytes"], a["dtype"],
+                                       a["stream"])
+
+
+def test_prefill_into_cache_validation(lib):
+    """The cache-filling prefill checks everything attn_prefill checks, plus
+    its caches (present, aligned, disjoint from every other buffer and from
+    each other), row_offset and the 8-dim granularity of its K/V pass."""
+    assert _into_cache(lib, kc=None) == 1
+    assert _into_cache(lib, vc=None) == 1
+    assert _into_cache(lib, off=None) == 1
+    assert _into_cache(lib, q=None) == 1
+    assert _into_cache(lib, Dk=60, Dv=60, rope=R(0, 1e4)) == 2      # not a multiple of 8
+    assert _into_cache(lib, rope=R(12, 1e4)) == 2
+    assert _into_cache(lib, rows=7) == 2                            # fewer rows than T
+    assert _into_cache(lib, kc=P(0x1000008)) == 2                   # misaligned cache
+    assert _into_cache(lib, off=P(0x3000004)) == 2                  # misaligned row_offset
+    assert _into_cache(lib, kc=P(0x10000)) == 6                     # cache over q
+    assert _into_cache(lib, vc=P(0x1000000 + 64)) == 6              # caches overlap
+    assert _into_cache(lib, off=P(0x1000000 + 8)) == 6              # row_offset in the cache
+    assert _into_cache(lib, ws=P(0x1000000)) == 6                   # workspace in the cache
+    assert b"prefill_into_cache" in lib.attn_last_error()
+    assert _into_cache(lib, ws=None, ws_bytes=0) == 4               # K turns: workspace
+    assert _into_cache(lib, dtype=7) == 3
+    assert _into_cache(lib, B=0, q=None, kc=None) == 0              # empty: no-op
+
+
 def _decode(lib, **kw):
     a = dict(q=FAKE, k=FAKE, v=FAKE, off=FAKE, kvl=FAKE, o=FAKE2, B=2, Hq=8, Hkv=1,
              Dk=128, Dv=128, window=0, scale=0.1, rope=R(32, 1e6), max_kv_len=100,

@@ -124,3 +124,47 @@ def test_drafter_cross_attention(gpu_lib, shape):
         ref = oracle.cross_attend(q.cpu(), kc.cpu(), vc.cpu(), off, kvl, qpos, window=W,
                                   scale=Dk ** -0.5, rotary_dims=R, theta=theta)
         assert_close(o, ref, torch.bfloat16, f"drafter step {j}")
+
+
+@pytest.mark.parametrize("shape", ["local", "global"])
+def test_prefill_into_cache(gpu_lib, shape):
+    """attn_prefill_into_cache fills the decode cache in its K/V pass:
+    - o is attn_prefill's output bit for bit (the same kernels read keys
+      turned by the same arithmetic);
+    - each sequence's cache rows hold its keys turned at their positions (the
+      oracle's rope, to bf16 rounding) and its values bit for bit;
+    - rows outside the sequences' ranges keep their NaN poison;
+    - decoding each sequence's last token over the filled cache gives the
+      oracle's last prefill row, as a decode after a prompt should."""
+    base, W = {"local": (inputs.LOCAL, 100), "global": (inputs.GLOBAL, 0)}[shape]
+    c = inputs.PrefillCase(2, 300, window=W, dtype=torch.bfloat16, pos0=0, **base)
+    print(f"prefill_into_cache {shape} B={c.B} T={c.T}", flush=True)
+    q, k, v = inputs.prefill_inputs(c, 31, device=DEV)
+    offsets = [17, 17 + c.T + 40]
+    rows = offsets[-1] + c.T + 23
+    kc = torch.full((rows, c.Hkv, c.Dk), float("nan"), dtype=torch.bfloat16, device=DEV)
+    vc = torch.full((rows, c.Hkv, c.Dv), float("nan"), dtype=torch.bfloat16, device=DEV)
+    off = torch.tensor(offsets, dtype=torch.int64, device=DEV)
+    kw = dict(window=W, scale=c.scale, rotary_dims=c.rotary_dims, theta=c.theta)
+    o = gpu_lib.prefill_into_cache(q, k, v, kc, vc, off, **kw)
+    o_plain = gpu_lib.prefill(q, k, v, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o_plain)
+
+    pos = np.arange(c.T)
+    used = np.zeros(rows, dtype=bool)
+    for b, r0 in enumerate(offsets):
+        kr = oracle.rope(k[b].cpu(), pos, c.rotary_dims, c.theta)
+        assert_close(kc[r0:r0 + c.T], kr, torch.bfloat16, f"cached keys b={b}")
+        assert torch.equal(vc[r0:r0 + c.T], v[b])
+        used[r0:r0 + c.T] = True
+    assert torch.isnan(kc[torch.from_numpy(~used).to(DEV)].float()).all()
+    assert torch.isnan(vc[torch.from_numpy(~used).to(DEV)].float()).all()
+
+    # the prompt's last token decoded over its own cache rows
+    kvl = torch.full((c.B,), c.T, dtype=torch.int32, device=DEV)
+    od = gpu_lib.decode(q[:, -1].contiguous(), kc, vc, off, kvl, window=W, scale=c.scale,
+                        rotary_dims=c.rotary_dims, theta=c.theta, max_kv_len=c.T)
+    torch.cuda.synchronize()
+    ref = oracle.prefill(q[:, -1:].cpu(), k.cpu(), v.cpu(), rows=[c.T - 1], **kw)
+    assert_close(od, ref[:, 0], torch.bfloat16, "decode after prefill_into_cache")
