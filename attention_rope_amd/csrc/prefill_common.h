@@ -1,5 +1,6 @@
-// prefill_common.h — LDS layout and RoPE helpers shared by the MFMA prefill
-// kernels (prefill_mfma.hip, prefill_mfma2g.hip, prefill_mfma1w.hip).
+// prefill_common.h — LDS layout, operand reads, masking, output staging and
+// RoPE helpers shared by the MFMA prefill kernels (prefill_mfma.hip,
+// prefill_mfma2g.hip, prefill_mfma1w.hip).
 #pragma once
 #include "attn_common.h"
 
@@ -105,6 +106,89 @@ __device__ __forceinline__ void rotate_q_chunks(u32x4* qw, const lds_float2* slo
     qw[u] = rotate4(qw[u], f32x4{cs[0], cs[1], cs[2], cs[3]}, f32x4{cs[4], cs[5], cs[6], cs[7]});
   }
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+}
+
+// K operand of QK step s for key row r32 of a tile: dims 16s + 8h .. +7, the
+// rotated region's chunk 2s + h while s < RCH / 2, else the plain region's;
+// stored at chunk (2s + h) ^ mask, i.e. byte (32 s) ^ kx of the region row.
+template <int RCH>
+__device__ __forceinline__ bf16x8 k_operand(const lds_u8* kr, const lds_u8* kp, int kxr,
+                                            int kxp, int s) {
+  if (s < RCH / 2) return *(const lds_bf16x8*)(kr + ((32 * s) ^ kxr));
+  return *(const lds_bf16x8*)(kp + ((32 * (s - RCH / 2)) ^ kxp));
+}
+
+// V^T operand of P.V step i (key half j = i / NDT, dim tile dt = i % NDT) of
+// a tile whose rows hold VC 16-byte chunks swizzled by vswz: two transposing
+// reads of 4 keys each, 8 key rows apart, from this lane's row offset v and
+// row mask vx.
+template <int NDT, int VC>
+__device__ __forceinline__ bf16x8 vt_operand(const lds_u8* v, int vx, int i) {
+  const int j = i / NDT, dt = i % NDT;
+  const lds_u8* p = v + (((dt & 3) << 6) ^ vx) + (dt >> 2) * 256 + j * 16 * VC * 16;
+  const bf16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)p);
+  const bf16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p + 8 * VC * 16));
+  return __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// Scores of a 32-key tile starting at key j0, for a wave whose row
+// positions run wlo .. whi: a tile crossing the diagonal or the window edge
+// gets the per-score test (key j visible from position pos iff
+// 0 <= pos - j < wcap; wcap is W, or 2^31 for causal), any other tile is
+// left as it is. Element e of sc holds key j0 + 8(e/4) + 4h + (e%4). The
+// empty asm keeps the test a branch (the selects would otherwise run on
+// every tile); scores are masked in place.
+__device__ __forceinline__ void mask_edge_tile(f32x16& sc, int j0, int wlo, int whi, int W,
+                                               int pos, int h, unsigned wcap) {
+  if ((j0 + 31 > wlo) || (W > 0 && j0 <= whi - W)) {
+    asm volatile("");
+    const int d0 = pos - j0 - 4 * h;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const unsigned d = (unsigned)(d0 - (8 * (e / 4) + (e % 4)));  // pos - key
+      sc[e] = (d < wcap) ? sc[e] : -INFINITY;
+    }
+  }
+}
+
+// The output tile of one wave through LDS: stage_o writes O^T / l (NDT dim
+// tiles of 32) as bf16 rows of this wave's staging area, where element e of
+// dim tile dt is dim 32dt + 8(e/4) + 4h + (e%4), half h of 16-byte chunk
+// 4dt + e/4 of row r32, chunks XOR-swizzled by the row; store_o reads whole
+// 16-byte chunks back (64 / (DV/8) rows per instruction) and writes row r to
+// dst(r), skipping rows for which dst returns nullptr. A wave reads back only
+// what it wrote, and its LDS operations complete in order, so one
+// lgkmcnt wait between the two suffices.
+template <int NDT>
+__device__ __forceinline__ void stage_o(__attribute__((address_space(3))) unsigned char* ost,
+                                        const f32x16* oacc, float inv, int r32, int h) {
+  constexpr int ORB = NDT * 64, VCM = NDT * 4 - 1;
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const uint32_t w0 = pack_bf16x2(oacc[dt][4 * jj] * inv, oacc[dt][4 * jj + 1] * inv);
+      const uint32_t w1 = pack_bf16x2(oacc[dt][4 * jj + 2] * inv, oacc[dt][4 * jj + 3] * inv);
+      const int c = 4 * dt + jj;
+      *(__attribute__((address_space(3))) u32x2*)(ost + r32 * ORB + ((c ^ (r32 & VCM)) << 4) +
+                                                  8 * h) = u32x2{w0, w1};
+    }
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+}
+
+template <int DV, int RW, typename Dst>
+__device__ __forceinline__ void store_o(const lds_u8* ost, int lane, Dst&& dst) {
+  constexpr int VC = DV / 8, VCM = VC - 1, ORB = DV * 2;
+  constexpr int RPI = 64 / VC;  // rows per store instruction
+  const int c = lane % VC;
+#pragma unroll
+  for (int i = 0; i < RW / RPI; ++i) {
+    const int row = i * RPI + lane / VC;
+    const u32x4 val = *(const __attribute__((address_space(3))) u32x4*)(
+        ost + row * ORB + ((c ^ (row & VCM)) << 4));
+    uint16_t* d = dst(row);
+    if (d) *(u32x4*)(d + 8 * c) = val;
+  }
 }
 
 }  // namespace prefill

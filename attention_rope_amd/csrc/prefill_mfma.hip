@@ -299,19 +299,12 @@ __global__ __launch_bounds__((Cfg<DK, DV, G, RCH>::NT), 1) void prefill_mfma_ker
     return ad;
   };
   // K operand of QK step s (one 16-byte read per lane).
-  auto kread = [&](const Addr& ad, int s) -> bf16x8 {
-    if (s < RCH / 2) return *(const lds_bf16x8*)(ad.kr + ((32 * s) ^ ad.kxr));
-    return *(const lds_bf16x8*)(ad.kp + ((32 * (s - RCH / 2)) ^ ad.kxp));
+  auto kread = [&](const Addr& ad, int s) {
+    return k_operand<RCH>(ad.kr, ad.kp, ad.kxr, ad.kxp, s);
   };
   // V^T operand of P.V step i (key half j = i / NDT, dim tile dt = i % NDT):
   // two transposing reads of 4 keys each, 8 key rows apart.
-  auto vread = [&](const Addr& ad, int i) -> bf16x8 {
-    const int j = i / NDT, dt = i % NDT;
-    const lds_u8* p = ad.v + (((dt & 3) << 6) ^ ad.vx) + (dt >> 2) * 256 + j * 16 * C::VC * 16;
-    const bf16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)p);
-    const bf16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p + 8 * C::VC * 16));
-    return __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
-  };
+  auto vread = [&](const Addr& ad, int i) { return vt_operand<NDT, C::VC>(ad.v, ad.vx, i); };
 
   // S^T[32 keys][32 rows] of the tile in flight: element e holds key
   // 8(e/4) + 4h + (e%4). P^T operands of the tile whose softmax ran last.
@@ -356,19 +349,7 @@ __global__ __launch_bounds__((Cfg<DK, DV, G, RCH>::NT), 1) void prefill_mfma_ker
   // Softmax of the scores in sc (tile kb) into pop.
   auto softmax = [&](int kb) {
     const int j0 = kb * BN;
-    // Only tiles crossing the diagonal or a window edge of this wave's rows
-    // pay for the per-score test; the empty asm keeps this a branch (the
-    // compiler would otherwise run the selects on every tile). Scores are
-    // masked in place: a separate copy costs 16 moves per tile.
-    if ((j0 + BN - 1 > wlo) || (W > 0 && j0 <= whi - W)) {
-      asm volatile("");
-      const int d0 = pos - j0 - 4 * h;
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const unsigned d = (unsigned)(d0 - (8 * (e / 4) + (e % 4)));  // pos - key
-        sc[e] = (d < wcap) ? sc[e] : -INFINITY;
-      }
-    }
+    mask_edge_tile(sc, j0, wlo, whi, W, pos, h, wcap);
     float sv[16];
 #pragma unroll
     for (int e = 0; e < 16; ++e) sv[e] = sc[e];
@@ -485,39 +466,13 @@ __global__ __launch_bounds__((Cfg<DK, DV, G, RCH>::NT), 1) void prefill_mfma_ker
     l_run = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
   }
   static_assert(C::ROWS * DV * 2 <= C::LDS_BYTES, "output staging fits the ring");
-  constexpr int ORB = DV * 2;     // bytes per staged row
-  constexpr int VCM = C::VC - 1;  // chunks per row - 1 (a power of two)
   __attribute__((address_space(3))) unsigned char* ost =
-      (__attribute__((address_space(3))) unsigned char*)lds + wave * (RW * ORB);
-  {
-    const float inv = valid ? 1.f / l_run : 0.f;
-    // O^T element e of dim tile dt: dim 32dt + 8(e/4) + 4h + (e%4), i.e. half
-    // h of 16-byte chunk 4dt + e/4 of row r32; chunks XOR-swizzled by the row.
-#pragma unroll
-    for (int dt = 0; dt < DV / 32; ++dt)
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const uint32_t w0 = pack_bf16x2(oacc[dt][4 * jj] * inv, oacc[dt][4 * jj + 1] * inv);
-        const uint32_t w1 = pack_bf16x2(oacc[dt][4 * jj + 2] * inv, oacc[dt][4 * jj + 3] * inv);
-        const int c = 4 * dt + jj;
-        *(__attribute__((address_space(3))) u32x2*)(ost + r32 * ORB + ((c ^ (r32 & VCM)) << 4) +
-                                                    8 * h) = u32x2{w0, w1};
-      }
-  }
-  // A wave reads back only what it wrote; its LDS operations run in order.
-  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-  {
-    constexpr int RPI = 64 / C::VC;  // rows per store instruction
-    const int c = lane % C::VC;
-#pragma unroll
-    for (int i = 0; i < RW / RPI; ++i) {
-      const int row = i * RPI + lane / C::VC;
-      const u32x4 val =
-          *(const __attribute__((address_space(3))) u32x4*)(ost + row * ORB + ((c ^ (row & VCM)) << 4));
-      const int p = wlo + row;
-      if (p < T) *(u32x4*)((uint16_t*)a.o + (((int64_t)b * T + p) * a.Hq + head) * DV + 8 * c) = val;
-    }
-  }
+      (__attribute__((address_space(3))) unsigned char*)lds + wave * (RW * DV * 2);
+  stage_o<DV / 32>(ost, oacc, valid ? 1.f / l_run : 0.f, r32, h);
+  store_o<DV, RW>(ost, lane, [&](int row) -> uint16_t* {
+    const int p = wlo + row;
+    return p < T ? (uint16_t*)a.o + (((int64_t)b * T + p) * a.Hq + head) * DV : nullptr;
+  });
 }
 
 template <int DK, int DV, int G, int RCH>

@@ -303,17 +303,10 @@ __global__ __launch_bounds__(NT, 1) void prefill_mfma1w_kernel(PrefillArgs a, in
   };
   constexpr int NS = DK / 16;                 // QK MFMAs per tile
   constexpr int NDT = DV / 32, NPV = 2 * NDT;  // P.V MFMAs per tile
-  auto kread = [&](const Addr& ad, int s) -> bf16x8 {
-    if (s < RCH / 2) return *(const lds_bf16x8*)(ad.kr + ((32 * s) ^ ad.kxr));
-    return *(const lds_bf16x8*)(ad.kp + ((32 * (s - RCH / 2)) ^ ad.kxp));
+  auto kread = [&](const Addr& ad, int s) {
+    return k_operand<RCH>(ad.kr, ad.kp, ad.kxr, ad.kxp, s);
   };
-  auto vread = [&](const Addr& ad, int i) -> bf16x8 {
-    const int j = i / NDT, dt = i % NDT;
-    const lds_u8* p = ad.v + (((dt & 3) << 6) ^ ad.vx) + (dt >> 2) * 256 + j * 16 * C::VC * 16;
-    const bf16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)p);
-    const bf16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p + 8 * C::VC * 16));
-    return __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
-  };
+  auto vread = [&](const Addr& ad, int i) { return vt_operand<NDT, C::VC>(ad.v, ad.vx, i); };
 
   // ---- state -------------------------------------------------------------------
   // scores to log2 units; kept > 0 so a masked -inf score never meets a zero
@@ -452,18 +445,7 @@ __global__ __launch_bounds__(NT, 1) void prefill_mfma1w_kernel(PrefillArgs a, in
 
   // Before the softmax of tile kb: tiles crossing this wave's diagonal or
   // window edge (or outside its band) get the per-score mask.
-  auto mask = [&](int kb) {
-    const int j0 = kb * BN;
-    if ((j0 + BN - 1 > wlo) || (W > 0 && j0 <= whi - W)) {
-      asm volatile("");
-      const int d0 = pos - j0 - 4 * h;
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const unsigned d = (unsigned)(d0 - (8 * (e / 4) + (e % 4)));  // pos - key
-        sc[e] = (d < wcap) ? sc[e] : -INFINITY;
-      }
-    }
-  };
+  auto mask = [&](int kb) { mask_edge_tile(sc, kb * BN, wlo, whi, W, pos, h, wcap); };
   // After a stream with a softmax: fold it into l and O, hand its P^T on.
   auto settle = [&] {
     l_run = l_run * salpha + ssum;
@@ -538,42 +520,17 @@ __global__ __launch_bounds__(NT, 1) void prefill_mfma1w_kernel(PrefillArgs a, in
                                                      __float_as_uint(l_run), false, false);
     l_run = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
   }
-  constexpr int ORB = DV * 2;     // bytes per staged row
-  constexpr int VCM = C::VC - 1;  // chunks per row - 1 (a power of two)
   __attribute__((address_space(3))) unsigned char* ost =
-      (__attribute__((address_space(3))) unsigned char*)lds + wave * (RW * ORB);
-  {
-    const float inv = valid ? 1.f / l_run : 0.f;
-    // O^T element e of dim tile dt: dim 32dt + 8(e/4) + 4h + (e%4), i.e. half
-    // h of 16-byte chunk 4dt + e/4 of row r32; chunks XOR-swizzled by the row.
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const uint32_t w0 = pack_bf16x2(oacc[dt][4 * jj] * inv, oacc[dt][4 * jj + 1] * inv);
-        const uint32_t w1 = pack_bf16x2(oacc[dt][4 * jj + 2] * inv, oacc[dt][4 * jj + 3] * inv);
-        const int c = 4 * dt + jj;
-        *(__attribute__((address_space(3))) u32x2*)(ost + r32 * ORB + ((c ^ (r32 & VCM)) << 4) +
-                                                    8 * h) = u32x2{w0, w1};
-      }
-  }
+      (__attribute__((address_space(3))) unsigned char*)lds + wave * (RW * DV * 2);
+  stage_o<NDT>(ost, oacc, valid ? 1.f / l_run : 0.f, r32, h);
   const int64_t o_tok = a.o_tok ? a.o_tok : (int64_t)a.Hq * DV;
   const int64_t o_head = a.o_head ? a.o_head : DV;
-  // A wave reads back only what it wrote; its LDS operations run in order.
-  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-  {
-    constexpr int RPI = 64 / C::VC;  // rows per store instruction
-    const int c = lane % C::VC;
-#pragma unroll
-    for (int i = 0; i < RW / RPI; ++i) {
-      const int row = i * RPI + lane / C::VC;
-      const u32x4 val = *(const __attribute__((address_space(3))) u32x4*)(
-          ost + row * ORB + ((c ^ (row & VCM)) << 4));
-      const int p = wlo + row % C::PPW;
-      const int hd = kvh * G + hg * C::HW + row / C::PPW;
-      if (p < T) *(u32x4*)((uint16_t*)a.o + ((int64_t)b * T + p) * o_tok + hd * o_head + 8 * c) = val;
-    }
-  }
+  // row r of a wave: head group hg's head r / PPW at position wlo + r % PPW
+  store_o<DV, RW>(ost, lane, [&](int row) -> uint16_t* {
+    const int p = wlo + row % C::PPW;
+    const int hd = kvh * G + hg * C::HW + row / C::PPW;
+    return p < T ? (uint16_t*)a.o + ((int64_t)b * T + p) * o_tok + hd * o_head : nullptr;
+  });
 }
 
 template <int DK, int DV, int G, int RCH>

@@ -238,17 +238,10 @@ __global__ __launch_bounds__((Cfg2<DK, DV, G, RCH>::NT), 2) void prefill_mfma2g_
     asm volatile("" : "+v"(ad.kxr), "+v"(ad.kxp), "+v"(ad.vx));
     return ad;
   };
-  auto kread = [&](const Addr& ad, int s) -> bf16x8 {
-    if (s < RCH / 2) return *(const lds_bf16x8*)(ad.kr + ((32 * s) ^ ad.kxr));
-    return *(const lds_bf16x8*)(ad.kp + ((32 * (s - RCH / 2)) ^ ad.kxp));
+  auto kread = [&](const Addr& ad, int s) {
+    return k_operand<RCH>(ad.kr, ad.kp, ad.kxr, ad.kxp, s);
   };
-  auto vread = [&](const Addr& ad, int i) -> bf16x8 {
-    const int j = i / NDT, dt = i % NDT;
-    const lds_u8* p = ad.v + (((dt & 3) << 6) ^ ad.vx) + (dt >> 2) * 256 + j * 16 * C::VC * 16;
-    const bf16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)p);
-    const bf16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p + 8 * C::VC * 16));
-    return __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
-  };
+  auto vread = [&](const Addr& ad, int i) { return vt_operand<NDT, C::VC>(ad.v, ad.vx, i); };
 
   f32x16 sc = f32x16{};
   bf16x8 pop[2];
@@ -278,15 +271,7 @@ __global__ __launch_bounds__((Cfg2<DK, DV, G, RCH>::NT), 2) void prefill_mfma2g_
 
   auto softmax = [&](int kb) {
     const int j0 = kb * BN;
-    if ((j0 + BN - 1 > wlo) || (W > 0 && j0 <= whi - W)) {
-      asm volatile("");
-      const int d0 = pos - j0 - 4 * h;
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const unsigned d = (unsigned)(d0 - (8 * (e / 4) + (e % 4)));
-        sc[e] = (d < wcap) ? sc[e] : -INFINITY;
-      }
-    }
+    mask_edge_tile(sc, j0, wlo, whi, W, pos, h, wcap);
     float sv[16];
 #pragma unroll
     for (int e = 0; e < 16; ++e) sv[e] = sc[e];
@@ -359,36 +344,13 @@ __global__ __launch_bounds__((Cfg2<DK, DV, G, RCH>::NT), 2) void prefill_mfma2g_
                                                      __float_as_uint(l_run), false, false);
     l_run = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
   }
-  constexpr int ORB = DV * 2;
-  constexpr int VCM = C::VC - 1;
   __attribute__((address_space(3))) unsigned char* ost =
-      (__attribute__((address_space(3))) unsigned char*)lds + wave * (RW * ORB);
-  {
-    const float inv = valid ? 1.f / l_run : 0.f;
-#pragma unroll
-    for (int dt = 0; dt < DV / 32; ++dt)
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const uint32_t w0 = pack_bf16x2(oacc[dt][4 * jj] * inv, oacc[dt][4 * jj + 1] * inv);
-        const uint32_t w1 = pack_bf16x2(oacc[dt][4 * jj + 2] * inv, oacc[dt][4 * jj + 3] * inv);
-        const int c = 4 * dt + jj;
-        *(__attribute__((address_space(3))) u32x2*)(ost + r32 * ORB + ((c ^ (r32 & VCM)) << 4) +
-                                                    8 * h) = u32x2{w0, w1};
-      }
-  }
-  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-  {
-    constexpr int RPI = 64 / C::VC;
-    const int c = lane % C::VC;
-#pragma unroll
-    for (int i = 0; i < RW / RPI; ++i) {
-      const int row = i * RPI + lane / C::VC;
-      const u32x4 val =
-          *(const __attribute__((address_space(3))) u32x4*)(ost + row * ORB + ((c ^ (row & VCM)) << 4));
-      const int p = wlo + row;
-      if (p < T) *(u32x4*)((uint16_t*)a.o + (((int64_t)b * T + p) * a.Hq + head) * DV + 8 * c) = val;
-    }
-  }
+      (__attribute__((address_space(3))) unsigned char*)lds + wave * (RW * DV * 2);
+  stage_o<DV / 32>(ost, oacc, valid ? 1.f / l_run : 0.f, r32, h);
+  store_o<DV, RW>(ost, lane, [&](int row) -> uint16_t* {
+    const int p = wlo + row;
+    return p < T ? (uint16_t*)a.o + (((int64_t)b * T + p) * a.Hq + head) * DV : nullptr;
+  });
 }
 
 template <int DK, int DV, int G, int RCH>
