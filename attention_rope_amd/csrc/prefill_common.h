@@ -108,6 +108,32 @@ __device__ __forceinline__ void rotate_q_chunks(u32x4* qw, const lds_float2* slo
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 }
 
+// Per-lane DMA offsets. Block m of a tile region (64 lanes x 16 bytes) moves
+// chunks 64m .. 64m + 63 of the region, row by row; each returns the byte
+// offset of this lane's chunk inside the tile's first row (HBM side), where
+// the chunk that lands at LDS chunk index c of row r is stored chunk
+// swizzle(r, c). A tile then adds j0 times the region's row stride.
+// K's turned region: rows of RCH chunks (the workspace rows, stride rrow).
+template <int RCH>
+__device__ __forceinline__ uint32_t k_rot_dma_off(int m, int lane, int rrow) {
+  constexpr int W = RCH > 0 ? RCH : 1;  // unused when RCH == 0
+  const int q = m * 64 + lane, r = q / W;
+  return r * rrow + kswz<W>(r, q % W) * 16;
+}
+// K's plain region: rows of NP chunks starting at chunk RCH of k's rows.
+template <int RCH, int NP>
+__device__ __forceinline__ uint32_t k_plain_dma_off(int m, int lane, int krow) {
+  constexpr int W = NP > 0 ? NP : 1;
+  const int q = m * 64 + lane, r = q / W;
+  return r * krow + (RCH + kswz<W>(r, q % W)) * 16;
+}
+// V rows of VC chunks.
+template <int VC>
+__device__ __forceinline__ uint32_t v_dma_off(int m, int lane, int vrow) {
+  const int q = m * 64 + lane, r = q / VC;
+  return r * vrow + vswz(r, q % VC) * 16;
+}
+
 // K operand of QK step s for key row r32 of a tile: dims 16s + 8h .. +7, the
 // rotated region's chunk 2s + h while s < RCH / 2, else the plain region's;
 // stored at chunk (2s + h) ^ mask, i.e. byte (32 s) ^ kx of the region row.

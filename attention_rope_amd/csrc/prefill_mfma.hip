@@ -168,18 +168,12 @@ __global__ __launch_bounds__((Cfg<DK, DV, G, RCH>::NT), 1) void prefill_mfma_ker
 #pragma unroll
   for (int i = 0; i < C::DMA_W; ++i) {
     const int n = i * NW + wave;
-    if (n < C::KR_DMA) {
-      constexpr int RCHd = RCH > 0 ? RCH : 1;  // branch is dead when RCH == 0
-      const int q = n * 64 + lane, r = q / RCHd;
-      dma_off[i] = r * rrow + kswz<RCHd>(r, q % RCHd) * 16;
-    } else if (n < C::KR_DMA + C::KP_DMA) {
-      constexpr int NPd = C::NP > 0 ? C::NP : 1;
-      const int q = (n - C::KR_DMA) * 64 + lane, r = q / NPd;
-      dma_off[i] = r * krow + (RCH + kswz<NPd>(r, q % NPd)) * 16;
-    } else {
-      const int q = (n - C::KR_DMA - C::KP_DMA) * 64 + lane, r = q / C::VC;
-      dma_off[i] = r * vrow + vswz(r, q % C::VC) * 16;
-    }
+    if (n < C::KR_DMA)
+      dma_off[i] = k_rot_dma_off<RCH>(n, lane, rrow);
+    else if (n < C::KR_DMA + C::KP_DMA)
+      dma_off[i] = k_plain_dma_off<RCH, C::NP>(n - C::KR_DMA, lane, krow);
+    else
+      dma_off[i] = v_dma_off<C::VC>(n - C::KR_DMA - C::KP_DMA, lane, vrow);
   }
   // Tiles past the range are issued too (one vmcnt value then covers every
   // step), but at an offset past the descriptors' end: they return zeros

@@ -117,21 +117,11 @@ __global__ __launch_bounds__((Cfg2<DK, DV, G, RCH>::NT), 2) void prefill_mfma2g_
 #pragma unroll
   for (int i = 0; i < C::KW; ++i) {
     const int n = i * NW + wave;
-    if (n < C::KR_DMA) {
-      constexpr int RCHd = RCH > 0 ? RCH : 1;
-      const int q = n * 64 + lane, r = q / RCHd;
-      koff[i] = r * rrow + kswz<RCHd>(r, q % RCHd) * 16;
-    } else {
-      constexpr int NPd = C::NP > 0 ? C::NP : 1;
-      const int q = (n - C::KR_DMA) * 64 + lane, r = q / NPd;
-      koff[i] = r * krow + (RCH + kswz<NPd>(r, q % NPd)) * 16;
-    }
+    koff[i] = n < C::KR_DMA ? k_rot_dma_off<RCH>(n, lane, rrow)
+                            : k_plain_dma_off<RCH, C::NP>(n - C::KR_DMA, lane, krow);
   }
 #pragma unroll
-  for (int i = 0; i < C::VW; ++i) {
-    const int q = (i * NW + wave) * 64 + lane, r = q / C::VC;
-    voff[i] = r * vrow + vswz(r, q % C::VC) * 16;
-  }
+  for (int i = 0; i < C::VW; ++i) voff[i] = v_dma_off<C::VC>(i * NW + wave, lane, vrow);
   auto dma_k = [&](int kb, int stage) {
     const int j0 = kb * BN;
     const uint32_t st = lds_addr(lds) + stage * C::KT_BYTES;
