@@ -7,12 +7,14 @@
 // sections 3a-3c): query i of a local layer sees keys i-W+1..i, of a global
 // layer keys 0..i; query head h reads KV head h / (Hq/Hkv).
 //
-// One wavefront per (batch, query head, query row). Lane l owns dimension
+// One workgroup of 4 waves per (batch, query head, query row); wave w takes
+// key blocks w, w + 4, ... and the four softmax states are merged at the end
+// (four shorter dependent chains instead of one). Lane l owns dimension
 // pairs l, l+64, ... of q/k and of v/o, so RoPE pairs stay inside a lane. The
 // query's angles are formed in fp64 here; K's rotary pairs arrive turned by
 // the pre-pass (k_rot).
-// Keys stream in order, 8 at a time, with an online softmax (running max and
-// sum in fp32).
+// Each wave streams its keys 8 at a time with an online softmax (running max
+// and sum in fp32).
 #include "attn_common.h"
 #include "kernels.h"
 
@@ -35,10 +37,12 @@ __device__ __forceinline__ float2 load_pair(const void* base, int64_t elem) {
 // NE: dimension pairs per lane (ceil(max(Dk, Dv) / 128)). Lanes whose pair
 // is past the head read pair 0 and weigh it by 0 (a select, not a branch), so
 // every load of a key block goes out before the first is waited on.
+constexpr int kWaves = 4;  // waves per query row: each takes every 4th key block
+
 template <bool BF16, int NE>
-__global__ __launch_bounds__(256) void prefill_general_kernel(PrefillArgs a) {
-  const int lane = threadIdx.x & 63;
-  const int64_t row_id = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+__global__ __launch_bounds__(kWaves * 64) void prefill_general_kernel(PrefillArgs a) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t row_id = blockIdx.x;
   const int64_t n_rows = (int64_t)a.B * a.T * a.Hq;
   if (row_id >= n_rows) return;
   const int h = (int)(row_id % a.Hq);
@@ -78,7 +82,7 @@ __global__ __launch_bounds__(256) void prefill_general_kernel(PrefillArgs a) {
   // slower).
   constexpr int KB = 8;
   const int lo = (a.window > 0) ? max(0, i - a.window + 1) : 0;
-  for (int j0 = lo; j0 <= i; j0 += KB) {
+  for (int j0 = lo + KB * wave; j0 <= i; j0 += KB * kWaves) {
     float s[KB];
 #pragma unroll
     for (int u = 0; u < KB; ++u) {
@@ -171,6 +175,37 @@ __global__ __launch_bounds__(256) void prefill_general_kernel(PrefillArgs a) {
     }
   }
 
+  // The waves' online-softmax states (m, l, acc) merged by log-sum-exp: each
+  // is rescaled to the largest m (a wave that saw no key has m = -inf and
+  // weighs 0; wave 0 always sees key lo).
+  __shared__ float s_m[kWaves], s_l[kWaves];
+  __shared__ float2 s_acc[kWaves][NE * 64];
+#pragma unroll
+  for (int e = 0; e < NE; ++e) s_acc[wave][e * 64 + lane] = acc[e];
+  if (lane == 0) {
+    s_m[wave] = m;
+    s_l[wave] = l;
+  }
+  __syncthreads();
+  if (wave != 0) return;
+  float mm = s_m[0];
+#pragma unroll
+  for (int w = 1; w < kWaves; ++w) mm = fmaxf(mm, s_m[w]);
+  l = 0.f;
+#pragma unroll
+  for (int e = 0; e < NE; ++e) acc[e] = make_float2(0.f, 0.f);
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    const float f = s_m[w] == -INFINITY ? 0.f : __expf(s_m[w] - mm);
+    l += s_l[w] * f;
+#pragma unroll
+    for (int e = 0; e < NE; ++e) {
+      const float2 x = s_acc[w][e * 64 + lane];
+      acc[e].x += x.x * f;
+      acc[e].y += x.y * f;
+    }
+  }
+
   const float inv = 1.f / l;
   const int64_t obase = (((int64_t)b * a.T + i) * a.Hq + h) * a.Dv;
 #pragma unroll
@@ -189,14 +224,13 @@ __global__ __launch_bounds__(256) void prefill_general_kernel(PrefillArgs a) {
 }  // namespace
 
 hipError_t launch_prefill_general(const PrefillArgs& a, bool bf16, hipStream_t st) {
-  const int64_t rows = (int64_t)a.B * a.T * a.Hq;
-  const int64_t blocks = (rows + 3) / 4;
+  const int64_t blocks = (int64_t)a.B * a.T * a.Hq;  // one query row each
   if (blocks == 0) return hipSuccess;
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
   const int ne = ((a.Dk > a.Dv ? a.Dk : a.Dv) / 2 + 63) / 64;
   if (ne < 1 || ne > kMaxPairs) return hipErrorInvalidValue;
   auto go = [&](auto kern) {
-    hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(256), 0, st, a);
+    hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(kWaves * 64), 0, st, a);
   };
   if (bf16) {
     if (ne == 1) go(prefill_general_kernel<true, 1>);
