@@ -12,10 +12,12 @@
 
 namespace attn {
 
-// Pair (x0, x1) turned by the angle with cosine c and sine s, in fp32. Every
-// kernel here that turns K goes through this and turn_chunk, so a key turned
-// by any of them has the same bits.
+// Pair (x0, x1) turned by the angle with cosine c and sine s, in fp32, each
+// product rounded before the sum (no fused multiply-add, whose use the
+// compiler would otherwise choose per kernel). Every kernel here that turns a
+// vector goes through this, so a key turned by any of them has the same bits.
 __device__ __forceinline__ float2 turn_pair(float x0, float x1, float c, float s) {
+#pragma clang fp contract(off)
   return make_float2(x0 * c - x1 * s, x0 * s + x1 * c);
 }
 
@@ -72,12 +74,11 @@ __global__ void prope_kernel(const T_* __restrict__ x, T_* __restrict__ y,
         x0 = reinterpret_cast<const float*>(x)[off];
         x1 = reinterpret_cast<const float*>(x)[off + 1];
       }
-      const float y0 = x0 * c - x1 * s;
-      const float y1 = x0 * s + x1 * c;
+      const float2 r = turn_pair(x0, x1, c, s);
       if constexpr (sizeof(T_) == 2) {
-        reinterpret_cast<uint32_t*>(y)[off / 2] = pack_bf16x2(y0, y1);
+        reinterpret_cast<uint32_t*>(y)[off / 2] = pack_bf16x2(r.x, r.y);
       } else {
-        reinterpret_cast<float2*>(y)[off / 2] = make_float2(y0, y1);
+        reinterpret_cast<float2*>(y)[off / 2] = r;
       }
     }
   } else {

@@ -152,10 +152,14 @@ def test_prefill_into_cache(gpu_lib, shape):
     assert torch.equal(o, o_plain)
 
     pos = np.arange(c.T)
+    pos_d = torch.arange(c.T, dtype=torch.int32, device=DEV)
     used = np.zeros(rows, dtype=bool)
     for b, r0 in enumerate(offsets):
         kr = oracle.rope(k[b].cpu(), pos, c.rotary_dims, c.theta)
         assert_close(kc[r0:r0 + c.T], kr, torch.bfloat16, f"cached keys b={b}")
+        # the same bits as turning the keys with prope_apply
+        kp = gpu_lib.prope(k[b].contiguous(), pos_d, rotary_dims=c.rotary_dims, theta=c.theta)
+        assert torch.equal(kc[r0:r0 + c.T], kp)
         assert torch.equal(vc[r0:r0 + c.T], v[b])
         used[r0:r0 + c.T] = True
     assert torch.isnan(kc[torch.from_numpy(~used).to(DEV)].float()).all()
@@ -168,3 +172,33 @@ def test_prefill_into_cache(gpu_lib, shape):
     torch.cuda.synchronize()
     ref = oracle.prefill(q[:, -1:].cpu(), k.cpu(), v.cpu(), rows=[c.T - 1], **kw)
     assert_close(od, ref[:, 0], torch.bfloat16, "decode after prefill_into_cache")
+
+
+def test_prefill_into_cache_fp32(gpu_lib):
+    """The fp32 form (general attention kernel, 4-element chunks in the K/V
+    pass): cache rows against the oracle's rope at fp32 tolerance, values bit
+    for bit, o equal to attn_prefill's."""
+    c = inputs.PrefillCase(2, 200, 8, 2, 64, 48, window=70, rotary_dims=32, theta=1e4,
+                           dtype=torch.float32, pos0=0)
+    print("prefill_into_cache fp32", flush=True)
+    q, k, v = inputs.prefill_inputs(c, 32, device=DEV)
+    offsets = [250, 5]
+    rows = 500
+    kc = torch.full((rows, c.Hkv, c.Dk), float("nan"), dtype=torch.float32, device=DEV)
+    vc = torch.full((rows, c.Hkv, c.Dv), float("nan"), dtype=torch.float32, device=DEV)
+    off = torch.tensor(offsets, dtype=torch.int64, device=DEV)
+    kw = dict(window=c.window, scale=c.scale, rotary_dims=c.rotary_dims, theta=c.theta,
+              pos0=7)
+    o = gpu_lib.prefill_into_cache(q, k, v, kc, vc, off, **kw)
+    o_plain = gpu_lib.prefill(q, k, v, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o_plain)
+    ref_o = oracle.prefill(q.cpu(), k.cpu(), v.cpu(), **kw)
+    assert_close(o, ref_o, torch.float32, "fp32 prefill_into_cache output")
+    used = np.zeros(rows, dtype=bool)
+    for b, r0 in enumerate(offsets):
+        kr = oracle.rope(k[b].cpu(), np.arange(7, 7 + c.T), c.rotary_dims, c.theta)
+        assert_close(kc[r0:r0 + c.T], kr, torch.float32, f"fp32 cached keys b={b}")
+        assert torch.equal(vc[r0:r0 + c.T], v[b])
+        used[r0:r0 + c.T] = True
+    assert torch.isnan(kc[torch.from_numpy(~used).to(DEV)]).all()
