@@ -278,7 +278,7 @@ def global_layer_roofline(r, traffic_workload):
 # ---------------------------------------------------------------------------
 # Decode
 # ---------------------------------------------------------------------------
-def bench_decode(ar, torch, inputs, cfg, warmup):
+def bench_decode(ar, torch, inputs, cfg, warmup, oracle=None):
     seed = cfg["seed"]
     calls = []
     for name in ("glob", "loc"):
@@ -361,9 +361,40 @@ def bench_decode(ar, torch, inputs, cfg, warmup):
                                              rotary_dims=d.rotary_dims, theta=d.theta,
                                              max_kv_len=g["maxl"], out=o_i8, workspace=ws_i8))
     del kq, vq, flush
+    cpu = cpu_baseline_decode(oracle, calls, cfg["seed"]) if oracle is not None else None
     return dict(g_ms=g_ms, l_ms=l_ms, g_bytes=g["bytes"], l_bytes=calls[1]["bytes"],
                 kv_ms=kv_ms, kv_bytes=kv_bytes, v_ms=v_ms, v_bytes=v_bytes, v_nq=n_q,
-                i8_ms=i8_ms, i8_bytes=i8_bytes)
+                i8_ms=i8_ms, i8_bytes=i8_bytes, cpu=cpu)
+
+
+def cpu_baseline_decode(oracle, calls, seed, n_seq=4):
+    """The oracle's one-token decode over a seeded sample of whole sequences
+    of both calls (their visible cache rows copied to the host); GB/s of the
+    visible rows' bf16 bytes, as the GPU legs count them."""
+    import numpy as np
+    rng = np.random.default_rng(seed)
+    tot_b, tot_s, parts = 0, 0.0, []
+    for cl in calls:
+        d = cl["d"]
+        seqs = sorted(rng.choice(d.n_seq, size=n_seq, replace=False).tolist())
+        off = cl["off"].cpu().tolist()
+        for b in seqs:
+            n = int(cl["kvl_host"][b])
+            row0 = max(0, n - d.window) if d.window > 0 else 0
+            r0 = off[b] + row0
+            kr, vr = cl["kc"][r0:off[b] + n].cpu(), cl["vc"][r0:off[b] + n].cpu()
+            qh = cl["q"][b].cpu()
+            t0 = time.perf_counter()
+            oracle.decode_one(qh, kr, vr, kv_len=n, row0=row0, window=d.window, scale=d.scale,
+                              rotary_dims=d.rotary_dims, theta=d.theta)
+            tot_s += time.perf_counter() - t0
+            tot_b += (n - row0) * d.Hkv * (d.Dk + d.Dv) * 2
+        parts.append(f"{cl['name']}: sequences {seqs}")
+    return {"value": tot_b / tot_s / 1e9, "unit": "GB/s", "cores": oracle.max_threads(),
+            "kind": "oracle",
+            "sample": f"{'; '.join(parts)} (seeded), every visible cache row of each; "
+                      f"fp64 incl. query rotation and KV replication; {tot_b / 1e9:.2f} GB "
+                      f"of bf16 rows in {tot_s:.1f} s"}
 
 
 # ---------------------------------------------------------------------------
@@ -400,16 +431,42 @@ def cpu_baseline_stack(oracle, cfg, r, target_s):
     rate = tot_fl / tot_s
     return {"value": rate / 1e12, "unit": "TFLOP/s", "cores": oracle.max_threads(),
             "kind": "oracle",
-            "sample": (f"{rows_done} of {rows_all} query rows over the 7 layers "
+            "sample": (f"{rows_done} of {rows_all} query rows over the {len(r['layers'])} layers "
                        f"(~{n_rand} seeded random rows per layer plus first/last/window-edge "
                        f"rows), x B={r['layers'][0]['c'].B} x all heads; fp64 incl. K "
                        f"rotation and KV replication per layer; {tot_s:.1f} s for "
-                       f"{tot_fl:.3e} FLOP; the full stack ({r['flops']:.3e} FLOP) "
+                       f"{tot_fl:.3e} FLOP; the whole stack ({r['flops']:.3e} FLOP) "
                        f"would take ~{r['flops'] / rate / 3600:.1f} h at this rate")}
 
 
+def cpu_baseline_prefill(oracle, c, tensors, rows=None, seed=0):
+    """The oracle on one prefill workload: every query row (rows None), or
+    the given rows plus seeded random ones (all batches and heads)."""
+    import numpy as np
+    import torch
+    q, k, v = tensors[:3]
+    if rows is not None:
+        rng = np.random.default_rng(seed)
+        rows = np.array(sorted(set(rows) | set(rng.choice(c.T, size=64, replace=False)
+                                                  .tolist())), dtype=np.int32)
+        q = q[:, torch.as_tensor(rows, dtype=torch.long, device=q.device)]
+    qh, kh, vh = q.cpu(), k.cpu(), v.cpu()
+    t0 = time.perf_counter()
+    oracle.prefill(qh, kh, vh, window=c.window, scale=c.scale, rotary_dims=c.rotary_dims,
+                   theta=c.theta, pos0=c.pos0, rows=rows)
+    dt = time.perf_counter() - t0
+    fl = rows_flops(c, rows if rows is not None else range(c.T))
+    what = (f"all {c.T} query rows" if rows is None else
+            f"{len(rows)} of {c.T} query rows (first/last/tile/window edges plus 64 seeded "
+            f"random rows)")
+    return {"value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.max_threads(),
+            "kind": "oracle",
+            "sample": f"{what} x B={c.B} x Hq={c.Hq}; fp64 incl. rotation and KV "
+                      f"replication; {fl:.3e} FLOP in {dt:.3f} s"}
+
+
 # ---------------------------------------------------------------------------
-def secondary_prefill(ar, torch, inputs, name, sc):
+def secondary_prefill(ar, torch, inputs, name, sc, oracle=None):
     fp32 = not str(sc["case"].dtype).endswith("bfloat16")
     peak = PEAK_FP32_TFLOPS if fp32 else PEAK_BF16_TFLOPS
     warm = 200 if name == "local_prefill" else (3 if name == "global_prefill" else 50)
@@ -431,6 +488,10 @@ def secondary_prefill(ar, torch, inputs, name, sc):
     if not fp32:
         rec["roofline"]["hbm_frac_at_algorithmic_bytes"] = round(
             rr["bytes"] / (rr["kern"]["median"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)
+    if oracle is not None:
+        # whole workload where it takes seconds; a row subset for the 32k-token one
+        edges = None if rr["flops"] < 1e12 else [0, 1, 2, 31, 32, 63, 64, c.T - 2, c.T - 1]
+        rec["cpu_baseline"] = cpu_baseline_prefill(oracle, c, rr["tensors"], edges, sc["seed"])
     del rr
     torch.cuda.empty_cache()
     if name == "global_prefill":
@@ -443,8 +504,8 @@ def secondary_prefill(ar, torch, inputs, name, sc):
     return rec
 
 
-def secondary_decode(ar, torch, inputs, sc):
-    rr = bench_decode(ar, torch, inputs, sc, 1)
+def secondary_decode(ar, torch, inputs, sc, oracle=None):
+    rr = bench_decode(ar, torch, inputs, sc, 1, oracle)
     g = rr["g_bytes"] / (rr["g_ms"] * 1e-3) / 1e9
     l = rr["l_bytes"] / (rr["l_ms"] * 1e-3) / 1e9
     step_ms = rr["g_ms"] + rr["l_ms"]
@@ -477,16 +538,19 @@ def secondary_decode(ar, torch, inputs, sc):
                                    ("decode_i8", "int8_global_decode")),
             "roofline": roofline("hbm", g, PEAK_HBM_GBS, "GB/s",
                                  _traffic("decode_ring", "global_decode")),
-            "timing": "median of 10 calls (local: 40), 1 GiB MALL-evicting write before each"}
+            "timing": "median of 10 calls (local: 40), 1 GiB MALL-evicting write before each",
+            **({"cpu_baseline": rr["cpu"]} if rr.get("cpu") else {})}
 
 
-def secondary_stack(ar, torch, inputs, name, sc):
+def secondary_stack(ar, torch, inputs, name, sc, oracle=None):
     rr = bench_stack(ar, torch, inputs, sc, 10, 2)
     tf = rr["flops"] / rr["step"]["median"] / 1e9
     rec = {"workload": sc["name"], "unit": "TFLOP/s", "value": round(tf, 3),
            "ms_per_step": round(rr["step"]["median"], 4), "timed_steps": 10,
            "layers": stack_record(sc, rr),
            "roofline": global_layer_roofline(rr, name)}
+    if oracle is not None:
+        rec["cpu_baseline"] = cpu_baseline_stack(oracle, sc, rr, 5.0)
     del rr
     return rec
 
@@ -576,6 +640,9 @@ def main():
     torch.cuda.empty_cache()
 
     secondary = {}
+    orc = None
+    if not args.no_cpu_baseline:
+        import oracle as orc
     for s in [x.strip() for x in args.secondary.split(",") if x.strip()]:
         if s == args.workload:
             continue
@@ -583,11 +650,11 @@ def main():
             raise SystemExit(f"--secondary: unknown workload {s!r}")
         sc = inputs.WORKLOADS[s]
         if sc["kind"] == "prefill":
-            secondary[s] = secondary_prefill(ar, torch, inputs, s, sc)
+            secondary[s] = secondary_prefill(ar, torch, inputs, s, sc, orc)
         elif sc["kind"] == "decode":
-            secondary[s] = secondary_decode(ar, torch, inputs, sc)
+            secondary[s] = secondary_decode(ar, torch, inputs, sc, orc)
         else:
-            secondary[s] = secondary_stack(ar, torch, inputs, s, sc)
+            secondary[s] = secondary_stack(ar, torch, inputs, s, sc, orc)
         torch.cuda.synchronize()
         torch.cuda.empty_cache()
         progress(f"{s} done")
