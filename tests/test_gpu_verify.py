@@ -202,3 +202,28 @@ def test_prefill_into_cache_fp32(gpu_lib):
         assert torch.equal(vc[r0:r0 + c.T], v[b])
         used[r0:r0 + c.T] = True
     assert torch.isnan(kc[torch.from_numpy(~used).to(DEV)]).all()
+
+
+def test_prefill_into_cache_out_of_range_rows_skipped(gpu_lib):
+    """A batch row whose cache rows would leave [0, cache_rows) is not written
+    to the cache (negative offset, or past the end); the others are, and o is
+    attn_prefill's for every batch row."""
+    c = inputs.PrefillCase(3, 96, window=0, dtype=torch.bfloat16, **inputs.SMALL_GLOBAL)
+    print("prefill_into_cache out-of-range rows", flush=True)
+    q, k, v = inputs.prefill_inputs(c, 33, device=DEV)
+    rows = 300
+    offsets = [-5, 100, rows - c.T + 1]
+    kc = torch.full((rows, c.Hkv, c.Dk), float("nan"), dtype=torch.bfloat16, device=DEV)
+    vc = torch.full((rows, c.Hkv, c.Dv), float("nan"), dtype=torch.bfloat16, device=DEV)
+    off = torch.tensor(offsets, dtype=torch.int64, device=DEV)
+    kw = dict(window=0, scale=c.scale, rotary_dims=c.rotary_dims, theta=c.theta)
+    o = gpu_lib.prefill_into_cache(q, k, v, kc, vc, off, **kw)
+    o_plain = gpu_lib.prefill(q, k, v, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o_plain)
+    assert torch.equal(vc[100:100 + c.T], v[1])
+    written = torch.zeros(rows, dtype=torch.bool, device=DEV)
+    written[100:100 + c.T] = True
+    assert not torch.isnan(kc[written].float()).any()
+    assert torch.isnan(kc[~written].float()).all()
+    assert torch.isnan(vc[~written].float()).all()
