@@ -511,10 +511,10 @@ hipError_t launch_prefill_mfma(const PrefillArgs& a, hipStream_t st) {
   if (!prefill_mfma_supported(a.Dk, a.Dv, a.Hq / a.Hkv, a.scale, rdims))
     return hipErrorNotSupported;
   if (a.rope_k && rdims > 0 && !a.k_rot) return hipErrorInvalidValue;
-  // 32-bit buffer offsets: one batch's K or V, and the cos/sin table, < 2 GiB.
+  // 32-bit buffer offsets: one batch's K, V (or turned K dims, at most Dk
+  // wide) must stay under 2 GiB.
   const int64_t per_b = (int64_t)a.T * a.Hkv * (a.Dk > a.Dv ? a.Dk : a.Dv) * 2;
-  if (per_b >= (int64_t)1 << 31 || (int64_t)a.T * a.rot_pairs * 8 >= (int64_t)1 << 31)
-    return hipErrorNotSupported;
+  if (per_b >= (int64_t)1 << 31) return hipErrorNotSupported;
   if (a.Dk == 512 && a.Dv == 256) return launch_prefill_mfma1w(a, st);
   if (a.Dk == 512 && a.Dv == 512) {
     // 512-dim values (a K = V layer, or separate ones) as two passes over
