@@ -273,6 +273,9 @@ attn_status_t prefill_call(const char* what, const void* q, const void* k, const
   a.pos0 = pos0;
   a.log2_theta = rot ? std::log2(rope.theta) : 0.0;
   a.rope_rho = rot ? std::pow(rope.theta, -2.0 / (double)Dk) : 1.0;
+#ifdef ATTN_DEBUG_TILES
+  if (attn::debug_visits_ptr(&a.dbg_visits) != hipSuccess) a.dbg_visits = nullptr;
+#endif
   if (fill) {
     // One pass over K and V: K's rotary dims turn once into the workspace
     // (as below) and whole turned key rows and value rows go to the cache.
@@ -313,6 +316,21 @@ attn_status_t attn_prefill(const void* q, const void* k, const void* v, void* o,
   return prefill_call("prefill", q, k, v, o, B, T, Hq, Hkv, Dk, Dv, window, scale, rope,
                       rope_mask, pos0, workspace, workspace_bytes, dtype, stream, CacheOut{});
 }
+
+#ifdef ATTN_DEBUG_TILES
+// Debug builds only (libattn_rope_dbg.so): the two prefill tile counters
+// (see PrefillArgs::dbg_visits), copied to out[0..1] after the device is idle;
+// reset != 0 zeroes them afterwards.
+extern "C" attn_status_t attn_debug_tile_visits(uint64_t* out, int32_t reset) {
+  unsigned long long* p = nullptr;
+  hipError_t e = attn::debug_visits_ptr(&p);
+  if (e == hipSuccess) e = hipDeviceSynchronize();
+  if (e == hipSuccess && out) e = hipMemcpy(out, p, 2 * sizeof(uint64_t), hipMemcpyDeviceToHost);
+  if (e == hipSuccess && reset) e = hipMemset(p, 0, 2 * sizeof(uint64_t));
+  if (e == hipSuccess) e = hipDeviceSynchronize();
+  return launch_status(e, "debug tile counters");
+}
+#endif
 
 attn_status_t attn_prefill_into_cache(const void* q, const void* k, const void* v, void* o,
                                       int32_t B, int32_t T, int32_t Hq, int32_t Hkv,

@@ -46,7 +46,15 @@ struct PrefillArgs {
   int pos0 = 0;
   double log2_theta = 0.0;
   double rope_rho = 1.0;
+  // Debug builds (ATTN_DEBUG_TILES) only: [0] += the (wave, key tile) pairs
+  // whose scores a wave computes and softmaxes, [1] += the key tiles each
+  // workgroup stages. Release kernels never read it.
+  unsigned long long* dbg_visits = nullptr;
 };
+#ifdef ATTN_DEBUG_TILES
+// Device address of the debug builds' two tile counters (prefill_general.hip).
+hipError_t debug_visits_ptr(unsigned long long** p);
+#endif
 
 // MFMA flash kernel (bf16). Returns hipErrorNotSupported for shapes it has no
 // instantiation for; the caller then uses the general kernel. When K turns,

@@ -223,6 +223,14 @@ __global__ __launch_bounds__(kWaves * 64) void prefill_general_kernel(PrefillArg
 
 }  // namespace
 
+#ifdef ATTN_DEBUG_TILES
+static __device__ unsigned long long g_dbg_visits[2];
+
+hipError_t debug_visits_ptr(unsigned long long** p) {
+  return hipGetSymbolAddress(reinterpret_cast<void**>(p), HIP_SYMBOL(g_dbg_visits));
+}
+#endif
+
 hipError_t launch_prefill_general(const PrefillArgs& a, bool bf16, hipStream_t st) {
   const int64_t blocks = (int64_t)a.B * a.T * a.Hq;  // one query row each
   if (blocks == 0) return hipSuccess;

@@ -268,9 +268,12 @@ __global__ __launch_bounds__((Cfg<DK, DV, G, RCH>::NT), 1) void prefill_mfma_ker
     vx = r << 6;
   }
 
+  // A wave computes a tile only if it holds a key one of its rows may see
+  // (a wave whose rows all lie past T, the padding of the last query tile,
+  // computes none).
   auto live = [&](int kb) {
     const int j0 = kb * BN;
-    return j0 <= whi && !(W > 0 && j0 + BN - 1 <= wlo - W);
+    return wlo < T && j0 <= whi && !(W > 0 && j0 + BN - 1 <= wlo - W);
   };
 
   // Operand reads run OD-1 MFMAs ahead of their use, in a ring of OD
@@ -412,9 +415,15 @@ __global__ __launch_bounds__((Cfg<DK, DV, G, RCH>::NT), 1) void prefill_mfma_ker
       lds_barrier();
     }
   }
+#ifdef ATTN_DEBUG_TILES
+  int dbg_live = 0;
+#endif
   for (int t = 0; t < n_tiles; ++t) {
     const int kb = kb_lo + t;
     const bool lv = live(kb), lv_next = t + 1 < n_tiles && live(kb + 1);
+#ifdef ATTN_DEBUG_TILES
+    dbg_live += lv;
+#endif
     // The stage offset goes through readfirstlane so the compiler treats it
     // as an opaque scalar: every LDS read is then base register + immediate,
     // instead of strength-reduced per-read induction registers.
@@ -444,6 +453,12 @@ __global__ __launch_bounds__((Cfg<DK, DV, G, RCH>::NT), 1) void prefill_mfma_ker
     lds_barrier();
   }
   if (n_tiles > 0 && !lag) lds_barrier();
+#ifdef ATTN_DEBUG_TILES
+  if (a.dbg_visits && lane == 0) {
+    atomicAdd(a.dbg_visits, (unsigned long long)dbg_live);
+    if (wave == 0) atomicAdd(a.dbg_visits + 1, (unsigned long long)n_tiles);
+  }
+#endif
   // ---- epilogue: O = O^T / l, bf16, through LDS ------------------------------
   // Once every wave's DMAs have landed and its reads returned, the ring is
   // free: each wave stages its 32 x DV output tile there, then writes whole

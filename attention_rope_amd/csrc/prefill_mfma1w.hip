@@ -502,6 +502,12 @@ __global__ __launch_bounds__(NT, 1) void prefill_mfma1w_kernel(PrefillArgs a, in
     }
   }
 
+#ifdef ATTN_DEBUG_TILES
+  if (a.dbg_visits && lane == 0) {  // every wave computes every staged tile
+    atomicAdd(a.dbg_visits, (unsigned long long)(n_tiles > 0 ? n_tiles : 0));
+    if (wave == 0) atomicAdd(a.dbg_visits + 1, (unsigned long long)(n_tiles > 0 ? n_tiles : 0));
+  }
+#endif
   // ---- epilogue: O = O^T / l, bf16, staged through LDS ---------------------------
   wait_vm<0>();
   lds_barrier();

@@ -204,9 +204,12 @@ __global__ __launch_bounds__((Cfg2<DK, DV, G, RCH>::NT), 2) void prefill_mfma2g_
     vx = r << 6;
   }
 
+  // A wave computes a tile only if it holds a key one of its rows may see
+  // (a wave whose rows all lie past T, the padding of the last query tile,
+  // computes none).
   auto live = [&](int kb) {
     const int j0 = kb * BN;
-    return j0 <= whi && !(W > 0 && j0 + BN - 1 <= wlo - W);
+    return wlo < T && j0 <= whi && !(W > 0 && j0 + BN - 1 <= wlo - W);
   };
 
   constexpr int OD = 4;
@@ -311,9 +314,15 @@ __global__ __launch_bounds__((Cfg2<DK, DV, G, RCH>::NT), 2) void prefill_mfma2g_
     }
     lds_barrier();  // every wave is done with K(0) before K(2) overwrites it
   }
+#ifdef ATTN_DEBUG_TILES
+  int dbg_live = 0;
+#endif
   for (int t = 0; t < n_tiles; ++t) {
     const int kb = kb_lo + t;
     const bool lv = live(kb), lv_next = t + 1 < n_tiles && live(kb + 1);
+#ifdef ATTN_DEBUG_TILES
+    dbg_live += lv;
+#endif
     dma_k(kb + 2, t & 1);
     dma_v(kb + 1, (t + 1) & 1);
     if (lv)
@@ -326,6 +335,12 @@ __global__ __launch_bounds__((Cfg2<DK, DV, G, RCH>::NT), 2) void prefill_mfma2g_
     lds_barrier();
   }
 
+#ifdef ATTN_DEBUG_TILES
+  if (a.dbg_visits && lane == 0) {
+    atomicAdd(a.dbg_visits, (unsigned long long)dbg_live);
+    if (wave == 0) atomicAdd(a.dbg_visits + 1, (unsigned long long)n_tiles);
+  }
+#endif
   // ---- epilogue: O = O^T / l, bf16, through LDS ------------------------------
   wait_vm<0>();
   lds_barrier();
