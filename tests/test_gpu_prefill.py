@@ -77,6 +77,11 @@ GENERAL_CASES = [
     # bf16 shapes the MFMA kernel does not cover run the general kernel
     (1, 70, 6, 2, 96, 64, 9, 32, 1e4, BF),
     (1, 40, 16, 1, 128, 128, 0, 32, 1e6, BF),   # 16 q heads per KV head
+    # 2 and 3 dim pairs per lane, and long rows over the four-wave key split
+    (1, 100, 4, 2, 256, 256, 17, 64, 1e4, F32),
+    (1, 90, 4, 1, 384, 192, 0, 96, 1e6, BF),
+    (1, 1500, 4, 2, 64, 64, 0, 32, 1e4, F32),
+    (2, 1200, 2, 1, 128, 64, 700, 128, 1e4, F32),
 ]
 
 
