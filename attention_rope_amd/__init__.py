@@ -60,7 +60,7 @@ def load(path: str = LIB_PATH):
         return _lib
     if not os.path.exists(path):
         raise RuntimeError(f"{path} is missing: build it with "
-                           "`python -c 'import __graft_entry__ as g; g.build()'`")
+                           "`python -m attention_rope_amd._build`")
     lib = ctypes.CDLL(path)
     vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
     lib.attn_prefill_workspace_bytes.argtypes = [i32, i32, i32, i32, _Rope, i32, ctypes.c_int]

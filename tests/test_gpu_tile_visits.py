@@ -28,7 +28,7 @@ LIB_DBG = os.path.join(os.path.dirname(os.path.abspath(ar.__file__)), "libattn_r
 @pytest.fixture(scope="module")
 def dbg():
     if not os.path.exists(LIB_DBG):
-        pytest.fail(f"{LIB_DBG} is missing: build with __graft_entry__.build()")
+        pytest.fail(f"{LIB_DBG} is missing: build with python -m attention_rope_amd._build")
     L = ctypes.CDLL(LIB_DBG)
     vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
     L.attn_prefill.argtypes = [vp] * 4 + [i32] * 7 + [ctypes.c_float, ar._Rope, i32, i32, vp,
