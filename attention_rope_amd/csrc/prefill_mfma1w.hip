@@ -119,9 +119,30 @@ __global__ __launch_bounds__(NT, 1) void prefill_mfma1w_kernel(PrefillArgs a, in
   const int r32 = lane & 31, h = lane >> 5;  // this lane's row; half of the k range
   const int T = a.T, W = a.window;
   const int n_wg = n_qt * a.Hkv * a.B;
-  const int L = contig ? xcd_contiguous((int)blockIdx.x, n_wg) : (int)blockIdx.x;
-  const int grp = L / n_qt;
-  const int qt = n_qt - 1 - (L % n_qt);  // longest causal tiles first
+  // Block -> (group = (batch, KV head), query tile). Blocks go round-robin
+  // over the 8 XCDs (block i to XCD i % 8, slot i / 8 there). Causal tiles of
+  // one group share their key prefix, so they run on the same XCDs, whose L2
+  // then streams that prefix once: with a multiple of 8 groups each XCD takes
+  // whole groups, with 8 / k groups each group takes k XCDs, which alternate
+  // its tiles (equal work per XCD either way), longest tiles first. Sliding
+  // windows keep neighbouring tiles together instead.
+  int grp, qt;
+  {
+    const int n_grp = n_wg / n_qt, x = (int)blockIdx.x % 8, slot = (int)blockIdx.x / 8;
+    if (!contig && n_grp % 8 == 0) {
+      const int gpx = n_grp / 8;  // groups per XCD
+      grp = x * gpx + slot % gpx;
+      qt = n_qt - 1 - slot / gpx;
+    } else if (!contig && 8 % n_grp == 0 && n_qt % (8 / n_grp) == 0) {
+      const int xpg = 8 / n_grp;  // XCDs per group
+      grp = x / xpg;
+      qt = n_qt - 1 - (slot * xpg + x % xpg);
+    } else {
+      const int L = contig ? xcd_contiguous((int)blockIdx.x, n_wg) : (int)blockIdx.x;
+      grp = L / n_qt;
+      qt = n_qt - 1 - (L % n_qt);  // longest causal tiles first
+    }
+  }
   const int kvh = grp % a.Hkv, b = grp / a.Hkv;
   const int p0 = qt * C::PW;
 
@@ -537,7 +558,7 @@ hipError_t launch_one(const PrefillArgs& a, hipStream_t st) {
   if (n == 0) return hipSuccess;
   if (n > 0x7fffffff) return hipErrorInvalidValue;
   // Sliding-window tiles reuse their neighbours' K/V: keep neighbours on one
-  // XCD. Causal tiles share the prefix of every key stream: interleave.
+  // XCD. Causal tiles are grouped per XCD by (batch, KV head) in the kernel.
   const int contig = (a.window > 0 && a.window < a.T) ? 1 : 0;
   hipLaunchKernelGGL((prefill_mfma1w_kernel<DK, DV, G, RCH>), dim3((unsigned)n), dim3(NT), 0, st,
                      a, n_qt, contig);
