@@ -64,6 +64,11 @@ bool prefill_mfma_supported(int Dk, int Dv, int G, float scale, int rotary_dims)
 // The variant for 512-dim keys (called by launch_prefill_mfma): 32-row
 // waves, one per SIMD, accumulators in AGPRs (prefill_mfma1w.hip).
 hipError_t launch_prefill_mfma1w(const PrefillArgs& a, hipStream_t st);
+// Keys as values (k == v, Dk = Dv = 512, K not turned in the call) in one pass:
+// O^T for 512 value dims in AGPRs, one key tile in LDS serving both products
+// (prefill_kv1w.hip); called by launch_prefill_mfma.
+bool prefill_kv1w_applies(const PrefillArgs& a);
+hipError_t launch_prefill_kv1w(const PrefillArgs& a, hipStream_t st);
 // The local-layer shape (256-dim heads, G = 2) with 4-wave workgroups, two
 // per CU (prefill_mfma2g.hip); called by launch_prefill_mfma.
 hipError_t launch_prefill_mfma2g(const PrefillArgs& a, hipStream_t st);

@@ -532,10 +532,12 @@ hipError_t launch_prefill_mfma(const PrefillArgs& a, hipStream_t st) {
   if (per_b >= (int64_t)1 << 31) return hipErrorNotSupported;
   if (a.Dk == 512 && a.Dv == 256) return launch_prefill_mfma1w(a, st);
   if (a.Dk == 512 && a.Dv == 512) {
-    // 512-dim values (a K = V layer, or separate ones) as two passes over
-    // 256-dim halves of v and o: the O accumulators of 512 dims would not fit
-    // beside the operands. Each pass recomputes Q.K^T (3/2 of the useful
-    // FLOPs in all).
+    // Keys as values (the same rotated keys as k and v): one pass, the key
+    // tile in LDS serving both products.
+    if (prefill_kv1w_applies(a)) return launch_prefill_kv1w(a, st);
+    // Separate 512-dim values as two passes over 256-dim halves of v and o:
+    // a second operand tile beside the 512-dim O accumulators would not fit.
+    // Each pass recomputes Q.K^T (3/2 of the useful FLOPs in all).
     PrefillArgs h = a;
     h.Dv = 256;
     h.v_tok = (int64_t)a.Hkv * 512;

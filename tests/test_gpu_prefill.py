@@ -203,21 +203,33 @@ def test_prefill_errors_raise(gpu_lib):
         gpu_lib.prefill(q, q[:, :, :2], q[:, :, :2])  # non-contiguous views
 
 
-@pytest.mark.parametrize("T,Hq,Hkv,D,W,R,th", [(150, 16, 2, 512, 0, 128, 1e6),
-                                               (300, 16, 8, 256, 100, 256, 1e4)])
-def test_prefill_keys_as_values(gpu_lib, T, Hq, Hkv, D, W, R, th):
+@pytest.mark.parametrize("B,T,Hq,Hkv,D,W,R,th,p0", [
+    (1, 150, 16, 2, 512, 0, 128, 1e6, 0),
+    (1, 300, 16, 8, 256, 100, 256, 1e4, 0),
+    (1, 333, 8, 8, 512, 0, 0, 1e6, 0),        # 512-dim: one query head per KV head, no rotation
+    (1, 517, 8, 4, 512, 130, 512, 1e4, 0),    # 2 heads per KV head, window, every dim turned
+    (2, 260, 16, 4, 512, 0, 128, 1e6, 5000),  # 4 heads per KV head, two sequences, pos0
+    (1, 97, 32, 4, 512, 33, 128, 1e6, 0),     # 8 heads per KV head, short window
+    (1, 700, 32, 4, 512, 0, 128, 1e6, 0),     # 22 key tiles: the tile ring wraps many times
+    (1, 1, 32, 4, 512, 0, 128, 1e6, 0),       # one token
+])
+def test_prefill_keys_as_values(gpu_lib, B, T, Hq, Hkv, D, W, R, th, p0):
     """K = V prefill: keys rotated once by prope_apply serve as keys (with
-    RoPE on q only) and as values; the oracle rotates them itself."""
-    c = inputs.PrefillCase(1, T, Hq, Hkv, D, D, window=W, rotary_dims=R, theta=th, dtype=BF)
+    RoPE on q only) and as values; the oracle rotates them itself. With
+    512-dim heads this is the one-pass kernel whose key tile in LDS feeds
+    both products."""
+    c = inputs.PrefillCase(B, T, Hq, Hkv, D, D, window=W, rotary_dims=R, theta=th, dtype=BF)
     q, k, _ = inputs.prefill_inputs(c, 21, device=DEV)
-    print(f"kv-shared prefill T={T} Hq={Hq} Hkv={Hkv} D={D} W={W}", flush=True)
-    pos = torch.arange(T, dtype=torch.int32, device=DEV)
-    kr = gpu_lib.prope(k[0], pos, rotary_dims=R, theta=th).unsqueeze(0)
-    o = gpu_lib.prefill(q, kr, kr, window=W, scale=c.scale, rotary_dims=R, theta=th,
+    print(f"kv-shared prefill B={B} T={T} Hq={Hq} Hkv={Hkv} D={D} W={W} R={R} pos0={p0}",
+          flush=True)
+    pos = (torch.arange(T, dtype=torch.int32, device=DEV) + p0).repeat(B)
+    kr = gpu_lib.prope(k.reshape(B * T, Hkv, D), pos, rotary_dims=R,
+                       theta=th).reshape(B, T, Hkv, D)
+    o = gpu_lib.prefill(q, kr, kr, window=W, scale=c.scale, rotary_dims=R, theta=th, pos0=p0,
                         rope_mask=gpu_lib.ROPE_Q)
     torch.cuda.synchronize()
     ref = oracle.prefill_kv_shared(q.cpu(), k.cpu(), window=W, scale=c.scale, rotary_dims=R,
-                                   theta=th)
+                                   theta=th, pos0=p0)
     assert_close(o, ref, BF, "prefill K=V")
 
 

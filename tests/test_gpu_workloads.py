@@ -59,6 +59,29 @@ def test_global_prefill_full_size():
     torch.cuda.empty_cache()
 
 
+def test_global_prefill_keys_as_values_full_size():
+    """The global prefill shape as a K = V layer, as the bench times it: keys
+    turned once by prope_apply, passed as both k and v (RoPE on q only), the
+    one-pass kernel over 512-dim values; sampled rows against the oracle."""
+    cfg = inputs.WORKLOADS["global_prefill"]
+    c = cfg["case"]
+    q, k, _ = inputs.prefill_inputs(c, cfg["seed"], device=DEV)
+    pos = torch.arange(c.T, dtype=torch.int32, device=DEV).repeat(c.B)
+    kr = ar.prope(k.reshape(c.B * c.T, c.Hkv, c.Dk), pos, rotary_dims=c.rotary_dims,
+                  theta=c.theta).reshape(c.B, c.T, c.Hkv, c.Dk)
+    o = ar.prefill(q, kr, kr, window=c.window, scale=c.scale, rotary_dims=c.rotary_dims,
+                   theta=c.theta, rope_mask=ar.ROPE_Q)
+    torch.cuda.synchronize()
+    rows = sample_rows(c.T, c.window, 24, cfg["seed"])
+    ref = oracle.prefill_kv_shared(q.cpu()[:, rows], k.cpu(), window=c.window, scale=c.scale,
+                                   rotary_dims=c.rotary_dims, theta=c.theta, rows=rows)
+    got = o[:, torch.as_tensor(rows, device=DEV, dtype=torch.long)]
+    mx, rel = assert_close(got, ref, c.dtype, "global K=V")
+    print(f"global K=V: rows={len(rows)} max_abs={mx:.3e} rel_rms={rel:.3e}", flush=True)
+    del q, k, kr, o
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("kind", ["glob", "loc", "glob_kv", "glob_verify", "glob_int8"])
 def test_decode_full_size(kind):
     """glob_kv: the global call with keys as values (its key cache passed as
