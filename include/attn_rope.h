@@ -86,7 +86,9 @@ enum { ATTN_ROPE_Q = 1, ATTN_ROPE_K = 2 };
  *   Dk, Dv even and <= 512. bf16 with (Dk, Dv) in {(128,128), (256,256),
  *   (512,256), (512,512)}, Hq/Hkv in {1, 2, 4, 8}, scale >= 0 and
  *   rotary_dims a multiple of 8 in {0, Dk/4, Dk} runs the MFMA flash kernel
- *   ((512,512) as two passes over 256-dim halves of v and o); every other
+ *   ((512,512) in one pass when k == v and K does not turn in the call,
+ *   the keys-as-values form below; with separate values as two passes over
+ *   256-dim halves of v and o); every other
  *   supported case runs a slower general kernel with the same results.
  *   Keys as values (K = V on a global layer): turn k once with prope_apply,
  *   pass it as both k and v with rope_mask = ATTN_ROPE_Q; the values are
