@@ -204,8 +204,9 @@ def bench_prefill_kv_shared(ar, torch, inputs, cfg, warmup):
     ev, _ = timed(torch, call, 10, warmup, 2)
     ms = statistics.median(ev.series(0, 1))
     flops = float(c.B * c.Hq * pairs(c.T, c.window) * 2 * (c.Dk + c.Dk))
+    nbytes = float((q.numel() + kr.numel() + o.numel()) * 2)  # q, keys (as values too), o
     del q, kr, o
-    return dict(flops=flops, ms=ms)
+    return dict(flops=flops, ms=ms, bytes=nbytes)
 
 
 def build_stack(ar, torch, inputs, cfg):
@@ -496,11 +497,16 @@ def secondary_prefill(ar, torch, inputs, name, sc, oracle=None):
     torch.cuda.empty_cache()
     if name == "global_prefill":
         kv = bench_prefill_kv_shared(ar, torch, inputs, sc, 1)
+        tf_kv = kv["flops"] / kv["ms"] / 1e9
         rec["keys_as_values"] = {
-            "TFLOP/s": round(kv["flops"] / kv["ms"] / 1e9, 3), "ms": round(kv["ms"], 4),
+            "TFLOP/s": round(tf_kv, 3), "ms": round(kv["ms"], 4),
             "what": "same shape as a K = V layer: rotated keys as both k and v, 512-dim "
-                    "values, attention call only (TFLOP/s counts the K = V layer's "
-                    "algorithmic FLOPs)"}
+                    "values, one pass (the call is the kernel: K does not turn in it); "
+                    "TFLOP/s counts the K = V layer's algorithmic FLOPs",
+            "roofline": dict(roofline("mfma", tf_kv, PEAK_BF16_TFLOPS, "TFLOP/s",
+                                      _traffic("prefill_kv1w", "global_prefill_kv")),
+                             kernel="prefill_kv1w_kernel", flops_per_launch=kv["flops"],
+                             algorithmic_bytes=kv["bytes"])}
     return rec
 
 

@@ -56,7 +56,7 @@ def needed(lo, hi, W, T):
 def expected(kernel, c, W):
     """(wave-tile pairs, staged tiles) for one call, from the mask."""
     G = c.Hq // c.Hkv
-    if kernel == "1w":   # 4 waves, 16 positions of all 8 heads; every wave runs every tile
+    if kernel in ("1w", "kv"):  # 4 waves of 32 rows; every wave runs every staged tile
         NW, PW = 4, 128 // G
         per_wave = None
     else:                # 32-row waves: head w % G, positions p0 + 32 (w // G)
@@ -76,23 +76,30 @@ def expected(kernel, c, W):
 CASES = [("2g", inputs.LOCAL, 1000, 512), ("2g", inputs.LOCAL, 333, 31),
          ("2g", inputs.LOCAL, 640, 1), ("2g", inputs.LOCAL, 257, 0),
          ("8w", inputs.SMALL_LOCAL, 700, 512), ("8w", inputs.SMALL_LOCAL, 300, 33),
-         ("1w", inputs.GLOBAL, 500, 0), ("1w", inputs.SMALL_GLOBAL, 300, 100)]
+         ("1w", inputs.GLOBAL, 500, 0), ("1w", inputs.SMALL_GLOBAL, 300, 100),
+         ("kv", inputs.GLOBAL, 400, 0), ("kv", inputs.GLOBAL, 300, 70)]
 
 
 @pytest.mark.parametrize("kernel,shape,T,W", CASES)
 def test_tile_visits_match_the_mask(dbg, kernel, shape, T, W):
+    if kernel == "kv":   # keys as values: the same keys as k and v, RoPE on q only
+        shape = {**shape, "Dv": shape["Dk"]}
     c = inputs.PrefillCase(2, T, window=W, dtype=torch.bfloat16, **shape)
-    print(f"tile visits {kernel} Hq={c.Hq} Hkv={c.Hkv} Dk={c.Dk} T={T} W={W}", flush=True)
+    print(f"tile visits {kernel} Hq={c.Hq} Hkv={c.Hkv} Dk={c.Dk} Dv={c.Dv} T={T} W={W}",
+          flush=True)
     q, k, v = inputs.prefill_inputs(c, 41, device=DEV)
+    mask = 3
+    if kernel == "kv":
+        v, mask = k, 1
     o = torch.empty((c.B, c.T, c.Hq, c.Dv), dtype=torch.bfloat16, device=DEV)
     rope = ar._Rope(c.rotary_dims, c.theta)
-    nws = dbg.attn_prefill_workspace_bytes(c.B, c.T, c.Hkv, c.Dk, rope, 3, ar.ATTN_BF16)
+    nws = dbg.attn_prefill_workspace_bytes(c.B, c.T, c.Hkv, c.Dk, rope, mask, ar.ATTN_BF16)
     ws = torch.empty(max(nws, 16), dtype=torch.uint8, device=DEV)
     got = (ctypes.c_uint64 * 2)()
     assert dbg.attn_debug_tile_visits(got, 1) == 0          # zero the counters
     st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
     rc = dbg.attn_prefill(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), c.B, c.T,
-                          c.Hq, c.Hkv, c.Dk, c.Dv, W, c.scale, rope, 3, 0, ws.data_ptr(), nws,
+                          c.Hq, c.Hkv, c.Dk, c.Dv, W, c.scale, rope, mask, 0, ws.data_ptr(), nws,
                           ar.ATTN_BF16, st)
     assert rc == 0
     assert dbg.attn_debug_tile_visits(got, 1) == 0
