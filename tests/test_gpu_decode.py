@@ -125,3 +125,37 @@ def test_decode_deterministic(gpu_lib):
     a = run(gpu_lib, 32, 4, 512, 256, 0, 128, 1e6, [4000, 17], seed=9)
     b = run(gpu_lib, 32, 4, 512, 256, 0, 128, 1e6, [4000, 17], seed=9)
     assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("shape", ["global", "local", "kv"])
+def test_decode_running_max_rescales(gpu_lib, shape):
+    """Cached keys whose dim D-2 climbs with the row (0.0005 t) and a query
+    whose dim D-2 is 2048: the scores gain ~2 (log2 units) per 32 rows, so
+    the streaming softmax moves its running max many times inside a chunk,
+    and the chunks of one sequence end with maxima hundreds of units apart
+    for the merge. Lengths up to 9000 rows take 3 chunks on the global
+    shape; the local call sees its last 1024 rows (the rest NaN)."""
+    Hq, Hkv, Dk, Dv, W, R, th = {"global": (32, 4, 512, 256, 0, 128, 1e6),
+                                 "local": (16, 8, 256, 256, 1024, 256, 1e4),
+                                 "kv": (32, 4, 512, 512, 0, 128, 1e6)}[shape]
+    lens = [700, 3000, 5000, 9000]
+    c = inputs.DecodeCase(len(lens), Hq, Hkv, Dk, Dv, window=W, rotary_dims=R, theta=th,
+                          len_lo=1, len_hi=1)
+    q, kc, vc, off, kvl = inputs.decode_inputs(c, 13, device=DEV,
+                                              kv_len=torch.tensor(lens, dtype=torch.int32))
+    q[..., Dk - 2] = 2048.0
+    q[..., Dk - 1] = 0.0
+    for b, n in enumerate(lens):
+        o0, lo = int(off[b]), (max(0, n - W) if W else 0)
+        t = torch.arange(lo, n, device=DEV, dtype=torch.float32)
+        kc[o0 + lo:o0 + n, :, Dk - 2] = (0.0005 * t).to(BF)[:, None]
+        kc[o0 + lo:o0 + n, :, Dk - 1] = 0.0
+    if shape == "kv":
+        vc = kc
+    print(f"decode rescales {shape} lens={lens}", flush=True)
+    o = gpu_lib.decode(q, kc, vc, off.to(DEV), kvl.to(DEV), window=W, scale=c.scale,
+                       rotary_dims=R, theta=th, max_kv_len=max(lens))
+    torch.cuda.synchronize()
+    ref = oracle.decode(q.cpu(), kc.cpu(), vc.cpu(), off, kvl, window=W, scale=c.scale,
+                        rotary_dims=R, theta=th)
+    assert_close(o, ref, BF, f"decode rescales {shape}")
