@@ -122,7 +122,8 @@ def test_prefill_uniform_values(gpu_lib):
 
 
 @pytest.mark.parametrize("shape,W", [("local", 0), ("local", 250), ("global", 0), ("global", 300),
-                                     ("kv", 0), ("kv", 300), ("small_local", 0), ("d128", 0)])
+                                     ("kv", 0), ("kv", 300), ("small_local", 0), ("d128", 0),
+                                     ("general_fp32", 0), ("general_bf16", 200)])
 def test_prefill_running_max_rescales(gpu_lib, shape, W):
     """Scores that climb with the key's position: one dim of q is 128 and the
     same dim of every key is 0.01 j (dim D-2, which p-RoPE leaves unturned
@@ -130,18 +131,22 @@ def test_prefill_running_max_rescales(gpu_lib, shape, W):
     2.6-5 (log2 units) per 32-key tile, so the online softmax must move its
     running max, and rescale O, two or more times inside each long row, not only
     at the first tile as with N(0,1) inputs. Every MFMA kernel, causal and
-    windowed; "kv" passes the turned keys as values too."""
+    windowed; "kv" passes the turned keys as values too. The general kernel
+    (fp32, and a bf16 head size the MFMA kernels do not take) as well."""
     Hq, Hkv, D, Dv, R, th = {"local": (16, 8, 256, 256, 256, 1e4),
                              "global": (32, 4, 512, 256, 128, 1e6),
                              "kv": (32, 4, 512, 512, 128, 1e6),
                              "small_local": (8, 1, 256, 256, 256, 1e4),
-                             "d128": (8, 1, 128, 128, 128, 1e4)}[shape]
+                             "d128": (8, 1, 128, 128, 128, 1e4),
+                             "general_fp32": (8, 1, 128, 128, 32, 1e6),
+                             "general_bf16": (6, 2, 96, 64, 32, 1e4)}[shape]
     T = 400
-    c = inputs.PrefillCase(1, T, Hq, Hkv, D, Dv, window=W, rotary_dims=R, theta=th, dtype=BF)
+    dt = F32 if shape == "general_fp32" else BF
+    c = inputs.PrefillCase(1, T, Hq, Hkv, D, Dv, window=W, rotary_dims=R, theta=th, dtype=dt)
     q, k, v = inputs.prefill_inputs(c, 5, device=DEV)
     q[..., D - 2] = 128.0
     q[..., D - 1] = 0.0
-    k[..., D - 2] = (0.01 * torch.arange(T, device=DEV, dtype=torch.float32)).to(BF)[None, :, None]
+    k[..., D - 2] = (0.01 * torch.arange(T, device=DEV, dtype=torch.float32)).to(dt)[None, :, None]
     k[..., D - 1] = 0.0
     # the climb over the longest visible range, in log2 units of the scores
     span = (min(W, T) if W else T) - 1
@@ -160,7 +165,7 @@ def test_prefill_running_max_rescales(gpu_lib, shape, W):
         torch.cuda.synchronize()
         ref = oracle.prefill(q.cpu(), k.cpu(), v.cpu(), window=W, scale=c.scale,
                              rotary_dims=R, theta=th)
-    assert_close(o, ref, BF, f"rescales {shape}")
+    assert_close(o, ref, dt, f"rescales {shape}")
 
 
 @pytest.mark.parametrize("Dk,Dv,Hq,Hkv", [(256, 256, 4, 2), (512, 256, 16, 2), (128, 128, 8, 1)])
