@@ -1,11 +1,31 @@
-// prefill_common.h — LDS layout, operand reads, masking, output staging and
-// RoPE helpers shared by the MFMA prefill kernels (prefill_mfma.hip,
-// prefill_mfma2g.hip, prefill_mfma1w.hip).
+// prefill_common.h — LDS layout, operand reads, masking, output staging,
+// RoPE helpers, the one-wave kernels' row map and block mapping, and the
+// sliced online softmax, shared by the MFMA prefill kernels (prefill_mfma.hip,
+// prefill_mfma2g.hip, prefill_mfma1w.hip, prefill_kv1w.hip).
 #pragma once
+#include <type_traits>
+
 #include "attn_common.h"
 
 namespace attn {
 namespace prefill {
+
+// log2(e); and the log2 headroom the online softmax keeps before it moves its
+// running max (and with it rescales O).
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLazy = 8.0f;
+
+template <int N>
+using IC = std::integral_constant<int, N>;
+
+// Calls f(IC<I>{}) for I = 0 .. N-1 at compile time.
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(IC<I>{});
+    static_for<I + 1, N>(f);
+  }
+}
 
 // XOR swizzle of 16-byte chunks inside a region row of `width` chunks. The
 // mask P-1 uses the largest power of two P <= 16 dividing the width, so the
@@ -216,6 +236,142 @@ __device__ __forceinline__ void store_o(const lds_u8* ost, int lane, Dst&& dst) 
     if (d) *(u32x4*)(d + 8 * c) = val;
   }
 }
+
+// Rows of the one-wave kernels (prefill_mfma1w.hip, prefill_kv1w.hip): 4
+// waves, one per SIMD, of 32 (head, position) rows each. Wave w takes head
+// group w % NHG (HW heads) and position block w / NHG (PPW positions); its
+// row r is head r / PPW of the group at position r % PPW of the block. A
+// workgroup covers PW positions of all G query heads of one KV head.
+template <int G>
+struct WaveRows {
+  static constexpr int HW = G >= 8 ? G / 4 : 1;  // heads per wave
+  static constexpr int PPW = 32 / HW;            // positions per wave
+  static constexpr int NHG = G / HW;             // head groups across waves
+  static constexpr int NPB = 4 / NHG;            // position blocks per workgroup
+  static constexpr int PW = NPB * PPW;           // positions per workgroup
+  static_assert(HW * NHG == G && 4 % NHG == 0 && NPB * NHG == 4, "wave -> rows map");
+};
+
+// Block -> (group = (batch, KV head), query tile) of the one-wave kernels.
+// Blocks go round-robin over the 8 XCDs (block i to XCD i % 8, slot i / 8
+// there). Causal tiles of one group share their key prefix, so they run on
+// the same XCDs, whose L2 then streams that prefix once: with a multiple of 8
+// groups each XCD takes whole groups, with 8 / k groups each group takes k
+// XCDs, which alternate its tiles (equal work per XCD either way), longest
+// tiles first. Sliding windows (contig) keep neighbouring tiles on one XCD
+// instead.
+__device__ __forceinline__ void block_tile(int block, int n_wg, int n_qt, int contig, int& grp,
+                                           int& qt) {
+  const int n_grp = n_wg / n_qt, x = block % 8, slot = block / 8;
+  if (!contig && n_grp % 8 == 0) {
+    const int gpx = n_grp / 8;  // groups per XCD
+    grp = x * gpx + slot % gpx;
+    qt = n_qt - 1 - slot / gpx;
+  } else if (!contig && 8 % n_grp == 0 && n_qt % (8 / n_grp) == 0) {
+    const int xpg = 8 / n_grp;  // XCDs per group
+    grp = x / xpg;
+    qt = n_qt - 1 - (slot * xpg + x % xpg);
+  } else {
+    const int L = contig ? xcd_contiguous(block, n_wg) : block;
+    grp = L / n_qt;
+    qt = n_qt - 1 - (L % n_qt);  // longest causal tiles first
+  }
+}
+
+// Online softmax of one 32-key tile of S^T (each lane holds 16 scores of its
+// row, element e for key 8(e/4) + 4h + (e%4); the partner lane l ^ 32 holds
+// the other 16), cut into NSL slices that a kernel spreads between the MFMAs
+// of its stream. The slices form a pipeline: every value a slice needs comes
+// from an earlier slice, so none stalls the wave's in-order issue (and with
+// it the next MFMA) on its own dependency chain.
+//  0-3   partial maxima of 4 scores each
+//  4     max of the partials; 5 the partner lane's half (row max)
+//  6     scaled row max; 7 lazy-rescale vote; 8 new max, rescale factor
+//  9     factor select, max in use
+//  10-27 slice 10+j scales score j, exponentiates score j-1 and adds
+//        probability j-2 to the row sum
+//  28-29 the two bf16 P^T operands
+// The running max moves, and O must be multiplied by alpha, only when a row's
+// tile max exceeds the max in use by more than 2^kLazy (the first tile always
+// does: alpha is then 0). The vote goes through a vector register, so the
+// updates are selects, not a branch that would split the stream.
+struct SliceSoftmax {
+  static constexpr int NSL = 30;
+  // scores to log2 units; kept > 0 so a masked -inf score never meets a zero
+  // factor (scale 0 then acts as 1e-30: every visible key weighs the same)
+  float c2;
+  float m_run = -INFINITY;  // max in use (log2 units)
+  float l_run = 0.f;        // this lane's half of the row sum
+  float alpha = 1.f;        // factor for O and l of the tile just softmaxed
+  bool rescale = false;     // wave-uniform: alpha != 1 for some row
+  float smx[4] = {}, sst = 1.f, ssum = 0.f, muse = 0.f, smc = 0.f, smn = 0.f;
+  int srv = 0;
+
+  __device__ explicit SliceSoftmax(float scale) : c2(fmaxf(scale * kLog2e, 1e-30f)) {}
+
+  // Slice k of the softmax of the scores in s: the scaled scores go to t and
+  // the probabilities to p, either of which may be s itself (in place); slices
+  // 28-29 write the P^T operands to pn. Plain register arrays for t and p are
+  // pinned per element so the pipeline stays in the order the slices give.
+  template <int k, class S, class Tt, class Pp>
+  __device__ __forceinline__ void slice(S& s, Tt& t, Pp& p, bf16x8 (&pn)[2]) {
+    if constexpr (k < 4) {
+      smx[k] = fmaxf(fmaxf(s[4 * k], s[4 * k + 1]), fmaxf(s[4 * k + 2], s[4 * k + 3]));
+      asm volatile("" : "+v"(smx[k]));
+    } else if constexpr (k == 4) {
+      smx[0] = fmaxf(fmaxf(smx[0], smx[1]), fmaxf(smx[2], smx[3]));
+      asm volatile("" : "+v"(smx[0]));
+    } else if constexpr (k == 5) {
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(smx[0]),
+                                                       __float_as_uint(smx[0]), false, false);
+      smx[1] = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+      asm volatile("" : "+v"(smx[1]));
+    } else if constexpr (k == 6) {
+      smc = (smx[1] == -INFINITY) ? -INFINITY : smx[1] * c2;
+      asm volatile("" : "+v"(smc));
+    } else if constexpr (k == 7) {
+      rescale = __any(smc > m_run + kLazy);  // wave-uniform
+      srv = rescale;
+      asm volatile("" : "+v"(srv));
+    } else if constexpr (k == 8) {
+      smn = srv ? fmaxf(m_run, smc) : m_run;
+      sst = fast_exp2(m_run - smn);
+      asm volatile("" : "+v"(smn), "+v"(sst));
+    } else if constexpr (k == 9) {
+      const float keep = (m_run == -INFINITY) ? 0.f : sst;
+      alpha = srv ? keep : 1.f;
+      m_run = smn;
+      muse = (m_run == -INFINITY) ? 0.f : m_run;
+      ssum = 0.f;
+      asm volatile("" : "+v"(alpha), "+v"(muse), "+v"(ssum));
+    } else if constexpr (k < 28) {
+      constexpr int j = k - 10;
+      if constexpr (j < 16) {  // masked scores are -inf: exactly 0 after exp2
+        t[j] = fmaf(s[j], c2, -muse);
+        if constexpr (std::is_array_v<Tt>) asm volatile("" : "+v"(t[j]));
+      }
+      if constexpr (j >= 1 && j <= 16) {
+        p[j - 1] = fast_exp2(t[j - 1]);
+        if constexpr (std::is_array_v<Pp>) asm volatile("" : "+v"(p[j - 1]));
+      }
+      if constexpr (j >= 2) {
+        ssum += p[j - 2];
+        asm volatile("" : "+v"(ssum));
+      }
+    } else {
+      constexpr int jj = k - 28;  // P^T operand of key step jj: elements 8jj .. 8jj+7
+      const f32x4 lo = {p[8 * jj], p[8 * jj + 1], p[8 * jj + 2], p[8 * jj + 3]};
+      const f32x4 hi = {p[8 * jj + 4], p[8 * jj + 5], p[8 * jj + 6], p[8 * jj + 7]};
+      pn[jj] = __builtin_shufflevector(__builtin_convertvector(lo, bf16x4),
+                                       __builtin_convertvector(hi, bf16x4), 0, 1, 2, 3, 4, 5, 6, 7);
+      asm volatile("" : "+v"(pn[jj]));
+    }
+  }
+
+  // After the tile's last slice: fold its probabilities into the row sum (the
+  // caller multiplies O by alpha when `rescale`).
+  __device__ __forceinline__ void fold() { l_run = l_run * alpha + ssum; }
+};
 
 }  // namespace prefill
 }  // namespace attn

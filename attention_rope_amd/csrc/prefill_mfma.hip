@@ -61,8 +61,6 @@
 namespace attn {
 namespace {
 
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kLazy = 8.0f;  // log2 headroom before the running max moves
 constexpr int RW = 32;         // query rows per wave
 constexpr int BN = 32;         // keys per tile
 

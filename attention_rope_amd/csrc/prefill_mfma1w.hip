@@ -48,21 +48,15 @@
 namespace attn {
 namespace {
 
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kLazy = 8.0f;  // log2 headroom before the running max moves
 constexpr int RW = 32;         // query rows per wave
 constexpr int BN = 32;         // keys per tile
 constexpr int NW = 4;          // waves per workgroup (one per SIMD)
 constexpr int NT = NW * 64;
 
 template <int DK, int DV, int G, int RCH>
-struct Cfg1 {
-  static constexpr int HW = G >= 8 ? G / 4 : 1;  // heads per wave
-  static constexpr int PPW = RW / HW;            // positions per wave
-  static constexpr int NHG = G / HW;             // head groups across waves
-  static constexpr int NPB = NW / NHG;           // position blocks per workgroup
-  static constexpr int PW = NPB * PPW;           // positions per workgroup
-  static_assert(HW * NHG == G && NW % NHG == 0 && NPB * NHG == NW, "wave -> rows map");
+struct Cfg1 : prefill::WaveRows<G> {
+  using R = prefill::WaveRows<G>;
+  static_assert(RW == 32 && NW == 4, "the row map is for 4 waves of 32 rows");
   static constexpr int NC = DK / 8;              // 16-byte chunks per K row
   static constexpr int NP = NC - RCH;            // plain (unrotated) chunks per K row
   static constexpr int KR_BYTES = BN * RCH * 16;  // K tile: rotated region, then plain
@@ -90,18 +84,6 @@ struct Cfg1 {
 
 using namespace prefill;
 
-template <int N>
-using IC = std::integral_constant<int, N>;
-
-// Calls f(IC<I>{}) for I = 0 .. N-1 at compile time.
-template <int I, int N, typename F>
-__device__ __forceinline__ void static_for(F&& f) {
-  if constexpr (I < N) {
-    f(IC<I>{});
-    static_for<I + 1, N>(f);
-  }
-}
-
 template <int DK, int DV, int G, int RCH>
 __global__ __launch_bounds__(NT, 1) void prefill_mfma1w_kernel(PrefillArgs a, int n_qt,
                                                                int contig) {
@@ -119,30 +101,8 @@ __global__ __launch_bounds__(NT, 1) void prefill_mfma1w_kernel(PrefillArgs a, in
   const int r32 = lane & 31, h = lane >> 5;  // this lane's row; half of the k range
   const int T = a.T, W = a.window;
   const int n_wg = n_qt * a.Hkv * a.B;
-  // Block -> (group = (batch, KV head), query tile). Blocks go round-robin
-  // over the 8 XCDs (block i to XCD i % 8, slot i / 8 there). Causal tiles of
-  // one group share their key prefix, so they run on the same XCDs, whose L2
-  // then streams that prefix once: with a multiple of 8 groups each XCD takes
-  // whole groups, with 8 / k groups each group takes k XCDs, which alternate
-  // its tiles (equal work per XCD either way), longest tiles first. Sliding
-  // windows keep neighbouring tiles together instead.
   int grp, qt;
-  {
-    const int n_grp = n_wg / n_qt, x = (int)blockIdx.x % 8, slot = (int)blockIdx.x / 8;
-    if (!contig && n_grp % 8 == 0) {
-      const int gpx = n_grp / 8;  // groups per XCD
-      grp = x * gpx + slot % gpx;
-      qt = n_qt - 1 - slot / gpx;
-    } else if (!contig && 8 % n_grp == 0 && n_qt % (8 / n_grp) == 0) {
-      const int xpg = 8 / n_grp;  // XCDs per group
-      grp = x / xpg;
-      qt = n_qt - 1 - (slot * xpg + x % xpg);
-    } else {
-      const int L = contig ? xcd_contiguous((int)blockIdx.x, n_wg) : (int)blockIdx.x;
-      grp = L / n_qt;
-      qt = n_qt - 1 - (L % n_qt);  // longest causal tiles first
-    }
-  }
+  block_tile((int)blockIdx.x, n_wg, n_qt, contig, grp, qt);
   const int kvh = grp % a.Hkv, b = grp / a.Hkv;
   const int p0 = qt * C::PW;
 
@@ -320,91 +280,22 @@ __global__ __launch_bounds__(NT, 1) void prefill_mfma1w_kernel(PrefillArgs a, in
   auto vread = [&](const Addr& ad, int i) { return vt_operand<NDT, C::VC>(ad.v, ad.vx, i); };
 
   // ---- state -------------------------------------------------------------------
-  // scores to log2 units; kept > 0 so a masked -inf score never meets a zero
-  // factor (scale 0 then acts as 1e-30: every visible key weighs the same)
-  const float c2 = fmaxf(a.scale * kLog2e, 1e-30f);
   const unsigned wcap = (W > 0) ? (unsigned)W : 0x80000000u;
-  float m_run = -INFINITY, l_run = 0.f;
   f32x16 oacc[NDT];
 #pragma unroll
   for (int d = 0; d < NDT; ++d) oacc[d] = f32x16{};
   // S^T of the tile whose softmax runs next (sc; element e holds key
   // 8(e/4) + 4h + (e%4)) and of the tile whose QK runs in the current stream
   // (sn). P^T operands of the tile whose P.V is in the stream (pop) and of the
-  // tile whose softmax is in the stream (pn).
+  // tile whose softmax is in the stream (pn). The softmax of sc runs in
+  // SliceSoftmax::NSL slices with its scaled scores in stt and probabilities
+  // in sp.
   f32x16 sc = f32x16{}, sn = f32x16{};
   bf16x8 pop[2] = {bf16x8{}, bf16x8{}}, pn[2];
-  // softmax state of the tile in flight
-  float smx[4], sst[4], ssum = 0.f, salpha = 1.f, muse = 0.f, smc = 0.f, smn = 0.f;
+  SliceSoftmax sm(a.scale);
   float sp[16], stt[16];
-  int srv = 0;
-  bool sresc = false;
-
-  // Softmax of sc in NSL slices, laid out as a pipeline: every value a slice
-  // needs comes from an earlier slice, so no slice stalls the wave's
-  // in-order issue (and with it the next MFMA) on its own dependency chain.
-  //  0-3   partial maxima of 4 scores each
-  //  4     max of the partials; 5 the partner lane's half (row max)
-  //  6     scaled row max; 7 lazy-rescale vote; 8 new max, rescale factor
-  //  9     factor select, max in use
-  //  10-27 probability pipeline: slice 10+j scales score j, exponentiates
-  //        score j-1, adds probability j-2 to the row sum
-  //  28-29 bf16 P^T operands
-  constexpr int NSL = 30;
-  auto sm_slice = [&](auto K_) {
-    constexpr int k = decltype(K_)::value;
-    if constexpr (k < 4) {
-      smx[k] = fmaxf(fmaxf(sc[4 * k], sc[4 * k + 1]), fmaxf(sc[4 * k + 2], sc[4 * k + 3]));
-      asm volatile("" : "+v"(smx[k]));
-    } else if constexpr (k == 4) {
-      smx[0] = fmaxf(fmaxf(smx[0], smx[1]), fmaxf(smx[2], smx[3]));
-      asm volatile("" : "+v"(smx[0]));
-    } else if constexpr (k == 5) {
-      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(smx[0]),
-                                                       __float_as_uint(smx[0]), false, false);
-      smx[1] = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
-      asm volatile("" : "+v"(smx[1]));
-    } else if constexpr (k == 6) {
-      smc = (smx[1] == -INFINITY) ? -INFINITY : smx[1] * c2;
-      asm volatile("" : "+v"(smc));
-    } else if constexpr (k == 7) {
-      sresc = __any(smc > m_run + kLazy);  // wave-uniform
-      // through a vector register, so the updates are selects, not a branch
-      srv = sresc;
-      asm volatile("" : "+v"(srv));
-    } else if constexpr (k == 8) {
-      smn = srv ? fmaxf(m_run, smc) : m_run;
-      sst[0] = fast_exp2(m_run - smn);
-      asm volatile("" : "+v"(smn), "+v"(sst[0]));
-    } else if constexpr (k == 9) {
-      salpha = srv ? ((m_run == -INFINITY) ? 0.f : sst[0]) : 1.f;
-      m_run = smn;
-      muse = (m_run == -INFINITY) ? 0.f : m_run;
-      ssum = 0.f;
-      asm volatile("" : "+v"(salpha), "+v"(muse), "+v"(ssum));
-    } else if constexpr (k < 28) {
-      constexpr int j = k - 10;
-      if constexpr (j < 16) {  // masked scores are -inf: exactly 0 after exp2
-        stt[j] = fmaf(sc[j], c2, -muse);
-        asm volatile("" : "+v"(stt[j]));
-      }
-      if constexpr (j >= 1 && j <= 16) {
-        sp[j - 1] = fast_exp2(stt[j - 1]);
-        asm volatile("" : "+v"(sp[j - 1]));
-      }
-      if constexpr (j >= 2) {
-        ssum += sp[j - 2];
-        asm volatile("" : "+v"(ssum));
-      }
-    } else {
-      constexpr int jj = k - 28;  // P^T operand of key step jj: elements 8jj .. 8jj+7
-      const f32x4 lo = {sp[8 * jj], sp[8 * jj + 1], sp[8 * jj + 2], sp[8 * jj + 3]};
-      const f32x4 hi = {sp[8 * jj + 4], sp[8 * jj + 5], sp[8 * jj + 6], sp[8 * jj + 7]};
-      pn[jj] = __builtin_shufflevector(__builtin_convertvector(lo, bf16x4),
-                                       __builtin_convertvector(hi, bf16x4), 0, 1, 2, 3, 4, 5, 6, 7);
-      asm volatile("" : "+v"(pn[jj]));
-    }
-  };
+  constexpr int NSL = SliceSoftmax::NSL;
+  auto sm_slice = [&](auto K_) { sm.slice<decltype(K_)::value>(sc, stt, sp, pn); };
 
   // One stream: P.V of the tile in pop (V at av) and QK of the next tile (K
   // at ak, into sn), MFMAs interleaved (P.V first for PV_ ops, then QK), with
@@ -459,10 +350,10 @@ __global__ __launch_bounds__(NT, 1) void prefill_mfma1w_kernel(PrefillArgs a, in
   auto mask = [&](int kb) { mask_edge_tile(sc, kb * BN, wlo, whi, W, pos, h, wcap); };
   // After a stream with a softmax: fold it into l and O, hand its P^T on.
   auto settle = [&] {
-    l_run = l_run * salpha + ssum;
-    if (sresc) {
+    sm.fold();
+    if (sm.rescale) {
 #pragma unroll
-      for (int d = 0; d < NDT; ++d) oacc[d] *= salpha;
+      for (int d = 0; d < NDT; ++d) oacc[d] *= sm.alpha;
     }
     pop[0] = pn[0];
     pop[1] = pn[1];
@@ -533,13 +424,13 @@ __global__ __launch_bounds__(NT, 1) void prefill_mfma1w_kernel(PrefillArgs a, in
   wait_vm<0>();
   lds_barrier();
   {
-    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_run),
-                                                     __float_as_uint(l_run), false, false);
-    l_run = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(sm.l_run),
+                                                     __float_as_uint(sm.l_run), false, false);
+    sm.l_run = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
   }
   __attribute__((address_space(3))) unsigned char* ost =
       (__attribute__((address_space(3))) unsigned char*)lds + wave * (RW * DV * 2);
-  stage_o<NDT>(ost, oacc, valid ? 1.f / l_run : 0.f, r32, h);
+  stage_o<NDT>(ost, oacc, valid ? 1.f / sm.l_run : 0.f, r32, h);
   const int64_t o_tok = a.o_tok ? a.o_tok : (int64_t)a.Hq * DV;
   const int64_t o_head = a.o_head ? a.o_head : DV;
   // row r of a wave: head group hg's head r / PPW at position wlo + r % PPW
