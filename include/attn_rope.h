@@ -176,7 +176,11 @@ attn_status_t attn_prefill_into_cache(const void *q, const void *k, const void *
  *     multiply the cached (rotated) keys, and each cache row is read once for
  *     both products.
  *   row_offset: device int64 [B]; kv_len: device int32 [B], 0 <= kv_len[b] <=
- *     max_kv_len. kv_len[b] == 0 gives o[b] = 0.
+ *     max_kv_len. kv_len[b] == 0 gives o[b] = 0. The caches carry no row
+ *     count, and these two arrays live on the device, so the library cannot
+ *     check them against the caches' size: the caller guarantees that every
+ *     row a sequence owns lies inside both caches (a kv_len[b] above
+ *     max_kv_len is caught in-kernel: o[b] becomes NaN and no row is read).
  *   window: <= 0: all rows; otherwise only the last `window` rows
  *     [kv_len - window, kv_len) are read (rows before are never touched, so
  *     they may hold anything).
