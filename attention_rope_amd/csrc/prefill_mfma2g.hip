@@ -315,9 +315,9 @@ __global__ __launch_bounds__((Cfg2<DK, DV, G, RCH>::NT), 2) void prefill_mfma2g_
 #ifdef ATTN_DEBUG_TILES
   int dbg_live = 0;
 #endif
-  for (int t = 0; t < n_tiles; ++t) {
+  for (int t = 0; t + 1 < n_tiles; ++t) {
     const int kb = kb_lo + t;
-    const bool lv = live(kb), lv_next = t + 1 < n_tiles && live(kb + 1);
+    const bool lv = live(kb), lv_next = live(kb + 1);
 #ifdef ATTN_DEBUG_TILES
     dbg_live += lv;
 #endif
@@ -330,6 +330,23 @@ __global__ __launch_bounds__((Cfg2<DK, DV, G, RCH>::NT), 2) void prefill_mfma2g_
     wait_vm<C::KW + C::VW>();
     lds_barrier();
     if (lv || lv_next) mfma_stream(T_{}, T_{}, addr(kst(t + 1), vst(t)), addr(kst(t + 1), vst(t)));
+    lds_barrier();
+  }
+  // The last tile has no next one: no DMAs (every later tile is past the
+  // range), and its matrix phase is P.V alone.
+  if (n_tiles > 0) {
+    const int t = n_tiles - 1, kb = kb_lo + t;
+    const bool lv = live(kb);
+#ifdef ATTN_DEBUG_TILES
+    dbg_live += lv;
+#endif
+    if (lv)
+      softmax(kb);
+    else
+      pop[0] = pop[1] = bf16x8{};
+    wait_vm<0>();
+    lds_barrier();
+    if (lv) mfma_stream(T_{}, F_{}, addr(kst(t + 1), vst(t)), addr(kst(t + 1), vst(t)));
     lds_barrier();
   }
 
