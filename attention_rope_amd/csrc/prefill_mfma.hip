@@ -416,9 +416,9 @@ __global__ __launch_bounds__((Cfg<DK, DV, G, RCH>::NT), 1) void prefill_mfma_ker
 #ifdef ATTN_DEBUG_TILES
   int dbg_live = 0;
 #endif
-  for (int t = 0; t < n_tiles; ++t) {
+  for (int t = 0; t + 1 < n_tiles; ++t) {
     const int kb = kb_lo + t;
-    const bool lv = live(kb), lv_next = t + 1 < n_tiles && live(kb + 1);
+    const bool lv = live(kb), lv_next = live(kb + 1);
 #ifdef ATTN_DEBUG_TILES
     dbg_live += lv;
 #endif
@@ -442,6 +442,33 @@ __global__ __launch_bounds__((Cfg<DK, DV, G, RCH>::NT), 1) void prefill_mfma_ker
     auto issue = [&] { dma_tile(kb + 3, (t + 3) & 3); };
     if (any)
       mfma_stream(T_{}, T_{}, at, an, issue);
+    else
+      issue();
+    if (lag)
+      wait_vm<C::DMA_W>();
+    else
+      wait_vm<2 * C::DMA_W>();
+    lds_barrier();
+  }
+  // The last tile has no next one: its matrix phase is P.V alone (its DMA
+  // issue, all past the range, keeps the waits above uniform).
+  if (n_tiles > 0) {
+    const int t = n_tiles - 1, kb = kb_lo + t;
+    const bool lv = live(kb);
+#ifdef ATTN_DEBUG_TILES
+    dbg_live += lv;
+#endif
+    const Addr at = addr(stage(t)), an = addr(stage(t + 1));
+    if (lv)
+      softmax(kb);
+    else
+      pop[0] = pop[1] = bf16x8{};
+    if (lv) stream_head(T_{}, at, an);
+    wait_vm<C::DMA_W>();
+    lds_barrier();
+    auto issue = [&] { dma_tile(kb + 3, (t + 3) & 3); };
+    if (lv)
+      mfma_stream(T_{}, F_{}, at, an, issue);
     else
       issue();
     if (lag)
