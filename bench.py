@@ -583,7 +583,7 @@ def main():
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(json.dumps({"error": "this build runs on one GPU only: the hot path has no "
+        print(json.dumps({"error": "this library runs on one GPU only: the hot path has no "
                           "multi-GPU mode, so --gpus must be 1"}), flush=True)
         sys.exit(2)
 
