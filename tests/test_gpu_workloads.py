@@ -55,7 +55,7 @@ def test_local_prefill_full_size():
 
 
 def test_global_prefill_full_size():
-    prefill_case("global_prefill", 40)
+    prefill_case("global_prefill", 512)
     torch.cuda.empty_cache()
 
 
@@ -72,7 +72,7 @@ def test_global_prefill_keys_as_values_full_size():
     o = ar.prefill(q, kr, kr, window=c.window, scale=c.scale, rotary_dims=c.rotary_dims,
                    theta=c.theta, rope_mask=ar.ROPE_Q)
     torch.cuda.synchronize()
-    rows = sample_rows(c.T, c.window, 24, cfg["seed"])
+    rows = sample_rows(c.T, c.window, 128, cfg["seed"])
     ref = oracle.prefill_kv_shared(q.cpu()[:, rows], k.cpu(), window=c.window, scale=c.scale,
                                    rotary_dims=c.rotary_dims, theta=c.theta, rows=rows)
     got = o[:, torch.as_tensor(rows, device=DEV, dtype=torch.long)]
@@ -204,12 +204,12 @@ def stack_case(name, rows_random):
 
 
 def test_stack_full_size():
-    stack_case("stack", 12)
+    stack_case("stack", 512)
 
 
 def test_small_stack_full_size():
     """The small models' 4:1 stack (window 512, 8 query heads per KV head)."""
-    stack_case("small_stack", 12)
+    stack_case("small_stack", 512)
 
 
 @pytest.mark.parametrize("shape", ["global", "local_w512", "local_w1024", "small_local_w512"])
