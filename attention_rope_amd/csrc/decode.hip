@@ -70,24 +70,26 @@ struct RCfg {
   static_assert(!SHARED || DK == DV, "shared K/V rows have one width");
 };
 
-template <class C, int DK, int DV>
+template <class C, int DK, int DV, int NCG>
 __global__ __launch_bounds__(C::RW * 64, 1) void decode_ring_kernel(DecodeArgs a, int ch, int n_split) {
   constexpr int kRW = C::RW, kRBN = C::RBN;
   __shared__ __attribute__((aligned(1024))) unsigned char lds[C::LDS];
 
   // KV heads vary fastest in the grid, so the workgroups that share a chunk's
   // cache rows run side by side. The MFMA's 16 columns are (token, head)
-  // pairs: column c of group cg is q = 16 cg + c, token q / G, head q % G.
-  const int cg = blockIdx.x / a.Hkv, kvh = blockIdx.x - cg * a.Hkv;
+  // pairs: column c of group cg is q = 16 cg + c, token q / G, head q % G. A
+  // workgroup serves NCG consecutive groups (many new tokens of a verify
+  // call) from the same cache bytes: group NCG cgb + i is its group i.
+  const int cgb = blockIdx.x / a.Hkv, kvh = blockIdx.x - cgb * a.Hkv;
   const int split = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 15, g = lane >> 4;
   const int G = a.Hq / a.Hkv, n_q = a.n_q, ncol = n_q * G;
-  auto col_ok = [&](int c) { return 16 * cg + c < ncol; };
-  auto col_tok = [&](int c) { return (16 * cg + c) / G; };
-  auto col_row = [&](int c) -> int64_t {  // row of q and o: [B, n_q, Hq]
-    const int q = 16 * cg + c, j = q / G;
+  auto col_ok = [&](int i, int c) { return 16 * (NCG * cgb + i) + c < ncol; };
+  auto col_tok = [&](int i, int c) { return (16 * (NCG * cgb + i) + c) / G; };
+  auto col_row = [&](int i, int c) -> int64_t {  // row of q and o: [B, n_q, Hq]
+    const int q = 16 * (NCG * cgb + i) + c, j = q / G;
     return ((int64_t)b * n_q + j) * a.Hq + kvh * G + (q - j * G);
   };
 
@@ -96,10 +98,10 @@ __global__ __launch_bounds__(C::RW * 64, 1) void decode_ring_kernel(DecodeArgs a
     // No rows: o = 0; kv_len past max_kv_len or short of the new tokens:
     // poisoned (NaN). With several chunks the merge writes these rows.
     if (n_split == 1) {
-      for (int idx = tid; idx < 16 * DV; idx += kRW * 64) {
-        const int c = idx / DV;
-        if (col_ok(c))
-          ((uint16_t*)a.o)[col_row(c) * DV + idx % DV] = kv_len == 0 ? 0 : 0x7fc0;
+      for (int idx = tid; idx < NCG * 16 * DV; idx += kRW * 64) {
+        const int i = idx / (16 * DV), c = (idx / DV) % 16;
+        if (col_ok(i, c))
+          ((uint16_t*)a.o)[col_row(i, c) * DV + idx % DV] = kv_len == 0 ? 0 : 0x7fc0;
       }
     }
     return;
@@ -158,17 +160,21 @@ __global__ __launch_bounds__(C::RW * 64, 1) void decode_ring_kernel(DecodeArgs a
   // The angle of each rotary pair is formed once per wave (one pair per lane,
   // fp64) into a small LDS table; every lane then reads the pairs it holds.
   __shared__ float2 cs_tab[kRW][DK / 2];
-  bf16x8 qf[DK / 32];
+  bf16x8 qf[NCG][DK / 32];
   if (a.q_rotated) {
-    const bool hv = col_ok(col);
-    const uint16_t* qrow = (const uint16_t*)a.q + col_row(hv ? col : 0) * DK;
 #pragma unroll
-    for (int s = 0; s < DK / 32; ++s) {
-      u32x4 w = *(const u32x4*)(qrow + 32 * s + 8 * g);
-      if (!hv) w = u32x4{0, 0, 0, 0};
-      qf[s] = __builtin_bit_cast(bf16x8, w);
+    for (int i = 0; i < NCG; ++i) {
+      const bool hv = col_ok(i, col);
+      const uint16_t* qrow = (const uint16_t*)a.q + col_row(i, hv ? col : 0) * DK;
+#pragma unroll
+      for (int s = 0; s < DK / 32; ++s) {
+        u32x4 w = *(const u32x4*)(qrow + 32 * s + 8 * g);
+        if (!hv) w = u32x4{0, 0, 0, 0};
+        qf[i][s] = __builtin_bit_cast(bf16x8, w);
+      }
     }
-  } else {  // one token per sequence (n_q = 1), turned here at kv_len - 1
+  } else {  // one token per sequence (n_q = 1, one group), turned here at kv_len - 1
+    static_assert(NCG == 1 || NCG == 2, "one or two column groups");
     const int qpos = kv_len - 1;
     const double l2t = log2(a.theta);
     for (int p = lane; p < a.rot_pairs; p += 64) {
@@ -179,8 +185,8 @@ __global__ __launch_bounds__(C::RW * 64, 1) void decode_ring_kernel(DecodeArgs a
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    const bool hv = col_ok(col);
-    const uint16_t* qrow = (const uint16_t*)a.q + col_row(hv ? col : 0) * DK;
+    const bool hv = col_ok(0, col);
+    const uint16_t* qrow = (const uint16_t*)a.q + col_row(0, hv ? col : 0) * DK;
 #pragma unroll
     for (int s = 0; s < DK / 32; ++s) {
       const int d0 = 32 * s + 8 * g;
@@ -196,26 +202,39 @@ __global__ __launch_bounds__(C::RW * 64, 1) void decode_ring_kernel(DecodeArgs a
         }
       }
       if (!hv) w = u32x4{0, 0, 0, 0};
-      qf[s] = __builtin_bit_cast(bf16x8, w);
+      qf[0][s] = __builtin_bit_cast(bf16x8, w);
     }
+#pragma unroll
+    for (int i = 1; i < NCG; ++i)
+#pragma unroll
+      for (int s = 0; s < DK / 32; ++s) qf[i][s] = bf16x8{};
   }
   wait_vm<(C::AHEAD - 1) * C::DMA_W>();
   lds_barrier();
 
   // Visible keys of this lane's column, and the tile-uniform bounds inside
   // which no column masks anything.
-  const int col_pos = kv_len - n_q + (col_ok(col) ? col_tok(col) : 0);
-  const int col_lo = (a.window > 0) ? max(0, col_pos + 1 - a.window) : 0;
-  const int col_hi = min(c1, col_pos + 1);
+  int col_lo[NCG], col_hi[NCG];
+#pragma unroll
+  for (int i = 0; i < NCG; ++i) {
+    const int col_pos = kv_len - n_q + (col_ok(i, col) ? col_tok(i, col) : 0);
+    col_lo[i] = (a.window > 0) ? max(0, col_pos + 1 - a.window) : 0;
+    col_hi[i] = min(c1, col_pos + 1);
+  }
   const int mask_lo = (a.window > 0) ? max(0, kv_len - a.window) : 0;
   const int mask_hi = min(c1, kv_len - n_q + 1);
 
   // scores to log2 units; kept > 0 so a masked -inf never meets a zero factor
   const float c2 = fmaxf(a.scale * kLog2e, 1e-30f);
-  float m_run = -INFINITY, l_run = 0.f;  // per head `col`
-  f32x4 oacc[DV / 16];
+  float m_run[NCG], l_run[NCG];  // per column `col` of each group
+  f32x4 oacc[NCG][DV / 16];
 #pragma unroll
-  for (int d = 0; d < DV / 16; ++d) oacc[d] = f32x4{};
+  for (int i = 0; i < NCG; ++i) {
+    m_run[i] = -INFINITY;
+    l_run[i] = 0.f;
+#pragma unroll
+    for (int d = 0; d < DV / 16; ++d) oacc[i][d] = f32x4{};
+  }
 
   // Per-lane LDS offsets. K: row 16*wave + col, chunk 4s + g, swizzled by
   // col: 4(s ^ (col >> 2)) + (g ^ (col & 3)); s = 4A + B gives 4 bases plus
@@ -238,43 +257,58 @@ __global__ __launch_bounds__(C::RW * 64, 1) void decode_ring_kernel(DecodeArgs a
   for (int t = 0; t < n_tiles; ++t) {
     dma_tile(t + C::AHEAD, cur == 0 ? C::AHEAD : cur - 1);
     const lds_u8* st = (const lds_u8*)lds + __builtin_amdgcn_readfirstlane(cur * C::ST);
-    // S^T[16 keys][16 heads]: lane holds keys 4g + i of head col.
-    f32x4 s = f32x4{};
+    // S^T[16 keys][16 heads] of each group: lane holds keys 4g + e of
+    // column col; every K operand read feeds all groups.
+    f32x4 s[NCG];
+#pragma unroll
+    for (int i = 0; i < NCG; ++i) s[i] = f32x4{};
 #pragma unroll
     for (int k = 0; k < DK / 32; ++k) {
       const bf16x8 kv = *(const lds_bf16x8*)(st + ko[k % 4] + (k / 4) * 256);
-      s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, qf[k], s, 0, 0, 0);
+#pragma unroll
+      for (int i = 0; i < NCG; ++i)
+        s[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, qf[i][k], s[i], 0, 0, 0);
     }
     const int key0 = c0 + t * kRBN + 16 * wave + 4 * g;
     // Edge tiles only: the chunk's end, the new tokens' own rows (each sees
     // the rows up to its own) and a window's start (later tokens start later).
     if (c0 + t * kRBN < mask_lo || c0 + (t + 1) * kRBN > mask_hi) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) s[i] = (key0 + i >= col_lo && key0 + i < col_hi) ? s[i] : -INFINITY;
-    }
-    float mx = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
-    mx = xor32_16_max(mx);
-    const float mc = (mx == -INFINITY) ? -INFINITY : mx * c2;
-    if (__any(mc > m_run + 8.f)) {  // move the max only when it grows by 2^8
-      const float m_new = fmaxf(m_run, mc);
-      const float alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
-      l_run *= alpha;
+      for (int i = 0; i < NCG; ++i)
 #pragma unroll
-      for (int d = 0; d < DV / 16; ++d) oacc[d] *= alpha;
-      m_run = m_new;
+        for (int e = 0; e < 4; ++e)
+          s[i][e] = (key0 + e >= col_lo[i] && key0 + e < col_hi[i]) ? s[i][e] : -INFINITY;
     }
-    const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
-    f32x4 p;
+    s16x4 pb[NCG];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(fmaf(s[i], c2, -m_use));
-    l_run += (p[0] + p[1]) + (p[2] + p[3]);
-    const s16x4 pb = __builtin_bit_cast(s16x4, __builtin_convertvector(p, bf16x4));
+    for (int i = 0; i < NCG; ++i) {
+      float mx = fmaxf(fmaxf(s[i][0], s[i][1]), fmaxf(s[i][2], s[i][3]));
+      mx = xor32_16_max(mx);
+      const float mc = (mx == -INFINITY) ? -INFINITY : mx * c2;
+      if (__any(mc > m_run[i] + 8.f)) {  // move the max only when it grows by 2^8
+        const float m_new = fmaxf(m_run[i], mc);
+        const float alpha = (m_run[i] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run[i] - m_new);
+        l_run[i] *= alpha;
+#pragma unroll
+        for (int d = 0; d < DV / 16; ++d) oacc[i][d] *= alpha;
+        m_run[i] = m_new;
+      }
+      const float m_use = (m_run[i] == -INFINITY) ? 0.f : m_run[i];
+      f32x4 p;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) p[e] = __builtin_amdgcn_exp2f(fmaf(s[i][e], c2, -m_use));
+      l_run[i] += (p[0] + p[1]) + (p[2] + p[3]);
+      pb[i] = __builtin_bit_cast(s16x4, __builtin_convertvector(p, bf16x4));
+    }
+    // every V^T operand read feeds all groups
 #pragma unroll
     for (int d = 0; d < DV / 16; ++d) {
       const bf16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
           (lds_bf16x4*)(st + vo[d % 8] + (d / 8) * 256));
-      oacc[d] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, v), pb,
-                                                          oacc[d], 0, 0, 0);
+#pragma unroll
+      for (int i = 0; i < NCG; ++i)
+        oacc[i][d] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, v), pb[i],
+                                                               oacc[i][d], 0, 0, 0);
     }
     wait_vm<(C::AHEAD - 1) * C::DMA_W>();  // tile t+1 landed
     lds_barrier();
@@ -285,61 +319,67 @@ __global__ __launch_bounds__(C::RW * 64, 1) void decode_ring_kernel(DecodeArgs a
 
   // The 4 lanes of a head (col, col+16, col+32, col+48) hold different keys
   // under the same running max: sum their sums.
-  l_run = xor32_16_sum(l_run);
+#pragma unroll
+  for (int i = 0; i < NCG; ++i) l_run[i] = xor32_16_sum(l_run[i]);
 
-  // ---- merge the 2 waves through LDS, write this split's partial ---------
+  // ---- merge the waves through LDS, write this split's partial, group by
+  // group (the groups take turns in the same LDS area) ------------------------
   float* red = reinterpret_cast<float*>(lds);  // [wave][16][DV + 2]
   const int RS = DV + 2;
-  {
-    float* wr = red + (wave * 16 + col) * RS;
-    if (g == 0) {
-      wr[DV] = m_run;
-      wr[DV + 1] = l_run;
-    }
-    // O^T layout: lane holds dims 16d + 4g + i of head col.
-#pragma unroll
-    for (int d = 0; d < DV / 16; ++d)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) wr[16 * d + 4 * g + i] = oacc[d][i];
-  }
-  __syncthreads();
-  if (n_split == 1) {  // one chunk per sequence: normalise and write o here
-    for (int idx = tid; idx < 16 * DV; idx += kRW * 64) {
-      const int h = idx / DV, d = idx % DV;
-      if (!col_ok(h)) continue;
-      float M = -INFINITY;
-#pragma unroll
-      for (int w = 0; w < kRW; ++w) M = fmaxf(M, red[(w * 16 + h) * RS + DV]);
-      float num = 0.f, den = 0.f;
-#pragma unroll
-      for (int w = 0; w < kRW; ++w) {
-        const float f = exp2f(red[(w * 16 + h) * RS + DV] - M);
-        num += f * red[(w * 16 + h) * RS + d];
-        den += f * red[(w * 16 + h) * RS + DV + 1];
-      }
-      ((uint16_t*)a.o)[col_row(h) * DV + d] = f32_to_bf16(num / den);
-    }
-    return;
-  }
   float* part = reinterpret_cast<float*>(a.workspace);
-  for (int idx = tid; idx < 16 * (DV + 2); idx += kRW * 64) {
-    const int h = idx / (DV + 2), d = idx % (DV + 2);
-    if (!col_ok(h)) continue;
-    float M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < kRW; ++w) M = fmaxf(M, red[(w * 16 + h) * RS + DV]);
-    float val = 0.f;
-    if (d == DV) {
-      val = M;
-    } else if (M != -INFINITY) {
+  for (int i = 0; i < NCG; ++i) {
+    if (i > 0) __syncthreads();  // the previous group's reads are done
+    {
+      float* wr = red + (wave * 16 + col) * RS;
+      if (g == 0) {
+        wr[DV] = m_run[i];
+        wr[DV + 1] = l_run[i];
+      }
+      // O^T layout: lane holds dims 16d + 4g + e of column col.
 #pragma unroll
-      for (int w = 0; w < kRW; ++w) {
-        const float f = exp2f(red[(w * 16 + h) * RS + DV] - M);
-        val += f * red[(w * 16 + h) * RS + d];
+      for (int d = 0; d < DV / 16; ++d)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) wr[16 * d + 4 * g + e] = oacc[i][d][e];
+    }
+    __syncthreads();
+    if (n_split == 1) {  // one chunk per sequence: normalise and write o here
+      for (int idx = tid; idx < 16 * DV; idx += kRW * 64) {
+        const int h = idx / DV, d = idx % DV;
+        if (!col_ok(i, h)) continue;
+        float M = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < kRW; ++w) M = fmaxf(M, red[(w * 16 + h) * RS + DV]);
+        float num = 0.f, den = 0.f;
+#pragma unroll
+        for (int w = 0; w < kRW; ++w) {
+          const float f = exp2f(red[(w * 16 + h) * RS + DV] - M);
+          num += f * red[(w * 16 + h) * RS + d];
+          den += f * red[(w * 16 + h) * RS + DV + 1];
+        }
+        ((uint16_t*)a.o)[col_row(i, h) * DV + d] = f32_to_bf16(num / den);
+      }
+    } else {
+      for (int idx = tid; idx < 16 * (DV + 2); idx += kRW * 64) {
+        const int h = idx / (DV + 2), d = idx % (DV + 2);
+        if (!col_ok(i, h)) continue;
+        float M = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < kRW; ++w) M = fmaxf(M, red[(w * 16 + h) * RS + DV]);
+        float val = 0.f;
+        if (d == DV) {
+          val = M;
+        } else if (M != -INFINITY) {
+#pragma unroll
+          for (int w = 0; w < kRW; ++w) {
+            const float f = exp2f(red[(w * 16 + h) * RS + DV] - M);
+            val += f * red[(w * 16 + h) * RS + d];
+          }
+        }
+        const int64_t slot = col_row(i, h) * n_split + split;
+        part[slot * (DV + 2) + d] = val;  // d == DV+1 sums the l's by the same rule
       }
     }
-    const int64_t slot = col_row(h) * n_split + split;
-    part[slot * (DV + 2) + d] = val;  // d == DV+1 sums the l's by the same rule
   }
 }
 
@@ -399,30 +439,42 @@ hipError_t launch_merge_dv(const DecodeArgs& a, const SplitPlan& pl, hipStream_t
   return hipGetLastError();
 }
 
-template <int DK, int DV, bool SHARED>
-hipError_t launch_ring(const DecodeArgs& a, const SplitPlan& pl, int ncg, hipStream_t st) {
+template <int DK, int DV, bool SHARED, int NCG>
+hipError_t launch_ring(const DecodeArgs& a, const SplitPlan& pl, int ncb, hipStream_t st) {
   using C = RingCfg<DK, DV, SHARED>;
   // Chunk-relative 32-bit buffer offsets: ch rows plus the read-ahead tiles.
   const int64_t row = (int64_t)a.Hkv * (DK > DV ? DK : DV) * 2;
   static_assert((C::STAGES + 1) * C::RBN <= 192, "read-ahead bound of decode_shape_fits");
   if (((int64_t)pl.ch + (C::STAGES + 1) * C::RBN) * row >= ((int64_t)1 << 31))
     return hipErrorInvalidValue;
-  hipLaunchKernelGGL((decode_ring_kernel<C, DK, DV>), dim3(a.Hkv * ncg, pl.ns, a.B),
+  hipLaunchKernelGGL((decode_ring_kernel<C, DK, DV, NCG>), dim3(a.Hkv * ncb, pl.ns, a.B),
                      dim3(C::RW * 64), 0, st, a, pl.ch, pl.ns);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || pl.ns == 1) return e;  // one chunk: the ring kernel wrote o
   return launch_merge_dv<DV>(a, pl, st);
 }
 
-template <int DK, int DV>
-hipError_t launch_dk_dv(const DecodeArgs& a, hipStream_t st) {
-  const int ncg = decode_column_groups(a.n_q, a.Hq / a.Hkv);
-  const SplitPlan pl = decode_plan(a.B, a.Hkv * ncg, a.max_kv_len, a.window, a.n_q);
+template <int DK, int DV, int NCG>
+hipError_t launch_dk_dv_g(const DecodeArgs& a, int ncb, hipStream_t st) {
+  const SplitPlan pl = decode_plan(a.B, a.Hkv * ncb, a.max_kv_len, a.window, a.n_q);
   if (pl.ns > 65535) return hipErrorInvalidValue;
   if constexpr (DK == DV) {
-    if (a.k_cache == a.v_cache) return launch_ring<DK, DV, true>(a, pl, ncg, st);
+    if (a.k_cache == a.v_cache) return launch_ring<DK, DV, true, NCG>(a, pl, ncb, st);
   }
-  return launch_ring<DK, DV, false>(a, pl, ncg, st);
+  return launch_ring<DK, DV, false, NCG>(a, pl, ncb, st);
+}
+
+// Column groups per workgroup: two when a verify call has more (token, head)
+// pairs per KV head than one 16-column group holds (each cache row is then
+// read once for both), one otherwise.
+template <int DK, int DV>
+hipError_t launch_dk_dv(const DecodeArgs& a, hipStream_t st) {
+  const int G = a.Hq / a.Hkv;
+  const int ncb = decode_column_blocks(a.n_q, G, a.Dv);
+  if constexpr (DV <= 256) {
+    if (decode_groups_per_block(a.n_q, G, a.Dv) == 2) return launch_dk_dv_g<DK, DV, 2>(a, ncb, st);
+  }
+  return launch_dk_dv_g<DK, DV, 1>(a, ncb, st);
 }
 
 // Several new tokens: turn every query once at its own position

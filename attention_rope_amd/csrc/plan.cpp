@@ -29,6 +29,20 @@ SplitPlan decode_plan(int B, int groups, int max_kv_len, int window, int n_q) {
 // 16-column groups of (token, head) pairs per KV head.
 int decode_column_groups(int n_q, int G) { return (n_q * G + 15) / 16; }
 
+// Column groups one decode workgroup serves from the same cache rows: two
+// when there are several (a verify call with more than 16 (token, head)
+// pairs per KV head) and the values are at most 256 wide (two groups' query
+// and output registers then fit one wave), else one.
+int decode_groups_per_block(int n_q, int G, int Dv) {
+  return (decode_column_groups(n_q, G) >= 2 && Dv <= 256) ? 2 : 1;
+}
+
+// Workgroups per (sequence, chunk, KV head).
+int decode_column_blocks(int n_q, int G, int Dv) {
+  const int n = decode_groups_per_block(n_q, G, Dv);
+  return (decode_column_groups(n_q, G) + n - 1) / n;
+}
+
 // Turned queries of a verify call (n_q > 1) ahead of the partials.
 size_t decode_rotated_q_bytes(int B, int n_q, int Hq, int Dk) {
   if (n_q <= 1) return 0;
@@ -38,19 +52,19 @@ size_t decode_rotated_q_bytes(int B, int n_q, int Hq, int Dk) {
 size_t decode_workspace_bytes(int B, int n_q, int Hq, int Hkv, int Dk, int Dv, int max_kv_len,
                               int window) {
   if (B <= 0 || n_q <= 0 || Hq <= 0 || Hkv <= 0 || Dv <= 0 || max_kv_len <= 0) return 0;
-  const int ncg = decode_column_groups(n_q, Hq / Hkv);
-  const int ns = decode_plan(B, Hkv * ncg, max_kv_len, window, n_q).ns;
+  const int ncb = decode_column_blocks(n_q, Hq / Hkv, Dv);
+  const int ns = decode_plan(B, Hkv * ncb, max_kv_len, window, n_q).ns;
   return decode_rotated_q_bytes(B, n_q, Hq, Dk) + (size_t)B * n_q * Hq * ns * (Dv + 2) * sizeof(float);
 }
 
 bool decode_shape_fits(int B, int n_q, int Hq, int Hkv, int Dk, int Dv, int max_kv_len,
                        int window) {
-  const int ncg = decode_column_groups(n_q, Hq / Hkv);
-  const SplitPlan pl = decode_plan(B, Hkv * ncg, max_kv_len, window, n_q);
+  const int ncb = decode_column_blocks(n_q, Hq / Hkv, Dv);
+  const SplitPlan pl = decode_plan(B, Hkv * ncb, max_kv_len, window, n_q);
   // 32-bit chunk-relative offsets (chunk plus the deepest read-ahead) and the
   // grid's x and y extents.
   const int64_t row = (int64_t)Hkv * (Dk > Dv ? Dk : Dv) * 2;
-  return pl.ns <= 65535 && (int64_t)Hkv * ncg < ((int64_t)1 << 31) &&
+  return pl.ns <= 65535 && (int64_t)Hkv * ncb < ((int64_t)1 << 31) &&
          ((int64_t)pl.ch + 192) * row < ((int64_t)1 << 31);
 }
 

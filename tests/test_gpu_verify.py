@@ -48,6 +48,21 @@ def test_verify_global_two_tokens(gpu_lib):
     run(gpu_lib, 2, 32, 4, 512, 256, 0, 128, 1e6, LENS)
 
 
+@pytest.mark.parametrize("n_q", [3, 4, 5])
+def test_verify_global_column_groups(gpu_lib, n_q):
+    """24, 32 and 40 (token, head) pairs per KV head: two or three 16-column
+    groups, which one workgroup serves two at a time from the same cache rows
+    (with 5 tokens the second workgroup's second group is empty)."""
+    run(gpu_lib, n_q, 32, 4, 512, 256, 0, 128, 1e6, LENS)
+
+
+@pytest.mark.parametrize("W", [1024, 5])
+def test_verify_local_two_column_groups(gpu_lib, W):
+    """9 tokens x 2 heads: 18 pairs per KV head, two groups in one workgroup,
+    each token with its own window start."""
+    run(gpu_lib, 9, 16, 8, 256, 256, W, 256, 1e4, LENS)
+
+
 def test_verify_global_four_tokens_keys_as_values(gpu_lib):
     """32 (token, head) pairs per KV head: two column groups; K = V."""
     run(gpu_lib, 4, 32, 4, 512, 512, 0, 128, 1e6, LENS, shared=True)
