@@ -346,6 +346,21 @@ def bench_decode(ar, torch, inputs, cfg, warmup, oracle=None):
                                        window=d.window, scale=d.scale,
                                        rotary_dims=d.rotary_dims, theta=d.theta,
                                        max_kv_len=g["maxl"], out=o_v, workspace=ws_v))
+    # 4 new tokens: 32 (token, head) pairs per KV head, two 16-column groups,
+    # which one workgroup serves from the same cache rows.
+    n_q4 = 4
+    q_v4 = inputs.normal((d.n_seq, n_q4, d.Hq, d.Dk), seed, 91, d.dtype, "cuda")
+    o_v4 = torch.empty((d.n_seq, n_q4, d.Hq, d.Dv), dtype=d.dtype, device="cuda")
+    ws_v4 = torch.empty(ar.verify_workspace_bytes(d.n_seq, n_q4, d.Hq, d.Hkv, d.Dk, d.Dv,
+                                                  g["maxl"], d.window),
+                        dtype=torch.uint8, device="cuda")
+    v4_bytes = (sum(g["vis"]) * d.Hkv * (d.Dk + d.Dv) * 2
+                + d.n_seq * n_q4 * d.Hq * (d.Dk + d.Dv) * 2)
+    v4_ms = time_call(lambda: ar.verify(q_v4, g["kc"], g["vc"], g["off"], g["kvl"],
+                                        window=d.window, scale=d.scale,
+                                        rotary_dims=d.rotary_dims, theta=d.theta,
+                                        max_kv_len=g["maxl"], out=o_v4, workspace=ws_v4))
+    del q_v4, o_v4, ws_v4
 
     # int8 cache: the global call's caches quantised once (outside the timed
     # region), one scale per (row, KV head); the decode reads codes + scales.
@@ -365,6 +380,7 @@ def bench_decode(ar, torch, inputs, cfg, warmup, oracle=None):
     cpu = cpu_baseline_decode(oracle, calls, cfg["seed"]) if oracle is not None else None
     return dict(g_ms=g_ms, l_ms=l_ms, g_bytes=g["bytes"], l_bytes=calls[1]["bytes"],
                 kv_ms=kv_ms, kv_bytes=kv_bytes, v_ms=v_ms, v_bytes=v_bytes, v_nq=n_q,
+                v4_ms=v4_ms, v4_bytes=v4_bytes, v4_nq=n_q4,
                 i8_ms=i8_ms, i8_bytes=i8_bytes, cpu=cpu)
 
 
@@ -538,6 +554,11 @@ def secondary_decode(ar, torch, inputs, sc, oracle=None):
                                f"global call with {rr['v_nq']} new tokens per sequence "
                                "(speculative-decoding verify)",
                                ("decode_ring", "verify_global_decode")),
+            "verify4_call": leg(rr["v4_ms"], rr["v4_bytes"],
+                                f"global call with {rr['v4_nq']} new tokens per sequence: "
+                                "32 (token, head) pairs per KV head, two column groups "
+                                "served from the same cache rows",
+                                ("decode_ring", "verify4_global_decode")),
             "int8_cache_call": leg(rr["i8_ms"], rr["i8_bytes"],
                                    "global call over int8 codes + fp32 per-row scales "
                                    "(same tokens; bytes counted as read)",
