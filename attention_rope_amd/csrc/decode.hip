@@ -471,9 +471,7 @@ template <int DK, int DV>
 hipError_t launch_dk_dv(const DecodeArgs& a, hipStream_t st) {
   const int G = a.Hq / a.Hkv;
   const int ncb = decode_column_blocks(a.n_q, G, a.Dv);
-  if constexpr (DV <= 256) {
-    if (decode_groups_per_block(a.n_q, G, a.Dv) == 2) return launch_dk_dv_g<DK, DV, 2>(a, ncb, st);
-  }
+  if (decode_groups_per_block(a.n_q, G, a.Dv) == 2) return launch_dk_dv_g<DK, DV, 2>(a, ncb, st);
   return launch_dk_dv_g<DK, DV, 1>(a, ncb, st);
 }
 

@@ -31,10 +31,11 @@ int decode_column_groups(int n_q, int G) { return (n_q * G + 15) / 16; }
 
 // Column groups one decode workgroup serves from the same cache rows: two
 // when there are several (a verify call with more than 16 (token, head)
-// pairs per KV head) and the values are at most 256 wide (two groups' query
-// and output registers then fit one wave), else one.
+// pairs per KV head), else one. (Dv is part of the signature so the choice
+// can follow the value width; every width takes two today.)
 int decode_groups_per_block(int n_q, int G, int Dv) {
-  return (decode_column_groups(n_q, G) >= 2 && Dv <= 256) ? 2 : 1;
+  (void)Dv;
+  return decode_column_groups(n_q, G) >= 2 ? 2 : 1;
 }
 
 // Workgroups per (sequence, chunk, KV head).
