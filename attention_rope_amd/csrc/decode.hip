@@ -470,8 +470,8 @@ hipError_t launch_dk_dv_g(const DecodeArgs& a, int ncb, hipStream_t st) {
 template <int DK, int DV>
 hipError_t launch_dk_dv(const DecodeArgs& a, hipStream_t st) {
   const int G = a.Hq / a.Hkv;
-  const int ncb = decode_column_blocks(a.n_q, G, a.Dv);
-  if (decode_groups_per_block(a.n_q, G, a.Dv) == 2) return launch_dk_dv_g<DK, DV, 2>(a, ncb, st);
+  const int ncb = decode_column_blocks(a.n_q, G);
+  if (decode_groups_per_block(a.n_q, G) == 2) return launch_dk_dv_g<DK, DV, 2>(a, ncb, st);
   return launch_dk_dv_g<DK, DV, 1>(a, ncb, st);
 }
 

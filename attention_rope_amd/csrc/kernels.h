@@ -110,8 +110,8 @@ SplitPlan decode_plan(int B, int groups, int max_kv_len, int window, int n_q = 1
 // 16-column MFMA groups of (token, head) pairs per KV head, and the bytes of
 // the turned queries a verify call keeps ahead of its partials.
 int decode_column_groups(int n_q, int G);
-int decode_groups_per_block(int n_q, int G, int Dv);
-int decode_column_blocks(int n_q, int G, int Dv);
+int decode_groups_per_block(int n_q, int G);
+int decode_column_blocks(int n_q, int G);
 size_t decode_rotated_q_bytes(int B, int n_q, int Hq, int Dk);
 // Merge of the chunk partials into o (any supported Dv).
 hipError_t launch_decode_merge(const DecodeArgs& a, const SplitPlan& pl, hipStream_t st);

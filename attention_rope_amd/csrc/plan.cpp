@@ -31,16 +31,12 @@ int decode_column_groups(int n_q, int G) { return (n_q * G + 15) / 16; }
 
 // Column groups one decode workgroup serves from the same cache rows: two
 // when there are several (a verify call with more than 16 (token, head)
-// pairs per KV head), else one. (Dv is part of the signature so the choice
-// can follow the value width; every width takes two today.)
-int decode_groups_per_block(int n_q, int G, int Dv) {
-  (void)Dv;
-  return decode_column_groups(n_q, G) >= 2 ? 2 : 1;
-}
+// pairs per KV head), else one.
+int decode_groups_per_block(int n_q, int G) { return decode_column_groups(n_q, G) >= 2 ? 2 : 1; }
 
 // Workgroups per (sequence, chunk, KV head).
-int decode_column_blocks(int n_q, int G, int Dv) {
-  const int n = decode_groups_per_block(n_q, G, Dv);
+int decode_column_blocks(int n_q, int G) {
+  const int n = decode_groups_per_block(n_q, G);
   return (decode_column_groups(n_q, G) + n - 1) / n;
 }
 
@@ -53,14 +49,14 @@ size_t decode_rotated_q_bytes(int B, int n_q, int Hq, int Dk) {
 size_t decode_workspace_bytes(int B, int n_q, int Hq, int Hkv, int Dk, int Dv, int max_kv_len,
                               int window) {
   if (B <= 0 || n_q <= 0 || Hq <= 0 || Hkv <= 0 || Dv <= 0 || max_kv_len <= 0) return 0;
-  const int ncb = decode_column_blocks(n_q, Hq / Hkv, Dv);
+  const int ncb = decode_column_blocks(n_q, Hq / Hkv);
   const int ns = decode_plan(B, Hkv * ncb, max_kv_len, window, n_q).ns;
   return decode_rotated_q_bytes(B, n_q, Hq, Dk) + (size_t)B * n_q * Hq * ns * (Dv + 2) * sizeof(float);
 }
 
 bool decode_shape_fits(int B, int n_q, int Hq, int Hkv, int Dk, int Dv, int max_kv_len,
                        int window) {
-  const int ncb = decode_column_blocks(n_q, Hq / Hkv, Dv);
+  const int ncb = decode_column_blocks(n_q, Hq / Hkv);
   const SplitPlan pl = decode_plan(B, Hkv * ncb, max_kv_len, window, n_q);
   // 32-bit chunk-relative offsets (chunk plus the deepest read-ahead) and the
   // grid's x and y extents.
