@@ -46,7 +46,9 @@ constexpr float kLog2e = 1.4426950408889634f;
 // of head col) is exactly what the score MFMA left in the lane, and V^T comes
 // from one transposing LDS read (ds_read_b64_tr_b16) per MFMA.
 // RW waves per workgroup, 16 rows per wave and tile, a STAGES-deep ring
-// filled STAGES - 1 tiles ahead. SHARED: the values are the cached keys
+// filled STAGES - 1 tiles ahead. A verify call with more than 16 (token,
+// head) pairs per KV head adds a second set of RW waves that take the same
+// rows for the next 16 pairs, so the tiles serve both. SHARED: the values are the cached keys
 // (one cache serves as both), so a tile holds K rows only and P.V reads its
 // transposed operand from them.
 template <int DK, int DV, int RW_, int STAGES_, bool SHARED_ = false>
@@ -70,38 +72,47 @@ struct RCfg {
   static_assert(!SHARED || DK == DV, "shared K/V rows have one width");
 };
 
-template <class C, int DK, int DV, int NCG>
-__global__ __launch_bounds__(C::RW * 64, 1) void decode_ring_kernel(DecodeArgs a, int ch, int n_split) {
-  constexpr int kRW = C::RW, kRBN = C::RBN;
+template <class C, int DK, int DV, int NGW>
+__global__ __launch_bounds__(C::RW * NGW * 64, 1) void decode_ring_kernel(DecodeArgs a, int ch, int n_split) {
+  // kRW row waves split each tile's rows; NGW column groups each have their
+  // own kRW waves over the same rows, so a workgroup has kW waves.
+  constexpr int kRW = C::RW, kRBN = C::RBN, kW = kRW * NGW;
+  constexpr int DMA_W = C::N_DMA / kW;  // DMAs per wave per tile
+  static_assert(C::N_DMA % kW == 0 && C::K_DMA % kW == 0, "uniform DMA counts");
+  static_assert((C::AHEAD - 1) * DMA_W < 64, "vmcnt field");
   __shared__ __attribute__((aligned(1024))) unsigned char lds[C::LDS];
 
   // KV heads vary fastest in the grid, so the workgroups that share a chunk's
   // cache rows run side by side. The MFMA's 16 columns are (token, head)
   // pairs: column c of group cg is q = 16 cg + c, token q / G, head q % G. A
-  // workgroup serves NCG consecutive groups (many new tokens of a verify
-  // call) from the same cache bytes: group NCG cgb + i is its group i.
+  // workgroup serves NGW consecutive groups (many new tokens of a verify
+  // call) from the same cache bytes: wave w takes rows 16 (w % kRW) of each
+  // tile for group NGW cgb + w / kRW.
   const int cgb = blockIdx.x / a.Hkv, kvh = blockIdx.x - cgb * a.Hkv;
   const int split = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wr = wave % kRW, wg = wave / kRW;  // row wave, column group
   const int col = lane & 15, g = lane >> 4;
   const int G = a.Hq / a.Hkv, n_q = a.n_q, ncol = n_q * G;
-  auto col_ok = [&](int i, int c) { return 16 * (NCG * cgb + i) + c < ncol; };
-  auto col_tok = [&](int i, int c) { return (16 * (NCG * cgb + i) + c) / G; };
-  auto col_row = [&](int i, int c) -> int64_t {  // row of q and o: [B, n_q, Hq]
-    const int q = 16 * (NCG * cgb + i) + c, j = q / G;
+  auto col_ok_g = [&](int i, int c) { return 16 * (NGW * cgb + i) + c < ncol; };
+  auto col_row_g = [&](int i, int c) -> int64_t {  // row of q and o: [B, n_q, Hq]
+    const int q = 16 * (NGW * cgb + i) + c, j = q / G;
     return ((int64_t)b * n_q + j) * a.Hq + kvh * G + (q - j * G);
   };
+  auto col_ok = [&](int c) { return col_ok_g(wg, c); };
+  auto col_tok = [&](int c) { return (16 * (NGW * cgb + wg) + c) / G; };
+  auto col_row = [&](int c) { return col_row_g(wg, c); };
 
   const int kv_len = a.kv_len[b];
   if (kv_len <= 0 || kv_len > a.max_kv_len || kv_len < n_q) {
     // No rows: o = 0; kv_len past max_kv_len or short of the new tokens:
     // poisoned (NaN). With several chunks the merge writes these rows.
     if (n_split == 1) {
-      for (int idx = tid; idx < NCG * 16 * DV; idx += kRW * 64) {
+      for (int idx = tid; idx < NGW * 16 * DV; idx += kW * 64) {
         const int i = idx / (16 * DV), c = (idx / DV) % 16;
-        if (col_ok(i, c))
-          ((uint16_t*)a.o)[col_row(i, c) * DV + idx % DV] = kv_len == 0 ? 0 : 0x7fc0;
+        if (col_ok_g(i, c))
+          ((uint16_t*)a.o)[col_row_g(i, c) * DV + idx % DV] = kv_len == 0 ? 0 : 0x7fc0;
       }
     }
     return;
@@ -122,12 +133,12 @@ __global__ __launch_bounds__(C::RW * 64, 1) void decode_ring_kernel(DecodeArgs a
                                   (uint32_t)((c1 - 1 - c0) * krow + DK * 2));
   const u32x4 vdesc = buffer_desc((const char*)a.v_cache + (row0 * a.Hkv + kvh) * DV * 2,
                                   (uint32_t)((c1 - 1 - c0) * vrow + DV * 2));
-  // Block n (n = i*kRW + wave) of a tile holds 64 chunks; K rows first, then V
+  // Block n (n = i*kW + wave) of a tile holds 64 chunks; K rows first, then V
   // rows, each row's chunks XOR-swizzled by (row & 15).
-  uint32_t dma_off[C::DMA_W];
+  uint32_t dma_off[DMA_W];
 #pragma unroll
-  for (int i = 0; i < C::DMA_W; ++i) {
-    const int n = i * kRW + wave;
+  for (int i = 0; i < DMA_W; ++i) {
+    const int n = i * kW + wave;
     if (n < C::K_DMA) {
       const int q = n * 64 + lane, r = q / C::KC;
       dma_off[i] = r * krow + ((q % C::KC) ^ (r & 15)) * 16;
@@ -144,9 +155,9 @@ __global__ __launch_bounds__(C::RW * 64, 1) void decode_ring_kernel(DecodeArgs a
     const uint32_t st = lds_addr(lds) + stage * C::ST;
     const uint32_t far = t < n_tiles ? 0u : 0x80000000u;
 #pragma unroll
-    for (int i = 0; i < C::DMA_W; ++i) {
-      const int n = i * kRW + wave;
-      if (i * kRW < C::K_DMA)  // same region for both waves (K_DMA % kRW == 0)
+    for (int i = 0; i < DMA_W; ++i) {
+      const int n = i * kW + wave;
+      if (i * kW < C::K_DMA)  // same region for every wave (K_DMA % kW == 0)
         dma16<true>(kdesc, st + n * 1024, (dma_off[i] + j0 * krow) | far);
       else
         dma16<true>(vdesc, st + n * 1024, (dma_off[i] + j0 * vrow) | far);
@@ -159,22 +170,18 @@ __global__ __launch_bounds__(C::RW * 64, 1) void decode_ring_kernel(DecodeArgs a
   // ---- rotated queries as the B operand: col = head, k = dims -------------
   // The angle of each rotary pair is formed once per wave (one pair per lane,
   // fp64) into a small LDS table; every lane then reads the pairs it holds.
-  __shared__ float2 cs_tab[kRW][DK / 2];
-  bf16x8 qf[NCG][DK / 32];
+  __shared__ float2 cs_tab[kW][DK / 2];
+  bf16x8 qf[DK / 32];
   if (a.q_rotated) {
+    const bool hv = col_ok(col);
+    const uint16_t* qrow = (const uint16_t*)a.q + col_row(hv ? col : 0) * DK;
 #pragma unroll
-    for (int i = 0; i < NCG; ++i) {
-      const bool hv = col_ok(i, col);
-      const uint16_t* qrow = (const uint16_t*)a.q + col_row(i, hv ? col : 0) * DK;
-#pragma unroll
-      for (int s = 0; s < DK / 32; ++s) {
-        u32x4 w = *(const u32x4*)(qrow + 32 * s + 8 * g);
-        if (!hv) w = u32x4{0, 0, 0, 0};
-        qf[i][s] = __builtin_bit_cast(bf16x8, w);
-      }
+    for (int s = 0; s < DK / 32; ++s) {
+      u32x4 w = *(const u32x4*)(qrow + 32 * s + 8 * g);
+      if (!hv) w = u32x4{0, 0, 0, 0};
+      qf[s] = __builtin_bit_cast(bf16x8, w);
     }
-  } else {  // one token per sequence (n_q = 1, one group), turned here at kv_len - 1
-    static_assert(NCG == 1 || NCG == 2, "one or two column groups");
+  } else {  // one token per sequence (n_q = 1), turned here at kv_len - 1
     const int qpos = kv_len - 1;
     const double l2t = log2(a.theta);
     for (int p = lane; p < a.rot_pairs; p += 64) {
@@ -185,8 +192,8 @@ __global__ __launch_bounds__(C::RW * 64, 1) void decode_ring_kernel(DecodeArgs a
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    const bool hv = col_ok(0, col);
-    const uint16_t* qrow = (const uint16_t*)a.q + col_row(0, hv ? col : 0) * DK;
+    const bool hv = col_ok(col);
+    const uint16_t* qrow = (const uint16_t*)a.q + col_row(hv ? col : 0) * DK;
 #pragma unroll
     for (int s = 0; s < DK / 32; ++s) {
       const int d0 = 32 * s + 8 * g;
@@ -202,39 +209,26 @@ __global__ __launch_bounds__(C::RW * 64, 1) void decode_ring_kernel(DecodeArgs a
         }
       }
       if (!hv) w = u32x4{0, 0, 0, 0};
-      qf[0][s] = __builtin_bit_cast(bf16x8, w);
+      qf[s] = __builtin_bit_cast(bf16x8, w);
     }
-#pragma unroll
-    for (int i = 1; i < NCG; ++i)
-#pragma unroll
-      for (int s = 0; s < DK / 32; ++s) qf[i][s] = bf16x8{};
   }
-  wait_vm<(C::AHEAD - 1) * C::DMA_W>();
+  wait_vm<(C::AHEAD - 1) * DMA_W>();
   lds_barrier();
 
   // Visible keys of this lane's column, and the tile-uniform bounds inside
   // which no column masks anything.
-  int col_lo[NCG], col_hi[NCG];
-#pragma unroll
-  for (int i = 0; i < NCG; ++i) {
-    const int col_pos = kv_len - n_q + (col_ok(i, col) ? col_tok(i, col) : 0);
-    col_lo[i] = (a.window > 0) ? max(0, col_pos + 1 - a.window) : 0;
-    col_hi[i] = min(c1, col_pos + 1);
-  }
+  const int col_pos = kv_len - n_q + (col_ok(col) ? col_tok(col) : 0);
+  const int col_lo = (a.window > 0) ? max(0, col_pos + 1 - a.window) : 0;
+  const int col_hi = min(c1, col_pos + 1);
   const int mask_lo = (a.window > 0) ? max(0, kv_len - a.window) : 0;
   const int mask_hi = min(c1, kv_len - n_q + 1);
 
   // scores to log2 units; kept > 0 so a masked -inf never meets a zero factor
   const float c2 = fmaxf(a.scale * kLog2e, 1e-30f);
-  float m_run[NCG], l_run[NCG];  // per column `col` of each group
-  f32x4 oacc[NCG][DV / 16];
+  float m_run = -INFINITY, l_run = 0.f;  // per head `col`
+  f32x4 oacc[DV / 16];
 #pragma unroll
-  for (int i = 0; i < NCG; ++i) {
-    m_run[i] = -INFINITY;
-    l_run[i] = 0.f;
-#pragma unroll
-    for (int d = 0; d < DV / 16; ++d) oacc[i][d] = f32x4{};
-  }
+  for (int d = 0; d < DV / 16; ++d) oacc[d] = f32x4{};
 
   // Per-lane LDS offsets. K: row 16*wave + col, chunk 4s + g, swizzled by
   // col: 4(s ^ (col >> 2)) + (g ^ (col & 3)); s = 4A + B gives 4 bases plus
@@ -243,11 +237,11 @@ __global__ __launch_bounds__(C::RW * 64, 1) void decode_ring_kernel(DecodeArgs a
   // chunk 2(d ^ (x >> 1)) + (((col & 3) >> 1) ^ (x & 1)) gives 8 bases.
   int ko[4], vo[8];
   {
-    const int krow_l = (16 * wave + col) * C::KC * 16 + ((g ^ (col & 3)) << 4);
+    const int krow_l = (16 * wr + col) * C::KC * 16 + ((g ^ (col & 3)) << 4);
 #pragma unroll
     for (int B = 0; B < 4; ++B) ko[B] = krow_l + ((B ^ (col >> 2)) << 6);
     const int x = 4 * g + (col >> 2), c4 = col & 3;
-    const int vrow_l = C::V_OFF + (16 * wave + x) * C::VC * 16 +
+    const int vrow_l = C::V_OFF + (16 * wr + x) * C::VC * 16 +
                        ((((c4 >> 1) ^ (x & 1))) << 4) + ((c4 & 1) << 3);
 #pragma unroll
     for (int B = 0; B < 8; ++B) vo[B] = vrow_l + ((B ^ (x >> 1)) << 5);
@@ -257,60 +251,45 @@ __global__ __launch_bounds__(C::RW * 64, 1) void decode_ring_kernel(DecodeArgs a
   for (int t = 0; t < n_tiles; ++t) {
     dma_tile(t + C::AHEAD, cur == 0 ? C::AHEAD : cur - 1);
     const lds_u8* st = (const lds_u8*)lds + __builtin_amdgcn_readfirstlane(cur * C::ST);
-    // S^T[16 keys][16 heads] of each group: lane holds keys 4g + e of
-    // column col; every K operand read feeds all groups.
-    f32x4 s[NCG];
-#pragma unroll
-    for (int i = 0; i < NCG; ++i) s[i] = f32x4{};
+    // S^T[16 keys][16 heads]: lane holds keys 4g + i of head col.
+    f32x4 s = f32x4{};
 #pragma unroll
     for (int k = 0; k < DK / 32; ++k) {
       const bf16x8 kv = *(const lds_bf16x8*)(st + ko[k % 4] + (k / 4) * 256);
-#pragma unroll
-      for (int i = 0; i < NCG; ++i)
-        s[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, qf[i][k], s[i], 0, 0, 0);
+      s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, qf[k], s, 0, 0, 0);
     }
-    const int key0 = c0 + t * kRBN + 16 * wave + 4 * g;
+    const int key0 = c0 + t * kRBN + 16 * wr + 4 * g;
     // Edge tiles only: the chunk's end, the new tokens' own rows (each sees
     // the rows up to its own) and a window's start (later tokens start later).
     if (c0 + t * kRBN < mask_lo || c0 + (t + 1) * kRBN > mask_hi) {
 #pragma unroll
-      for (int i = 0; i < NCG; ++i)
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          s[i][e] = (key0 + e >= col_lo[i] && key0 + e < col_hi[i]) ? s[i][e] : -INFINITY;
+      for (int i = 0; i < 4; ++i) s[i] = (key0 + i >= col_lo && key0 + i < col_hi) ? s[i] : -INFINITY;
     }
-    s16x4 pb[NCG];
+    float mx = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+    mx = xor32_16_max(mx);
+    const float mc = (mx == -INFINITY) ? -INFINITY : mx * c2;
+    if (__any(mc > m_run + 8.f)) {  // move the max only when it grows by 2^8
+      const float m_new = fmaxf(m_run, mc);
+      const float alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
+      l_run *= alpha;
 #pragma unroll
-    for (int i = 0; i < NCG; ++i) {
-      float mx = fmaxf(fmaxf(s[i][0], s[i][1]), fmaxf(s[i][2], s[i][3]));
-      mx = xor32_16_max(mx);
-      const float mc = (mx == -INFINITY) ? -INFINITY : mx * c2;
-      if (__any(mc > m_run[i] + 8.f)) {  // move the max only when it grows by 2^8
-        const float m_new = fmaxf(m_run[i], mc);
-        const float alpha = (m_run[i] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run[i] - m_new);
-        l_run[i] *= alpha;
-#pragma unroll
-        for (int d = 0; d < DV / 16; ++d) oacc[i][d] *= alpha;
-        m_run[i] = m_new;
-      }
-      const float m_use = (m_run[i] == -INFINITY) ? 0.f : m_run[i];
-      f32x4 p;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) p[e] = __builtin_amdgcn_exp2f(fmaf(s[i][e], c2, -m_use));
-      l_run[i] += (p[0] + p[1]) + (p[2] + p[3]);
-      pb[i] = __builtin_bit_cast(s16x4, __builtin_convertvector(p, bf16x4));
+      for (int d = 0; d < DV / 16; ++d) oacc[d] *= alpha;
+      m_run = m_new;
     }
-    // every V^T operand read feeds all groups
+    const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
+    f32x4 p;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(fmaf(s[i], c2, -m_use));
+    l_run += (p[0] + p[1]) + (p[2] + p[3]);
+    const s16x4 pb = __builtin_bit_cast(s16x4, __builtin_convertvector(p, bf16x4));
 #pragma unroll
     for (int d = 0; d < DV / 16; ++d) {
       const bf16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
           (lds_bf16x4*)(st + vo[d % 8] + (d / 8) * 256));
-#pragma unroll
-      for (int i = 0; i < NCG; ++i)
-        oacc[i][d] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, v), pb[i],
-                                                               oacc[i][d], 0, 0, 0);
+      oacc[d] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, v), pb,
+                                                          oacc[d], 0, 0, 0);
     }
-    wait_vm<(C::AHEAD - 1) * C::DMA_W>();  // tile t+1 landed
+    wait_vm<(C::AHEAD - 1) * DMA_W>();  // tile t+1 landed
     lds_barrier();
     cur = cur == C::AHEAD ? 0 : cur + 1;
   }
@@ -319,34 +298,33 @@ __global__ __launch_bounds__(C::RW * 64, 1) void decode_ring_kernel(DecodeArgs a
 
   // The 4 lanes of a head (col, col+16, col+32, col+48) hold different keys
   // under the same running max: sum their sums.
-#pragma unroll
-  for (int i = 0; i < NCG; ++i) l_run[i] = xor32_16_sum(l_run[i]);
+  l_run = xor32_16_sum(l_run);
 
-  // ---- merge the waves through LDS, write this split's partial, group by
-  // group (the groups take turns in the same LDS area) ------------------------
-  float* red = reinterpret_cast<float*>(lds);  // [wave][16][DV + 2]
+  // ---- merge each group's row waves through LDS, write this split's
+  // partial; the groups take turns in the same LDS area ------------------------
+  float* red = reinterpret_cast<float*>(lds);  // [row wave][16][DV + 2]
   const int RS = DV + 2;
   float* part = reinterpret_cast<float*>(a.workspace);
 #pragma unroll
-  for (int i = 0; i < NCG; ++i) {
-    if (i > 0) __syncthreads();  // the previous group's reads are done
-    {
-      float* wr = red + (wave * 16 + col) * RS;
+  for (int gi = 0; gi < NGW; ++gi) {
+    if (gi > 0) __syncthreads();  // the previous group's reads are done
+    if (wg == gi) {
+      float* wrp = red + (wr * 16 + col) * RS;
       if (g == 0) {
-        wr[DV] = m_run[i];
-        wr[DV + 1] = l_run[i];
+        wrp[DV] = m_run;
+        wrp[DV + 1] = l_run;
       }
-      // O^T layout: lane holds dims 16d + 4g + e of column col.
+      // O^T layout: lane holds dims 16d + 4g + i of head col.
 #pragma unroll
       for (int d = 0; d < DV / 16; ++d)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) wr[16 * d + 4 * g + e] = oacc[i][d][e];
+        for (int i = 0; i < 4; ++i) wrp[16 * d + 4 * g + i] = oacc[d][i];
     }
     __syncthreads();
     if (n_split == 1) {  // one chunk per sequence: normalise and write o here
-      for (int idx = tid; idx < 16 * DV; idx += kRW * 64) {
+      for (int idx = tid; idx < 16 * DV; idx += kW * 64) {
         const int h = idx / DV, d = idx % DV;
-        if (!col_ok(i, h)) continue;
+        if (!col_ok_g(gi, h)) continue;
         float M = -INFINITY;
 #pragma unroll
         for (int w = 0; w < kRW; ++w) M = fmaxf(M, red[(w * 16 + h) * RS + DV]);
@@ -357,12 +335,12 @@ __global__ __launch_bounds__(C::RW * 64, 1) void decode_ring_kernel(DecodeArgs a
           num += f * red[(w * 16 + h) * RS + d];
           den += f * red[(w * 16 + h) * RS + DV + 1];
         }
-        ((uint16_t*)a.o)[col_row(i, h) * DV + d] = f32_to_bf16(num / den);
+        ((uint16_t*)a.o)[col_row_g(gi, h) * DV + d] = f32_to_bf16(num / den);
       }
     } else {
-      for (int idx = tid; idx < 16 * (DV + 2); idx += kRW * 64) {
+      for (int idx = tid; idx < 16 * (DV + 2); idx += kW * 64) {
         const int h = idx / (DV + 2), d = idx % (DV + 2);
-        if (!col_ok(i, h)) continue;
+        if (!col_ok_g(gi, h)) continue;
         float M = -INFINITY;
 #pragma unroll
         for (int w = 0; w < kRW; ++w) M = fmaxf(M, red[(w * 16 + h) * RS + DV]);
@@ -376,7 +354,7 @@ __global__ __launch_bounds__(C::RW * 64, 1) void decode_ring_kernel(DecodeArgs a
             val += f * red[(w * 16 + h) * RS + d];
           }
         }
-        const int64_t slot = col_row(i, h) * n_split + split;
+        const int64_t slot = col_row_g(gi, h) * n_split + split;
         part[slot * (DV + 2) + d] = val;  // d == DV+1 sums the l's by the same rule
       }
     }
@@ -448,7 +426,7 @@ hipError_t launch_ring(const DecodeArgs& a, const SplitPlan& pl, int ncb, hipStr
   if (((int64_t)pl.ch + (C::STAGES + 1) * C::RBN) * row >= ((int64_t)1 << 31))
     return hipErrorInvalidValue;
   hipLaunchKernelGGL((decode_ring_kernel<C, DK, DV, NCG>), dim3(a.Hkv * ncb, pl.ns, a.B),
-                     dim3(C::RW * 64), 0, st, a, pl.ch, pl.ns);
+                     dim3(C::RW * NCG * 64), 0, st, a, pl.ch, pl.ns);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || pl.ns == 1) return e;  // one chunk: the ring kernel wrote o
   return launch_merge_dv<DV>(a, pl, st);
