@@ -47,8 +47,8 @@ constexpr float kLog2e = 1.4426950408889634f;
 // from one transposing LDS read (ds_read_b64_tr_b16) per MFMA.
 // RW waves per workgroup, 16 rows per wave and tile, a STAGES-deep ring
 // filled STAGES - 1 tiles ahead. A verify call with more than 16 (token,
-// head) pairs per KV head adds a second set of RW waves that take the same
-// rows for the next 16 pairs, so the tiles serve both. SHARED: the values are the cached keys
+// head) pairs per KV head adds sets of RW waves (up to 4 sets) that take the
+// same rows for the next 16 pairs each, so the tiles serve all of them. SHARED: the values are the cached keys
 // (one cache serves as both), so a tile holds K rows only and P.V reads its
 // transposed operand from them.
 template <int DK, int DV, int RW_, int STAGES_, bool SHARED_ = false>
@@ -170,7 +170,9 @@ __global__ __launch_bounds__(C::RW * NGW * 64, 1) void decode_ring_kernel(Decode
   // ---- rotated queries as the B operand: col = head, k = dims -------------
   // The angle of each rotary pair is formed once per wave (one pair per lane,
   // fp64) into a small LDS table; every lane then reads the pairs it holds.
-  __shared__ float2 cs_tab[kW][DK / 2];
+  // (one-token calls only, which have one column group: NGW == 1)
+  constexpr int kCS = NGW == 1 ? kW : 1;
+  __shared__ float2 cs_tab[kCS][DK / 2];
   bf16x8 qf[DK / 32];
   if (a.q_rotated) {
     const bool hv = col_ok(col);
@@ -187,7 +189,7 @@ __global__ __launch_bounds__(C::RW * NGW * 64, 1) void decode_ring_kernel(Decode
     for (int p = lane; p < a.rot_pairs; p += 64) {
       float c, sn;
       rope_cos_sin(qpos, rope_freq(p, DK, l2t), &c, &sn);
-      cs_tab[wave][p] = make_float2(c, sn);
+      cs_tab[wave % kCS][p] = make_float2(c, sn);
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
@@ -202,7 +204,7 @@ __global__ __launch_bounds__(C::RW * NGW * 64, 1) void decode_ring_kernel(Decode
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           if (d0 / 2 + e < a.rot_pairs) {
-            const float2 t = cs_tab[wave][d0 / 2 + e];
+            const float2 t = cs_tab[wave % kCS][d0 / 2 + e];
             const float x0 = bf16_lo(w[e]), x1 = bf16_hi(w[e]);
             w[e] = pack_bf16x2(x0 * t.x - x1 * t.y, x0 * t.y + x1 * t.x);
           }
@@ -442,14 +444,16 @@ hipError_t launch_dk_dv_g(const DecodeArgs& a, int ncb, hipStream_t st) {
   return launch_ring<DK, DV, false, NCG>(a, pl, ncb, st);
 }
 
-// Column groups per workgroup: two when a verify call has more (token, head)
-// pairs per KV head than one 16-column group holds (each cache row is then
-// read once for both), one otherwise.
+// Column groups per workgroup: up to four when a verify call has more (token,
+// head) pairs per KV head than one 16-column group holds (each cache row is
+// then read once for all of them), one otherwise.
 template <int DK, int DV>
 hipError_t launch_dk_dv(const DecodeArgs& a, hipStream_t st) {
   const int G = a.Hq / a.Hkv;
   const int ncb = decode_column_blocks(a.n_q, G);
-  if (decode_groups_per_block(a.n_q, G) == 2) return launch_dk_dv_g<DK, DV, 2>(a, ncb, st);
+  const int ngw = decode_groups_per_block(a.n_q, G);
+  if (ngw == 4) return launch_dk_dv_g<DK, DV, 4>(a, ncb, st);
+  if (ngw == 2) return launch_dk_dv_g<DK, DV, 2>(a, ncb, st);
   return launch_dk_dv_g<DK, DV, 1>(a, ncb, st);
 }
 

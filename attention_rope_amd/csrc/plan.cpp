@@ -29,10 +29,14 @@ SplitPlan decode_plan(int B, int groups, int max_kv_len, int window, int n_q) {
 // 16-column groups of (token, head) pairs per KV head.
 int decode_column_groups(int n_q, int G) { return (n_q * G + 15) / 16; }
 
-// Column groups one decode workgroup serves from the same cache rows: two
-// when there are several (a verify call with more than 16 (token, head)
-// pairs per KV head), else one.
-int decode_groups_per_block(int n_q, int G) { return decode_column_groups(n_q, G) >= 2 ? 2 : 1; }
+// Column groups one decode workgroup serves from the same cache rows (one set
+// of waves each): 1, 2 or 4 (a verify call with more than 16 (token, head)
+// pairs per KV head; 3 groups take 4 with one idle set rather than a second
+// pass over the rows).
+int decode_groups_per_block(int n_q, int G) {
+  const int n = decode_column_groups(n_q, G);
+  return n >= 3 ? 4 : n;
+}
 
 // Workgroups per (sequence, chunk, KV head).
 int decode_column_blocks(int n_q, int G) {

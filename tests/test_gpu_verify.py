@@ -48,11 +48,12 @@ def test_verify_global_two_tokens(gpu_lib):
     run(gpu_lib, 2, 32, 4, 512, 256, 0, 128, 1e6, LENS)
 
 
-@pytest.mark.parametrize("n_q", [3, 4, 5])
+@pytest.mark.parametrize("n_q", [3, 4, 5, 6, 8, 12])
 def test_verify_global_column_groups(gpu_lib, n_q):
-    """24, 32 and 40 (token, head) pairs per KV head: two or three 16-column
-    groups, which one workgroup serves two at a time from the same cache rows
-    (with 5 tokens the second workgroup's second group is empty)."""
+    """24 to 96 (token, head) pairs per KV head: 2 to 6 16-column groups,
+    which one workgroup serves up to four at a time from the same cache rows
+    (3 groups take a 4-group workgroup with one idle set of waves; 6 take two
+    workgroups, the second half idle)."""
     run(gpu_lib, n_q, 32, 4, 512, 256, 0, 128, 1e6, LENS)
 
 
@@ -63,9 +64,11 @@ def test_verify_local_two_column_groups(gpu_lib, W):
     run(gpu_lib, 9, 16, 8, 256, 256, W, 256, 1e4, LENS)
 
 
-def test_verify_global_four_tokens_keys_as_values(gpu_lib):
-    """32 (token, head) pairs per KV head: two column groups; K = V."""
-    run(gpu_lib, 4, 32, 4, 512, 512, 0, 128, 1e6, LENS, shared=True)
+@pytest.mark.parametrize("n_q", [4, 8])
+def test_verify_global_tokens_keys_as_values(gpu_lib, n_q):
+    """32 and 64 (token, head) pairs per KV head: two and four column groups
+    in one workgroup; K = V (one 512-wide cache)."""
+    run(gpu_lib, n_q, 32, 4, 512, 512, 0, 128, 1e6, LENS, shared=True)
 
 
 @pytest.mark.parametrize("W", [1024, 5, 1])
