@@ -249,9 +249,9 @@ attn_status_t attn_decode_noalloc(const void *q, const void *k_cache, const void
  *   the supported shapes as for attn_decode; n_q in [1, 4096].
  *   kv_len[b] == 0 gives o[b] = 0; 0 < kv_len[b] < n_q (tokens without
  *   their rows) or kv_len[b] > max_kv_len poison o[b] with NaN.
- *   n_q * (Hq / Hkv) <= 32 reads each cache row once per KV head (pairs
- *   in groups of 16, two groups per workgroup); more (token, head) pairs
- *   re-read it once per 32.
+ *   n_q * (Hq / Hkv) <= 64 reads each cache row once per KV head (pairs
+ *   in groups of 16, up to four groups per workgroup); more (token, head)
+ *   pairs re-read it once per 64.
  * Workspace: attn_verify_workspace_bytes() bytes (the turned queries and the
  *   split-K partials); contents are scratch.
  */
