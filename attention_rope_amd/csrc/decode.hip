@@ -419,7 +419,7 @@ hipError_t launch_merge_dv(const DecodeArgs& a, const SplitPlan& pl, hipStream_t
   return hipGetLastError();
 }
 
-template <int DK, int DV, bool SHARED, int NCG>
+template <int DK, int DV, bool SHARED, int NGW>
 hipError_t launch_ring(const DecodeArgs& a, const SplitPlan& pl, int ncb, hipStream_t st) {
   using C = RingCfg<DK, DV, SHARED>;
   // Chunk-relative 32-bit buffer offsets: ch rows plus the read-ahead tiles.
@@ -427,21 +427,21 @@ hipError_t launch_ring(const DecodeArgs& a, const SplitPlan& pl, int ncb, hipStr
   static_assert((C::STAGES + 1) * C::RBN <= 192, "read-ahead bound of decode_shape_fits");
   if (((int64_t)pl.ch + (C::STAGES + 1) * C::RBN) * row >= ((int64_t)1 << 31))
     return hipErrorInvalidValue;
-  hipLaunchKernelGGL((decode_ring_kernel<C, DK, DV, NCG>), dim3(a.Hkv * ncb, pl.ns, a.B),
-                     dim3(C::RW * NCG * 64), 0, st, a, pl.ch, pl.ns);
+  hipLaunchKernelGGL((decode_ring_kernel<C, DK, DV, NGW>), dim3(a.Hkv * ncb, pl.ns, a.B),
+                     dim3(C::RW * NGW * 64), 0, st, a, pl.ch, pl.ns);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || pl.ns == 1) return e;  // one chunk: the ring kernel wrote o
   return launch_merge_dv<DV>(a, pl, st);
 }
 
-template <int DK, int DV, int NCG>
+template <int DK, int DV, int NGW>
 hipError_t launch_dk_dv_g(const DecodeArgs& a, int ncb, hipStream_t st) {
   const SplitPlan pl = decode_plan(a.B, a.Hkv * ncb, a.max_kv_len, a.window, a.n_q);
   if (pl.ns > 65535) return hipErrorInvalidValue;
   if constexpr (DK == DV) {
-    if (a.k_cache == a.v_cache) return launch_ring<DK, DV, true, NCG>(a, pl, ncb, st);
+    if (a.k_cache == a.v_cache) return launch_ring<DK, DV, true, NGW>(a, pl, ncb, st);
   }
-  return launch_ring<DK, DV, false, NCG>(a, pl, ncb, st);
+  return launch_ring<DK, DV, false, NGW>(a, pl, ncb, st);
 }
 
 // Column groups per workgroup: up to four when a verify call has more (token,
