@@ -57,11 +57,12 @@ def test_verify_global_column_groups(gpu_lib, n_q):
     run(gpu_lib, n_q, 32, 4, 512, 256, 0, 128, 1e6, LENS)
 
 
-@pytest.mark.parametrize("W", [1024, 5])
-def test_verify_local_two_column_groups(gpu_lib, W):
-    """9 tokens x 2 heads: 18 pairs per KV head, two groups in one workgroup,
-    each token with its own window start."""
-    run(gpu_lib, 9, 16, 8, 256, 256, W, 256, 1e4, LENS)
+@pytest.mark.parametrize("n_q,W", [(9, 1024), (9, 5), (32, 1024), (27, 40)])
+def test_verify_local_column_groups(gpu_lib, n_q, W):
+    """9 tokens x 2 heads: 18 pairs per KV head, two groups in one workgroup;
+    32 and 27 tokens: four groups (the last partly empty), each token with
+    its own window start."""
+    run(gpu_lib, n_q, 16, 8, 256, 256, W, 256, 1e4, LENS)
 
 
 @pytest.mark.parametrize("n_q", [4, 8])
