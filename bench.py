@@ -155,11 +155,18 @@ def prefill_ws(ar, torch, cases):
     return torch.empty(max(n, 256), dtype=torch.uint8, device="cuda")
 
 
-def bench_prefill(ar, torch, inputs, cfg, warmup, iters=None):
+def bench_prefill(ar, torch, inputs, cfg, warmup, iters=None, graph_burst=0):
     """The attn_prefill call (K rotation pre-pass, flash kernel) and,
     separately, the flash kernel alone: a call with Q-only rotation launches
     the same kernel instantiation with the same DMA volume (K's rotary dims
-    then come from k itself) and nothing else."""
+    then come from k itself) and nothing else.
+
+    graph_burst > 0: the kernel alone is timed as replays of a captured graph
+    of that many kernel-only calls (replay time / graph_burst). A kernel of a
+    few tens of microseconds is shorter than one call's host-side cost, so
+    events around single calls would time the host, not the kernel; in a
+    graph the launches run back to back. The replay's output is checked
+    against an eager call's."""
     c = cfg["case"]
     q, k, v = inputs.prefill_inputs(c, cfg["seed"], device="cuda")
     o = torch.empty((c.B, c.T, c.Hq, c.Dv), dtype=c.dtype, device="cuda")
@@ -175,12 +182,37 @@ def bench_prefill(ar, torch, inputs, cfg, warmup, iters=None):
     ev, wall = timed(torch, call, n, warmup, 2)
     call_ms = ev.series(0, 1)
     kernel_only = lambda e, i: call(e, i, ar.ROPE_Q)
-    evk, _ = timed(torch, kernel_only, n, 3, 2)
-    kern_ms = evk.series(0, 1)
+    timing = "HIP events around each kernel-only call"
+    if graph_burst:
+        kernel_only(None, 0)
+        torch.cuda.synchronize()
+        eager = o.clone()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(graph_burst):
+                kernel_only(None, 0)
+
+        def replay(e, i):
+            if e: e.mark(i, 0)
+            g.replay()
+            if e: e.mark(i, 1)
+
+        o.zero_()
+        evk, _ = timed(torch, replay, max(10, n // graph_burst), 3, 2)
+        kern_ms = [x / graph_burst for x in evk.series(0, 1)]
+        same = bool(torch.equal(o, eager))
+        del g, eager
+        timing = (f"HIP events around replays of a captured graph of {graph_burst} "
+                  f"kernel-only calls, / {graph_burst}; replay output equal to an eager "
+                  f"call's: {same}")
+    else:
+        evk, _ = timed(torch, kernel_only, n, 3, 2)
+        kern_ms = evk.series(0, 1)
     call(None, 0)  # leave o holding the full result
     torch.cuda.synchronize()
     return dict(flops=prefill_flops(c), bytes=prefill_bytes(c), call=stats(call_ms),
-                kern=stats(kern_ms), iters=n, wall_s=wall, tensors=(q, k, v, o))
+                kern=stats(kern_ms), iters=n, wall_s=wall, tensors=(q, k, v, o),
+                kern_timing=timing)
 
 
 def bench_prefill_kv_shared(ar, torch, inputs, cfg, warmup):
@@ -488,7 +520,8 @@ def secondary_prefill(ar, torch, inputs, name, sc, oracle=None):
     peak = PEAK_FP32_TFLOPS if fp32 else PEAK_BF16_TFLOPS
     warm = 200 if name == "local_prefill" else (3 if name == "global_prefill" else 50)
     rr = bench_prefill(ar, torch, inputs, sc, warm,
-                       iters=10 if name == "global_prefill" else None)
+                       iters=10 if name == "global_prefill" else None,
+                       graph_burst=20 if fp32 else 0)
     c = sc["case"]
     kname = ("prefill_general" if fp32 else "prefill_mfma2g" if c.window and c.Hq // c.Hkv == 2
              else "prefill_mfma1w" if c.Dk == 512 else "prefill_mfma")
@@ -501,6 +534,7 @@ def secondary_prefill(ar, torch, inputs, name, sc, oracle=None):
                                      _traffic(kname, name)),
                             kernel=kname + "_kernel",
                             kernel_ms=round(rr["kern"]["median"], 5),
+                            kernel_timing=rr["kern_timing"],
                             flops_per_launch=rr["flops"])}
     if not fp32:
         rec["roofline"]["hbm_frac_at_algorithmic_bytes"] = round(
