@@ -82,6 +82,13 @@ GENERAL_CASES = [
     (1, 90, 4, 1, 384, 192, 0, 96, 1e6, BF),
     (1, 1500, 4, 2, 64, 64, 0, 32, 1e4, F32),
     (2, 1200, 2, 1, 128, 64, 700, 128, 1e4, F32),
+    # query heads per workgroup (4, 2 or 1 of a KV head's heads) against dim
+    # pairs per lane: 4 heads x 2 pairs (windowed), 2 x 4, 2 x 3 with 6 heads
+    # per KV head, 4 heads over long windowed bf16 rows
+    (1, 150, 8, 2, 256, 192, 40, 64, 1e4, F32),
+    (1, 77, 4, 2, 512, 512, 0, 128, 1e6, F32),
+    (2, 60, 12, 2, 320, 160, 0, 80, 1e6, F32),
+    (1, 700, 16, 2, 128, 128, 300, 32, 1e6, BF),
 ]
 
 
